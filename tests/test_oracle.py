@@ -1,0 +1,455 @@
+"""Pins for the fp64 oracle: it is checked against things other than itself.
+
+* worked examples derived in closed form (tests/golden/worked_examples.json),
+* a brute-force loop that walks the block table token by token,
+* torch's own scaled_dot_product_attention on an identity block table,
+* invariances the pages state: scattered placement and shared blocks do not
+  change the result,
+* closed forms (one key, equal keys, zero query, constant values, GQA head
+  mapping), and
+* planted mistakes in the oracle that at least one pin must catch.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import paged as opa
+from workloads import build_workload
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
+NAN = float("nan")
+
+
+def _load_golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+def _nanify(x):
+    return np.array(json.loads(json.dumps(x).replace("null", "NaN")), dtype=np.float64)
+
+
+def contiguous_to_pool(K, V, bs):
+    """Contiguous per-kv-head K/V ``[Hkv, n, D]`` -> pools with an identity table.
+
+    The pool formats are the storage contract: K ``[NB, Hkv, bs, D]``, V
+    ``[NB, Hkv, D, bs]``; tail slots are NaN.
+    """
+    Hkv, n, D = K.shape
+    NB = max(1, (n + bs - 1) // bs)
+    Kp = np.full((Hkv, NB * bs, D), NAN, np.float32)
+    Vp = np.full((Hkv, NB * bs, D), NAN, np.float32)
+    Kp[:, :n] = K
+    Vp[:, :n] = V
+    k_pool = Kp.reshape(Hkv, NB, bs, D).transpose(1, 0, 2, 3).copy()
+    v_pool = Vp.reshape(Hkv, NB, bs, D).transpose(1, 0, 3, 2).copy()
+    table = np.arange(NB, dtype=np.int32)[None, :]
+    return k_pool, v_pool, table
+
+
+def run_dense_case(Q, K, V, scale, bs=16, mods=None):
+    """Oracle on one sequence given contiguous Q ``[Lq,Hq,D]`` and K/V ``[Hkv,n,D]``."""
+    k_pool, v_pool, table = contiguous_to_pool(K, V, bs)
+    n = K.shape[1]
+    Lq = Q.shape[0]
+    return oracle.paged_attention(Q.astype(np.float32), k_pool, v_pool, table, [n], [0, Lq],
+                                  np.float32(scale), bs, "f32", mods)
+
+
+# --------------------------------------------------------------------------------------
+# worked examples
+# --------------------------------------------------------------------------------------
+
+def check_golden():
+    g = _load_golden()
+    for name in ["two_token_logistic", "softcap_two_token", "alibi_three_keys", "sliding_window"]:
+        c = g[name]
+        K = np.array(c["K"], np.float32)[None]
+        V = np.array(c["V"], np.float32)[None]
+        q = np.array(c["q"], np.float32)[None, None]
+        mods = oracle.ScoreMods(window=c.get("window", 0), softcap=c.get("softcap", 0.0),
+                                alibi_slopes=np.array([c["alibi_slope"]]) if "alibi_slope" in c else None)
+        out = run_dense_case(q, K, V, c["scale"], c["bs"], mods)
+        np.testing.assert_allclose(out[0, 0], c["expected"], rtol=0, atol=1e-12, err_msg=name)
+    c = g["causal_chunk_bottom_right"]
+    out = run_dense_case(np.array(c["Q"], np.float32)[:, None], np.array(c["K"], np.float32)[None],
+                         np.array(c["V"], np.float32)[None], c["scale"], c["bs"],
+                         oracle.ScoreMods(causal=True))
+    np.testing.assert_allclose(out[:, 0], c["expected"], rtol=0, atol=1e-12)
+    c = g["paged_scattered_blocks"]
+    k_pool = _nanify(c["k_pool"]).astype(np.float32)
+    v_pool = _nanify(c["v_pool"]).astype(np.float32)
+    out = oracle.paged_attention(np.array(c["q"], np.float32)[None, None], k_pool, v_pool,
+                                 np.array([c["table"]], np.int32), [c["n"]], [0, 1],
+                                 np.float32(c["scale"]), c["bs"], "f32")
+    np.testing.assert_allclose(out[0, 0], c["expected"], rtol=0, atol=1e-12)
+    c = g["kv_append_bs4"]
+    shape_k = (c["NB"], c["Hkv"], c["bs"], c["D"])
+    shape_v = (c["NB"], c["Hkv"], c["D"], c["bs"])
+    kp, vp = oracle.kv_append(np.zeros(shape_k, np.float32), np.zeros(shape_v, np.float32),
+                              np.array(c["k_new"], np.float32), np.array(c["v_new"], np.float32),
+                              np.array(c["slot_mapping"], np.int32), c["bs"])
+    np.testing.assert_array_equal(kp, np.array(c["expected_k_pool"], np.float32))
+    np.testing.assert_array_equal(vp, np.array(c["expected_v_pool"], np.float32))
+
+
+def test_golden_worked_examples():
+    check_golden()
+
+
+# --------------------------------------------------------------------------------------
+# brute force: walk the block table token by token in plain Python
+# --------------------------------------------------------------------------------------
+
+def brute_force(w, mods):
+    """Two-pass softmax with math.exp, reading each key through its table entry."""
+    q = opa.bits_to_f64(w.q, w.dtype)
+    kp = opa.bits_to_f64(w.k_pool, w.dtype)
+    vp = opa.bits_to_f64(w.v_pool, w.dtype)
+    g = w.Hq // w.Hkv
+    out = np.zeros(q.shape)
+    for b in range(w.B):
+        n = int(w.context_lens[b])
+        r0, r1 = int(w.cu_q_lens[b]), int(w.cu_q_lens[b + 1])
+        for r in range(r0, r1):
+            pos = n - (r1 - r0) + (r - r0)
+            for h in range(w.Hq):
+                c = h // g
+                scores = []
+                for j in range(n):
+                    if mods.causal and j > pos:
+                        continue
+                    if mods.window and pos - j >= mods.window:
+                        continue
+                    blk = int(w.block_table[b][j // w.bs])
+                    off = j % w.bs
+                    s = 0.0
+                    for d in range(w.D):
+                        s += q[r, h, d] * kp[blk, c, off, d]
+                    s *= float(w.scale)
+                    if mods.softcap:
+                        s = mods.softcap * math.tanh(s / mods.softcap)
+                    if mods.alibi_slopes is not None:
+                        s += float(mods.alibi_slopes[h]) * (j - pos)
+                    scores.append((j, blk, off, s))
+                if not scores:
+                    continue
+                m = max(s for _, _, _, s in scores)
+                den = sum(math.exp(s - m) for _, _, _, s in scores)
+                for d in range(w.D):
+                    acc = 0.0
+                    for _, blk, off, s in scores:
+                        acc += math.exp(s - m) * vp[blk, c, d, off]
+                    out[r, h, d] = acc / den
+    return out
+
+
+def _tiny(kind, seed, bs=4, dtype="f32", ctx=(13, 40), q_lens=None, Hq=4, Hkv=2, D=8, causal=False):
+    return build_workload(name="tiny", seed=seed, kind=kind, dtype=dtype, Hq=Hq, Hkv=Hkv, D=D, bs=bs,
+                          context_lens=list(ctx), q_lens=q_lens, causal=causal, threads=1)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("kind", ["decode", "prefill"])
+def test_brute_force_loops(kind, dtype):
+    w = _tiny(kind, 11, dtype=dtype, q_lens=None if kind == "decode" else [5, 7], causal=kind == "prefill")
+    mods = oracle.ScoreMods(causal=w.causal)
+    got = oracle.paged_attention(w.q, w.k_pool, w.v_pool, w.block_table, w.context_lens, w.cu_q_lens,
+                                 w.scale, w.bs, w.dtype, mods)
+    np.testing.assert_allclose(got, brute_force(w, mods), rtol=0, atol=1e-12)
+
+
+def test_brute_force_with_mods():
+    w = _tiny("prefill", 12, ctx=(9, 33), q_lens=[4, 6], causal=True)
+    mods = oracle.ScoreMods(causal=True, window=5, softcap=0.7,
+                            alibi_slopes=np.array([0.5, 0.25, 0.125, 0.0625]))
+    got = oracle.paged_attention(w.q, w.k_pool, w.v_pool, w.block_table, w.context_lens, w.cu_q_lens,
+                                 w.scale, w.bs, w.dtype, mods)
+    np.testing.assert_allclose(got, brute_force(w, mods), rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------------------
+# library special case: identity table == torch SDPA (fp64, CPU)
+# --------------------------------------------------------------------------------------
+
+def check_sdpa(n=37, Lq=9, Hq=8, Hkv=2, D=16, bs=16, alibi=False, seed=3):
+    rng = np.random.default_rng(seed)
+    Q = rng.standard_normal((Lq, Hq, D)).astype(np.float32)
+    K = rng.standard_normal((Hkv, n, D)).astype(np.float32)
+    V = rng.standard_normal((Hkv, n, D)).astype(np.float32)
+    scale = np.float32(1 / math.sqrt(D))
+    slopes = 2.0 ** -np.arange(1, Hq + 1) if alibi else None
+    got = run_dense_case(Q, K, V, scale, bs, oracle.ScoreMods(causal=True, alibi_slopes=slopes))
+    qt = torch.from_numpy(Q.astype(np.float64)).permute(1, 0, 2)[None]  # [1, Hq, Lq, D]
+    kt = torch.from_numpy(K.astype(np.float64))[None]
+    vt = torch.from_numpy(V.astype(np.float64))[None]
+    pos = torch.arange(n - Lq, n)[:, None]
+    kv = torch.arange(n)[None, :]
+    allowed = kv <= pos
+    if alibi:
+        bias = torch.from_numpy(slopes)[:, None, None] * (kv - pos).to(torch.float64)[None]
+        mask = torch.where(allowed[None], bias, torch.tensor(-math.inf, dtype=torch.float64))[None]
+    else:
+        mask = allowed
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask,
+                                                           scale=float(scale), enable_gqa=True)
+    ref = ref[0].permute(1, 0, 2).numpy()
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_identity_table_matches_torch_sdpa():
+    check_sdpa()
+    check_sdpa(n=1, Lq=1, Hq=4, Hkv=4, D=8, bs=16)
+    check_sdpa(n=64, Lq=1, Hq=8, Hkv=1, D=32, bs=32)
+
+
+def test_alibi_matches_torch_sdpa_bias():
+    check_sdpa(alibi=True)
+
+
+# --------------------------------------------------------------------------------------
+# invariances stated on the pages
+# --------------------------------------------------------------------------------------
+
+def _run(w, mods=None, **over):
+    a = dict(q=w.q, k_pool=w.k_pool, v_pool=w.v_pool, block_table=w.block_table,
+             context_lens=w.context_lens, cu_q_lens=w.cu_q_lens, scale=w.scale, bs=w.bs, dtype=w.dtype)
+    a.update(over)
+    return oracle.paged_attention(mods=mods or oracle.ScoreMods(causal=w.causal), **a)
+
+
+def check_permutation_invariance(dtype="bf16"):
+    w = _tiny("prefill", 21, bs=16, dtype=dtype, ctx=(50, 100), q_lens=[3, 17], causal=True)
+    base = _run(w)
+    perm = np.random.default_rng(5).permutation(w.NB)
+    kp = np.empty_like(w.k_pool)
+    vp = np.empty_like(w.v_pool)
+    kp[perm] = w.k_pool
+    vp[perm] = w.v_pool
+    table = np.where(w.block_table >= 0, perm[np.maximum(w.block_table, 0)], -1).astype(np.int32)
+    got = _run(w, k_pool=kp, v_pool=vp, block_table=table)
+    assert np.array_equal(got, base)
+
+
+def test_block_permutation_invariance():
+    check_permutation_invariance("bf16")
+    check_permutation_invariance("f32")
+
+
+def test_shared_prefix_equals_private_copies():
+    w = build_workload(name="shared", seed=4, kind="decode", dtype="bf16", Hq=8, Hkv=2, D=32, bs=16,
+                       context_lens=[80, 80, 80], shared_prefix_blocks=3, threads=1)
+    base = _run(w)
+    # give every sequence private copies of the shared blocks
+    S = 3
+    extra = w.B * S
+    kp = np.concatenate([w.k_pool, np.zeros((extra,) + w.k_pool.shape[1:], w.k_pool.dtype)])
+    vp = np.concatenate([w.v_pool, np.zeros((extra,) + w.v_pool.shape[1:], w.v_pool.dtype)])
+    table = w.block_table.copy()
+    nxt = w.NB
+    for b in range(w.B):
+        for j in range(S):
+            kp[nxt] = w.k_pool[w.block_table[b, j]]
+            vp[nxt] = w.v_pool[w.block_table[b, j]]
+            table[b, j] = nxt
+            nxt += 1
+    assert len({tuple(r[:S]) for r in table}) == w.B
+    assert np.array_equal(_run(w, k_pool=kp, v_pool=vp, block_table=table), base)
+
+
+# --------------------------------------------------------------------------------------
+# closed forms
+# --------------------------------------------------------------------------------------
+
+def test_one_token_context_returns_v_row():
+    w = _tiny("decode", 31, bs=16, dtype="bf16", ctx=(1, 1))
+    got = _run(w)
+    for b in range(w.B):
+        pb = w.block_table[b, 0]
+        v = opa.bits_to_f64(w.v_pool[pb, :, :, 0], "bf16")  # [Hkv, D]
+        assert np.array_equal(got[b], np.repeat(v, w.Hq // w.Hkv, axis=0))
+
+
+def test_equal_tokens_and_zero_query_and_constant_v():
+    rng = np.random.default_rng(9)
+    n, D, Hq, Hkv = 29, 8, 4, 2
+    k = rng.standard_normal(D).astype(np.float32)
+    v = rng.standard_normal(D).astype(np.float32)
+    Q = rng.standard_normal((1, Hq, D)).astype(np.float32)
+    K = np.broadcast_to(k, (Hkv, n, D)).copy()
+    V = np.broadcast_to(v, (Hkv, n, D)).copy()
+    out = run_dense_case(Q, K, V, 0.3)
+    np.testing.assert_allclose(out[0], np.broadcast_to(v, (Hq, D)), rtol=0, atol=1e-12)
+    # zero query (or zero scale): plain mean of the value rows
+    K = rng.standard_normal((Hkv, n, D)).astype(np.float32)
+    V = rng.standard_normal((Hkv, n, D)).astype(np.float32)
+    out = run_dense_case(np.zeros((1, Hq, D), np.float32), K, V, 0.3)
+    mean = V.astype(np.float64).mean(axis=1)
+    np.testing.assert_allclose(out[0], np.repeat(mean, Hq // Hkv, axis=0), rtol=0, atol=1e-12)
+    out = run_dense_case(Q, K, V, 0.0)
+    np.testing.assert_allclose(out[0], np.repeat(mean, Hq // Hkv, axis=0), rtol=0, atol=1e-12)
+    # constant value rows: that constant whatever the scores
+    V = np.full((Hkv, n, D), 0.75, np.float32)
+    out = run_dense_case(Q, K, V, 5.0)
+    np.testing.assert_allclose(out, 0.75, rtol=0, atol=1e-12)
+
+
+def test_gqa_head_mapping_consecutive_groups():
+    rng = np.random.default_rng(2)
+    n, D, Hq, Hkv = 20, 4, 8, 2
+    K = rng.standard_normal((Hkv, n, D)).astype(np.float32)
+    V = np.stack([np.full((n, D), c + 1.0, np.float32) for c in range(Hkv)])
+    out = run_dense_case(rng.standard_normal((1, Hq, D)).astype(np.float32), K, V, 0.5)
+    for h in range(Hq):
+        np.testing.assert_allclose(out[0, h], h // (Hq // Hkv) + 1.0, rtol=0, atol=1e-12)
+
+
+def test_chunk_rows_equal_truncated_decode():
+    w = _tiny("prefill", 41, bs=16, ctx=(70,), q_lens=[9], causal=True)
+    chunk = _run(w)
+    n = int(w.context_lens[0])
+    for i in range(9):
+        pos = n - 9 + i
+        dec = _run(w, q=w.q[i:i + 1], context_lens=np.array([pos + 1], np.int32), cu_q_lens=np.array([0, 1]),
+                   mods=oracle.ScoreMods())
+        np.testing.assert_allclose(chunk[i], dec[0], rtol=0, atol=1e-12)
+
+
+def test_window_equals_truncated_context():
+    rng = np.random.default_rng(8)
+    n, D, W = 50, 8, 7
+    Q = rng.standard_normal((1, 2, D)).astype(np.float32)
+    K = rng.standard_normal((2, n, D)).astype(np.float32)
+    V = rng.standard_normal((2, n, D)).astype(np.float32)
+    win = run_dense_case(Q, K, V, 0.4, mods=oracle.ScoreMods(window=W))
+    ref = run_dense_case(Q, K[:, n - W:], V[:, n - W:], 0.4)
+    np.testing.assert_allclose(win, ref, rtol=0, atol=1e-12)
+
+
+def test_large_softcap_is_identity():
+    rng = np.random.default_rng(6)
+    Q = rng.standard_normal((1, 2, 8)).astype(np.float32)
+    K = rng.standard_normal((2, 30, 8)).astype(np.float32)
+    V = rng.standard_normal((2, 30, 8)).astype(np.float32)
+    a = run_dense_case(Q, K, V, 0.3, mods=oracle.ScoreMods(softcap=1e7))
+    b = run_dense_case(Q, K, V, 0.3)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-9)
+
+
+def test_empty_context_outputs_zero():
+    w = _tiny("decode", 51, bs=16, ctx=(0, 5))
+    out = _run(w)
+    assert np.all(out[0] == 0.0) and np.all(np.isfinite(out[1]))
+
+
+def test_poisoned_slots_never_read():
+    for kind in ["decode", "prefill"]:
+        w = _tiny(kind, 61, bs=16, ctx=(33, 47), q_lens=None if kind == "decode" else [4, 4],
+                  causal=kind == "prefill")
+        assert np.isnan(opa.bits_to_f64(w.k_pool, "f32")).any()
+        assert np.all(np.isfinite(_run(w)))
+
+
+# --------------------------------------------------------------------------------------
+# kv_append
+# --------------------------------------------------------------------------------------
+
+def test_kv_append_roundtrip_through_block_table():
+    w = build_workload(name="app", seed=7, kind="decode", dtype="bf16", Hq=4, Hkv=2, D=16, bs=16,
+                       context_lens=[40, 17], append_lens=[20, 17], threads=1)
+    kp, vp = oracle.kv_append(w.k_pool, w.v_pool, w.k_new, w.v_new, w.slot_mapping, w.bs)
+    t = 0
+    for b in range(w.B):
+        n = int(w.context_lens[b])
+        K, V = oracle.gather_sequence(kp, vp, w.block_table[b], n, w.bs)
+        for p in range(n - 20 if b == 0 else 0, n):
+            assert np.array_equal(K[:, p], w.k_new[t]) and np.array_equal(V[:, p], w.v_new[t])
+            t += 1
+        K0, _ = oracle.gather_sequence(w.k_pool, w.v_pool, w.block_table[b], n, w.bs)
+        keep = n - (20 if b == 0 else 17)
+        assert np.array_equal(K[:, :keep], K0[:, :keep])
+    changed = np.nonzero((kp != w.k_pool).any(axis=(1, 2, 3)))[0]
+    assert set(changed.tolist()) <= set(w.block_table[w.block_table >= 0].tolist())
+
+
+def test_kv_append_rejects_duplicates_and_skips_negative():
+    z = np.zeros((2, 1, 4, 2), np.float32)
+    zv = np.zeros((2, 1, 2, 4), np.float32)
+    new = np.ones((2, 1, 2), np.float32)
+    with pytest.raises(ValueError):
+        oracle.kv_append(z, zv, new, new, np.array([3, 3]), 4)
+    kp, vp = oracle.kv_append(z, zv, new, new, np.array([-1, -7]), 4)
+    assert not kp.any() and not vp.any()
+
+
+# --------------------------------------------------------------------------------------
+# planted mistakes: each must make at least one pin fail
+# --------------------------------------------------------------------------------------
+
+def _all_pins():
+    check_golden()
+    check_sdpa()
+    check_permutation_invariance("f32")
+    test_gqa_head_mapping_consecutive_groups()
+    test_chunk_rows_equal_truncated_decode()
+    w = _tiny("prefill", 11, q_lens=[5, 7], causal=True)
+    mods = oracle.ScoreMods(causal=True)
+    np.testing.assert_allclose(_run(w, mods), brute_force(w, mods), rtol=0, atol=1e-12)
+
+
+def _mutant_gather_v_not_transposed(k_pool, v_pool, table_row, n, bs):
+    nb = (n + bs - 1) // bs
+    phys = np.asarray(table_row[:nb], dtype=np.int64)
+    Hkv, D = k_pool.shape[1], k_pool.shape[3]
+    K = k_pool[phys].transpose(1, 0, 2, 3).reshape(Hkv, nb * bs, D)[:, :n]
+    V = v_pool[phys].transpose(1, 0, 2, 3).reshape(Hkv, nb * bs, D)[:, :n]  # wrong: V slab is [D, bs]
+    return K, V
+
+
+def _mutant_gather_ignores_table(k_pool, v_pool, table_row, n, bs):
+    return opa.__dict__["_orig_gather"](k_pool, v_pool, np.arange(len(table_row)), n, bs)
+
+
+def _make_attention_mutant(kind):
+    orig = opa.__dict__["_orig_attention"]
+
+    def mutant(Q, K, V, scale, q_pos, mods=None):
+        mods = mods or oracle.ScoreMods()
+        if kind == "no_scale":
+            return orig(Q, K, V, 1.0, q_pos, mods)
+        if kind == "top_left_causal":
+            return orig(Q, K, V, scale, np.arange(len(q_pos)), mods)
+        if kind == "gqa_modulo":
+            Hq, Hkv = Q.shape[1], K.shape[0]
+            idx = np.arange(Hq) % Hkv  # wrong grouping
+            Kx = K[idx]
+            Vx = V[idx]
+            return orig(Q, Kx, Vx, scale, q_pos, mods)
+        if kind == "no_max_sub_sign":
+            return orig(Q, K, V, -scale, q_pos, mods)
+        raise AssertionError(kind)
+
+    return mutant
+
+
+@pytest.mark.parametrize("mutant", ["v_layout", "ignore_table", "no_scale", "top_left_causal",
+                                    "gqa_modulo", "sign"])
+def test_planted_mistakes_are_caught(monkeypatch, mutant):
+    monkeypatch.setitem(opa.__dict__, "_orig_gather", opa.gather_sequence)
+    monkeypatch.setitem(opa.__dict__, "_orig_attention", opa.attention_dense)
+    if mutant == "v_layout":
+        monkeypatch.setattr(opa, "gather_sequence", _mutant_gather_v_not_transposed)
+    elif mutant == "ignore_table":
+        monkeypatch.setattr(opa, "gather_sequence", _mutant_gather_ignores_table)
+    else:
+        kind = {"no_scale": "no_scale", "top_left_causal": "top_left_causal",
+                "gqa_modulo": "gqa_modulo", "sign": "no_max_sub_sign"}[mutant]
+        monkeypatch.setattr(opa, "attention_dense", _make_attention_mutant(kind))
+    with pytest.raises(AssertionError):
+        _all_pins()
