@@ -1,0 +1,208 @@
+/*
+ * pagedattn.h -- C ABI of the MI355X (gfx950) paged KV-cache attention library.
+ *
+ * The method: the KV cache is cut into fixed-size blocks that sit anywhere in
+ * one shared pool; each sequence finds its blocks through a block table that
+ * maps logical positions to physical blocks, and the attention kernel reads
+ * the scattered blocks directly, with no contiguous copy ("Ultimate Guide to
+ * PagedAttention", newline: KV blocks, block table, non-contiguous storage;
+ * Kwon et al., "Efficient Memory Management for Large Language Model Serving
+ * with PagedAttention", abstract; Joshi et al., "Paged Attention Meets
+ * FlexAttention", abstract: a fused kernel that gathers the scattered KV
+ * data).  The result is exact softmax attention (Dao et al., "FlashAttention",
+ * abstract), optionally with FlexAttention-style mask/score modification.
+ *
+ * ---------------------------------------------------------------------------
+ * Storage (device memory, owned by the caller)
+ *
+ *   element type   PA_F32 (float) or PA_BF16 (bfloat16 bits); q, the pools,
+ *                  new tokens and outputs of one call share it.  Arithmetic
+ *                  accumulates in fp32.
+ *   k_cache        [num_blocks, num_kv_heads, block_size, head_dim]
+ *                  (token-major rows inside each (block, kv-head) slab)
+ *   v_cache        [num_blocks, num_kv_heads, head_dim, block_size]
+ *                  (dimension-major: each row holds block_size tokens)
+ *   block_tables   int32 [num_seqs, block_table_stride]; entry [b, j] is the
+ *                  physical block of logical tokens [j*bs, (j+1)*bs) of
+ *                  sequence b.  Only entries j < ceil(context_lens[b]/bs) are
+ *                  read.
+ *   context_lens   int32 [num_seqs]: keys of sequence b (including tokens
+ *                  appended for this step).  Key j sits at logical position j.
+ *   query row i of a sequence with n keys and L query rows sits at logical
+ *   position n - L + i (decode: L = 1, position n - 1).  Query head h reads
+ *   kv-head h / (num_heads / num_kv_heads).
+ *
+ * All calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ * stream).  No call allocates device or host memory, and none keeps state
+ * between calls except a per-process cache of the current device's compute-
+ * unit count.  Calls are thread-safe.
+ *
+ * Status: 0 = success.  A negative value is an invalid argument found on the
+ * host before anything is enqueued (no buffer is touched).  A positive value
+ * is the hipError_t of a failed launch.  paged_attn_status_string() names
+ * every code.
+ *
+ * Device contents are not validated (that would need a device->host sync):
+ * block ids must lie in [0, num_blocks), context_lens[b] must not exceed
+ * block_table_stride * block_size, a prefill sequence must have
+ * q_len <= context_len, and the slots of one kv_append must be distinct.
+ * Breaking these is undefined behaviour.
+ * ---------------------------------------------------------------------------
+ */
+#ifndef PAGEDATTN_H_
+#define PAGEDATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+enum {
+  PA_OK = 0,
+  PA_ERR_NULL = -1,          /* a required pointer is NULL                      */
+  PA_ERR_SIZE = -2,          /* a count is negative or exceeds the index range   */
+  PA_ERR_HEADS = -3,         /* heads <= 0, or num_heads % num_kv_heads != 0     */
+  PA_ERR_HEAD_DIM = -4,      /* head_dim not 64 or 128                          */
+  PA_ERR_BLOCK_SIZE = -5,    /* block_size not a power of two in [16, 256]      */
+  PA_ERR_SPLIT = -6,         /* split_tokens not 0, -1 or a power of two >= 16  */
+  PA_ERR_WORKSPACE = -7,     /* workspace NULL or smaller than required         */
+  PA_ERR_DTYPE = -8,         /* dtype not PA_F32 / PA_BF16                      */
+  PA_ERR_FLAG = -9,          /* causal not 0 or 1                               */
+  PA_ERR_MODS = -10,         /* window < 0, softcap < 0 or not finite           */
+  PA_ERR_TABLE_STRIDE = -11  /* block_table_stride < 1                          */
+};
+
+/*
+ * FlexAttention-style modifications on logical positions (Joshi et al.,
+ * "Paged Attention Meets FlexAttention", abstract: the paged kernel keeps
+ * FlexAttention's programmable masks and score mods).  With s = scale * q.k:
+ *   softcap > 0   : s = softcap * tanh(s / softcap)
+ *   alibi_slopes  : s = s + alibi_slopes[h] * (key_pos - query_pos)
+ *                   (device pointer to num_heads floats; NULL = none)
+ *   window > 0    : keys with query_pos - key_pos >= window are masked out
+ * Passing NULL for the struct means none of them.  The struct itself is read
+ * on the host during the call and may be freed on return.
+ */
+typedef struct {
+  int32_t window;
+  float softcap;
+  const float* alibi_slopes;
+} pa_score_mods;
+
+/*
+ * kv_append -- store the key/value vectors of new tokens in the paged cache.
+ *
+ * New tokens' vectors are written into the blocks a growing sequence owns;
+ * existing data never moves ("Ultimate Guide to PagedAttention": KV cache,
+ * dynamic growth).  For every t < num_tokens with s = slot_mapping[t] >= 0:
+ *   k_cache[s / bs][h][s % bs][:] = k_new[t][h][:]
+ *   v_cache[s / bs][h][:][s % bs] = v_new[t][h][:]     for every kv-head h.
+ * Tokens with a negative slot are skipped.  The copy is bit-exact (no
+ * conversion).  k_new / v_new: [num_tokens, num_kv_heads, head_dim].
+ * num_tokens == 0 is a no-op.
+ */
+int kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+              const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+              int32_t head_dim, int32_t block_size, int64_t num_blocks, int32_t dtype,
+              void* stream);
+
+/*
+ * Bytes of fp32 workspace paged_attn_decode needs for these sizes.  The
+ * split-KV partitioning (a long context cut into split_tokens-long pieces
+ * whose partial softmax states are merged afterwards) is this library's
+ * reading of how to spread one decode row over many compute units; the pages
+ * only motivate long contexts.  split_tokens: 0 = choose automatically from
+ * (num_seqs, num_kv_heads, max_context_len), -1 = never split, else a power
+ * of two >= 16.  Returns 0 for invalid arguments.
+ */
+size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_heads,
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t max_context_len, int32_t split_tokens);
+
+/* The split size paged_attn_decode will use (resolves split_tokens == 0). */
+int32_t paged_attn_decode_split_tokens(int32_t num_seqs, int32_t num_kv_heads,
+                                       int32_t max_context_len, int32_t split_tokens);
+
+/*
+ * paged_attn_decode -- one query row per sequence over its paged context.
+ *
+ *   out  [num_seqs, num_heads, head_dim]  (written)
+ *   q    [num_seqs, num_heads, head_dim]
+ *   out[b][h] = softmax_j(scale * q[b][h] . K_b[j] (+ mods)) V_b[j], j < context_lens[b]
+ *
+ * max_context_len is a host-side upper bound of context_lens that sizes the
+ * launch (no device->host sync); larger device values are undefined
+ * behaviour.  A sequence with context_len 0 gets a zero output.  The
+ * workspace (device memory of at least
+ * paged_attn_decode_workspace_size(...) bytes; may be NULL when that size is
+ * 0) holds per-partition partial results between the two kernels.
+ * Equivalent to paged_attn_decode_partials followed by
+ * paged_attn_decode_merge with the same arguments.
+ */
+int paged_attn_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, int32_t block_table_stride,
+                      const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                      int64_t num_blocks, int32_t max_context_len, float scale,
+                      int32_t split_tokens, const pa_score_mods* mods, void* workspace,
+                      size_t workspace_bytes, int32_t dtype, void* stream);
+
+/*
+ * The two phases of paged_attn_decode as separate calls (same arguments).
+ * _partials runs the partition kernel: sequences whose context fits one
+ * partition get their final output; the others leave unnormalised partial
+ * outputs with their running max and sum in the workspace.  _merge combines
+ * those partials (log-sum-exp weighting, fixed partition order) into out and
+ * launches nothing when no sequence can span more than one partition.
+ */
+int paged_attn_decode_partials(void* out, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_tables,
+                               int32_t block_table_stride, const int32_t* context_lens,
+                               int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                               int32_t max_context_len, float scale, int32_t split_tokens,
+                               const pa_score_mods* mods, void* workspace,
+                               size_t workspace_bytes, int32_t dtype, void* stream);
+
+int paged_attn_decode_merge(void* out, const int32_t* context_lens, int32_t num_seqs,
+                            int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t max_context_len, int32_t split_tokens,
+                            const pa_score_mods* mods, const void* workspace,
+                            size_t workspace_bytes, int32_t dtype, void* stream);
+
+/*
+ * paged_attn_prefill -- several query rows per sequence (prefill, or a
+ * chunk appended after an existing paged context) over the paged context.
+ *
+ *   q, out  [total_q, num_heads, head_dim]; sequence b owns rows
+ *           cu_q_lens[b] .. cu_q_lens[b+1]-1 (cu_q_lens: int32 [num_seqs+1],
+ *           device), its L = cu_q_lens[b+1]-cu_q_lens[b] rows sit at logical
+ *           positions context_lens[b]-L .. context_lens[b]-1.
+ *   causal  1: a row sees keys at positions <= its own; 0: all keys.
+ *   max_q_len: host-side upper bound of the per-sequence row counts.
+ *
+ * The chunk's own keys/values must already be in the cache (kv_append first),
+ * so a row always sees itself.  bf16 runs on matrix cores (bf16 products, fp32
+ * accumulation, softmax weights rounded to bf16 before the P.V product); fp32
+ * runs on vector ALUs in fp32.  Rows with no admissible key are zero.
+ */
+int paged_attn_prefill(void* out, const void* q, const int32_t* cu_q_lens, const void* k_cache,
+                       const void* v_cache, const int32_t* block_tables,
+                       int32_t block_table_stride, const int32_t* context_lens,
+                       int32_t num_seqs, int32_t max_q_len, int32_t num_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                       int64_t num_blocks, float scale, int32_t causal,
+                       const pa_score_mods* mods, int32_t dtype, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* paged_attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H_ */

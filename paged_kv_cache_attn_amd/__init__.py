@@ -1,0 +1,19 @@
+"""Paged KV-cache attention for AMD MI355X (gfx950).
+
+The compute lives in ``libpagedattn.so`` (hand-written HIP kernels, C ABI in
+``include/pagedattn.h``); this package only builds it and binds it.
+"""
+
+from .binding import (  # noqa: F401
+    PA_BF16,
+    PA_F32,
+    decode_split_tokens,
+    decode_workspace,
+    decode_workspace_size,
+    kv_append,
+    lib,
+    lib_path,
+    paged_attn_decode,
+    paged_attn_prefill,
+    status_string,
+)

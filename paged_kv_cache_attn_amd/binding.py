@@ -1,0 +1,222 @@
+"""Thin Python binding of ``libpagedattn.so`` (ctypes, same names as the C ABI).
+
+Marshalling only: tensors are checked for device, dtype, shape and
+contiguity, their device pointers and torch's current HIP stream are passed
+to the C entry points, and status codes become exceptions (negative codes
+-> ``ValueError``, positive hip errors -> ``RuntimeError``).  Every step of the
+computation runs in the library's gfx950 kernels; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
+
+PA_F32 = 0
+PA_BF16 = 1
+_DTYPES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16}
+
+
+class ScoreMods(ctypes.Structure):
+    """``pa_score_mods``: window (0 = none), softcap (0 = none), alibi slopes."""
+
+    _fields_ = [("window", ctypes.c_int32), ("softcap", ctypes.c_float),
+                ("alibi_slopes", ctypes.c_void_p)]
+
+
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+_f32 = ctypes.c_float
+_sz = ctypes.c_size_t
+_mods_p = ctypes.POINTER(ScoreMods)
+
+# name -> (restype, argtypes), mirroring include/pagedattn.h
+SIGNATURES = {
+    "kv_append": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _i32, _vp]),
+    "paged_attn_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "paged_attn_decode_split_tokens": (_i32, [_i32, _i32, _i32, _i32]),
+    "paged_attn_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i64,
+                                 _i32, _f32, _i32, _mods_p, _vp, _sz, _i32, _vp]),
+    "paged_attn_decode_partials": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
+                                          _i64, _i32, _f32, _i32, _mods_p, _vp, _sz, _i32, _vp]),
+    "paged_attn_decode_merge": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _mods_p, _vp, _sz, _i32,
+                                       _vp]),
+    "paged_attn_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                  _i64, _f32, _i32, _mods_p, _i32, _vp]),
+    "paged_attn_status_string": (ctypes.c_char_p, [_i32]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the library (built beforehand by ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def status_string(code: int) -> str:
+    return lib().paged_attn_status_string(int(code)).decode()
+
+
+def _check(code: int, what: str):
+    if code == 0:
+        return
+    msg = f"{what}: {status_string(code)} (status {code})"
+    if code < 0:
+        raise ValueError(msg)
+    raise RuntimeError(msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {t.dim()}")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {t.dtype}")
+    return _DTYPES[t.dtype]
+
+
+def _mods(window=0, softcap=0.0, alibi_slopes=None):
+    if not window and not softcap and alibi_slopes is None:
+        return None, None
+    if alibi_slopes is not None:
+        _need(alibi_slopes, "alibi_slopes", torch.float32, 1)
+    m = ScoreMods(int(window), float(softcap), None if alibi_slopes is None else alibi_slopes.data_ptr())
+    return ctypes.pointer(m), m
+
+
+def _pool_dims(k_cache, v_cache):
+    _need(k_cache, "k_cache", ndim=4)
+    _need(v_cache, "v_cache", ndim=4)
+    NB, Hkv, bs, D = k_cache.shape
+    if tuple(v_cache.shape) != (NB, Hkv, D, bs) or v_cache.dtype != k_cache.dtype:
+        raise ValueError("v_cache must be [num_blocks, num_kv_heads, head_dim, block_size] of k_cache's dtype")
+    return NB, Hkv, bs, D
+
+
+def kv_append(k_new, v_new, k_cache, v_cache, slot_mapping):
+    """Write ``k_new/v_new [T, Hkv, D]`` into the slots ``slot_mapping [T]`` (int32)."""
+    NB, Hkv, bs, D = _pool_dims(k_cache, v_cache)
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, n, k_cache.dtype, 3)
+    _need(slot_mapping, "slot_mapping", torch.int32, 1)
+    T = slot_mapping.shape[0]
+    if tuple(k_new.shape) != (T, Hkv, D) or tuple(v_new.shape) != (T, Hkv, D):
+        raise ValueError("k_new/v_new must be [T, num_kv_heads, head_dim]")
+    code = lib().kv_append(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), T, Hkv,
+                           D, bs, NB, _dtype_code(k_cache), _stream())
+    _check(code, "kv_append")
+
+
+def decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len, split_tokens=0) -> int:
+    return int(lib().paged_attn_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim,
+                                                      max_context_len, split_tokens))
+
+
+def decode_split_tokens(num_seqs, num_kv_heads, max_context_len, split_tokens=0) -> int:
+    return int(lib().paged_attn_decode_split_tokens(num_seqs, num_kv_heads, max_context_len, split_tokens))
+
+
+def decode_workspace(q, num_kv_heads, max_context_len, split_tokens=0):
+    B, Hq, D = q.shape
+    n = decode_workspace_size(B, Hq, num_kv_heads, D, max_context_len, split_tokens)
+    return torch.empty(max(n, 4) // 4, dtype=torch.float32, device=q.device)
+
+
+def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens):
+    NB, Hkv, bs, D = _pool_dims(k_cache, v_cache)
+    _need(q, "q", k_cache.dtype, 3)
+    _need(out, "out", k_cache.dtype, 3)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(context_lens, "context_lens", torch.int32, 1)
+    B, Hq, Dq = q.shape
+    if Dq != D or tuple(out.shape) != tuple(q.shape) or block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("shape mismatch between q/out/block_tables/context_lens/pools")
+    return NB, Hkv, bs, D, B, Hq
+
+
+def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+                      split_tokens=0, workspace=None, window=0, softcap=0.0, alibi_slopes=None, phase="both"):
+    """One query row per sequence; writes ``out [B, Hq, D]``.
+
+    ``phase`` selects ``paged_attn_decode`` ("both"), ``..._partials`` or
+    ``..._merge``.  ``workspace`` defaults to a fresh buffer of the size the
+    library asks for.
+    """
+    NB, Hkv, bs, D, B, Hq = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens)
+    if workspace is None:
+        workspace = decode_workspace(q, Hkv, max_context_len, split_tokens)
+    _need(workspace, "workspace")
+    mp, _keep = _mods(window, softcap, alibi_slopes)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    L = lib()
+    if phase == "merge":
+        code = L.paged_attn_decode_merge(_ptr(out), _ptr(context_lens), B, Hq, Hkv, D, int(max_context_len),
+                                         int(split_tokens), mp, _ptr(workspace), ws_bytes, _dtype_code(q),
+                                         _stream())
+    else:
+        fn = L.paged_attn_decode if phase == "both" else L.paged_attn_decode_partials
+        code = fn(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1],
+                  _ptr(context_lens), B, Hq, Hkv, D, bs, NB, int(max_context_len), float(scale), int(split_tokens),
+                  mp, _ptr(workspace), ws_bytes, _dtype_code(q), _stream())
+    _check(code, f"paged_attn_decode[{phase}]")
+    return out
+
+
+def paged_attn_prefill(out, q, cu_q_lens, k_cache, v_cache, block_tables, context_lens, scale, max_q_len,
+                       causal=True, window=0, softcap=0.0, alibi_slopes=None):
+    """Query rows ``q [total_q, Hq, D]`` grouped by ``cu_q_lens [B+1]``; writes ``out``."""
+    NB, Hkv, bs, D = _pool_dims(k_cache, v_cache)
+    _need(q, "q", k_cache.dtype, 3)
+    _need(out, "out", k_cache.dtype, 3)
+    _need(cu_q_lens, "cu_q_lens", torch.int32, 1)
+    _need(block_tables, "block_tables", torch.int32, 2)
+    _need(context_lens, "context_lens", torch.int32, 1)
+    B = context_lens.shape[0]
+    if cu_q_lens.shape[0] != B + 1 or block_tables.shape[0] != B or tuple(out.shape) != tuple(q.shape) \
+            or q.shape[2] != D:
+        raise ValueError("shape mismatch between q/out/cu_q_lens/block_tables/context_lens/pools")
+    mp, _keep = _mods(window, softcap, alibi_slopes)
+    code = lib().paged_attn_prefill(_ptr(out), _ptr(q), _ptr(cu_q_lens), _ptr(k_cache), _ptr(v_cache),
+                                    _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, int(max_q_len),
+                                    q.shape[1], Hkv, D, bs, NB, float(scale), int(bool(causal)), mp, _dtype_code(q),
+                                    _stream())
+    _check(code, "paged_attn_prefill")
+    return out

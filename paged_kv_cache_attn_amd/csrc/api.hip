@@ -1,0 +1,323 @@
+// C ABI entry points: host-side validation, split-KV sizing and launches.
+// Every check happens before anything is enqueued; see include/pagedattn.h.
+#include <math.h>
+
+#include "pagedattn.h"
+#include "pa_kernels.h"
+
+namespace {
+
+constexpr int kUnsplitLog2 = 30;
+constexpr int kAutoSplitMax = 512;
+constexpr int kAutoSplitMin = 64;
+constexpr long long kAutoTargetUnits = 2048;  // ~8 wavefronts per compute unit
+
+int ilog2(long long x) {
+  int r = 0;
+  while ((1ll << r) < x) ++r;
+  return r;
+}
+bool is_pow2(long long x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int check_dtype(int32_t dtype) { return (dtype == PA_F32 || dtype == PA_BF16) ? PA_OK : PA_ERR_DTYPE; }
+int check_dim(int32_t d) { return (d == 64 || d == 128) ? PA_OK : PA_ERR_HEAD_DIM; }
+int check_bs(int32_t bs) { return (is_pow2(bs) && bs >= 16 && bs <= 256) ? PA_OK : PA_ERR_BLOCK_SIZE; }
+int check_heads(int32_t hq, int32_t hkv) {
+  if (hq <= 0 || hkv <= 0 || hq % hkv != 0) return PA_ERR_HEADS;
+  return PA_OK;
+}
+int check_split(int32_t split) {
+  if (split == 0 || split == -1) return PA_OK;
+  return (is_pow2(split) && split >= 16 && split <= (1 << 29)) ? PA_OK : PA_ERR_SPLIT;
+}
+int check_mods(const pa_score_mods* m) {
+  if (!m) return PA_OK;
+  if (m->window < 0) return PA_ERR_MODS;
+  if (!(m->softcap >= 0.f) || isinf(m->softcap)) return PA_ERR_MODS;
+  return PA_OK;
+}
+
+// log2 of the partition length, kUnsplitLog2 for "never split".
+int resolve_split_log2(int32_t B, int32_t Hkv, int32_t max_ctx, int32_t split) {
+  if (split == -1) return kUnsplitLog2;
+  if (split > 0) return ilog2(split);
+  long long s = kAutoSplitMax;
+  auto units = [&](long long sp) { return (long long)B * Hkv * ((max_ctx + sp - 1) / sp); };
+  while (s > kAutoSplitMin && units(s) < kAutoTargetUnits) s >>= 1;
+  return ilog2(s);
+}
+
+int partitions(int32_t max_ctx, int split_log2) {
+  if (split_log2 >= kUnsplitLog2 || max_ctx <= 0) return 1;
+  const long long sp = 1ll << split_log2;
+  return (int)((max_ctx + sp - 1) / sp);
+}
+
+int group_pad(int g) { return g <= 4 ? 4 : 8; }
+
+struct Shape {
+  int g, GP, NG, P, split_log2;
+};
+
+int decode_shape(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_ctx, int32_t split, Shape& s) {
+  s.g = Hq / Hkv;
+  s.GP = group_pad(s.g);
+  s.NG = (s.g + s.GP - 1) / s.GP;
+  s.split_log2 = resolve_split_log2(B, Hkv, max_ctx, split);
+  s.P = partitions(max_ctx, s.split_log2);
+  return PA_OK;
+}
+
+size_t workspace_bytes_for(int32_t B, int32_t Hkv, int32_t D, const Shape& s) {
+  if (s.P <= 1) return 0;
+  return (size_t)B * Hkv * s.NG * s.GP * (size_t)s.P * (size_t)(D + 2) * sizeof(float);
+}
+
+int common_decode_checks(int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int64_t NB,
+                         int32_t bt_stride, int32_t max_ctx, int32_t split, int32_t dtype,
+                         const pa_score_mods* mods) {
+  int st;
+  if ((st = check_dtype(dtype))) return st;
+  if (B < 0 || NB < 0 || max_ctx < 0) return PA_ERR_SIZE;
+  if ((st = check_heads(Hq, Hkv))) return st;
+  if ((st = check_dim(D))) return st;
+  if ((st = check_bs(bs))) return st;
+  if ((st = check_split(split))) return st;
+  if ((st = check_mods(mods))) return st;
+  if (B > 0 && bt_stride < 1) return PA_ERR_TABLE_STRIDE;
+  return PA_OK;
+}
+
+void fill_row_args(pa::RowAttnArgs& a, void* out, const void* q, const void* kc, const void* vc,
+                   const int32_t* bt, int32_t bt_stride, const int32_t* ctx, const int32_t* cu,
+                   int32_t B, int32_t max_q, int32_t Hq, int32_t Hkv, int32_t bs, const Shape& s,
+                   float scale, int32_t causal, const pa_score_mods* mods, void* ws, int32_t D) {
+  a.out = out;
+  a.q = q;
+  a.k_cache = kc;
+  a.v_cache = vc;
+  a.block_tables = bt;
+  a.context_lens = ctx;
+  a.cu_q_lens = cu;
+  a.bt_stride = bt_stride;
+  a.max_q_len = max_q;
+  a.num_seqs = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.g = s.g;
+  a.NG = s.NG;
+  a.bs_log2 = ilog2(bs);
+  a.split_log2 = s.split_log2;
+  a.P = s.P;
+  a.causal = causal;
+  a.window = mods ? mods->window : 0;
+  a.scale = scale;
+  a.softcap = mods ? mods->softcap : 0.f;
+  a.alibi = mods ? mods->alibi_slopes : nullptr;
+  float* w = static_cast<float*>(ws);
+  const size_t units = (size_t)B * max_q * Hkv * s.NG * s.GP * (size_t)s.P;
+  a.ws_o = w;
+  a.ws_ml = w ? w + units * D : nullptr;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? PA_OK : (int)e; }
+
+int decode_impl(bool do_partials, bool do_merge, void* out, const void* q, const void* k_cache,
+                const void* v_cache, const int32_t* block_tables, int32_t bt_stride,
+                const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                int32_t bs, int64_t NB, int32_t max_ctx, float scale, int32_t split,
+                const pa_score_mods* mods, void* workspace, size_t workspace_bytes, int32_t dtype,
+                void* stream) {
+  int st = common_decode_checks(B, Hq, Hkv, D, bs, NB, bt_stride, max_ctx, split, dtype, mods);
+  if (st) return st;
+  if (B == 0) return PA_OK;
+  if (!out || !context_lens) return PA_ERR_NULL;
+  if (do_partials && (!q || !k_cache || !v_cache || !block_tables)) return PA_ERR_NULL;
+  Shape s;
+  decode_shape(B, Hq, Hkv, max_ctx, split, s);
+  const size_t need = workspace_bytes_for(B, Hkv, D, s);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return PA_ERR_WORKSPACE;
+  const long long blocks = (long long)B * Hkv * s.NG * s.P;
+  if (blocks > 0x7fffffffll || (long long)B * Hq > 0x7fffffffll) return PA_ERR_SIZE;
+  pa::RowAttnArgs a;
+  fill_row_args(a, out, q, k_cache, v_cache, block_tables, bt_stride, context_lens, nullptr, B, 1,
+                Hq, Hkv, bs, s, scale, 1, mods, need > 0 ? workspace : nullptr, D);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (do_partials) {
+    if ((st = launch_status(pa::launch_row_partials(a, dtype, D, hs)))) return st;
+  }
+  if (do_merge && s.P > 1) {
+    if ((st = launch_status(pa::launch_row_merge(a, dtype, D, hs)))) return st;
+  }
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+              const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+              int32_t head_dim, int32_t block_size, int64_t num_blocks, int32_t dtype,
+              void* stream) {
+  int st;
+  if ((st = check_dtype(dtype))) return st;
+  if (num_tokens < 0 || num_blocks < 0) return PA_ERR_SIZE;
+  if (num_kv_heads <= 0) return PA_ERR_HEADS;
+  if ((st = check_dim(head_dim))) return st;
+  if ((st = check_bs(block_size))) return st;
+  if (num_tokens == 0) return PA_OK;
+  if (!k_new || !v_new || !k_cache || !v_cache || !slot_mapping) return PA_ERR_NULL;
+  if ((long long)num_tokens * num_kv_heads > 0x7fffffffll) return PA_ERR_SIZE;
+  pa::AppendArgs a;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.slots = slot_mapping;
+  a.T = num_tokens;
+  a.Hkv = num_kv_heads;
+  a.D = head_dim;
+  a.bs_log2 = ilog2(block_size);
+  return launch_status(pa::launch_kv_append(a, dtype, static_cast<hipStream_t>(stream)));
+}
+
+int32_t paged_attn_decode_split_tokens(int32_t num_seqs, int32_t num_kv_heads,
+                                       int32_t max_context_len, int32_t split_tokens) {
+  if (check_split(split_tokens) || num_seqs < 0 || num_kv_heads <= 0 || max_context_len < 0) return 0;
+  const int l2 = resolve_split_log2(num_seqs, num_kv_heads, max_context_len, split_tokens);
+  return l2 >= kUnsplitLog2 ? -1 : (1 << l2);
+}
+
+size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_heads,
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t max_context_len, int32_t split_tokens) {
+  if (num_seqs < 0 || max_context_len < 0 || check_heads(num_heads, num_kv_heads) ||
+      check_dim(head_dim) || check_split(split_tokens))
+    return 0;
+  Shape s;
+  decode_shape(num_seqs, num_heads, num_kv_heads, max_context_len, split_tokens, s);
+  return workspace_bytes_for(num_seqs, num_kv_heads, head_dim, s);
+}
+
+int paged_attn_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, int32_t block_table_stride,
+                      const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                      int64_t num_blocks, int32_t max_context_len, float scale,
+                      int32_t split_tokens, const pa_score_mods* mods, void* workspace,
+                      size_t workspace_bytes, int32_t dtype, void* stream) {
+  return decode_impl(true, true, out, q, k_cache, v_cache, block_tables, block_table_stride,
+                     context_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                     num_blocks, max_context_len, scale, split_tokens, mods, workspace,
+                     workspace_bytes, dtype, stream);
+}
+
+int paged_attn_decode_partials(void* out, const void* q, const void* k_cache,
+                               const void* v_cache, const int32_t* block_tables,
+                               int32_t block_table_stride, const int32_t* context_lens,
+                               int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                               int32_t max_context_len, float scale, int32_t split_tokens,
+                               const pa_score_mods* mods, void* workspace,
+                               size_t workspace_bytes, int32_t dtype, void* stream) {
+  return decode_impl(true, false, out, q, k_cache, v_cache, block_tables, block_table_stride,
+                     context_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                     num_blocks, max_context_len, scale, split_tokens, mods, workspace,
+                     workspace_bytes, dtype, stream);
+}
+
+int paged_attn_decode_merge(void* out, const int32_t* context_lens, int32_t num_seqs,
+                            int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t max_context_len, int32_t split_tokens,
+                            const pa_score_mods* mods, const void* workspace,
+                            size_t workspace_bytes, int32_t dtype, void* stream) {
+  return decode_impl(false, true, out, nullptr, nullptr, nullptr, nullptr, 1, context_lens,
+                     num_seqs, num_heads, num_kv_heads, head_dim, 16, 0, max_context_len, 1.f,
+                     split_tokens, mods, const_cast<void*>(workspace), workspace_bytes, dtype,
+                     stream);
+}
+
+int paged_attn_prefill(void* out, const void* q, const int32_t* cu_q_lens, const void* k_cache,
+                       const void* v_cache, const int32_t* block_tables,
+                       int32_t block_table_stride, const int32_t* context_lens,
+                       int32_t num_seqs, int32_t max_q_len, int32_t num_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                       int64_t num_blocks, float scale, int32_t causal,
+                       const pa_score_mods* mods, int32_t dtype, void* stream) {
+  int st;
+  if ((st = check_dtype(dtype))) return st;
+  if (num_seqs < 0 || num_blocks < 0 || max_q_len < 0) return PA_ERR_SIZE;
+  if ((st = check_heads(num_heads, num_kv_heads))) return st;
+  if ((st = check_dim(head_dim))) return st;
+  if ((st = check_bs(block_size))) return st;
+  if (causal != 0 && causal != 1) return PA_ERR_FLAG;
+  if ((st = check_mods(mods))) return st;
+  if (num_seqs > 0 && block_table_stride < 1) return PA_ERR_TABLE_STRIDE;
+  if (num_seqs == 0 || max_q_len == 0) return PA_OK;
+  if (!out || !q || !cu_q_lens || !k_cache || !v_cache || !block_tables || !context_lens)
+    return PA_ERR_NULL;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const int g = num_heads / num_kv_heads;
+  if (dtype == PA_BF16 && 128 % g == 0) {
+    pa::PrefillArgs a;
+    a.out = out;
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.context_lens = context_lens;
+    a.cu_q_lens = cu_q_lens;
+    a.alibi = mods ? mods->alibi_slopes : nullptr;
+    a.bt_stride = block_table_stride;
+    a.num_seqs = num_seqs;
+    a.Hq = num_heads;
+    a.Hkv = num_kv_heads;
+    a.g = g;
+    a.bs_log2 = ilog2(block_size);
+    const int qt = pa::prefill_rows_per_tile(g);
+    a.q_tiles = (max_q_len + qt - 1) / qt;
+    a.causal = causal;
+    a.window = mods ? mods->window : 0;
+    a.scale = scale;
+    a.softcap = mods ? mods->softcap : 0.f;
+    if ((long long)num_seqs * num_kv_heads * a.q_tiles > 0x7fffffffll) return PA_ERR_SIZE;
+    return launch_status(pa::launch_prefill_mfma(a, head_dim, hs));
+  }
+  // fp32 (and group sizes that do not divide 128): one query row per
+  // wavefront over its whole admissible key range, no split.
+  Shape s;
+  s.g = g;
+  s.GP = group_pad(g);
+  s.NG = (g + s.GP - 1) / s.GP;
+  s.split_log2 = kUnsplitLog2;
+  s.P = 1;
+  if ((long long)num_seqs * max_q_len * num_kv_heads * s.NG > 0x7fffffffll) return PA_ERR_SIZE;
+  pa::RowAttnArgs a;
+  fill_row_args(a, out, q, k_cache, v_cache, block_tables, block_table_stride, context_lens,
+                cu_q_lens, num_seqs, max_q_len, num_heads, num_kv_heads, block_size, s, scale,
+                causal, mods, nullptr, head_dim);
+  return launch_status(pa::launch_row_partials(a, dtype, head_dim, hs));
+}
+
+const char* paged_attn_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "a required pointer is NULL";
+    case PA_ERR_SIZE: return "a count is negative or too large";
+    case PA_ERR_HEADS: return "heads must be positive and num_heads a multiple of num_kv_heads";
+    case PA_ERR_HEAD_DIM: return "head_dim must be 64 or 128";
+    case PA_ERR_BLOCK_SIZE: return "block_size must be a power of two in [16, 256]";
+    case PA_ERR_SPLIT: return "split_tokens must be 0, -1 or a power of two >= 16";
+    case PA_ERR_WORKSPACE: return "workspace missing or too small";
+    case PA_ERR_DTYPE: return "dtype must be PA_F32 or PA_BF16";
+    case PA_ERR_FLAG: return "causal must be 0 or 1";
+    case PA_ERR_MODS: return "score mods: window and softcap must be finite and >= 0";
+    case PA_ERR_TABLE_STRIDE: return "block_table_stride must be >= 1";
+    default: break;
+  }
+  if (status > 0) return hipGetErrorString(static_cast<hipError_t>(status));
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -1,0 +1,510 @@
+// Paged attention for query rows that each attend to (a range of) their own
+// sequence's paged context: decode (one row per sequence) and the fp32 path
+// of prefill (one row per query position).  gfx950 / CDNA4, wave64.
+//
+// Method: attention reads the K/V blocks of a sequence where they lie in the
+// shared pool, found through the block table, with no contiguous copy
+// (Joshi et al., "Paged Attention Meets FlexAttention", abstract; "Ultimate
+// Guide to PagedAttention", block table), computing exact softmax attention
+// with a running (online) softmax over tiles of keys (Dao et al.,
+// "FlashAttention", abstract: tiling between HBM and on-chip memory).
+//
+// Work decomposition (one wavefront = one work-group):
+//   (row slot, head group, partition) -- a head group is the GP <= 8 query
+//   heads of one kv-head, so each K/V byte is read once for all of them;
+//   a partition is 2^split_log2 consecutive keys (split-KV).
+// Per 16-token chunk (always inside one block, since block sizes are powers
+// of two >= 16):
+//   * q.k on VALU: GP lanes share a token, each holding 1/GP of head_dim for
+//     all GP heads; bf16 uses v_dot2_f32_bf16.  A reduce-scatter across the
+//     GP lanes (DPP row_ror:8, permlane16_swap, permlane32_swap) leaves each
+//     lane with one head's full score, with no select instructions: q rows
+//     are loaded in a lane-dependent order that makes every step an add.
+//   * online softmax in the log2 domain; the running max is raised lazily
+//     (only when a new score exceeds it by more than 2^8), so rescaling of
+//     the accumulators is rare after the first chunk.
+//   * P.V with lanes over head_dim: V slabs are dimension-major, so one dword
+//     holds two consecutive tokens of one dimension -- exactly the bf16 pair
+//     v_dot2 wants against a (p_j, p_j+1) pair read from LDS.
+#include "pa_device.h"
+#include "pa_kernels.h"
+
+namespace pa {
+namespace {
+
+constexpr float kLazyRescale = 8.0f;  // log2 units
+
+template <typename E, int D, int GP>
+struct Cfg {
+  static constexpr int ES = E::kBytes;
+  static constexpr bool kBf16 = (ES == 2);
+  static constexpr int kRowBytes = D * ES;        // one K row
+  static constexpr int kPieces = kRowBytes / 16;  // 16-byte pieces per K row
+  static constexpr int TPI = 64 / GP;             // tokens per pass
+  static constexpr int NPASS = 16 / TPI;          // passes per 16-token chunk
+  static constexpr int PPL = kPieces / GP;        // pieces per lane per token
+  static constexpr int RPL = D / 64;              // V rows (dims) per lane
+  static constexpr int VPR = 16 * ES / 16;        // 16-byte loads per V row of a chunk
+  static_assert(PPL >= 1 && RPL >= 1, "unsupported shape");
+};
+
+template <typename E, int D, int GP>
+struct Chunk {
+  using C = Cfg<E, D, GP>;
+  u32x4 k[C::NPASS][C::PPL];
+  u32x4 v[C::RPL][C::VPR];
+};
+
+// Which head (0..GP-1 within the group) lane group e holds after the reduce.
+template <int GP>
+__device__ __forceinline__ int final_head(int e) {
+  if constexpr (GP == 8) {
+    return ((e & 1) << 2) | (e & 2) | ((e >> 2) & 1);
+  } else {
+    return ((e & 1) << 1) | ((e >> 1) & 1);
+  }
+}
+
+// Head loaded into q slot s by lane group e (makes every reduce step an add).
+template <int GP>
+__device__ __forceinline__ int slot_head(int s, int e) {
+  if constexpr (GP == 8) return (e & 1) ? (s ^ 4) : s;
+  return s;
+}
+
+template <int GP>
+__device__ __forceinline__ float reduce_scatter(const float (&acc)[GP]) {
+  if constexpr (GP == 8) {
+    float r4[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r4[k] = acc[k] + dpp<kDppRowRor8>(acc[k + 4]);
+    float r2[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) r2[k] = swap_add16(r4[k], r4[k + 2]);
+    return swap_add32(r2[0], r2[1]);
+  } else {
+    float r2[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) r2[k] = swap_add16(acc[k], acc[k + 2]);
+    return swap_add32(r2[0], r2[1]);
+  }
+}
+
+// max / sum over the TPI consecutive lanes that hold one head
+template <int TPI, bool kMax>
+__device__ __forceinline__ float group_reduce(float x) {
+  auto op = [](float a, float b) { return kMax ? fmaxf(a, b) : a + b; };
+  x = op(x, dpp<kDppQuadXor1>(x));
+  x = op(x, dpp<kDppQuadXor2>(x));
+  x = op(x, dpp<kDppRowHalfMirror>(x));
+  if constexpr (TPI == 16) x = op(x, dpp<kDppRowMirror>(x));
+  return x;
+}
+
+struct RowRange {
+  int qrow;   // query / output row
+  int pos;    // logical position of the query
+  int lo;     // first admissible key
+  int hi;     // one past the last admissible key
+  int start;  // lo rounded down to a chunk
+  int nparts; // partitions the row uses (>= 1)
+};
+
+__device__ __forceinline__ bool row_range(const RowAttnArgs& a, int slot, RowRange& r) {
+  const int b = slot / a.max_q_len;
+  const int i = slot - b * a.max_q_len;
+  const int n = a.context_lens[b];
+  int Lq = 1, q0 = b;
+  if (a.cu_q_lens) {
+    q0 = a.cu_q_lens[b];
+    Lq = a.cu_q_lens[b + 1] - q0;
+  }
+  if (i >= Lq) return false;
+  r.qrow = q0 + i;
+  r.pos = n - Lq + i;
+  r.hi = a.causal ? min(n, r.pos + 1) : n;
+  r.lo = a.window > 0 ? max(0, r.pos - a.window + 1) : 0;
+  if (r.hi < 0) r.hi = 0;
+  if (r.lo > r.hi) r.lo = r.hi;
+  r.start = r.lo & ~15;
+  const int span = r.hi - r.start;
+  r.nparts = span > 0 ? ((span + (1 << a.split_log2) - 1) >> a.split_log2) : 1;
+  // a context longer than the host's max_context_len breaks the caller
+  // contract; clamping keeps every workspace access inside the buffer
+  r.nparts = min(r.nparts, a.P);
+  return true;
+}
+
+template <typename E, int D, int GP, bool kMods>
+__global__ __launch_bounds__(64) void row_partials_kernel(const RowAttnArgs a) {
+  using C = Cfg<E, D, GP>;
+  constexpr int TPI = C::TPI;
+  __shared__ __attribute__((aligned(16))) uint32_t p_lds[16 * GP];  // bf16 pairs or f32
+  __shared__ __attribute__((aligned(16))) float stat_lds[2 * GP];
+
+  const int lane = threadIdx.x;
+  const int HG = a.Hkv * a.NG;
+  const int flat = blockIdx.x;
+  const int p = flat % a.P;
+  const int hg = (flat / a.P) % HG;
+  const int slot = flat / (a.P * HG);
+
+  RowRange rr;
+  if (!row_range(a, slot, rr)) return;
+  if (p >= rr.nparts) return;
+  const int c_begin = rr.start + (p << a.split_log2);
+  const int c_end = min(rr.hi, c_begin + (1 << a.split_log2));
+
+  const int kvh = hg / a.NG;
+  const int head0 = kvh * a.g + (hg - kvh * a.NG) * GP;  // first global head of the group
+  const int nvalid = min(GP, a.g - (hg - kvh * a.NG) * GP);
+
+  const int t = lane % TPI;
+  const int e = lane / TPI;
+  const int my_head = final_head<GP>(e);
+
+  // ---- q slice of every head in the group (lane-dependent head order) ----
+  u32x4 qv[GP][C::PPL];
+  {
+    const char* qbase = static_cast<const char*>(a.q) + (size_t)rr.qrow * a.Hq * D * C::ES;
+#pragma unroll
+    for (int s = 0; s < GP; ++s) {
+      const int h = slot_head<GP>(s, e);
+#pragma unroll
+      for (int i = 0; i < C::PPL; ++i) {
+        if (h < nvalid) {
+          qv[s][i] = load16(qbase + ((size_t)(head0 + h) * D) * C::ES + (e + GP * i) * 16);
+        } else {
+          qv[s][i] = u32x4{0, 0, 0, 0};
+        }
+      }
+    }
+  }
+
+  const float scale_log2 = a.scale * kLog2e;
+  float alibi_slope = 0.f;
+  if constexpr (kMods) {
+    if (a.alibi && my_head < nvalid) alibi_slope = a.alibi[head0 + my_head];
+  }
+
+  float m_run = kNegInf;  // log2 domain, for head my_head
+  float l_run = 0.f;      // partial sum over this lane's tokens
+  float o[GP][C::RPL];
+#pragma unroll
+  for (int h = 0; h < GP; ++h)
+#pragma unroll
+    for (int r = 0; r < C::RPL; ++r) o[h][r] = 0.f;
+
+  const int b = slot / a.max_q_len;
+  const int n = a.context_lens[b];
+  const int32_t* table = a.block_tables + (size_t)b * a.bt_stride;
+  const int bs = 1 << a.bs_log2;
+  const size_t kslab_bytes = (size_t)bs * D * C::ES;
+  const char* kpool = static_cast<const char*>(a.k_cache);
+  const char* vpool = static_cast<const char*>(a.v_cache);
+
+  auto load_chunk = [&](Chunk<E, D, GP>& ch, int tok0) {
+    const int blk = table[tok0 >> a.bs_log2];
+    const int off = tok0 & (bs - 1);
+    const size_t slab = ((size_t)blk * a.Hkv + kvh) * kslab_bytes;
+    const char* ks = kpool + slab + (size_t)off * C::kRowBytes;
+    const char* vs = vpool + slab + (size_t)off * C::ES;
+#pragma unroll
+    for (int ps = 0; ps < C::NPASS; ++ps)
+#pragma unroll
+      for (int i = 0; i < C::PPL; ++i)
+        ch.k[ps][i] = load16(ks + (ps * TPI + t) * C::kRowBytes + (e + GP * i) * 16);
+#pragma unroll
+    for (int r = 0; r < C::RPL; ++r)
+#pragma unroll
+      for (int w = 0; w < C::VPR; ++w)
+        ch.v[r][w] = load16(vs + (size_t)(lane + 64 * r) * bs * C::ES + w * 16);
+  };
+
+  Chunk<E, D, GP> cur, nxt;
+  if (c_begin < c_end) load_chunk(cur, c_begin);
+
+  for (int tok0 = c_begin; tok0 < c_end; tok0 += 16) {
+    if (tok0 + 16 < c_end) load_chunk(nxt, tok0 + 16);
+
+    // ---- scores for this lane's tokens, head my_head ----
+    float s[C::NPASS];
+#pragma unroll
+    for (int ps = 0; ps < C::NPASS; ++ps) {
+      float acc[GP];
+#pragma unroll
+      for (int h = 0; h < GP; ++h) {
+        float x = 0.f;
+#pragma unroll
+        for (int i = 0; i < C::PPL; ++i) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            if constexpr (C::kBf16) {
+              x = dot2_bf16(qv[h][i][w], cur.k[ps][i][w], x);
+            } else {
+              x = fmaf(__uint_as_float(qv[h][i][w]), __uint_as_float(cur.k[ps][i][w]), x);
+            }
+          }
+        }
+        acc[h] = x;
+      }
+      const float dotv = reduce_scatter<GP>(acc);
+      const int tok = tok0 + ps * TPI + t;
+      float sc;
+      if constexpr (kMods) {
+        float x = dotv * a.scale;
+        if (a.softcap > 0.f) {
+          const float z = x / a.softcap;
+          const float ez = fast_exp2(2.f * kLog2e * z);
+          x = a.softcap * (1.f - 2.f / (ez + 1.f));
+        }
+        x += alibi_slope * (float)(tok - rr.pos);
+        sc = x * kLog2e;
+      } else {
+        sc = dotv * scale_log2;
+      }
+      const bool ok = (tok >= rr.lo) && (tok < c_end);
+      s[ps] = ok ? sc : kNegInf;
+    }
+
+    // ---- online softmax (lazy max) ----
+    float cmax = s[0];
+#pragma unroll
+    for (int ps = 1; ps < C::NPASS; ++ps) cmax = fmaxf(cmax, s[ps]);
+    cmax = group_reduce<TPI, true>(cmax);
+    const float m_new = fmaxf(m_run, cmax);
+    const bool need = m_new > m_run + kLazyRescale;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
+      if (need) m_run = m_new;
+      l_run *= alpha;
+      if (t == 0) stat_lds[my_head] = alpha;
+      __builtin_amdgcn_wave_barrier();
+      float al[GP];
+#pragma unroll
+      for (int h = 0; h < GP; ++h) al[h] = stat_lds[h];
+#pragma unroll
+      for (int h = 0; h < GP; ++h)
+#pragma unroll
+        for (int r = 0; r < C::RPL; ++r) o[h][r] *= al[h];
+      __builtin_amdgcn_wave_barrier();
+    }
+    const float msafe = (m_run == kNegInf) ? 0.f : m_run;
+#pragma unroll
+    for (int ps = 0; ps < C::NPASS; ++ps) {
+      const float pv = fast_exp2(s[ps] - msafe);
+      const int j = ps * TPI + t;
+      if constexpr (C::kBf16) {
+        const uint32_t bits = f32_to_bf16_bits(pv);
+        l_run += __uint_as_float(bits << 16);
+        reinterpret_cast<uint16_t*>(p_lds)[((j >> 1) * GP + my_head) * 2 + (j & 1)] = (uint16_t)bits;
+      } else {
+        l_run += pv;
+        reinterpret_cast<float*>(p_lds)[j * GP + my_head] = pv;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    // ---- keys past the sequence end may hold anything: zero their V ----
+    if (tok0 + 16 > n) {
+#pragma unroll
+      for (int r = 0; r < C::RPL; ++r)
+#pragma unroll
+        for (int w = 0; w < C::VPR; ++w)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            if constexpr (C::kBf16) {
+              const int j0 = tok0 + w * 8 + c * 2;
+              uint32_t m = (j0 < n ? 0xffffu : 0u) | (j0 + 1 < n ? 0xffff0000u : 0u);
+              cur.v[r][w][c] &= m;
+            } else {
+              const int j0 = tok0 + w * 4 + c;
+              if (j0 >= n) cur.v[r][w][c] = 0u;
+            }
+          }
+    }
+
+    // ---- o += P.V ----
+    if constexpr (C::kBf16) {
+#pragma unroll
+      for (int jp = 0; jp < 8; ++jp) {
+        uint32_t pp[GP];
+#pragma unroll
+        for (int h4 = 0; h4 < GP / 4; ++h4) {
+          const u32x4 x = *reinterpret_cast<const u32x4*>(&p_lds[jp * GP + h4 * 4]);
+          pp[h4 * 4 + 0] = x[0];
+          pp[h4 * 4 + 1] = x[1];
+          pp[h4 * 4 + 2] = x[2];
+          pp[h4 * 4 + 3] = x[3];
+        }
+#pragma unroll
+        for (int r = 0; r < C::RPL; ++r) {
+          const uint32_t v2 = cur.v[r][jp >> 2][jp & 3];
+#pragma unroll
+          for (int h = 0; h < GP; ++h) o[h][r] = dot2_bf16(pp[h], v2, o[h][r]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        float pj[GP];
+#pragma unroll
+        for (int h4 = 0; h4 < GP / 4; ++h4) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(&reinterpret_cast<const float*>(p_lds)[j * GP + h4 * 4]);
+          pj[h4 * 4 + 0] = x[0];
+          pj[h4 * 4 + 1] = x[1];
+          pj[h4 * 4 + 2] = x[2];
+          pj[h4 * 4 + 3] = x[3];
+        }
+#pragma unroll
+        for (int r = 0; r < C::RPL; ++r) {
+          const float vj = __uint_as_float(cur.v[r][j >> 2][j & 3]);
+#pragma unroll
+          for (int h = 0; h < GP; ++h) o[h][r] = fmaf(pj[h], vj, o[h][r]);
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    cur = nxt;
+  }
+
+  // ---- finish: per-head (m, l) to every lane ----
+  const float l_tot = group_reduce<TPI, false>(l_run);
+  if (t == 0) {
+    stat_lds[2 * my_head] = m_run;
+    stat_lds[2 * my_head + 1] = l_tot;
+  }
+  __builtin_amdgcn_wave_barrier();
+  float mh[GP], lh[GP];
+#pragma unroll
+  for (int h = 0; h < GP; ++h) {
+    mh[h] = stat_lds[2 * h];
+    lh[h] = stat_lds[2 * h + 1];
+  }
+
+  if (rr.nparts == 1) {
+#pragma unroll
+    for (int h = 0; h < GP; ++h) {
+      if (h >= nvalid) continue;
+      const float inv = lh[h] > 0.f ? 1.f / lh[h] : 0.f;
+      char* orow = static_cast<char*>(a.out) + ((size_t)rr.qrow * a.Hq + head0 + h) * D * C::ES;
+#pragma unroll
+      for (int r = 0; r < C::RPL; ++r) {
+        const int d = lane + 64 * r;
+        const float val = o[h][r] * inv;
+        if constexpr (C::kBf16) {
+          reinterpret_cast<uint16_t*>(orow)[d] = (uint16_t)f32_to_bf16_bits(val);
+        } else {
+          reinterpret_cast<float*>(orow)[d] = val;
+        }
+      }
+    }
+  } else {
+    const size_t unit = ((size_t)slot * HG + hg) * a.P + p;
+    float* wo = a.ws_o + unit * GP * D;
+#pragma unroll
+    for (int h = 0; h < GP; ++h)
+#pragma unroll
+      for (int r = 0; r < C::RPL; ++r) wo[h * D + lane + 64 * r] = o[h][r];
+    if (lane < GP) {
+      a.ws_ml[unit * GP * 2 + 2 * lane] = mh[lane];
+      a.ws_ml[unit * GP * 2 + 2 * lane + 1] = lh[lane];
+    }
+  }
+}
+
+// One work-group (one wave) per (row slot, query head): log-sum-exp merge of
+// the row's partitions in fixed order.
+template <typename E, int D, int GP>
+__global__ __launch_bounds__(64) void row_merge_kernel(const RowAttnArgs a) {
+  constexpr int ES = E::kBytes;
+  const int lane = threadIdx.x;
+  const int h = blockIdx.x % a.Hq;
+  const int slot = blockIdx.x / a.Hq;
+  RowRange rr;
+  if (!row_range(a, slot, rr)) return;
+  if (rr.nparts <= 1) return;
+  const int kvh = h / a.g;
+  const int hin = h - kvh * a.g;
+  const int hg = kvh * a.NG + hin / GP;
+  const int hs = hin % GP;
+  const int HG = a.Hkv * a.NG;
+  const size_t unit0 = ((size_t)slot * HG + hg) * a.P;
+
+  float M = kNegInf;
+  for (int p = 0; p < rr.nparts; ++p) M = fmaxf(M, a.ws_ml[(unit0 + p) * GP * 2 + 2 * hs]);
+  float L = 0.f;
+  float acc[D / 64];
+#pragma unroll
+  for (int r = 0; r < D / 64; ++r) acc[r] = 0.f;
+  if (M != kNegInf) {
+    for (int p = 0; p < rr.nparts; ++p) {
+      const float mp = a.ws_ml[(unit0 + p) * GP * 2 + 2 * hs];
+      const float lp = a.ws_ml[(unit0 + p) * GP * 2 + 2 * hs + 1];
+      const float w = fast_exp2(mp - M);
+      L += w * lp;
+      const float* op = a.ws_o + ((unit0 + p) * GP + hs) * D;
+#pragma unroll
+      for (int r = 0; r < D / 64; ++r) acc[r] = fmaf(w, op[lane + 64 * r], acc[r]);
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  char* orow = static_cast<char*>(a.out) + ((size_t)rr.qrow * a.Hq + h) * D * ES;
+#pragma unroll
+  for (int r = 0; r < D / 64; ++r) {
+    const int d = lane + 64 * r;
+    if constexpr (ES == 2) {
+      reinterpret_cast<uint16_t*>(orow)[d] = (uint16_t)f32_to_bf16_bits(acc[r] * inv);
+    } else {
+      reinterpret_cast<float*>(orow)[d] = acc[r] * inv;
+    }
+  }
+}
+
+template <typename E, int D, int GP>
+hipError_t launch_partials_t(const RowAttnArgs& a, bool mods, hipStream_t s) {
+  const long long blocks = (long long)a.num_seqs * a.max_q_len * a.Hkv * a.NG * a.P;
+  if (blocks <= 0) return hipSuccess;
+  if (mods) {
+    hipLaunchKernelGGL((row_partials_kernel<E, D, GP, true>), dim3((unsigned)blocks), dim3(64), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((row_partials_kernel<E, D, GP, false>), dim3((unsigned)blocks), dim3(64), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+template <typename E, int D, int GP>
+hipError_t launch_merge_t(const RowAttnArgs& a, hipStream_t s) {
+  const long long blocks = (long long)a.num_seqs * a.max_q_len * a.Hq;
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL((row_merge_kernel<E, D, GP>), dim3((unsigned)blocks), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+template <typename E, int D>
+hipError_t dispatch_gp(const RowAttnArgs& a, bool merge, bool mods, hipStream_t s) {
+  const int GP = a.g <= 4 ? 4 : 8;
+  if (GP == 4) return merge ? launch_merge_t<E, D, 4>(a, s) : launch_partials_t<E, D, 4>(a, mods, s);
+  return merge ? launch_merge_t<E, D, 8>(a, s) : launch_partials_t<E, D, 8>(a, mods, s);
+}
+
+template <typename E>
+hipError_t dispatch_d(const RowAttnArgs& a, int D, bool merge, bool mods, hipStream_t s) {
+  if (D == 64) return dispatch_gp<E, 64>(a, merge, mods, s);
+  return dispatch_gp<E, 128>(a, merge, mods, s);
+}
+
+bool has_mods(const RowAttnArgs& a) { return a.softcap > 0.f || a.alibi != nullptr; }
+
+}  // namespace
+
+hipError_t launch_row_partials(const RowAttnArgs& a, int dtype, int D, hipStream_t s) {
+  return dtype == 1 ? dispatch_d<BF16>(a, D, false, has_mods(a), s)
+                    : dispatch_d<F32>(a, D, false, has_mods(a), s);
+}
+
+hipError_t launch_row_merge(const RowAttnArgs& a, int dtype, int D, hipStream_t s) {
+  return dtype == 1 ? dispatch_d<BF16>(a, D, true, false, s) : dispatch_d<F32>(a, D, true, false, s);
+}
+
+}  // namespace pa

@@ -1,0 +1,49 @@
+// kv_append: store new tokens' key/value vectors in the paged cache.
+//
+// A growing sequence writes its new tokens into the blocks it owns (possibly
+// freshly allocated ones) and nothing already stored moves ("Ultimate Guide
+// to PagedAttention", newline: KV cache and dynamic growth).  Token t goes to
+// slot s = slot_mapping[t]: block s >> log2(bs), offset s & (bs - 1).  The
+// copy is of raw bits.  One wavefront per (token, kv-head).
+#include "pa_device.h"
+#include "pa_kernels.h"
+
+namespace pa {
+namespace {
+
+template <typename W>  // W: uint16_t (bf16) or uint32_t (fp32) -- a raw element
+__global__ __launch_bounds__(64) void kv_append_kernel(const AppendArgs a) {
+  const int t = blockIdx.x / a.Hkv;
+  const int h = blockIdx.x - t * a.Hkv;
+  const int slot = a.slots[t];
+  if (slot < 0) return;
+  const int bs = 1 << a.bs_log2;
+  const int blk = slot >> a.bs_log2;
+  const int off = slot & (bs - 1);
+  const int D = a.D;
+  const size_t slab = ((size_t)blk * a.Hkv + h) * (size_t)bs * D;  // elements
+  const size_t src = ((size_t)t * a.Hkv + h) * D;
+  const W* kn = static_cast<const W*>(a.k_new) + src;
+  const W* vn = static_cast<const W*>(a.v_new) + src;
+  W* kc = static_cast<W*>(a.k_cache) + slab + (size_t)off * D;  // row of bs x D slab
+  W* vc = static_cast<W*>(a.v_cache) + slab + off;              // column of D x bs slab
+  for (int d = threadIdx.x; d < D; d += 64) {
+    kc[d] = kn[d];
+    vc[(size_t)d * bs] = vn[d];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_kv_append(const AppendArgs& a, int dtype, hipStream_t s) {
+  const long long blocks = (long long)a.T * a.Hkv;
+  if (blocks <= 0) return hipSuccess;
+  if (dtype == 1) {
+    hipLaunchKernelGGL(kv_append_kernel<uint16_t>, dim3((unsigned)blocks), dim3(64), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(kv_append_kernel<uint32_t>, dim3((unsigned)blocks), dim3(64), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,279 @@
+// Paged (chunked) prefill on CDNA4 matrix cores, bf16 in / fp32 accumulate.
+//
+// A chunk of query rows per sequence attends to the sequence's paged context
+// (the chunk's own keys are appended first).  The kernel gathers each key tile
+// from the blocks the block table names, straight into LDS, and never builds a
+// contiguous K/V copy (Joshi et al., "Paged Attention Meets FlexAttention",
+// abstract: the fused kernel gathers scattered KV data; "Ultimate Guide to
+// PagedAttention": block table).  Attention is exact, computed tile by tile
+// with an online softmax (Dao et al., "FlashAttention", abstract).
+//
+// Work-group: 4 wavefronts, 128 query rows = QT = 128/g query positions x the
+// g query heads of one kv-head, so every K/V tile read from HBM serves all g
+// heads (GQA).  Per 64-key tile:
+//   S^T = K Q^T   with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q^T
+//                 kept in registers); each lane then owns one query row's
+//                 scores, so softmax statistics are per-lane scalars;
+//   O^T += V^T P^T with the same MFMA (A = V^T rows from LDS -- V slabs are
+//                 dimension-major in the pool, so no transpose is needed --
+//                 B = P^T straight from the S^T accumulators, rounded to bf16).
+// The K rows of the S^T product are read in a permuted order inside each
+// 16-key group (quarters 1 and 2 swapped) so that the accumulator registers
+// a lane holds are exactly the 8 consecutive keys the next MFMA's B operand
+// needs; no shuffles between the two products.
+#include "pa_device.h"
+#include "pa_kernels.h"
+
+namespace pa {
+namespace {
+
+constexpr float kLazyRescale = 8.0f;  // log2 units
+constexpr int kTileKeys = 64;
+constexpr int kRowsPerWG = 128;
+
+// key slot (0..31) of a 32-key group -> key offset inside the group
+__device__ __forceinline__ int key_of_slot(int u) {
+  const int q = (u >> 2) & 3;
+  const int qs = ((q & 1) << 1) | ((q >> 1) & 1);
+  return (u & 16) | (qs << 2) | (u & 3);
+}
+
+template <int D, bool kMods>
+__global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) {
+  constexpr int KCH = D / 8;   // 16-byte chunks per K row
+  constexpr int KSTEPS = D / 16;
+  constexpr int DT = D / 32;   // output 32-dim tiles
+  __shared__ u32x4 k_lds[kTileKeys * KCH];
+  __shared__ u32x4 v_lds[D * (kTileKeys / 8)];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int hl = lane >> 5;      // half of the wave
+  const int col = lane & 31;     // query row inside the wave's 32 rows
+
+  const int QT = kRowsPerWG / a.g;
+  const int BH = a.num_seqs * a.Hkv;
+  const int flat = blockIdx.x;
+  const int qtile = a.q_tiles - 1 - flat / BH;
+  const int b = (flat % BH) / a.Hkv;
+  const int kvh = flat % a.Hkv;
+
+  const int n = a.context_lens[b];
+  const int q0 = a.cu_q_lens[b];
+  const int Lq = a.cu_q_lens[b + 1] - q0;
+  const int q_start = qtile * QT;
+  if (q_start >= Lq) return;
+
+  // this lane's query row (column of S^T / O^T)
+  const int r = wave * 32 + col;
+  const int head_in = r / QT;
+  const int qi = q_start + (r - head_in * QT);
+  const bool row_ok = qi < Lq;
+  const int pos = n - Lq + qi;
+  int row_hi = row_ok ? (a.causal ? min(n, pos + 1) : n) : 0;
+  int row_lo = (row_ok && a.window > 0) ? max(0, pos - a.window + 1) : 0;
+  if (row_lo > row_hi) row_lo = row_hi;
+  const int head = kvh * a.g + head_in;
+
+  // key range of the whole work-group (uniform)
+  const int q_last = min(Lq, q_start + QT) - 1;
+  const int pos_first = n - Lq + q_start;
+  const int pos_last = n - Lq + q_last;
+  const int wg_hi = a.causal ? min(n, pos_last + 1) : n;
+  const int wg_lo = a.window > 0 ? max(0, pos_first - a.window + 1) : 0;
+  const int safe_hi = a.causal ? min(n, pos_first + 1) : n;            // every row admits keys < safe_hi
+  const int safe_lo = a.window > 0 ? max(0, pos_last - a.window + 1) : 0;  // ... and >= safe_lo
+
+  // Q^T operand (B of S^T): this lane's row, dims 16*ks + 8*hl .. +8
+  bf16x8 qb[KSTEPS];
+  {
+    const char* qrow = static_cast<const char*>(a.q) + ((size_t)(q0 + (row_ok ? qi : 0)) * a.Hq + head) * D * 2;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      u32x4 x = row_ok ? load16(qrow + (16 * ks + 8 * hl) * 2) : u32x4{0, 0, 0, 0};
+      qb[ks] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+
+  const float scale_log2 = a.scale * kLog2e;
+  float alibi_slope = 0.f;
+  if constexpr (kMods) {
+    if (a.alibi) alibi_slope = a.alibi[head];
+  }
+
+  f32x16 oacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
+  float m_run = kNegInf, l_run = 0.f;
+
+  const int32_t* table = a.block_tables + (size_t)b * a.bt_stride;
+  const int bs = 1 << a.bs_log2;
+  const size_t slab_bytes = (size_t)bs * D * 2;
+  const char* kpool = static_cast<const char*>(a.k_cache);
+  const char* vpool = static_cast<const char*>(a.v_cache);
+
+  const int k_begin = wg_lo & ~(kTileKeys - 1);
+  for (int k0 = k_begin; k0 < wg_hi; k0 += kTileKeys) {
+    __syncthreads();
+    // ---- gather the K tile (64 rows x D) and the V^T tile (D rows x 64) ----
+#pragma unroll
+    for (int it = 0; it < (kTileKeys * KCH) / 256; ++it) {
+      const int pi = tid + 256 * it;
+      const int key = pi / KCH;
+      const int c = pi % KCH;
+      const int tok = k0 + key;
+      u32x4 x = {0, 0, 0, 0};
+      if (tok < n) {
+        const int blk = table[tok >> a.bs_log2];
+        const char* src = kpool + ((size_t)blk * a.Hkv + kvh) * slab_bytes +
+                          ((size_t)(tok & (bs - 1)) * D + c * 8) * 2;
+        x = load16(src);
+      }
+      k_lds[key * KCH + (c ^ (key & (KCH - 1) & 15))] = x;
+    }
+#pragma unroll
+    for (int it = 0; it < (D * (kTileKeys / 8)) / 256; ++it) {
+      const int pi = tid + 256 * it;
+      const int d = pi >> 3;
+      const int c = pi & 7;  // 8-key chunk
+      const int tok = k0 + 8 * c;
+      u32x4 x = {0, 0, 0, 0};
+      if (tok < n) {
+        const int blk = table[tok >> a.bs_log2];
+        const char* src = vpool + ((size_t)blk * a.Hkv + kvh) * slab_bytes +
+                          ((size_t)d * bs + (tok & (bs - 1))) * 2;
+        x = load16(src);
+        if (tok + 8 > n) {  // keys past the end may hold anything
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const int j = tok + 2 * w;
+            x[w] &= (j < n ? 0xffffu : 0u) | (j + 1 < n ? 0xffff0000u : 0u);
+          }
+        }
+      }
+      v_lds[d * 8 + (c ^ (d & 7))] = x;
+    }
+    __syncthreads();
+
+    // ---- S^T = K Q^T : two 32-key groups ----
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[kg][i] = 0.f;
+      const int krow = 32 * kg + key_of_slot(col);
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const int c = 2 * ks + hl;
+        const bf16x8 ka = __builtin_bit_cast(bf16x8, k_lds[krow * KCH + (c ^ (krow & (KCH - 1) & 15))]);
+        sacc[kg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[ks], sacc[kg], 0, 0, 0);
+      }
+    }
+
+    // ---- scores (log2 domain), masks ----
+    const bool full = (k0 >= safe_lo) && (k0 + kTileKeys <= safe_hi);
+    float cmax = kNegInf;
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int slot = 8 * (i >> 2) + 4 * hl + (i & 3);
+        const int key = k0 + 32 * kg + key_of_slot(slot);
+        float sv;
+        if constexpr (kMods) {
+          float x = sacc[kg][i] * a.scale;
+          if (a.softcap > 0.f) {
+            const float ez = fast_exp2(2.f * kLog2e * (x / a.softcap));
+            x = a.softcap * (1.f - 2.f / (ez + 1.f));
+          }
+          x += alibi_slope * (float)(key - pos);
+          sv = x * kLog2e;
+        } else {
+          sv = sacc[kg][i] * scale_log2;
+        }
+        if (!full) sv = (key >= row_lo && key < row_hi) ? sv : kNegInf;
+        sacc[kg][i] = sv;
+        cmax = fmaxf(cmax, sv);
+      }
+    }
+    cmax = fmaxf(cmax, shfl_xor32(cmax));
+    const float m_new = fmaxf(m_run, cmax);
+    const bool need = m_new > m_run + kLazyRescale;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
+      if (need) m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+    }
+    const float msafe = (m_run == kNegInf) ? 0.f : m_run;
+
+    // ---- P (bf16) as the B operand of O^T += V^T P^T ----
+    bf16x8 pb[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 w;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p0 = fast_exp2(sacc[s >> 1][8 * (s & 1) + 2 * j] - msafe);
+        const float p1 = fast_exp2(sacc[s >> 1][8 * (s & 1) + 2 * j + 1] - msafe);
+        const uint32_t packed = pack_bf16x2(p0, p1);
+        l_run += bf16lo(packed) + bf16hi(packed);
+        w[j] = packed;
+      }
+      pb[s] = __builtin_bit_cast(bf16x8, w);
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int d = 32 * dt + col;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int c = 2 * s + hl;
+        const bf16x8 va = __builtin_bit_cast(bf16x8, v_lds[d * 8 + (c ^ (d & 7))]);
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[s], oacc[dt], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- normalise and store: lane holds row `r`, dims 32dt + 8(i/4) + 4hl + i%4 ----
+  const float l_tot = l_run + shfl_xor32(l_run);
+  if (!row_ok) return;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  char* orow = static_cast<char*>(a.out) + ((size_t)(q0 + qi) * a.Hq + head) * D * 2;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const int d = 32 * dt + 8 * g4 + 4 * hl;
+      uint2 w;
+      w.x = pack_bf16x2(oacc[dt][4 * g4 + 0] * inv, oacc[dt][4 * g4 + 1] * inv);
+      w.y = pack_bf16x2(oacc[dt][4 * g4 + 2] * inv, oacc[dt][4 * g4 + 3] * inv);
+      *reinterpret_cast<uint2*>(orow + d * 2) = w;
+    }
+  }
+}
+
+}  // namespace
+
+int prefill_rows_per_tile(int g) { return kRowsPerWG / g; }
+
+hipError_t launch_prefill_mfma(const PrefillArgs& a, int D, hipStream_t s) {
+  const long long blocks = (long long)a.num_seqs * a.Hkv * a.q_tiles;
+  if (blocks <= 0) return hipSuccess;
+  const bool mods = a.softcap > 0.f || a.alibi != nullptr;
+  if (D == 64) {
+    if (mods) hipLaunchKernelGGL((prefill_mfma_kernel<64, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((prefill_mfma_kernel<64, false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+  } else {
+    if (mods) hipLaunchKernelGGL((prefill_mfma_kernel<128, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((prefill_mfma_kernel<128, false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -22,3 +22,11 @@ def gpu_lib():
     from paged_kv_cache_attn_amd import binding
 
     return binding
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    """Name each test on the real stderr before it runs (survives a hard GPU fault)."""
+    sys.__stderr__.write(f"\n[start] {request.node.nodeid}\n")
+    sys.__stderr__.flush()
+    yield

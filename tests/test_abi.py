@@ -1,0 +1,160 @@
+"""The C-ABI library on the host: it loads, exports what the header declares,
+and rejects invalid arguments with the documented codes before any HIP call.
+No compute is launched here (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_kv_cache_attn_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagedattn.h")
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+NULL = None
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "defined")))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ["kv_append", "paged_attn_decode", "paged_attn_prefill", "paged_attn_decode_partials",
+              "paged_attn_decode_merge", "paged_attn_decode_workspace_size", "paged_attn_decode_split_tokens",
+              "paged_attn_status_string"]:
+        assert n in names, n
+    assert set(names) == set(binding.SIGNATURES), names
+
+
+def test_library_exports_every_declared_symbol():
+    L = binding.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    out = os.popen(f"nm -D --defined-only {binding.lib_path()}").read()
+    exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
+    assert set(declared_functions()) <= exported
+
+
+def test_status_strings():
+    assert binding.status_string(0) == "ok"
+    for code in range(-11, 0):
+        s = binding.status_string(code)
+        assert s and s != "unknown status", code
+    assert binding.status_string(-99) == "unknown status"
+
+
+def _append(**over):
+    a = dict(k_new=FAKE, v_new=FAKE, k_cache=FAKE, v_cache=FAKE, slots=FAKE, T=4, Hkv=8, D=128, bs=16, NB=10,
+             dtype=1)
+    a.update(over)
+    return binding.lib().kv_append(a["k_new"], a["v_new"], a["k_cache"], a["v_cache"], a["slots"], a["T"],
+                                   a["Hkv"], a["D"], a["bs"], a["NB"], a["dtype"], None)
+
+
+def test_kv_append_validation():
+    assert _append(dtype=2) == -8
+    assert _append(T=-1) == -2
+    assert _append(NB=-1) == -2
+    assert _append(Hkv=0) == -3
+    assert _append(D=96) == -4
+    assert _append(bs=8) == -5
+    assert _append(bs=24) == -5
+    assert _append(bs=512) == -5
+    assert _append(k_cache=NULL) == -1
+    assert _append(slots=NULL) == -1
+    assert _append(T=0, k_new=NULL, v_new=NULL, k_cache=NULL, v_cache=NULL, slots=NULL) == 0  # no-op
+
+
+def _decode(fn="paged_attn_decode", **over):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, stride=4, ctx=FAKE, B=2, Hq=32, Hkv=8, D=128, bs=16, NB=100,
+             max_ctx=64, scale=0.1, split=0, mods=None, ws=FAKE, ws_bytes=1 << 40, dtype=1)
+    a.update(over)
+    L = binding.lib()
+    if fn == "paged_attn_decode_merge":
+        return L.paged_attn_decode_merge(a["out"], a["ctx"], a["B"], a["Hq"], a["Hkv"], a["D"], a["max_ctx"],
+                                         a["split"], a["mods"], a["ws"], a["ws_bytes"], a["dtype"], None)
+    return getattr(L, fn)(a["out"], a["q"], a["k"], a["v"], a["bt"], a["stride"], a["ctx"], a["B"], a["Hq"],
+                          a["Hkv"], a["D"], a["bs"], a["NB"], a["max_ctx"], a["scale"], a["split"], a["mods"],
+                          a["ws"], a["ws_bytes"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("fn", ["paged_attn_decode", "paged_attn_decode_partials"])
+def test_decode_validation(fn):
+    assert _decode(fn, dtype=5) == -8
+    assert _decode(fn, B=-1) == -2
+    assert _decode(fn, max_ctx=-3) == -2
+    assert _decode(fn, Hq=30) == -3
+    assert _decode(fn, Hkv=0) == -3
+    assert _decode(fn, D=256) == -4
+    assert _decode(fn, bs=48) == -5
+    assert _decode(fn, split=100) == -6
+    assert _decode(fn, split=8) == -6
+    assert _decode(fn, split=-2) == -6
+    assert _decode(fn, stride=0) == -11
+    assert _decode(fn, q=NULL) == -1
+    assert _decode(fn, bt=NULL) == -1
+    assert _decode(fn, max_ctx=4096, ws=NULL) == -7
+    assert _decode(fn, max_ctx=4096, ws_bytes=16) == -7
+    bad = binding.ScoreMods(-1, 0.0, None)
+    assert _decode(fn, mods=ctypes.pointer(bad)) == -10
+    bad = binding.ScoreMods(0, float("nan"), None)
+    assert _decode(fn, mods=ctypes.pointer(bad)) == -10
+    bad = binding.ScoreMods(0, float("inf"), None)
+    assert _decode(fn, mods=ctypes.pointer(bad)) == -10
+    assert _decode(fn, B=0) == 0  # nothing to do, nothing launched
+
+
+def test_merge_validation():
+    assert _decode("paged_attn_decode_merge", dtype=9) == -8
+    assert _decode("paged_attn_decode_merge", out=NULL) == -1
+    assert _decode("paged_attn_decode_merge", max_ctx=4096, ws=NULL) == -7
+
+
+def _prefill(**over):
+    a = dict(out=FAKE, q=FAKE, cu=FAKE, k=FAKE, v=FAKE, bt=FAKE, stride=4, ctx=FAKE, B=2, maxq=16, Hq=32, Hkv=8,
+             D=128, bs=16, NB=100, scale=0.1, causal=1, mods=None, dtype=1)
+    a.update(over)
+    return binding.lib().paged_attn_prefill(a["out"], a["q"], a["cu"], a["k"], a["v"], a["bt"], a["stride"],
+                                            a["ctx"], a["B"], a["maxq"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["NB"],
+                                            a["scale"], a["causal"], a["mods"], a["dtype"], None)
+
+
+def test_prefill_validation():
+    assert _prefill(dtype=3) == -8
+    assert _prefill(B=-2) == -2
+    assert _prefill(maxq=-1) == -2
+    assert _prefill(Hq=12, Hkv=8) == -3
+    assert _prefill(D=32) == -4
+    assert _prefill(bs=1024) == -5
+    assert _prefill(causal=2) == -9
+    assert _prefill(stride=0) == -11
+    assert _prefill(cu=NULL) == -1
+    assert _prefill(v=NULL) == -1
+    bad = binding.ScoreMods(0, -1.0, None)
+    assert _prefill(mods=ctypes.pointer(bad)) == -10
+    assert _prefill(maxq=0) == 0
+    assert _prefill(B=0) == 0
+
+
+def test_split_resolution_and_workspace_size():
+    # explicit split sizes are taken as given; -1 never splits
+    assert binding.decode_split_tokens(64, 8, 32768, 512) == 512
+    assert binding.decode_split_tokens(64, 8, 32768, -1) == -1
+    assert binding.decode_split_tokens(64, 8, 32768, 100) == 0  # invalid
+    # automatic: 512 when there is enough parallelism, smaller for short/few rows
+    assert binding.decode_split_tokens(64, 8, 32768) == 512
+    assert binding.decode_split_tokens(8, 8, 2048) == 64
+    # workspace: B * Hkv * ceil(g/GP)*GP * P * (D + 2) * 4 bytes, 0 when unsplit
+    assert binding.decode_workspace_size(64, 64, 8, 128, 32768, 512) == 64 * 8 * 8 * 64 * 130 * 4
+    assert binding.decode_workspace_size(8, 32, 8, 128, 2048, 512) == 8 * 8 * 4 * 4 * 130 * 4
+    assert binding.decode_workspace_size(8, 32, 8, 128, 2048, -1) == 0
+    assert binding.decode_workspace_size(8, 32, 8, 128, 512, 512) == 0
+    assert binding.decode_workspace_size(1, 4, 4, 64, 128, 64) == 1 * 4 * 1 * 4 * 2 * 66 * 4
+    assert binding.decode_workspace_size(8, 30, 8, 128, 2048, 0) == 0  # invalid heads

@@ -1,0 +1,341 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances (max-abs error of the output against the fp64 oracle): 2e-2 for
+bf16 inputs with fp32 accumulation, 1e-4 for fp32; kv_append is bit-exact
+over the whole pool.  Invariances that the pages state (scattered placement
+and shared blocks give the same result) are checked bit for bit.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.paged import bits_to_f64
+from workloads import build_workload, config_workload
+from workloads.device import to_numpy_bits, to_tensor, upload
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 2e-2, "f32": 1e-4}
+
+
+# ------------------------------------------------------------------------------------------
+# helpers
+# ------------------------------------------------------------------------------------------
+
+def appended_pools(w):
+    if len(w.slot_mapping) == 0:
+        return w.k_pool, w.v_pool
+    return oracle.kv_append(w.k_pool, w.v_pool, w.k_new, w.v_new, w.slot_mapping, w.bs)
+
+
+def oracle_out(w, mods=None, seqs=None, causal=None):
+    kp, vp = appended_pools(w)
+    m = mods or oracle.ScoreMods()
+    if causal is not None:
+        m = oracle.ScoreMods(causal=causal, window=m.window, softcap=m.softcap, alibi_slopes=m.alibi_slopes)
+    return oracle.paged_attention(w.q, kp, vp, w.block_table, w.context_lens, w.cu_q_lens, w.scale, w.bs,
+                                  w.dtype, m, seqs=seqs)
+
+
+def gpu_decode(lib, w, t=None, split=0, phase="both", **mods):
+    t = t or upload(w)
+    if len(w.slot_mapping):
+        lib.kv_append(t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], t["slot_mapping"])
+    out = torch.empty_like(t["q"])
+    if phase == "both":
+        lib.paged_attn_decode(out, t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                              w.scale, w.max_context_len, split, **mods)
+    else:
+        ws = lib.decode_workspace(t["q"], w.Hkv, w.max_context_len, split)
+        lib.paged_attn_decode(out, t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                              w.scale, w.max_context_len, split, workspace=ws, phase="partials", **mods)
+        lib.paged_attn_decode(out, t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                              w.scale, w.max_context_len, split, workspace=ws, phase="merge", **mods)
+    torch.cuda.synchronize()
+    return to_numpy_bits(out)
+
+
+def gpu_prefill(lib, w, t=None, causal=True, **mods):
+    t = t or upload(w)
+    if len(w.slot_mapping):
+        lib.kv_append(t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], t["slot_mapping"])
+    out = torch.empty_like(t["q"])
+    lib.paged_attn_prefill(out, t["q"], t["cu_q_lens"], t["k_cache"], t["v_cache"], t["block_tables"],
+                           t["context_lens"], w.scale, w.max_q_len, causal, **mods)
+    torch.cuda.synchronize()
+    return to_numpy_bits(out)
+
+
+def assert_close(gpu_bits, ref, dtype, rows=None, tol=None):
+    got = bits_to_f64(gpu_bits, dtype)
+    if rows is not None:
+        got, ref = got[rows], ref[rows]
+    assert np.all(np.isfinite(got)), "non-finite output"
+    err = np.max(np.abs(got - ref)) if got.size else 0.0
+    assert err <= (tol or TOL[dtype]), f"max abs err {err}"
+    return err
+
+
+def small(kind="decode", seed=100, dtype="bf16", ctx=(37, 300, 1000), Hq=32, Hkv=8, D=128, bs=16, q_lens=None,
+          append=None, causal=False, shared=0, NB=None):
+    return build_workload(name="t", seed=seed, kind=kind, dtype=dtype, Hq=Hq, Hkv=Hkv, D=D, bs=bs,
+                          context_lens=list(ctx), q_lens=q_lens, append_lens=append, causal=causal,
+                          shared_prefix_blocks=shared, NB=NB)
+
+
+# ------------------------------------------------------------------------------------------
+# kv_append
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("case", ["config2", "config3", "bs64_f32", "negative_slots"])
+def test_kv_append_bit_exact(gpu_lib, case):
+    if case == "config2":
+        w = config_workload(2)
+    elif case == "config3":
+        w = config_workload(3)
+    elif case == "bs64_f32":
+        w = small(dtype="f32", bs=64, ctx=(200, 129), append=[70, 129], D=64, Hq=8, Hkv=2)
+    else:
+        w = small(ctx=(40, 50), append=[5, 9])
+        w.slot_mapping[::3] = -1
+    t = upload(w)
+    gpu_lib.kv_append(t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], t["slot_mapping"])
+    torch.cuda.synchronize()
+    kp, vp = oracle.kv_append(w.k_pool, w.v_pool, w.k_new, w.v_new, w.slot_mapping, w.bs)
+    ik = np.uint16 if w.dtype == "bf16" else np.uint32
+    assert np.array_equal(to_numpy_bits(t["k_cache"]).view(ik), kp.view(ik))
+    assert np.array_equal(to_numpy_bits(t["v_cache"]).view(ik), vp.view(ik))
+
+
+# ------------------------------------------------------------------------------------------
+# the five workloads
+# ------------------------------------------------------------------------------------------
+
+def test_config1_decode_f32(gpu_lib):
+    w = config_workload(1)
+    for split in (0, -1, 16):
+        assert_close(gpu_decode(gpu_lib, w, split=split), oracle_out(w), "f32")
+
+
+def test_config2_gqa_decode_with_append(gpu_lib):
+    w = config_workload(2)
+    ref = oracle_out(w)
+    for split in (0, 512, -1):
+        assert_close(gpu_decode(gpu_lib, w, split=split), ref, "bf16")
+
+
+def test_config3_chunked_prefill(gpu_lib):
+    w = config_workload(3)
+    assert_close(gpu_prefill(gpu_lib, w), oracle_out(w, causal=True), "bf16")
+
+
+def test_config4_shared_prefix_decode(gpu_lib):
+    w = config_workload(4)
+    assert_close(gpu_decode(gpu_lib, w), oracle_out(w), "bf16")
+
+
+def test_config5_long_decode_subset(gpu_lib):
+    w = config_workload(5, batch=6)
+    assert_close(gpu_decode(gpu_lib, w, split=512), oracle_out(w), "bf16")
+
+
+@pytest.mark.parametrize("bs", [32, 64, 128, 256])
+def test_config5_page_size_variants_subset(gpu_lib, bs):
+    w = config_workload(5, bs=bs, batch=4)
+    assert_close(gpu_decode(gpu_lib, w, split=512), oracle_out(w), "bf16")
+
+
+def test_config5_full_size_sampled(gpu_lib):
+    """Full 64-sequence workload, split 512 (the benchmarked launch); the oracle
+    checks a sample of sequences: the shortest, the longest and a few others."""
+    w = config_workload(5)
+    got = gpu_decode(gpu_lib, w, split=512)
+    order = np.argsort(w.context_lens)
+    seqs = sorted(set([int(order[0]), int(order[-1]), int(order[len(order) // 2]), 3, 17, 42]))
+    ref = oracle_out(w, seqs=seqs)
+    assert_close(got, ref, "bf16", rows=seqs)
+    assert np.all(np.isfinite(bits_to_f64(got, "bf16")))
+
+
+# ------------------------------------------------------------------------------------------
+# invariances and special cases on the GPU
+# ------------------------------------------------------------------------------------------
+
+def test_block_permutation_bit_identical(gpu_lib):
+    w = small(ctx=(700, 45, 1300), append=[1, 1, 1])
+    base = gpu_decode(gpu_lib, w)
+    perm = np.random.default_rng(1).permutation(w.NB)
+    for pool in ("k_pool", "v_pool"):
+        p = np.empty_like(getattr(w, pool))
+        p[perm] = getattr(w, pool)
+        setattr(w, pool, p)
+    w.block_table = np.where(w.block_table >= 0, perm[np.maximum(w.block_table, 0)], -1).astype(np.int32)
+    w.slot_mapping = (perm[w.slot_mapping // w.bs] * w.bs + w.slot_mapping % w.bs).astype(np.int32)
+    assert np.array_equal(gpu_decode(gpu_lib, w), base)
+
+
+def test_prefill_block_permutation_bit_identical(gpu_lib):
+    w = small("prefill", ctx=(300, 520), q_lens=[77, 130], causal=True)
+    base = gpu_prefill(gpu_lib, w)
+    perm = np.random.default_rng(2).permutation(w.NB)
+    for pool in ("k_pool", "v_pool"):
+        p = np.empty_like(getattr(w, pool))
+        p[perm] = getattr(w, pool)
+        setattr(w, pool, p)
+    w.block_table = np.where(w.block_table >= 0, perm[np.maximum(w.block_table, 0)], -1).astype(np.int32)
+    assert np.array_equal(gpu_prefill(gpu_lib, w), base)
+
+
+def test_shared_prefix_equals_private_copies(gpu_lib):
+    w = config_workload(4, batch=4)
+    base = gpu_decode(gpu_lib, w)
+    S = int(w.meta["shared_prefix_blocks"])
+    kp = np.concatenate([w.k_pool, w.k_pool[w.block_table[:, :S].ravel()]])
+    vp = np.concatenate([w.v_pool, w.v_pool[w.block_table[:, :S].ravel()]])
+    table = w.block_table.copy()
+    table[:, :S] = (w.NB + np.arange(w.B * S)).reshape(w.B, S)
+    w.k_pool, w.v_pool, w.block_table, w.NB = kp, vp, table.astype(np.int32), kp.shape[0]
+    assert np.array_equal(gpu_decode(gpu_lib, w), base)
+
+
+def test_one_token_context_returns_v_row_exactly(gpu_lib):
+    w = small(ctx=(1, 1, 1), append=[1, 1, 1])
+    got = gpu_decode(gpu_lib, w)
+    g = w.Hq // w.Hkv
+    for b in range(w.B):
+        assert np.array_equal(got[b], np.repeat(w.v_new[b], g, axis=0))
+
+
+def test_deterministic_bits(gpu_lib):
+    w = config_workload(2)
+    t = upload(w)
+    a = gpu_decode(gpu_lib, w, t=t)
+    b = gpu_decode(gpu_lib, w, t=t)
+    assert np.array_equal(a, b)
+    w3 = config_workload(3, batch=2)
+    t3 = upload(w3)
+    assert np.array_equal(gpu_prefill(gpu_lib, w3, t=t3), gpu_prefill(gpu_lib, w3, t=t3))
+
+
+@pytest.mark.parametrize("split", [-1, 16, 64, 512])
+def test_split_invariance(gpu_lib, split):
+    w = small(ctx=(1500, 333, 2048, 17), append=[1, 1, 1, 1])
+    assert_close(gpu_decode(gpu_lib, w, split=split), oracle_out(w), "bf16")
+
+
+def test_two_phase_calls_equal_single_call(gpu_lib):
+    w = small(ctx=(1500, 333, 2048, 17), append=[1, 1, 1, 1])
+    assert np.array_equal(gpu_decode(gpu_lib, w, split=64, phase="two"), gpu_decode(gpu_lib, w, split=64))
+
+
+def test_decode_equals_prefill_with_one_row(gpu_lib):
+    w = small(ctx=(900, 31, 256), append=[1, 1, 1])
+    dec = gpu_decode(gpu_lib, w)
+    wp = small(ctx=(900, 31, 256), append=[1, 1, 1])
+    wp.kind = "prefill"
+    pre = gpu_prefill(gpu_lib, wp, causal=True)
+    assert np.max(np.abs(bits_to_f64(dec, "bf16") - bits_to_f64(pre, "bf16"))) <= 2e-2
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 4), (16, 4), (32, 8), (64, 8), (128, 8), (24, 8)])
+def test_gqa_group_sizes(gpu_lib, Hq, Hkv):
+    w = small(ctx=(129, 700), Hq=Hq, Hkv=Hkv, append=[1, 1])
+    assert_close(gpu_decode(gpu_lib, w), oracle_out(w), "bf16")
+    wp = small("prefill", ctx=(129, 300), q_lens=[40, 129], Hq=Hq, Hkv=Hkv, causal=True)
+    assert_close(gpu_prefill(gpu_lib, wp), oracle_out(wp, causal=True), "bf16")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_head_dims_and_dtypes(gpu_lib, dtype, D):
+    w = small(dtype=dtype, D=D, ctx=(77, 640), append=[1, 1])
+    assert_close(gpu_decode(gpu_lib, w), oracle_out(w), dtype)
+    wp = small("prefill", dtype=dtype, D=D, ctx=(64, 200), q_lens=[64, 57], causal=True)
+    assert_close(gpu_prefill(gpu_lib, wp), oracle_out(wp, causal=True), dtype)
+
+
+@pytest.mark.parametrize("bs", [16, 32, 64, 128, 256])
+def test_block_sizes_ragged(gpu_lib, bs):
+    w = small(bs=bs, ctx=(1, 15, 16, 17, 255, 257, 1000), append=[1] * 7)
+    assert_close(gpu_decode(gpu_lib, w), oracle_out(w), "bf16")
+    wp = small("prefill", bs=bs, ctx=(1, 65, 300), q_lens=[1, 65, 99], causal=True)
+    assert_close(gpu_prefill(gpu_lib, wp), oracle_out(wp, causal=True), "bf16")
+
+
+def test_empty_context_gives_zero(gpu_lib):
+    w = small(ctx=(0, 5, 0))
+    got = bits_to_f64(gpu_decode(gpu_lib, w), "bf16")
+    assert np.all(got[0] == 0) and np.all(got[2] == 0)
+    assert_close(gpu_decode(gpu_lib, w), oracle_out(w), "bf16")
+
+
+def test_non_causal_prefill(gpu_lib):
+    wp = small("prefill", ctx=(100, 300), q_lens=[30, 300])
+    assert_close(gpu_prefill(gpu_lib, wp, causal=False), oracle_out(wp, causal=False), "bf16")
+
+
+def test_chunk_rows_equal_full_prefill_rows(gpu_lib):
+    full = small("prefill", ctx=(600,), q_lens=[600], causal=True, seed=7)
+    chunk = small("prefill", ctx=(600,), q_lens=[200], causal=True, seed=7)
+    assert np.array_equal(chunk.k_pool, full.k_pool)
+    chunk.q = full.q[400:]
+    a = bits_to_f64(gpu_prefill(gpu_lib, full), "bf16")[400:]
+    b = bits_to_f64(gpu_prefill(gpu_lib, chunk), "bf16")
+    assert np.max(np.abs(a - b)) <= 2e-2
+
+
+@pytest.mark.parametrize("mods", ["window", "softcap", "alibi", "all"])
+def test_score_mods(gpu_lib, mods):
+    Hq, Hkv = 16, 4
+    slopes = (2.0 ** -np.arange(1, Hq + 1) * 0.5).astype(np.float32)
+    kw, om = {}, {}
+    if mods in ("window", "all"):
+        kw["window"] = om["window"] = 100
+    if mods in ("softcap", "all"):
+        kw["softcap"] = om["softcap"] = 0.5
+    if mods in ("alibi", "all"):
+        kw["alibi_slopes"] = torch.from_numpy(slopes).cuda()
+        om["alibi_slopes"] = slopes.astype(np.float64)
+    w = small(ctx=(90, 700, 1300), Hq=Hq, Hkv=Hkv, append=[1, 1, 1])
+    assert_close(gpu_decode(gpu_lib, w, **kw), oracle_out(w, oracle.ScoreMods(**om)), "bf16")
+    wp = small("prefill", ctx=(150, 400), q_lens=[150, 170], Hq=Hq, Hkv=Hkv, causal=True)
+    assert_close(gpu_prefill(gpu_lib, wp, **kw), oracle_out(wp, oracle.ScoreMods(causal=True, **om)), "bf16")
+    wf = small("prefill", dtype="f32", ctx=(150, 400), q_lens=[150, 170], Hq=Hq, Hkv=Hkv, causal=True)
+    assert_close(gpu_prefill(gpu_lib, wf, **kw), oracle_out(wf, oracle.ScoreMods(causal=True, **om)), "f32")
+
+
+def test_pool_beyond_4gib(gpu_lib):
+    """Block ids whose byte offsets exceed 32 bits (64-bit addressing)."""
+    w = small(ctx=(300, 1000), append=[1, 1])
+    base = gpu_decode(gpu_lib, w)
+    NB_big = (5 << 30) // (w.Hkv * w.bs * w.D * 2) + 64  # > 5 GiB per pool
+    used = np.unique(w.block_table[w.block_table >= 0])
+    new_ids = NB_big - 1 - np.arange(len(used))
+    remap = np.full(w.NB, -1, np.int64)
+    remap[used] = new_ids
+    t = upload(w)
+    kb = torch.full((NB_big, w.Hkv, w.bs, w.D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vb = torch.full((NB_big, w.Hkv, w.D, w.bs), float("nan"), dtype=torch.bfloat16, device="cuda")
+    idx_new = torch.from_numpy(new_ids).cuda()
+    idx_old = torch.from_numpy(used.astype(np.int64)).cuda()
+    kb[idx_new] = t["k_cache"][idx_old]
+    vb[idx_new] = t["v_cache"][idx_old]
+    t["k_cache"], t["v_cache"] = kb, vb
+    table = np.where(w.block_table >= 0, remap[np.maximum(w.block_table, 0)], -1).astype(np.int32)
+    t["block_tables"] = to_tensor(table, "i32", "cuda")
+    slots = (remap[w.slot_mapping // w.bs] * w.bs + w.slot_mapping % w.bs).astype(np.int32)
+    t["slot_mapping"] = to_tensor(slots, "i32", "cuda")
+    got = gpu_decode(gpu_lib, w, t=t)
+    del kb, vb
+    assert np.array_equal(got, base)
+
+
+def test_poisoned_table_tail_entries_ignored(gpu_lib):
+    w = small(ctx=(33, 100), append=[1, 1])
+    w.block_table = np.concatenate([w.block_table, np.full((w.B, 8), 2 ** 30, np.int32)], axis=1)
+    w.block_table[w.block_table == -1] = 2 ** 30
+    assert_close(gpu_decode(gpu_lib, w), oracle_out(w), "bf16")
