@@ -1,0 +1,309 @@
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  1. kv_append of one new token per sequence of the long-context decode batch
+     (64 sequences, log-normal contexts around 8192 tokens, 64 query / 8 KV
+     heads, head_dim 128, bf16, 16-token blocks scattered in a ~5.6 GB pool),
+  2. paged decode of that batch with 512-token split-KV partitions
+     (partition kernel, then the merge kernel),
+  3. kv_append of a 512-token chunk for each of 4 sequences, and
+  4. causal chunked prefill of those chunks after their 1536-token contexts
+     (32 query / 8 KV heads, head_dim 128, bf16, matrix cores).
+
+The headline ``value`` is the decode KV-read bandwidth: bytes of K and V the
+decode batch must read (sum of context lengths x 8 kv-heads x 128 x 2 x 2)
+divided by the measured time of the decode call (both kernels).  The prefill
+throughput is reported beside it.  Inputs are resident in HBM before timing.
+Per-kernel times come from HIP events recorded on the stream the kernels run
+on.  ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the
+same workload.
+
+Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+METRIC = "paged decode KV-read GB/s (% of HBM peak) + paged prefill TFLOP/s, 1 MI355X"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partials_traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_attn_amd", "csrc", f)
+                  for f in ("decode.hip", "pa_device.h", "pa_kernels.h")]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def prefill_flops(w) -> float:
+    """4*D flops (q.k and p.v) per admissible (query row, key) pair, every head."""
+    total = 0
+    for b in range(w.B):
+        n = int(w.context_lens[b])
+        L = int(w.q_lens[b])
+        pos = np.arange(n - L, n)
+        keys = np.minimum(n, pos + 1) if w.causal else np.full(L, n)
+        total += int(keys.sum())
+    return 4.0 * w.D * w.Hq * total
+
+
+def traffic_record():
+    """HBM bytes per launch of the partition kernel measured with rocprofv3
+    counters, if they were taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec
+
+
+def cpu_baseline(w5, w3, budget_s):
+    """fp64 oracle on a bounded sample: whole decode sequences of the long
+    batch (append + attention, on a compact copy of their blocks), then one
+    sequence of the chunked prefill."""
+    import threadpoolctl
+
+    import oracle
+
+    info = threadpoolctl.threadpool_info()
+    cores = max([i.get("num_threads", 1) for i in info] + [1])
+
+    done, t_dec, bytes_dec = [], 0.0, 0
+    for b in range(w5.B):
+        nb = (int(w5.context_lens[b]) + w5.bs - 1) // w5.bs
+        ids = w5.block_table[b, :nb].astype(np.int64)
+        kp, vp = w5.k_pool[ids], w5.v_pool[ids]
+        table = np.arange(nb, dtype=np.int32)[None]
+        s = int(w5.slot_mapping[b])
+        slot = np.array([int(np.nonzero(ids == s // w5.bs)[0][0]) * w5.bs + s % w5.bs], np.int32)
+        t0 = time.perf_counter()
+        kp2, vp2 = oracle.kv_append(kp, vp, w5.k_new[b:b + 1], w5.v_new[b:b + 1], slot, w5.bs)
+        oracle.paged_attention(w5.q[b:b + 1], kp2, vp2, table, w5.context_lens[b:b + 1], np.array([0, 1]),
+                               w5.scale, w5.bs, w5.dtype)
+        t_dec += time.perf_counter() - t0
+        done.append(b)
+        bytes_dec += int(w5.context_lens[b]) * w5.Hkv * w5.D * 2 * 2
+        if t_dec >= budget_s * 0.6:
+            break
+    t0 = time.perf_counter()
+    kp, vp = oracle.kv_append(w3.k_pool, w3.v_pool, w3.k_new[:512], w3.v_new[:512], w3.slot_mapping[:512], w3.bs)
+    oracle.paged_attention(w3.q[:512], kp, vp, w3.block_table[:1], w3.context_lens[:1], np.array([0, 512]),
+                           w3.scale, w3.bs, w3.dtype, oracle.ScoreMods(causal=True))
+    t_pre = time.perf_counter() - t0
+    pre_flops = prefill_flops(w3) / w3.B
+    return {
+        "value": round(bytes_dec / t_dec / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": (f"decode: {len(done)} of {w5.B} sequences of the long-context batch "
+                   f"({sum(int(w5.context_lens[b]) for b in done)} tokens, kv_append + fp64 attention) in "
+                   f"{t_dec:.2f} s; prefill: 1 of {w3.B} chunked-prefill sequences in {t_pre:.2f} s"),
+        "prefill_tflops": round(pre_flops / t_pre / 1e12, 6),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--page-size", type=int, default=16, help="block size of the decode pool (16..256)")
+    ap.add_argument("--split", type=int, default=512, help="decode split-KV partition length")
+    ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
+                    help="time budget of the oracle baseline (0: skip it)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_cache_attn_amd as pa
+    from workloads import CONFIG_NAMES, config_workload
+    from workloads.device import upload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pa.lib()
+
+    log("generating long-context decode batch")
+    t0 = time.time()
+    w5 = config_workload(5, bs=args.page_size)
+    w3 = config_workload(3)
+    log(f"inputs generated in {time.time() - t0:.1f} s; uploading")
+    t5 = upload(w5, dev)
+    t3 = upload(w3, dev)
+    out5 = torch.empty_like(t5["q"])
+    out3 = torch.empty_like(t3["q"])
+    ws = pa.decode_workspace(t5["q"], w5.Hkv, w5.max_context_len, args.split)
+    torch.cuda.synchronize()
+    log("inputs resident on the GPU")
+
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        pa.kv_append(t5["k_new"], t5["v_new"], t5["k_cache"], t5["v_cache"], t5["slot_mapping"])
+        if ev is not None:
+            ev[1].record(stream)
+        pa.paged_attn_decode(out5, t5["q"], t5["k_cache"], t5["v_cache"], t5["block_tables"], t5["context_lens"],
+                             w5.scale, w5.max_context_len, args.split, workspace=ws, phase="partials")
+        if ev is not None:
+            ev[2].record(stream)
+        pa.paged_attn_decode(out5, t5["q"], t5["k_cache"], t5["v_cache"], t5["block_tables"], t5["context_lens"],
+                             w5.scale, w5.max_context_len, args.split, workspace=ws, phase="merge")
+        if ev is not None:
+            ev[3].record(stream)
+        pa.kv_append(t3["k_new"], t3["v_new"], t3["k_cache"], t3["v_cache"], t3["slot_mapping"])
+        if ev is not None:
+            ev[4].record(stream)
+        pa.paged_attn_prefill(out3, t3["q"], t3["cu_q_lens"], t3["k_cache"], t3["v_cache"], t3["block_tables"],
+                              t3["context_lens"], w3.scale, w3.max_q_len, causal=True)
+        if ev is not None:
+            ev[5].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_begin = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    t_end = time.perf_counter()
+    log(f"timed {args.steps} steps")
+
+    def phase_ms(i, j):
+        return float(np.mean([e[i].elapsed_time(e[j]) for e in events]))
+
+    ms_append5 = phase_ms(0, 1)
+    ms_partials = phase_ms(1, 2)
+    ms_merge = phase_ms(2, 3)
+    ms_append3 = phase_ms(3, 4)
+    ms_prefill = phase_ms(4, 5)
+    ms_step = (t_end - t_begin) * 1e3 / args.steps
+    ms_decode = ms_partials + ms_merge
+
+    kv_bytes = w5.kv_bytes()
+    decode_gbs = kv_bytes / (ms_decode * 1e-3) / 1e9
+    partials_gbs = kv_bytes / (ms_partials * 1e-3) / 1e9
+    flops = prefill_flops(w3)
+    prefill_tflops = flops / (ms_prefill * 1e-3) / 1e12
+    append_bytes5 = 2 * 2 * w5.k_new.size * 2  # read new + write pool, K and V
+    append_bytes3 = 2 * 2 * w3.k_new.size * 2
+
+    traffic = None
+    rec = traffic_record()
+    if rec is not None:
+        traffic = rec["hbm_bytes_per_launch"]
+
+    result = {
+        "metric": METRIC,
+        "value": round(decode_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": CONFIG_NAMES[5] + ("" if args.page_size == 16 else f"_bs{args.page_size}")
+            + " + " + CONFIG_NAMES[3],
+            "decode_batch": w5.B,
+            "decode_context_tokens": int(w5.context_lens.sum()),
+            "decode_kv_bytes": int(kv_bytes),
+            "heads_q_kv": [w5.Hq, w5.Hkv],
+            "head_dim": w5.D,
+            "block_size": w5.bs,
+            "split_tokens": int(pa.decode_split_tokens(w5.B, w5.Hkv, w5.max_context_len, args.split)),
+            "prefill_batch": w3.B,
+            "prefill_rows": int(w3.q_lens.sum()),
+            "prefill_flops": flops,
+            "parallelism": "single GPU",
+        },
+        "decode_pct_hbm_peak": round(100.0 * decode_gbs / HBM_PEAK_GBS, 2),
+        "roofline": {
+            "kernel": "row_partials_kernel<BF16,128,8> (decode partitions)",
+            "bound": "hbm",
+            "achieved": round(partials_gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(partials_gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "avg_launch_ms": round(ms_partials, 5),
+            "algorithmic_bytes_per_launch": int(kv_bytes),
+        },
+        "prefill": {
+            "value": round(prefill_tflops, 2),
+            "unit": "TFLOP/s",
+            "ms": round(ms_prefill, 5),
+            "roofline": {
+                "kernel": "prefill_mfma_kernel<128> (chunked prefill)",
+                "bound": "mfma",
+                "achieved": round(prefill_tflops, 2),
+                "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s",
+                "frac": round(prefill_tflops / BF16_PEAK_TFLOPS, 4),
+                "algorithmic_flops_per_launch": flops,
+            },
+        },
+        "phases_ms": {
+            "kv_append_decode_batch": round(ms_append5, 5),
+            "decode_partitions": round(ms_partials, 5),
+            "decode_merge": round(ms_merge, 5),
+            "kv_append_prefill_chunks": round(ms_append3, 5),
+            "prefill": round(ms_prefill, 5),
+        },
+        "kv_append_gbs": {
+            "decode_batch": round(append_bytes5 / (ms_append5 * 1e-3) / 1e9, 2),
+            "prefill_chunks": round(append_bytes3 / (ms_append3 * 1e-3) / 1e9, 2),
+        },
+    }
+    if args.cpu_baseline_seconds > 0:
+        log("timing the fp64 oracle on the host")
+        result["cpu_baseline"] = cpu_baseline(w5, w3, args.cpu_baseline_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

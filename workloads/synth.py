@@ -23,7 +23,7 @@ any read of them shows up in the output.
 
 Draws: numpy PCG64 through ``SeedSequence(seed)``.  Child stream 0 draws the
 structure (lengths, block permutation), 1 the queries, 2 the appended tokens,
-3 the pool contents (spawned again per group of physical blocks so that the
+3 the pool contents (spawned again per range of physical blocks so that the
 pool can be filled by several threads and still be identical bit for bit).
 """
 
@@ -39,7 +39,7 @@ import numpy as np
 BF16_NAN_BITS = np.uint16(0x7FC0)
 F32_NAN_BITS = np.uint32(0x7FC00000)
 
-# Physical blocks per independently seeded draw group when filling a pool.
+# Consecutive physical blocks per independently seeded draw range when filling a pool.
 _POOL_GROUP_BLOCKS = 256
 
 
@@ -126,35 +126,46 @@ def _fill_pools(ss: np.random.SeedSequence, NB, Hkv, D, bs, live, dtype, threads
     """Pools of NaN with N(0,1) rows in the live slots.
 
     ``live[pb]`` is the number of leading live token slots of physical block
-    ``pb`` (-1: not referenced).  Referenced blocks are drawn in ascending
-    physical order, in groups with their own child streams.
+    ``pb`` (-1: not referenced).  The pool is processed in ranges of
+    consecutive physical blocks, each with its own child stream (so the
+    result does not depend on the thread count); inside a range the
+    referenced blocks are drawn in ascending physical order.
     """
-    k_pool = _nan_fill((NB, Hkv, bs, D), dtype)
-    v_pool = _nan_fill((NB, Hkv, D, bs), dtype)
-    ids = np.nonzero(live >= 0)[0]
-    groups = [ids[i:i + _POOL_GROUP_BLOCKS] for i in range(0, len(ids), _POOL_GROUP_BLOCKS)]
-    children = ss.spawn(len(groups))
+    if dtype == "bf16":
+        k_pool = np.empty((NB, Hkv, bs, D), np.uint16)
+        v_pool = np.empty((NB, Hkv, D, bs), np.uint16)
+    else:
+        k_pool = np.empty((NB, Hkv, bs, D), np.float32)
+        v_pool = np.empty((NB, Hkv, D, bs), np.float32)
+    ranges = [(i, min(NB, i + _POOL_GROUP_BLOCKS)) for i in range(0, NB, _POOL_GROUP_BLOCKS)]
+    children = ss.spawn(len(ranges))
     nan = _nan_value(dtype)
 
-    def work(gi):
-        g = groups[gi]
-        rng = np.random.default_rng(children[gi])
-        kv = _normal(rng, (len(g), Hkv, bs, D), dtype)
-        vv = _normal(rng, (len(g), Hkv, D, bs), dtype)
-        lv = live[g]
-        for i in np.nonzero(lv < bs)[0]:
-            kv[i, :, lv[i]:, :] = nan
-            vv[i, :, :, lv[i]:] = nan
-        k_pool[g] = kv
-        v_pool[g] = vv
+    def work(ri):
+        c0, c1 = ranges[ri]
+        lv = live[c0:c1]
+        ref = np.nonzero(lv >= 0)[0]
+        k_pool[c0:c1][lv < 0] = nan
+        v_pool[c0:c1][lv < 0] = nan
+        if len(ref) == 0:
+            return
+        rng = np.random.default_rng(children[ri])
+        kv = _normal(rng, (len(ref), Hkv, bs, D), dtype)
+        vv = _normal(rng, (len(ref), Hkv, D, bs), dtype)
+        lr = lv[ref]
+        for i in np.nonzero(lr < bs)[0]:
+            kv[i, :, lr[i]:, :] = nan
+            vv[i, :, :, lr[i]:] = nan
+        k_pool[c0 + ref] = kv
+        v_pool[c0 + ref] = vv
 
-    nthreads = max(1, min(threads or os.cpu_count() or 1, 16, len(groups) or 1))
+    nthreads = max(1, min(threads or os.cpu_count() or 1, 16, len(ranges) or 1))
     if nthreads == 1:
-        for gi in range(len(groups)):
-            work(gi)
+        for ri in range(len(ranges)):
+            work(ri)
     else:
         with ThreadPoolExecutor(nthreads) as ex:
-            list(ex.map(work, range(len(groups))))
+            list(ex.map(work, range(len(ranges))))
     return k_pool, v_pool
 
 
