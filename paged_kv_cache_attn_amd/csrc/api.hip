@@ -2,6 +2,8 @@
 // Every check happens before anything is enqueued; see include/pagedattn.h.
 #include <math.h>
 
+#include <algorithm>
+
 #include "pagedattn.h"
 #include "pa_kernels.h"
 
@@ -11,6 +13,10 @@ constexpr int kUnsplitLog2 = 30;
 constexpr int kAutoSplitMax = 512;
 constexpr int kAutoSplitMin = 64;
 constexpr long long kAutoTargetUnits = 2048;  // ~8 wavefronts per compute unit
+constexpr int kStreamWavesPerCU = 8;          // resident decode wavefronts per compute unit
+constexpr int kStreamMinChunks = 8;           // 16-token chunks per wavefront, at least
+constexpr int kStreamMaxSeqs = 16384;         // chunk prefix of all rows fits in LDS
+constexpr int kDefaultCUs = 256;              // MI355X, when no device is visible
 
 int ilog2(long long x) {
   int r = 0;
@@ -55,20 +61,45 @@ int partitions(int32_t max_ctx, int split_log2) {
 
 int group_pad(int g) { return g <= 4 ? 4 : 8; }
 
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return kDefaultCUs;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return kDefaultCUs;
+  return cus;
+}
+
 struct Shape {
   int g, GP, NG, P, split_log2;
+  int W;  // > 0: balanced split over W wavefronts
 };
 
 int decode_shape(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_ctx, int32_t split, Shape& s) {
   s.g = Hq / Hkv;
   s.GP = group_pad(s.g);
   s.NG = (s.g + s.GP - 1) / s.GP;
+  s.W = 0;
+  if (split == 0 && B <= kStreamMaxSeqs) {
+    // balanced split: as many wavefronts as stay resident, but at least
+    // kStreamMinChunks chunks of work each for the largest possible batch
+    const long long chunks = (long long)B * Hkv * s.NG * (((long long)max_ctx + 15) / 16 + 1);
+    long long w = (long long)device_cus() * kStreamWavesPerCU;
+    w = std::min(w, std::max(1ll, chunks / kStreamMinChunks));
+    s.W = (int)w;
+    s.split_log2 = kUnsplitLog2;
+    s.P = 1;
+    return PA_OK;
+  }
   s.split_log2 = resolve_split_log2(B, Hkv, max_ctx, split);
   s.P = partitions(max_ctx, s.split_log2);
   return PA_OK;
 }
 
 size_t workspace_bytes_for(int32_t B, int32_t Hkv, int32_t D, const Shape& s) {
+  if (s.W > 0) {
+    const size_t items = (size_t)B * Hkv * s.NG;
+    return ((size_t)s.W + items) * s.GP * (size_t)(D + 2) * sizeof(float) + items * 2 * sizeof(int32_t);
+  }
   if (s.P <= 1) return 0;
   return (size_t)B * Hkv * s.NG * s.GP * (size_t)s.P * (size_t)(D + 2) * sizeof(float);
 }
@@ -109,15 +140,18 @@ void fill_row_args(pa::RowAttnArgs& a, void* out, const void* q, const void* kc,
   a.bs_log2 = ilog2(bs);
   a.split_log2 = s.split_log2;
   a.P = s.P;
+  a.stream_waves = s.W;
   a.causal = causal;
   a.window = mods ? mods->window : 0;
   a.scale = scale;
   a.softcap = mods ? mods->softcap : 0.f;
   a.alibi = mods ? mods->alibi_slopes : nullptr;
   float* w = static_cast<float*>(ws);
-  const size_t units = (size_t)B * max_q * Hkv * s.NG * s.GP * (size_t)s.P;
+  const size_t units = s.W > 0 ? ((size_t)s.W + (size_t)B * Hkv * s.NG) * s.GP
+                               : (size_t)B * max_q * Hkv * s.NG * s.GP * (size_t)s.P;
   a.ws_o = w;
   a.ws_ml = w ? w + units * D : nullptr;
+  a.ws_meta = (w && s.W > 0) ? reinterpret_cast<int32_t*>(w + units * (D + 2)) : nullptr;
 }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? PA_OK : (int)e; }
@@ -146,7 +180,7 @@ int decode_impl(bool do_partials, bool do_merge, void* out, const void* q, const
   if (do_partials) {
     if ((st = launch_status(pa::launch_row_partials(a, dtype, D, hs)))) return st;
   }
-  if (do_merge && s.P > 1) {
+  if (do_merge && (s.P > 1 || s.W > 0)) {
     if ((st = launch_status(pa::launch_row_merge(a, dtype, D, hs)))) return st;
   }
   return PA_OK;
@@ -185,6 +219,7 @@ int kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache
 int32_t paged_attn_decode_split_tokens(int32_t num_seqs, int32_t num_kv_heads,
                                        int32_t max_context_len, int32_t split_tokens) {
   if (check_split(split_tokens) || num_seqs < 0 || num_kv_heads <= 0 || max_context_len < 0) return 0;
+  if (split_tokens == 0 && num_seqs <= kStreamMaxSeqs) return 0;  // balanced split
   const int l2 = resolve_split_log2(num_seqs, num_kv_heads, max_context_len, split_tokens);
   return l2 >= kUnsplitLog2 ? -1 : (1 << l2);
 }
@@ -292,6 +327,7 @@ int paged_attn_prefill(void* out, const void* q, const int32_t* cu_q_lens, const
   s.NG = (g + s.GP - 1) / s.GP;
   s.split_log2 = kUnsplitLog2;
   s.P = 1;
+  s.W = 0;
   if ((long long)num_seqs * max_q_len * num_kv_heads * s.NG > 0x7fffffffll) return PA_ERR_SIZE;
   pa::RowAttnArgs a;
   fill_row_args(a, out, q, k_cache, v_cache, block_tables, block_table_stride, context_lens,

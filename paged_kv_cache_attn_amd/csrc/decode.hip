@@ -43,8 +43,11 @@ struct Cfg {
   static constexpr int TPI = 64 / GP;             // tokens per pass
   static constexpr int NPASS = 16 / TPI;          // passes per 16-token chunk
   static constexpr int PPL = kPieces / GP;        // pieces per lane per token
-  static constexpr int RPL = D / 64;              // V rows (dims) per lane
-  static constexpr int VPR = 16 * ES / 16;        // 16-byte loads per V row of a chunk
+  // P.V: lane = (dimension row vr = lane/2, token half vh = lane%2); a V row
+  // of one 16-token chunk is 16*ES bytes, so the two halves of a wave's 32
+  // rows are one contiguous run when the block holds exactly the chunk.
+  static constexpr int RPL = D / 32;              // V rows (dims) per lane
+  static constexpr int VPR = 8 * ES / 16;         // 16-byte loads per (row, 8 tokens)
   static_assert(PPL >= 1 && RPL >= 1, "unsupported shape");
 };
 
@@ -135,26 +138,18 @@ __device__ __forceinline__ bool row_range(const RowAttnArgs& a, int slot, RowRan
   return true;
 }
 
+// Attention of one row slot over keys [c_begin, c_end) (a segment of its
+// admissible range), for the GP query heads of head group hg.  Writes the
+// normalised output when the segment is the whole range (`whole`), else the
+// unnormalised partial (o, m, l) at workspace unit `unit`.
 template <typename E, int D, int GP, bool kMods>
-__global__ __launch_bounds__(64) void row_partials_kernel(const RowAttnArgs a) {
+__device__ __forceinline__ void attend_segment(const RowAttnArgs& a, const RowRange& rr, const int slot,
+                                               const int hg, const int c_begin, const int c_end,
+                                               const bool whole, const size_t unit, uint32_t* p_lds,
+                                               float* stat_lds) {
   using C = Cfg<E, D, GP>;
   constexpr int TPI = C::TPI;
-  __shared__ __attribute__((aligned(16))) uint32_t p_lds[16 * GP];  // bf16 pairs or f32
-  __shared__ __attribute__((aligned(16))) float stat_lds[2 * GP];
-
   const int lane = threadIdx.x;
-  const int HG = a.Hkv * a.NG;
-  const int flat = blockIdx.x;
-  const int p = flat % a.P;
-  const int hg = (flat / a.P) % HG;
-  const int slot = flat / (a.P * HG);
-
-  RowRange rr;
-  if (!row_range(a, slot, rr)) return;
-  if (p >= rr.nparts) return;
-  const int c_begin = rr.start + (p << a.split_log2);
-  const int c_end = min(rr.hi, c_begin + (1 << a.split_log2));
-
   const int kvh = hg / a.NG;
   const int head0 = kvh * a.g + (hg - kvh * a.NG) * GP;  // first global head of the group
   const int nvalid = min(GP, a.g - (hg - kvh * a.NG) * GP);
@@ -162,6 +157,8 @@ __global__ __launch_bounds__(64) void row_partials_kernel(const RowAttnArgs a) {
   const int t = lane % TPI;
   const int e = lane / TPI;
   const int my_head = final_head<GP>(e);
+  const int vh = lane & 1;   // token half for P.V
+  const int vr = lane >> 1;  // first V row for P.V
 
   // ---- q slice of every head in the group (lane-dependent head order) ----
   u32x4 qv[GP][C::PPL];
@@ -189,7 +186,7 @@ __global__ __launch_bounds__(64) void row_partials_kernel(const RowAttnArgs a) {
 
   float m_run = kNegInf;  // log2 domain, for head my_head
   float l_run = 0.f;      // partial sum over this lane's tokens
-  float o[GP][C::RPL];
+  float o[GP][C::RPL];  // rows d = vr + 32 r, over this lane's token half
 #pragma unroll
   for (int h = 0; h < GP; ++h)
 #pragma unroll
@@ -213,19 +210,17 @@ __global__ __launch_bounds__(64) void row_partials_kernel(const RowAttnArgs a) {
     for (int ps = 0; ps < C::NPASS; ++ps)
 #pragma unroll
       for (int i = 0; i < C::PPL; ++i)
-        ch.k[ps][i] = load16(ks + (ps * TPI + t) * C::kRowBytes + (e + GP * i) * 16);
+        ch.k[ps][i] = load16_stream(ks + (ps * TPI + t) * C::kRowBytes + (e + GP * i) * 16);
 #pragma unroll
     for (int r = 0; r < C::RPL; ++r)
 #pragma unroll
       for (int w = 0; w < C::VPR; ++w)
-        ch.v[r][w] = load16(vs + (size_t)(lane + 64 * r) * bs * C::ES + w * 16);
+        ch.v[r][w] = load16_stream(vs + ((size_t)(vr + 32 * r) * bs + vh * 8) * C::ES + w * 16);
   };
 
-  Chunk<E, D, GP> cur, nxt;
-  if (c_begin < c_end) load_chunk(cur, c_begin);
-
-  for (int tok0 = c_begin; tok0 < c_end; tok0 += 16) {
-    if (tok0 + 16 < c_end) load_chunk(nxt, tok0 + 16);
+  // one 16-token chunk: scores, online softmax, P.V.  A chunk that starts at
+  // or past c_end is entirely masked and leaves the state unchanged.
+  auto process = [&](Chunk<E, D, GP>& cur, const int tok0) {
 
     // ---- scores for this lane's tokens, head my_head ----
     float s[C::NPASS];
@@ -314,11 +309,11 @@ __global__ __launch_bounds__(64) void row_partials_kernel(const RowAttnArgs a) {
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             if constexpr (C::kBf16) {
-              const int j0 = tok0 + w * 8 + c * 2;
+              const int j0 = tok0 + vh * 8 + w * 8 + c * 2;
               uint32_t m = (j0 < n ? 0xffffu : 0u) | (j0 + 1 < n ? 0xffff0000u : 0u);
               cur.v[r][w][c] &= m;
             } else {
-              const int j0 = tok0 + w * 4 + c;
+              const int j0 = tok0 + vh * 8 + w * 4 + c;
               if (j0 >= n) cur.v[r][w][c] = 0u;
             }
           }
@@ -327,7 +322,8 @@ __global__ __launch_bounds__(64) void row_partials_kernel(const RowAttnArgs a) {
     // ---- o += P.V ----
     if constexpr (C::kBf16) {
 #pragma unroll
-      for (int jp = 0; jp < 8; ++jp) {
+      for (int jl = 0; jl < 4; ++jl) {
+        const int jp = vh * 4 + jl;  // token pair inside the chunk
         uint32_t pp[GP];
 #pragma unroll
         for (int h4 = 0; h4 < GP / 4; ++h4) {
@@ -339,14 +335,15 @@ __global__ __launch_bounds__(64) void row_partials_kernel(const RowAttnArgs a) {
         }
 #pragma unroll
         for (int r = 0; r < C::RPL; ++r) {
-          const uint32_t v2 = cur.v[r][jp >> 2][jp & 3];
+          const uint32_t v2 = cur.v[r][0][jl];
 #pragma unroll
           for (int h = 0; h < GP; ++h) o[h][r] = dot2_bf16(pp[h], v2, o[h][r]);
         }
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
+      for (int jl = 0; jl < 8; ++jl) {
+        const int j = vh * 8 + jl;
         float pj[GP];
 #pragma unroll
         for (int h4 = 0; h4 < GP / 4; ++h4) {
@@ -358,17 +355,38 @@ __global__ __launch_bounds__(64) void row_partials_kernel(const RowAttnArgs a) {
         }
 #pragma unroll
         for (int r = 0; r < C::RPL; ++r) {
-          const float vj = __uint_as_float(cur.v[r][j >> 2][j & 3]);
+          const float vj = __uint_as_float(cur.v[r][jl >> 2][jl & 3]);
 #pragma unroll
           for (int h = 0; h < GP; ++h) o[h][r] = fmaf(pj[h], vj, o[h][r]);
         }
       }
     }
     __builtin_amdgcn_wave_barrier();
-    cur = nxt;
+  };
+
+  // Software pipeline over two register buffers: while one chunk is computed
+  // the next two are in flight.  Every load is unconditional (addresses past
+  // the partition are clamped to its last chunk, which is fetched again) and
+  // the loop is unrolled by two, so every path keeps the same loads in flight
+  // and each vmcnt wait covers exactly the chunk about to be used.
+  if (c_begin < c_end) {
+    const int last_chunk = c_begin + ((c_end - c_begin - 1) & ~15);
+    Chunk<E, D, GP> buf0, buf1;
+    load_chunk(buf0, c_begin);
+    load_chunk(buf1, min(c_begin + 16, last_chunk));
+    for (int tok0 = c_begin; tok0 < c_end; tok0 += 32) {
+      process(buf0, tok0);
+      load_chunk(buf0, min(tok0 + 32, last_chunk));
+      process(buf1, tok0 + 16);
+      load_chunk(buf1, min(tok0 + 48, last_chunk));
+    }
   }
 
-  // ---- finish: per-head (m, l) to every lane ----
+  // ---- finish: add the two token halves; per-head (m, l) to every lane ----
+#pragma unroll
+  for (int h = 0; h < GP; ++h)
+#pragma unroll
+    for (int r = 0; r < C::RPL; ++r) o[h][r] += dpp<kDppQuadXor1>(o[h][r]);
   const float l_tot = group_reduce<TPI, false>(l_run);
   if (t == 0) {
     stat_lds[2 * my_head] = m_run;
@@ -382,7 +400,7 @@ __global__ __launch_bounds__(64) void row_partials_kernel(const RowAttnArgs a) {
     lh[h] = stat_lds[2 * h + 1];
   }
 
-  if (rr.nparts == 1) {
+  if (whole) {
 #pragma unroll
     for (int h = 0; h < GP; ++h) {
       if (h >= nvalid) continue;
@@ -390,7 +408,8 @@ __global__ __launch_bounds__(64) void row_partials_kernel(const RowAttnArgs a) {
       char* orow = static_cast<char*>(a.out) + ((size_t)rr.qrow * a.Hq + head0 + h) * D * C::ES;
 #pragma unroll
       for (int r = 0; r < C::RPL; ++r) {
-        const int d = lane + 64 * r;
+        if ((r & 1) != vh) continue;  // each half writes every other row
+        const int d = vr + 32 * r;
         const float val = o[h][r] * inv;
         if constexpr (C::kBf16) {
           reinterpret_cast<uint16_t*>(orow)[d] = (uint16_t)f32_to_bf16_bits(val);
@@ -400,12 +419,12 @@ __global__ __launch_bounds__(64) void row_partials_kernel(const RowAttnArgs a) {
       }
     }
   } else {
-    const size_t unit = ((size_t)slot * HG + hg) * a.P + p;
     float* wo = a.ws_o + unit * GP * D;
 #pragma unroll
     for (int h = 0; h < GP; ++h)
 #pragma unroll
-      for (int r = 0; r < C::RPL; ++r) wo[h * D + lane + 64 * r] = o[h][r];
+      for (int r = 0; r < C::RPL; ++r)
+        if ((r & 1) == vh) wo[h * D + vr + 32 * r] = o[h][r];
     if (lane < GP) {
       a.ws_ml[unit * GP * 2 + 2 * lane] = mh[lane];
       a.ws_ml[unit * GP * 2 + 2 * lane + 1] = lh[lane];
@@ -413,45 +432,156 @@ __global__ __launch_bounds__(64) void row_partials_kernel(const RowAttnArgs a) {
   }
 }
 
-// One work-group (one wave) per (row slot, query head): log-sum-exp merge of
-// the row's partitions in fixed order.
-template <typename E, int D, int GP>
-__global__ __launch_bounds__(64) void row_merge_kernel(const RowAttnArgs a) {
-  constexpr int ES = E::kBytes;
-  const int lane = threadIdx.x;
-  const int h = blockIdx.x % a.Hq;
-  const int slot = blockIdx.x / a.Hq;
+// Fixed partitions: one wavefront per (row slot, head group, partition of
+// 2^split_log2 keys).  Also the unsplit path (P == 1) used by fp32 prefill.
+template <typename E, int D, int GP, bool kMods>
+__global__ __launch_bounds__(64) void row_partials_kernel(const RowAttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint32_t p_lds[16 * GP];  // bf16 pairs or f32
+  __shared__ __attribute__((aligned(16))) float stat_lds[2 * GP];
+  const int HG = a.Hkv * a.NG;
+  const int flat = blockIdx.x;
+  const int p = flat % a.P;
+  const int hg = (flat / a.P) % HG;
+  const int slot = flat / (a.P * HG);
   RowRange rr;
   if (!row_range(a, slot, rr)) return;
-  if (rr.nparts <= 1) return;
-  const int kvh = h / a.g;
-  const int hin = h - kvh * a.g;
-  const int hg = kvh * a.NG + hin / GP;
-  const int hs = hin % GP;
-  const int HG = a.Hkv * a.NG;
-  const size_t unit0 = ((size_t)slot * HG + hg) * a.P;
+  if (p >= rr.nparts) return;
+  const int c_begin = rr.start + (p << a.split_log2);
+  const int c_end = min(rr.hi, c_begin + (1 << a.split_log2));
+  attend_segment<E, D, GP, kMods>(a, rr, slot, hg, c_begin, c_end, rr.nparts == 1,
+                                  ((size_t)slot * HG + hg) * a.P + p, p_lds, stat_lds);
+}
 
+// 16-token chunks a decode row's admissible range spans (>= 1, so that an
+// empty context still gets a (fully masked) chunk and a zero output).
+__device__ __forceinline__ int decode_chunks(const RowAttnArgs& a, int b) {
+  const int n = a.context_lens[b];
+  const int lo = a.window > 0 ? max(0, n - a.window) : 0;
+  const int c = (n - (lo & ~15) + 15) >> 4;
+  return c > 1 ? c : 1;
+}
+
+// Inclusive prefix sum over the wave.
+__device__ __forceinline__ int wave_scan(int x) {
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if ((int)(threadIdx.x & 63) >= d) x += y;
+  }
+  return x;
+}
+
+// Exclusive chunk prefix of every decode row into pre[0..B] (LDS).
+__device__ __forceinline__ void chunk_prefix(const RowAttnArgs& a, int* pre) {
+  const int lane = threadIdx.x;
+  int carry = 0;
+  if (lane == 0) pre[0] = 0;
+  for (int base = 0; base < a.num_seqs; base += 64) {
+    const int b = base + lane;
+    const int c = b < a.num_seqs ? decode_chunks(a, b) : 0;
+    const int incl = wave_scan(c);
+    if (b < a.num_seqs) pre[b + 1] = carry + incl;
+    carry += __shfl(incl, 63, 64);
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Balanced decode ("stream" split): the items (row, head group) are laid end
+// to end as one sequence of 16-token chunks and wavefront w takes chunks
+// [w*S, (w+1)*S), S = ceil(total / waves), crossing item boundaries as it
+// goes.  Every wavefront does the same amount of work, so there is no tail of
+// long partitions, and no wavefront is launched just to find it has nothing
+// to do.  A wavefront that covers an item entirely writes its output; pieces
+// of items split between wavefronts leave partials at unit w + item (unique:
+// the wavefronts touching an item, and the items a wavefront touches, are
+// both contiguous) for the merge kernel.
+template <typename E, int D, int GP, bool kMods>
+__global__ __launch_bounds__(64) void decode_stream_kernel(const RowAttnArgs a) {
+  extern __shared__ int pre[];  // [num_seqs + 1]
+  __shared__ __attribute__((aligned(16))) uint32_t p_lds[16 * GP];
+  __shared__ __attribute__((aligned(16))) float stat_lds[2 * GP];
+  const int HG = a.Hkv * a.NG;
+  chunk_prefix(a, pre);
+  const long long total = (long long)pre[a.num_seqs] * HG;
+  const long long W = gridDim.x;
+  const long long S = (total + W - 1) / W;
+  long long g = (long long)blockIdx.x * S;
+  const long long g_end = min(total, g + S);
+  if (g >= g_end) return;
+  // row containing chunk g: largest b with pre[b] * HG <= g
+  int lo = 0, hi = a.num_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if ((long long)pre[mid] * HG <= g) lo = mid; else hi = mid - 1;
+  }
+  int b = lo;
+  while (g < g_end) {
+    const int nc = pre[b + 1] - pre[b];
+    const long long row0 = (long long)pre[b] * HG;
+    const int hg = (int)((g - row0) / nc);
+    const long long item0 = row0 + (long long)hg * nc;  // first chunk of item (b, hg)
+    const int c0 = (int)(g - item0);
+    const int c1 = (int)min((long long)nc, g_end - item0);
+    RowRange rr;
+    row_range(a, b, rr);
+    const int c_begin = rr.start + 16 * c0;
+    const int c_end = min(rr.hi, rr.start + 16 * c1);
+    const bool whole = (c0 == 0) && (c1 == nc);
+    const size_t item = (size_t)b * HG + hg;
+    if (c0 == 0 && threadIdx.x == 0) {
+      // where the merge finds this item's partials: units w0 + item .. w1 + item
+      const long long w1 = (item0 + nc - 1) / S;
+      a.ws_meta[2 * item] = (int)(blockIdx.x + item);
+      a.ws_meta[2 * item + 1] = (int)(w1 - blockIdx.x + 1);
+    }
+    attend_segment<E, D, GP, kMods>(a, rr, b, hg, c_begin, c_end, whole, blockIdx.x + item, p_lds,
+                                    stat_lds);
+    g = item0 + c1;
+    if (hg + 1 == HG) ++b;
+  }
+}
+
+// Combine np consecutive partials (units unit0 .. unit0+np-1, head slot hs)
+// into output row qrow, head h: log-sum-exp weights, ascending unit order.
+template <typename E, int D, int GP>
+__device__ __forceinline__ void merge_units(const RowAttnArgs& a, const size_t unit0, const int np,
+                                            const int hs, const int qrow, const int h) {
+  constexpr int ES = E::kBytes;
+  constexpr int R = D / 64;
+  const int lane = threadIdx.x;
+  const float* ml = a.ws_ml + unit0 * GP * 2 + 2 * hs;  // unit u at ml[u * 2 * GP]
+  const float* op = a.ws_o + (unit0 * GP + hs) * D;     // unit u at op[u * GP * D]
   float M = kNegInf;
-  for (int p = 0; p < rr.nparts; ++p) M = fmaxf(M, a.ws_ml[(unit0 + p) * GP * 2 + 2 * hs]);
+  for (int p = lane; p < np; p += 64) M = fmaxf(M, ml[(size_t)p * 2 * GP]);
+  M = wave_max(M);
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.f;
   float L = 0.f;
-  float acc[D / 64];
-#pragma unroll
-  for (int r = 0; r < D / 64; ++r) acc[r] = 0.f;
   if (M != kNegInf) {
-    for (int p = 0; p < rr.nparts; ++p) {
-      const float mp = a.ws_ml[(unit0 + p) * GP * 2 + 2 * hs];
-      const float lp = a.ws_ml[(unit0 + p) * GP * 2 + 2 * hs + 1];
-      const float w = fast_exp2(mp - M);
-      L += w * lp;
-      const float* op = a.ws_o + ((unit0 + p) * GP + hs) * D;
+    for (int p = lane; p < np; p += 64)
+      L += fast_exp2(ml[(size_t)p * 2 * GP] - M) * ml[(size_t)p * 2 * GP + 1];
+    L = wave_sum(L);
+    constexpr int U = 8;  // partials whose loads are in flight together
+    for (int p0 = 0; p0 < np; p0 += U) {
+      float w[U], x[U][R];
 #pragma unroll
-      for (int r = 0; r < D / 64; ++r) acc[r] = fmaf(w, op[lane + 64 * r], acc[r]);
+      for (int u = 0; u < U; ++u) {
+        const int p = min(p0 + u, np - 1);
+        w[u] = (p0 + u < np) ? fast_exp2(ml[(size_t)p * 2 * GP] - M) : 0.f;
+#pragma unroll
+        for (int r = 0; r < R; ++r) x[u][r] = op[(size_t)p * GP * D + lane + 64 * r];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = fmaf(w[u], x[u][r], acc[r]);
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  char* orow = static_cast<char*>(a.out) + ((size_t)rr.qrow * a.Hq + h) * D * ES;
+  char* orow = static_cast<char*>(a.out) + ((size_t)qrow * a.Hq + h) * D * ES;
 #pragma unroll
-  for (int r = 0; r < D / 64; ++r) {
+  for (int r = 0; r < R; ++r) {
     const int d = lane + 64 * r;
     if constexpr (ES == 2) {
       reinterpret_cast<uint16_t*>(orow)[d] = (uint16_t)f32_to_bf16_bits(acc[r] * inv);
@@ -461,8 +591,47 @@ __global__ __launch_bounds__(64) void row_merge_kernel(const RowAttnArgs a) {
   }
 }
 
+// Merge for the balanced split: one wavefront per (decode row, query head);
+// the item's partial units were recorded by the wavefront that started it.
+template <typename E, int D, int GP>
+__global__ __launch_bounds__(64) void decode_stream_merge_kernel(const RowAttnArgs a) {
+  const int h = blockIdx.x % a.Hq;
+  const int b = blockIdx.x / a.Hq;
+  const int kvh = h / a.g;
+  const int hin = h - kvh * a.g;
+  const size_t item = (size_t)b * a.Hkv * a.NG + kvh * a.NG + hin / GP;
+  const int unit0 = a.ws_meta[2 * item];
+  const int np = a.ws_meta[2 * item + 1];
+  if (np <= 1) return;  // written whole by the stream kernel
+  merge_units<E, D, GP>(a, (size_t)unit0, np, hin % GP, b, h);
+}
+
+// Merge for fixed partitions: one wavefront per (row slot, query head).
+template <typename E, int D, int GP>
+__global__ __launch_bounds__(64) void row_merge_kernel(const RowAttnArgs a) {
+  const int h = blockIdx.x % a.Hq;
+  const int slot = blockIdx.x / a.Hq;
+  RowRange rr;
+  if (!row_range(a, slot, rr)) return;
+  if (rr.nparts <= 1) return;
+  const int kvh = h / a.g;
+  const int hin = h - kvh * a.g;
+  const int hg = kvh * a.NG + hin / GP;
+  const int HG = a.Hkv * a.NG;
+  merge_units<E, D, GP>(a, ((size_t)slot * HG + hg) * a.P, rr.nparts, hin % GP, rr.qrow, h);
+}
+
 template <typename E, int D, int GP>
 hipError_t launch_partials_t(const RowAttnArgs& a, bool mods, hipStream_t s) {
+  if (a.stream_waves > 0) {
+    const size_t lds = (size_t)(a.num_seqs + 1) * sizeof(int);
+    if (mods) {
+      hipLaunchKernelGGL((decode_stream_kernel<E, D, GP, true>), dim3(a.stream_waves), dim3(64), lds, s, a);
+    } else {
+      hipLaunchKernelGGL((decode_stream_kernel<E, D, GP, false>), dim3(a.stream_waves), dim3(64), lds, s, a);
+    }
+    return hipGetLastError();
+  }
   const long long blocks = (long long)a.num_seqs * a.max_q_len * a.Hkv * a.NG * a.P;
   if (blocks <= 0) return hipSuccess;
   if (mods) {
@@ -477,7 +646,11 @@ template <typename E, int D, int GP>
 hipError_t launch_merge_t(const RowAttnArgs& a, hipStream_t s) {
   const long long blocks = (long long)a.num_seqs * a.max_q_len * a.Hq;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((row_merge_kernel<E, D, GP>), dim3((unsigned)blocks), dim3(64), 0, s, a);
+  if (a.stream_waves > 0) {
+    hipLaunchKernelGGL((decode_stream_merge_kernel<E, D, GP>), dim3((unsigned)blocks), dim3(64), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((row_merge_kernel<E, D, GP>), dim3((unsigned)blocks), dim3(64), 0, s, a);
+  }
   return hipGetLastError();
 }
 

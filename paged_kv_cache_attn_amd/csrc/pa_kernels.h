@@ -18,6 +18,7 @@ struct RowAttnArgs {
   const int32_t* cu_q_lens;  // nullptr: one row per sequence, row index b
   float* ws_o;               // [row_slots, head_groups, P, GP, D]
   float* ws_ml;              // [row_slots, head_groups, P, GP, 2]
+  int32_t* ws_meta;          // balanced split: per item (first partial unit, count)
   const float* alibi;        // [Hq] or nullptr
   int32_t bt_stride;
   int32_t max_q_len;
@@ -26,6 +27,7 @@ struct RowAttnArgs {
   int32_t bs_log2;
   int32_t split_log2;        // partition length in tokens (log2); 30 = unsplit
   int32_t P;                 // partitions per row slot in the workspace / grid
+  int32_t stream_waves;      // > 0: balanced decode split over this many wavefronts
   int32_t causal;
   int32_t window;
   float scale;               // softmax scale

@@ -144,17 +144,21 @@ def test_prefill_validation():
 
 
 def test_split_resolution_and_workspace_size():
-    # explicit split sizes are taken as given; -1 never splits
+    # explicit split sizes are taken as given; -1 never splits; 0 = balanced split
     assert binding.decode_split_tokens(64, 8, 32768, 512) == 512
     assert binding.decode_split_tokens(64, 8, 32768, -1) == -1
     assert binding.decode_split_tokens(64, 8, 32768, 100) == 0  # invalid
-    # automatic: 512 when there is enough parallelism, smaller for short/few rows
-    assert binding.decode_split_tokens(64, 8, 32768) == 512
-    assert binding.decode_split_tokens(8, 8, 2048) == 64
-    # workspace: B * Hkv * ceil(g/GP)*GP * P * (D + 2) * 4 bytes, 0 when unsplit
+    assert binding.decode_split_tokens(64, 8, 32768) == 0
+    assert binding.decode_split_tokens(8, 8, 2048) == 0
+    # fixed partitions: B * Hkv * ceil(g/GP)*GP * P * (D + 2) * 4 bytes, 0 when unsplit
     assert binding.decode_workspace_size(64, 64, 8, 128, 32768, 512) == 64 * 8 * 8 * 64 * 130 * 4
     assert binding.decode_workspace_size(8, 32, 8, 128, 2048, 512) == 8 * 8 * 4 * 4 * 130 * 4
     assert binding.decode_workspace_size(8, 32, 8, 128, 2048, -1) == 0
     assert binding.decode_workspace_size(8, 32, 8, 128, 512, 512) == 0
     assert binding.decode_workspace_size(1, 4, 4, 64, 128, 64) == 1 * 4 * 1 * 4 * 2 * 66 * 4
     assert binding.decode_workspace_size(8, 30, 8, 128, 2048, 0) == 0  # invalid heads
+    # balanced split: (W + items) * GP * (D + 2) * 4 + items * 8 bytes, items =
+    # B * Hkv * ceil(g/GP), W = min(8 * CUs, chunks / 8), chunks = items *
+    # (ceil(max_ctx/16) + 1); no device is visible here, so CUs = 256
+    assert binding.decode_workspace_size(64, 64, 8, 128, 32768, 0) == (2048 + 512) * 8 * 130 * 4 + 512 * 8
+    assert binding.decode_workspace_size(8, 32, 8, 128, 2048, 0) == (1032 + 64) * 4 * 130 * 4 + 64 * 8

@@ -221,15 +221,16 @@ def test_deterministic_bits(gpu_lib):
     assert np.array_equal(gpu_prefill(gpu_lib, w3, t=t3), gpu_prefill(gpu_lib, w3, t=t3))
 
 
-@pytest.mark.parametrize("split", [-1, 16, 64, 512])
+@pytest.mark.parametrize("split", [0, -1, 16, 64, 512])
 def test_split_invariance(gpu_lib, split):
     w = small(ctx=(1500, 333, 2048, 17), append=[1, 1, 1, 1])
     assert_close(gpu_decode(gpu_lib, w, split=split), oracle_out(w), "bf16")
 
 
-def test_two_phase_calls_equal_single_call(gpu_lib):
+@pytest.mark.parametrize("split", [0, 64])
+def test_two_phase_calls_equal_single_call(gpu_lib, split):
     w = small(ctx=(1500, 333, 2048, 17), append=[1, 1, 1, 1])
-    assert np.array_equal(gpu_decode(gpu_lib, w, split=64, phase="two"), gpu_decode(gpu_lib, w, split=64))
+    assert np.array_equal(gpu_decode(gpu_lib, w, split=split, phase="two"), gpu_decode(gpu_lib, w, split=split))
 
 
 def test_decode_equals_prefill_with_one_row(gpu_lib):
