@@ -4,8 +4,11 @@ One step = one pass of the whole path over one batch of synthetic input:
   1. kv_append of one new token per sequence of the long-context decode batch
      (64 sequences, log-normal contexts around 8192 tokens, 64 query / 8 KV
      heads, head_dim 128, bf16, 16-token blocks scattered in a ~5.6 GB pool),
-  2. paged decode of that batch with 512-token split-KV partitions
-     (partition kernel, then the merge kernel),
+  2. paged decode of that batch with split-KV (partition kernel, then the
+     merge kernel); by default the library's balanced split, which gives every
+     wavefront an equal share of the batch's 16-token chunks; ``--split 512``
+     selects fixed 512-token partitions instead (also measured and reported
+     under ``decode_fixed_split``),
   3. kv_append of a 512-token chunk for each of 4 sequences, and
   4. causal chunked prefill of those chunks after their 1536-token contexts
      (32 query / 8 KV heads, head_dim 128, bf16, matrix cores).
@@ -133,7 +136,13 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--page-size", type=int, default=16, help="block size of the decode pool (16..256)")
-    ap.add_argument("--split", type=int, default=512, help="decode split-KV partition length")
+    ap.add_argument("--split", type=int, default=0,
+                    help="decode split-KV: 0 balanced (default), -1 unsplit, else fixed partition length")
+    ap.add_argument("--fixed-split", type=int, default=512,
+                    help="fixed partition length measured beside the default (0: skip)")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (a known-size reference for "
+                         "HBM traffic counters)")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
                     help="time budget of the oracle baseline (0: skip it)")
     args = ap.parse_args()
@@ -193,6 +202,16 @@ def main():
         if ev is not None:
             ev[5].record(stream)
 
+    if args.calibration_copy_mib > 0:
+        nbytes = args.calibration_copy_mib << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"calibration copy of {args.calibration_copy_mib} MiB done")
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -225,6 +244,35 @@ def main():
     prefill_tflops = flops / (ms_prefill * 1e-3) / 1e12
     append_bytes5 = 2 * 2 * w5.k_new.size * 2  # read new + write pool, K and V
     append_bytes3 = 2 * 2 * w3.k_new.size * 2
+
+    fixed = None
+    if args.fixed_split > 0 and args.fixed_split != args.split:
+        ws_f = pa.decode_workspace(t5["q"], w5.Hkv, w5.max_context_len, args.fixed_split)
+        evs = []
+        for k in range(args.warmup + args.steps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(stream)
+            pa.paged_attn_decode(out5, t5["q"], t5["k_cache"], t5["v_cache"], t5["block_tables"],
+                                 t5["context_lens"], w5.scale, w5.max_context_len, args.fixed_split, workspace=ws_f,
+                                 phase="partials")
+            e[1].record(stream)
+            pa.paged_attn_decode(out5, t5["q"], t5["k_cache"], t5["v_cache"], t5["block_tables"],
+                                 t5["context_lens"], w5.scale, w5.max_context_len, args.fixed_split, workspace=ws_f,
+                                 phase="merge")
+            e[2].record(stream)
+            if k >= args.warmup:
+                evs.append(e)
+        torch.cuda.synchronize()
+        f_part = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+        f_merge = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+        fixed = {
+            "split_tokens": args.fixed_split,
+            "value": round(w5.kv_bytes() / ((f_part + f_merge) * 1e-3) / 1e9, 2),
+            "unit": "GB/s",
+            "partitions_ms": round(f_part, 5),
+            "merge_ms": round(f_merge, 5),
+        }
+        del ws_f
 
     traffic = None
     rec = traffic_record()
@@ -261,7 +309,8 @@ def main():
         },
         "decode_pct_hbm_peak": round(100.0 * decode_gbs / HBM_PEAK_GBS, 2),
         "roofline": {
-            "kernel": "row_partials_kernel<BF16,128,8> (decode partitions)",
+            "kernel": ("decode_stream_kernel<BF16,128,8>" if args.split == 0 else "row_partials_kernel<BF16,128,8>")
+            + " (decode partitions)",
             "bound": "hbm",
             "achieved": round(partials_gbs, 2),
             "peak": HBM_PEAK_GBS,
@@ -292,6 +341,7 @@ def main():
             "kv_append_prefill_chunks": round(ms_append3, 5),
             "prefill": round(ms_prefill, 5),
         },
+        "decode_fixed_split": fixed,
         "kv_append_gbs": {
             "decode_batch": round(append_bytes5 / (ms_append5 * 1e-3) / 1e9, 2),
             "prefill_chunks": round(append_bytes3 / (ms_append3 * 1e-3) / 1e9, 2),

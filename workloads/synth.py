@@ -277,7 +277,7 @@ CONFIG_NAMES = {
     2: "decode_gqa_bf16_b8_h32x8_d128_ctx128-2048_append",
     3: "chunked_prefill_bf16_b4_ctx1536+512_h32x8_d128_causal",
     4: "shared_prefix_decode_bf16_b16_prefix1024+256_h32x8_d128",
-    5: "long_decode_bf16_b64_lognormal8192_h64x8_d128_split512",
+    5: "long_decode_bf16_b64_lognormal8192_h64x8_d128",
 }
 
 
