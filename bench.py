@@ -155,7 +155,7 @@ def main():
     import torch
 
     import paged_kv_cache_attn_amd as pa
-    from workloads import CONFIG_NAMES, config_workload
+    from workloads import named_workload
     from workloads.device import upload
 
     if not torch.cuda.is_available():
@@ -167,8 +167,8 @@ def main():
 
     log("generating long-context decode batch")
     t0 = time.time()
-    w5 = config_workload(5, bs=args.page_size)
-    w3 = config_workload(3)
+    w5 = named_workload("long_decode_bf16", bs=args.page_size)
+    w3 = named_workload("chunked_prefill_bf16")
     log(f"inputs generated in {time.time() - t0:.1f} s; uploading")
     t5 = upload(w5, dev)
     t3 = upload(w3, dev)
@@ -293,8 +293,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": CONFIG_NAMES[5] + ("" if args.page_size == 16 else f"_bs{args.page_size}")
-            + " + " + CONFIG_NAMES[3],
+            "workload": "long_decode_bf16_b64_lognormal8192_h64x8_d128"
+            + ("" if args.page_size == 16 else f"_bs{args.page_size}")
+            + " + chunked_prefill_bf16_b4_ctx1536+512_h32x8_d128_causal",
             "decode_batch": w5.B,
             "decode_context_tokens": int(w5.context_lens.sum()),
             "decode_kv_bytes": int(kv_bytes),

@@ -14,7 +14,7 @@ import torch
 
 import oracle
 from oracle.paged import bits_to_f64
-from workloads import build_workload, config_workload
+from workloads import build_workload, named_workload
 from workloads.device import to_numpy_bits, to_tensor, upload
 
 pytestmark = pytest.mark.gpu
@@ -91,12 +91,12 @@ def small(kind="decode", seed=100, dtype="bf16", ctx=(37, 300, 1000), Hq=32, Hkv
 # kv_append
 # ------------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("case", ["config2", "config3", "bs64_f32", "negative_slots"])
+@pytest.mark.parametrize("case", ["gqa_decode", "chunked_prefill", "bs64_f32", "negative_slots"])
 def test_kv_append_bit_exact(gpu_lib, case):
-    if case == "config2":
-        w = config_workload(2)
-    elif case == "config3":
-        w = config_workload(3)
+    if case == "gqa_decode":
+        w = named_workload("gqa_decode_bf16")
+    elif case == "chunked_prefill":
+        w = named_workload("chunked_prefill_bf16")
     elif case == "bs64_f32":
         w = small(dtype="f32", bs=64, ctx=(200, 129), append=[70, 129], D=64, Hq=8, Hkv=2)
     else:
@@ -112,47 +112,47 @@ def test_kv_append_bit_exact(gpu_lib, case):
 
 
 # ------------------------------------------------------------------------------------------
-# the five workloads
+# the reference workloads
 # ------------------------------------------------------------------------------------------
 
-def test_config1_decode_f32(gpu_lib):
-    w = config_workload(1)
+def test_single_decode_f32(gpu_lib):
+    w = named_workload("single_decode_f32")
     for split in (0, -1, 16):
         assert_close(gpu_decode(gpu_lib, w, split=split), oracle_out(w), "f32")
 
 
-def test_config2_gqa_decode_with_append(gpu_lib):
-    w = config_workload(2)
+def test_gqa_decode_with_append(gpu_lib):
+    w = named_workload("gqa_decode_bf16")
     ref = oracle_out(w)
     for split in (0, 512, -1):
         assert_close(gpu_decode(gpu_lib, w, split=split), ref, "bf16")
 
 
-def test_config3_chunked_prefill(gpu_lib):
-    w = config_workload(3)
+def test_chunked_prefill(gpu_lib):
+    w = named_workload("chunked_prefill_bf16")
     assert_close(gpu_prefill(gpu_lib, w), oracle_out(w, causal=True), "bf16")
 
 
-def test_config4_shared_prefix_decode(gpu_lib):
-    w = config_workload(4)
+def test_shared_prefix_decode(gpu_lib):
+    w = named_workload("shared_prefix_decode_bf16")
     assert_close(gpu_decode(gpu_lib, w), oracle_out(w), "bf16")
 
 
-def test_config5_long_decode_subset(gpu_lib):
-    w = config_workload(5, batch=6)
+def test_long_decode_subset(gpu_lib):
+    w = named_workload("long_decode_bf16", batch=6)
     assert_close(gpu_decode(gpu_lib, w, split=512), oracle_out(w), "bf16")
 
 
 @pytest.mark.parametrize("bs", [32, 64, 128, 256])
-def test_config5_page_size_variants_subset(gpu_lib, bs):
-    w = config_workload(5, bs=bs, batch=4)
+def test_long_decode_page_size_variants_subset(gpu_lib, bs):
+    w = named_workload("long_decode_bf16", bs=bs, batch=4)
     assert_close(gpu_decode(gpu_lib, w, split=512), oracle_out(w), "bf16")
 
 
-def test_config5_full_size_sampled(gpu_lib):
+def test_long_decode_full_size_sampled(gpu_lib):
     """Full 64-sequence workload, split 512 (the benchmarked launch); the oracle
     checks a sample of sequences: the shortest, the longest and a few others."""
-    w = config_workload(5)
+    w = named_workload("long_decode_bf16")
     got = gpu_decode(gpu_lib, w, split=512)
     order = np.argsort(w.context_lens)
     seqs = sorted(set([int(order[0]), int(order[-1]), int(order[len(order) // 2]), 3, 17, 42]))
@@ -191,7 +191,7 @@ def test_prefill_block_permutation_bit_identical(gpu_lib):
 
 
 def test_shared_prefix_equals_private_copies(gpu_lib):
-    w = config_workload(4, batch=4)
+    w = named_workload("shared_prefix_decode_bf16", batch=4)
     base = gpu_decode(gpu_lib, w)
     S = int(w.meta["shared_prefix_blocks"])
     kp = np.concatenate([w.k_pool, w.k_pool[w.block_table[:, :S].ravel()]])
@@ -211,12 +211,12 @@ def test_one_token_context_returns_v_row_exactly(gpu_lib):
 
 
 def test_deterministic_bits(gpu_lib):
-    w = config_workload(2)
+    w = named_workload("gqa_decode_bf16")
     t = upload(w)
     a = gpu_decode(gpu_lib, w, t=t)
     b = gpu_decode(gpu_lib, w, t=t)
     assert np.array_equal(a, b)
-    w3 = config_workload(3, batch=2)
+    w3 = named_workload("chunked_prefill_bf16", batch=2)
     t3 = upload(w3)
     assert np.array_equal(gpu_prefill(gpu_lib, w3, t=t3), gpu_prefill(gpu_lib, w3, t=t3))
 

@@ -12,6 +12,6 @@ from .synth import (  # noqa: F401
     Workload,
     bf16_round_bits,
     build_workload,
-    config_workload,
-    CONFIG_NAMES,
+    WORKLOADS,
+    named_workload,
 )

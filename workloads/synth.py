@@ -272,51 +272,57 @@ def build_workload(
     )
 
 
-CONFIG_NAMES = {
-    1: "decode_f32_b1_h4_d64_ctx128",
-    2: "decode_gqa_bf16_b8_h32x8_d128_ctx128-2048_append",
-    3: "chunked_prefill_bf16_b4_ctx1536+512_h32x8_d128_causal",
-    4: "shared_prefix_decode_bf16_b16_prefix1024+256_h32x8_d128",
-    5: "long_decode_bf16_b64_lognormal8192_h64x8_d128",
+# The reference workloads: name -> (seed, description).
+WORKLOADS = {
+    "single_decode_f32": (1, "decode, fp32, 1 sequence of 128 tokens, 4 heads (no GQA), head_dim 64, "
+                             "8 blocks of 16 in a 64-block pool"),
+    "gqa_decode_bf16": (2, "decode, bf16, 8 sequences of 128..2048 tokens, 32/8 heads, head_dim 128, "
+                           "block 16, pool 2x the needed blocks, one appended token per sequence"),
+    "chunked_prefill_bf16": (3, "causal chunked prefill, bf16, 4 sequences: 512-token chunk after 1536 "
+                                "tokens, 32/8 heads, head_dim 128, block 16"),
+    "shared_prefix_decode_bf16": (4, "decode, bf16, 16 sequences sharing 64 physical blocks (1024-token "
+                                     "prefix) plus 256 private tokens each, 32/8 heads, head_dim 128"),
+    "long_decode_bf16": (5, "decode, bf16, 64 sequences, log-normal lengths (median 8192, clipped to "
+                            "2048..32768), 64/8 heads, head_dim 128, block 16, one appended token each"),
 }
 
 
-def config_workload(i: int, bs: int | None = None, threads: int | None = None,
-                    batch: int | None = None) -> Workload:
-    """The five reference workloads (seed = config number).
+def named_workload(name: str, bs: int | None = None, threads: int | None = None,
+                   batch: int | None = None) -> Workload:
+    """One of the reference workloads (seeded; see ``WORKLOADS``).
 
-    ``bs`` overrides the page size (power-of-two variant of config 5);
-    ``batch`` keeps only the first ``batch`` sequences' lengths (same draws).
+    ``bs`` overrides the page size (power-of-two page-size variants);
+    ``batch`` keeps only the first ``batch`` sequences (same draws).
     """
+    i = WORKLOADS[name][0]
     ss = np.random.SeedSequence(i)
     rng = np.random.default_rng(ss.spawn(1)[0])  # same stream as build's c_struct
     common = dict(seed=i, structure_rng=rng, threads=threads)
-    if i == 1:
-        # 1 sequence, 128 tokens = 8 blocks of 16 out of a 64-block pool
-        return build_workload(name=CONFIG_NAMES[1], kind="decode", dtype="f32", Hq=4, Hkv=4,
+    if name == "single_decode_f32":
+        return build_workload(name=name, kind="decode", dtype="f32", Hq=4, Hkv=4,
                               D=64, bs=bs or 16, context_lens=[128], NB=64, **common)
-    if i == 2:
+    if name == "gqa_decode_bf16":
         ctx = rng.integers(128, 2049, size=8)
         ctx = ctx[:batch] if batch else ctx
-        return build_workload(name=CONFIG_NAMES[2], kind="decode", dtype="bf16", Hq=32, Hkv=8,
+        return build_workload(name=name, kind="decode", dtype="bf16", Hq=32, Hkv=8,
                               D=128, bs=bs or 16, context_lens=ctx,
                               append_lens=np.ones(len(ctx), np.int64), **common)
-    if i == 3:
+    if name == "chunked_prefill_bf16":
         n = (batch or 4)
-        return build_workload(name=CONFIG_NAMES[3], kind="prefill", dtype="bf16", Hq=32, Hkv=8,
+        return build_workload(name=name, kind="prefill", dtype="bf16", Hq=32, Hkv=8,
                               D=128, bs=bs or 16, context_lens=[2048] * n, q_lens=[512] * n,
                               append_lens=[512] * n, causal=True, **common)
-    if i == 4:
+    if name == "shared_prefix_decode_bf16":
         n = (batch or 16)
         bsz = bs or 16
-        return build_workload(name=CONFIG_NAMES[4], kind="decode", dtype="bf16", Hq=32, Hkv=8,
+        return build_workload(name=name, kind="decode", dtype="bf16", Hq=32, Hkv=8,
                               D=128, bs=bsz, context_lens=[1280] * n,
                               shared_prefix_blocks=1024 // bsz, **common)
-    if i == 5:
+    if name == "long_decode_bf16":
         ctx = np.rint(rng.lognormal(mean=math.log(8192), sigma=math.log(2), size=64))
         ctx = np.clip(ctx, 2048, 32768).astype(np.int64)
         ctx = ctx[:batch] if batch else ctx
-        return build_workload(name=CONFIG_NAMES[5], kind="decode", dtype="bf16", Hq=64, Hkv=8,
+        return build_workload(name=name, kind="decode", dtype="bf16", Hq=64, Hkv=8,
                               D=128, bs=bs or 16, context_lens=ctx,
                               append_lens=np.ones(len(ctx), np.int64), **common)
-    raise ValueError(f"no config {i}")
+    raise ValueError(f"no workload {name}")
