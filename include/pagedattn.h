@@ -34,8 +34,7 @@
  *
  * All calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  * stream).  No call allocates device or host memory, and none keeps state
- * between calls except a per-process cache of the current device's compute-
- * unit count.  Calls are thread-safe.
+ * between calls.  Calls are thread-safe.
  *
  * Status: 0 = success.  A negative value is an invalid argument found on the
  * host before anything is enqueued (no buffer is touched).  A positive value
@@ -111,19 +110,25 @@ int kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache
               void* stream);
 
 /*
- * Bytes of fp32 workspace paged_attn_decode needs for these sizes.  The
- * split-KV partitioning (a long context cut into split_tokens-long pieces
- * whose partial softmax states are merged afterwards) is this library's
- * reading of how to spread one decode row over many compute units; the pages
- * only motivate long contexts.  split_tokens: 0 = choose automatically from
- * (num_seqs, num_kv_heads, max_context_len), -1 = never split, else a power
- * of two >= 16.  Returns 0 for invalid arguments.
+ * Bytes of workspace paged_attn_decode needs for these sizes.  Split-KV --
+ * cutting a row's context into pieces whose partial softmax states (output,
+ * running max, running sum) are merged afterwards -- is this library's
+ * reading of how to spread long decode rows over many compute units; the
+ * pages only motivate long contexts.  split_tokens:
+ *    0  balanced split: 8 wavefronts per compute unit of the current device
+ *       (256 units if none is visible) each take an equal share of the
+ *       batch's 16-token chunks, so the pieces follow the work, not a fixed
+ *       length;
+ *   -1  never split;
+ *  > 0  fixed pieces of split_tokens keys (a power of two >= 16).
+ * Returns 0 for invalid arguments.
  */
 size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_heads,
                                         int32_t num_kv_heads, int32_t head_dim,
                                         int32_t max_context_len, int32_t split_tokens);
 
-/* The split size paged_attn_decode will use (resolves split_tokens == 0). */
+/* The split paged_attn_decode will use: 0 for the balanced split, -1 for
+ * none, else the fixed piece length (0 also for invalid arguments). */
 int32_t paged_attn_decode_split_tokens(int32_t num_seqs, int32_t num_kv_heads,
                                        int32_t max_context_len, int32_t split_tokens);
 
