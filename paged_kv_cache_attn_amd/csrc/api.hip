@@ -15,7 +15,7 @@ constexpr int kAutoSplitMin = 64;
 constexpr long long kAutoTargetUnits = 2048;  // ~8 wavefronts per compute unit
 constexpr int kStreamWavesPerCU = 8;          // resident decode wavefronts per compute unit
 constexpr int kStreamMinChunks = 8;           // 16-token chunks per wavefront, at least
-constexpr int kStreamMaxSeqs = 16384;         // chunk prefix of all rows fits in LDS
+constexpr int kStreamMaxSeqs = 4096;          // chunk prefix of all rows fits in 16 KB of LDS
 constexpr int kDefaultCUs = 256;              // MI355X, when no device is visible
 
 int ilog2(long long x) {

@@ -10,13 +10,19 @@
 //
 // Work-group: 4 wavefronts, 128 query rows = QT = 128/g query positions x the
 // g query heads of one kv-head, so every K/V tile read from HBM serves all g
-// heads (GQA).  Per 64-key tile:
-//   S^T = K Q^T   with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q^T
-//                 kept in registers); each lane then owns one query row's
-//                 scores, so softmax statistics are per-lane scalars;
-//   O^T += V^T P^T with the same MFMA (A = V^T rows from LDS -- V slabs are
-//                 dimension-major in the pool, so no transpose is needed --
-//                 B = P^T straight from the S^T accumulators, rounded to bf16).
+// heads (GQA).  Two work-groups share a compute unit (<= 256 registers per
+// lane, 64 KB of LDS each), so one's softmax overlaps the other's MFMAs.
+// Per 64-key tile:
+//   * the tile's K (64 x D) and V^T (D x 64) are fetched with direct-to-LDS
+//     loads (global_load_lds_dwordx4) into one of two LDS buffers while the
+//     previous tile is computed; each lane picks the global piece that must
+//     land at its LDS slot, which is how the XOR swizzle is applied;
+//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q^T
+//     kept in registers); each lane then owns one query row's scores, so
+//     softmax statistics are per-lane scalars;
+//   * O^T += V^T P^T with the same MFMA (A = V^T rows from LDS -- V slabs are
+//     dimension-major in the pool, so no transpose is needed -- B = P^T
+//     straight from the S^T accumulators, rounded to bf16).
 // The K rows of the S^T product are read in a permuted order inside each
 // 16-key group (quarters 1 and 2 swapped) so that the accumulator registers
 // a lane holds are exactly the 8 consecutive keys the next MFMA's B operand
@@ -30,6 +36,10 @@ namespace {
 constexpr float kLazyRescale = 8.0f;  // log2 units
 constexpr int kTileKeys = 64;
 constexpr int kRowsPerWG = 128;
+constexpr int kThreads = 256;
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef __attribute__((address_space(1))) const void* global_ptr;
 
 // key slot (0..31) of a 32-key group -> key offset inside the group
 __device__ __forceinline__ int key_of_slot(int u) {
@@ -38,13 +48,25 @@ __device__ __forceinline__ int key_of_slot(int u) {
   return (u & 16) | (qs << 2) | (u & 3);
 }
 
+// 16-byte chunk position inside an LDS row (bank-conflict-free reads)
+template <int KCH>
+__device__ __forceinline__ int k_swz(int row, int c) { return c ^ (row & (KCH - 1) & 15); }
+__device__ __forceinline__ int v_swz(int d, int c) { return c ^ (d & 7); }
+
+template <int D>
+struct Tile {
+  u32x4 k[kTileKeys * (D / 8)];   // row-major [key][16-byte chunk], swizzled
+  u32x4 v[D * (kTileKeys / 8)];   // row-major [dim][8-key chunk], swizzled
+};
+
 template <int D, bool kMods>
-__global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const PrefillArgs a) {
   constexpr int KCH = D / 8;   // 16-byte chunks per K row
   constexpr int KSTEPS = D / 16;
   constexpr int DT = D / 32;   // output 32-dim tiles
-  __shared__ u32x4 k_lds[kTileKeys * KCH];
-  __shared__ u32x4 v_lds[D * (kTileKeys / 8)];
+  constexpr int KPIECES = kTileKeys * KCH / kThreads;       // K pieces per thread per tile
+  constexpr int VPIECES = D * (kTileKeys / 8) / kThreads;   // V^T pieces per thread per tile
+  __shared__ Tile<D> tiles[2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -82,8 +104,45 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
   const int pos_last = n - Lq + q_last;
   const int wg_hi = a.causal ? min(n, pos_last + 1) : n;
   const int wg_lo = a.window > 0 ? max(0, pos_first - a.window + 1) : 0;
-  const int safe_hi = a.causal ? min(n, pos_first + 1) : n;            // every row admits keys < safe_hi
+  const int safe_hi = a.causal ? min(n, pos_first + 1) : n;                // every row admits keys < safe_hi
   const int safe_lo = a.window > 0 ? max(0, pos_last - a.window + 1) : 0;  // ... and >= safe_lo
+
+  const int32_t* table = a.block_tables + (size_t)b * a.bt_stride;
+  const int bs = 1 << a.bs_log2;
+  const size_t slab_bytes = (size_t)bs * D * 2;
+  const char* kpool = static_cast<const char*>(a.k_cache) + (size_t)kvh * slab_bytes;
+  const char* vpool = static_cast<const char*>(a.v_cache) + (size_t)kvh * slab_bytes;
+  const size_t blk_stride = (size_t)a.Hkv * slab_bytes;
+  const int last_blk = (n - 1) >> a.bs_log2;
+
+  // Issue the direct-to-LDS loads of the tile starting at key k0 into buffer
+  // `buf`.  Keys at or past n are fetched from key k0 (finite data, masked).
+  auto issue_tile = [&](int k0, int buf) {
+    char* lk = reinterpret_cast<char*>(tiles[buf].k);
+    char* lv = reinterpret_cast<char*>(tiles[buf].v);
+#pragma unroll
+    for (int it = 0; it < KPIECES; ++it) {
+      const int p = (it * 4 + wave) * 64 + lane;   // LDS slot this lane fills
+      const int row = p / KCH;
+      const int c = k_swz<KCH>(row, p % KCH);       // logical chunk stored there
+      int tok = k0 + row;
+      if (tok >= n) tok = k0;
+      const int blk = table[min(tok >> a.bs_log2, last_blk)];
+      const char* src = kpool + (size_t)blk * blk_stride + ((size_t)(tok & (bs - 1)) * D + c * 8) * 2;
+      __builtin_amdgcn_global_load_lds((global_ptr)src, (lds_ptr)(lk + (it * 4 + wave) * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int it = 0; it < VPIECES; ++it) {
+      const int p = (it * 4 + wave) * 64 + lane;
+      const int d = p >> 3;
+      const int c = v_swz(d, p & 7);                // 8-key chunk stored there
+      int tok = k0 + 8 * c;
+      if (tok >= n) tok = k0;
+      const int blk = table[min(tok >> a.bs_log2, last_blk)];
+      const char* src = vpool + (size_t)blk * blk_stride + ((size_t)d * bs + (tok & (bs - 1))) * 2;
+      __builtin_amdgcn_global_load_lds((global_ptr)src, (lds_ptr)(lv + (it * 4 + wave) * 1024), 16, 0, 0);
+    }
+  };
 
   // Q^T operand (B of S^T): this lane's row, dims 16*ks + 8*hl .. +8
   bf16x8 qb[KSTEPS];
@@ -109,54 +168,41 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
     for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
   float m_run = kNegInf, l_run = 0.f;
 
-  const int32_t* table = a.block_tables + (size_t)b * a.bt_stride;
-  const int bs = 1 << a.bs_log2;
-  const size_t slab_bytes = (size_t)bs * D * 2;
-  const char* kpool = static_cast<const char*>(a.k_cache);
-  const char* vpool = static_cast<const char*>(a.v_cache);
-
   const int k_begin = wg_lo & ~(kTileKeys - 1);
-  for (int k0 = k_begin; k0 < wg_hi; k0 += kTileKeys) {
+  const int ntiles = wg_hi > k_begin ? (wg_hi - k_begin + kTileKeys - 1) / kTileKeys : 0;
+  if (ntiles > 0) issue_tile(k_begin, 0);
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int k0 = k_begin + t * kTileKeys;
+    const int buf = t & 1;
+    // tile t has landed in every wave's LDS slots; every wave is done with tile t-1
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
-    // ---- gather the K tile (64 rows x D) and the V^T tile (D rows x 64) ----
+    __asm__ volatile("" ::: "memory");
+    if (k0 + kTileKeys > n) {
+      // V^T entries of keys >= n hold whatever the pool had: zero them (P is 0 there)
 #pragma unroll
-    for (int it = 0; it < (kTileKeys * KCH) / 256; ++it) {
-      const int pi = tid + 256 * it;
-      const int key = pi / KCH;
-      const int c = pi % KCH;
-      const int tok = k0 + key;
-      u32x4 x = {0, 0, 0, 0};
-      if (tok < n) {
-        const int blk = table[tok >> a.bs_log2];
-        const char* src = kpool + ((size_t)blk * a.Hkv + kvh) * slab_bytes +
-                          ((size_t)(tok & (bs - 1)) * D + c * 8) * 2;
-        x = load16(src);
-      }
-      k_lds[key * KCH + (c ^ (key & (KCH - 1) & 15))] = x;
-    }
-#pragma unroll
-    for (int it = 0; it < (D * (kTileKeys / 8)) / 256; ++it) {
-      const int pi = tid + 256 * it;
-      const int d = pi >> 3;
-      const int c = pi & 7;  // 8-key chunk
-      const int tok = k0 + 8 * c;
-      u32x4 x = {0, 0, 0, 0};
-      if (tok < n) {
-        const int blk = table[tok >> a.bs_log2];
-        const char* src = vpool + ((size_t)blk * a.Hkv + kvh) * slab_bytes +
-                          ((size_t)d * bs + (tok & (bs - 1))) * 2;
-        x = load16(src);
-        if (tok + 8 > n) {  // keys past the end may hold anything
+      for (int it = 0; it < VPIECES; ++it) {
+        const int p = it * kThreads + tid;
+        const int d = p >> 3;
+        const int c = v_swz(d, p & 7);
+        const int tok = k0 + 8 * c;
+        if (tok + 8 > n) {
+          u32x4 x = tiles[buf].v[p];
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
             const int j = tok + 2 * w;
             x[w] &= (j < n ? 0xffffu : 0u) | (j + 1 < n ? 0xffff0000u : 0u);
           }
+          tiles[buf].v[p] = x;
         }
       }
-      v_lds[d * 8 + (c ^ (d & 7))] = x;
+      __syncthreads();
     }
-    __syncthreads();
+    if (t + 1 < ntiles) issue_tile(k0 + kTileKeys, buf ^ 1);
+
+    const u32x4* kt = tiles[buf].k;
+    const u32x4* vt = tiles[buf].v;
 
     // ---- S^T = K Q^T : two 32-key groups ----
     f32x16 sacc[2];
@@ -167,8 +213,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
       const int krow = 32 * kg + key_of_slot(col);
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
-        const int c = 2 * ks + hl;
-        const bf16x8 ka = __builtin_bit_cast(bf16x8, k_lds[krow * KCH + (c ^ (krow & (KCH - 1) & 15))]);
+        const bf16x8 ka = __builtin_bit_cast(bf16x8, kt[krow * KCH + k_swz<KCH>(krow, 2 * ks + hl)]);
         sacc[kg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[ks], sacc[kg], 0, 0, 0);
       }
     }
@@ -233,8 +278,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(const PrefillArgs a) 
       const int d = 32 * dt + col;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const int c = 2 * s + hl;
-        const bf16x8 va = __builtin_bit_cast(bf16x8, v_lds[d * 8 + (c ^ (d & 7))]);
+        const bf16x8 va = __builtin_bit_cast(bf16x8, vt[d * 8 + v_swz(d, 2 * s + hl)]);
         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[s], oacc[dt], 0, 0, 0);
       }
     }
@@ -267,11 +311,11 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, int D, hipStream_t s) {
   if (blocks <= 0) return hipSuccess;
   const bool mods = a.softcap > 0.f || a.alibi != nullptr;
   if (D == 64) {
-    if (mods) hipLaunchKernelGGL((prefill_mfma_kernel<64, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((prefill_mfma_kernel<64, false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    if (mods) hipLaunchKernelGGL((prefill_mfma_kernel<64, true>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((prefill_mfma_kernel<64, false>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
   } else {
-    if (mods) hipLaunchKernelGGL((prefill_mfma_kernel<128, true>), dim3((unsigned)blocks), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((prefill_mfma_kernel<128, false>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    if (mods) hipLaunchKernelGGL((prefill_mfma_kernel<128, true>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((prefill_mfma_kernel<128, false>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
   }
   return hipGetLastError();
 }
