@@ -51,12 +51,18 @@ __device__ __forceinline__ int key_of_slot(int u) {
 // 16-byte chunk position inside an LDS row (bank-conflict-free reads)
 template <int KCH>
 __device__ __forceinline__ int k_swz(int row, int c) { return c ^ (row & (KCH - 1) & 15); }
-__device__ __forceinline__ int v_swz(int d, int c) { return c ^ (d & 7); }
+// The V^T tile is stored per tile-block j (the keys of one pool block, at
+// most 64): [j][d][cpb chunks of 8 keys], cpb = min(bs, 64) / 8.  A row is
+// cpb*16 bytes, so rows d and d + 16/cpb share banks: swizzle the chunk by
+// d*cpb/16 to keep 16 consecutive rows on 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int v_swz(int d, int cpb_log2) {
+  return ((d << cpb_log2) >> 4) & ((1 << cpb_log2) - 1);
+}
 
 template <int D>
 struct Tile {
   u32x4 k[kTileKeys * (D / 8)];   // row-major [key][16-byte chunk], swizzled
-  u32x4 v[D * (kTileKeys / 8)];   // row-major [dim][8-key chunk], swizzled
+  u32x4 v[D * (kTileKeys / 8)];   // [tile-block][dim][8-key chunk], swizzled
 };
 
 template <int D, bool kMods>
@@ -70,7 +76,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar)
   const int hl = lane >> 5;      // half of the wave
   const int col = lane & 31;     // query row inside the wave's 32 rows
 
@@ -115,32 +121,44 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
   const size_t blk_stride = (size_t)a.Hkv * slab_bytes;
   const int last_blk = (n - 1) >> a.bs_log2;
 
+  // Tile geometry: a 64-key tile covers nbt = 64/kb pool blocks of kb keys.
+  const int kb_log2 = min(a.bs_log2, 6);
+  const int cpb_log2 = kb_log2 - 3;
+  const int cpb = 1 << cpb_log2;  // 8-key chunks per block row inside the tile
+  const int dcpb_log2 = cpb_log2 + (D == 128 ? 7 : 6);  // log2(D * cpb)
+
   // Issue the direct-to-LDS loads of the tile starting at key k0 into buffer
-  // `buf`.  Keys at or past n are fetched from key k0 (finite data, masked).
+  // `buf`.  Every instruction's 64 lanes fill 64 consecutive LDS slots that
+  // lie in one pool block, so the block id is a scalar (one table entry per
+  // wave-instruction); entries past the sequence's last block are clamped to
+  // it (those keys are masked, their V entries zeroed).
   auto issue_tile = [&](int k0, int buf) {
     char* lk = reinterpret_cast<char*>(tiles[buf].k);
     char* lv = reinterpret_cast<char*>(tiles[buf].v);
+    const int j0 = k0 >> a.bs_log2;
 #pragma unroll
     for (int it = 0; it < KPIECES; ++it) {
-      const int p = (it * 4 + wave) * 64 + lane;   // LDS slot this lane fills
-      const int row = p / KCH;
-      const int c = k_swz<KCH>(row, p % KCH);       // logical chunk stored there
-      int tok = k0 + row;
-      if (tok >= n) tok = k0;
-      const int blk = table[min(tok >> a.bs_log2, last_blk)];
+      const int q = wave * KPIECES + it;              // wave-uniform instruction index
+      const int row0 = q * (64 / KCH);
+      const int blk = table[min((k0 + row0) >> a.bs_log2, last_blk)];
+      const int row = row0 + lane / KCH;
+      const int c = k_swz<KCH>(row, lane % KCH);      // logical chunk of this LDS slot
+      const int tok = k0 + row;
       const char* src = kpool + (size_t)blk * blk_stride + ((size_t)(tok & (bs - 1)) * D + c * 8) * 2;
-      __builtin_amdgcn_global_load_lds((global_ptr)src, (lds_ptr)(lk + (it * 4 + wave) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((global_ptr)src, (lds_ptr)(lk + q * 1024), 16, 0, 0);
     }
 #pragma unroll
     for (int it = 0; it < VPIECES; ++it) {
-      const int p = (it * 4 + wave) * 64 + lane;
-      const int d = p >> 3;
-      const int c = v_swz(d, p & 7);                // 8-key chunk stored there
-      int tok = k0 + 8 * c;
-      if (tok >= n) tok = k0;
-      const int blk = table[min(tok >> a.bs_log2, last_blk)];
-      const char* src = vpool + (size_t)blk * blk_stride + ((size_t)d * bs + (tok & (bs - 1))) * 2;
-      __builtin_amdgcn_global_load_lds((global_ptr)src, (lds_ptr)(lv + (it * 4 + wave) * 1024), 16, 0, 0);
+      const int q = wave * VPIECES + it;
+      const int slot0 = q * 64;
+      const int j = slot0 >> dcpb_log2;               // tile-block of this instruction
+      const int blk = table[min(j0 + (j << kb_log2 >> a.bs_log2), last_blk)];
+      const int local = slot0 - (j << dcpb_log2) + lane;
+      const int d = local >> cpb_log2;
+      const int cc = (local & (cpb - 1)) ^ v_swz(d, cpb_log2);  // logical chunk of this LDS slot
+      const int off = ((k0 + (j << kb_log2)) & (bs - 1)) + cc * 8;
+      const char* src = vpool + (size_t)blk * blk_stride + ((size_t)d * bs + off) * 2;
+      __builtin_amdgcn_global_load_lds((global_ptr)src, (lds_ptr)(lv + q * 1024), 16, 0, 0);
     }
   };
 
@@ -184,9 +202,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
 #pragma unroll
       for (int it = 0; it < VPIECES; ++it) {
         const int p = it * kThreads + tid;
-        const int d = p >> 3;
-        const int c = v_swz(d, p & 7);
-        const int tok = k0 + 8 * c;
+        const int j = p >> dcpb_log2;
+        const int local = p - (j << dcpb_log2);
+        const int d = local >> cpb_log2;
+        const int cc = (local & (cpb - 1)) ^ v_swz(d, cpb_log2);
+        const int tok = k0 + (j << kb_log2) + 8 * cc;
         if (tok + 8 > n) {
           u32x4 x = tiles[buf].v[p];
 #pragma unroll
@@ -207,78 +227,117 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
     // ---- S^T = K Q^T : two 32-key groups ----
     f32x16 sacc[2];
 #pragma unroll
-    for (int kg = 0; kg < 2; ++kg) {
+    for (int kg = 0; kg < 2; ++kg)
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[kg][i] = 0.f;
-      const int krow = 32 * kg + key_of_slot(col);
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+#pragma unroll
+      for (int kg = 0; kg < 2; ++kg) {  // two independent accumulation chains
+        const int krow = 32 * kg + key_of_slot(col);
         const bf16x8 ka = __builtin_bit_cast(bf16x8, kt[krow * KCH + k_swz<KCH>(krow, 2 * ks + hl)]);
         sacc[kg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[ks], sacc[kg], 0, 0, 0);
       }
     }
 
-    // ---- scores (log2 domain), masks ----
+    // ---- scores, masks, online softmax; P (bf16) as the B operand of O^T += V^T P^T ----
     const bool full = (k0 >= safe_lo) && (k0 + kTileKeys <= safe_hi);
-    float cmax = kNegInf;
+    bf16x8 pb[4];
+    if constexpr (!kMods) {
+      // s * scale * log2(e) is folded into the exp argument; scale > 0 here
+      if (!full) {
 #pragma unroll
-    for (int kg = 0; kg < 2; ++kg) {
+        for (int kg = 0; kg < 2; ++kg)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int slot = 8 * (i >> 2) + 4 * hl + (i & 3);
-        const int key = k0 + 32 * kg + key_of_slot(slot);
-        float sv;
-        if constexpr (kMods) {
+          for (int i = 0; i < 16; ++i) {
+            const int key = k0 + 32 * kg + key_of_slot(8 * (i >> 2) + 4 * hl + (i & 3));
+            if (!(key >= row_lo && key < row_hi)) sacc[kg][i] = kNegInf;
+          }
+      }
+      float cmax = kNegInf;
+#pragma unroll
+      for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) cmax = fmaxf(cmax, sacc[kg][i]);
+      cmax = fmaxf(cmax, shfl_xor32(cmax)) * scale_log2;
+      const float m_new = fmaxf(m_run, cmax);
+      const bool need = m_new > m_run + kLazyRescale;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
+        if (need) m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+      }
+      const float nm = (m_run == kNegInf) ? 0.f : -m_run;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        u32x4 w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float p0 = fast_exp2(fmaf(sacc[s >> 1][8 * (s & 1) + 2 * j], scale_log2, nm));
+          const float p1 = fast_exp2(fmaf(sacc[s >> 1][8 * (s & 1) + 2 * j + 1], scale_log2, nm));
+          l_run += p0 + p1;
+          w[j] = cvt_bf16x2(p0, p1);
+        }
+        pb[s] = __builtin_bit_cast(bf16x8, w);
+      }
+    } else {
+      float cmax = kNegInf;
+#pragma unroll
+      for (int kg = 0; kg < 2; ++kg) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = k0 + 32 * kg + key_of_slot(8 * (i >> 2) + 4 * hl + (i & 3));
           float x = sacc[kg][i] * a.scale;
           if (a.softcap > 0.f) {
             const float ez = fast_exp2(2.f * kLog2e * (x / a.softcap));
             x = a.softcap * (1.f - 2.f / (ez + 1.f));
           }
           x += alibi_slope * (float)(key - pos);
-          sv = x * kLog2e;
-        } else {
-          sv = sacc[kg][i] * scale_log2;
+          float sv = x * kLog2e;
+          if (!full) sv = (key >= row_lo && key < row_hi) ? sv : kNegInf;
+          sacc[kg][i] = sv;
+          cmax = fmaxf(cmax, sv);
         }
-        if (!full) sv = (key >= row_lo && key < row_hi) ? sv : kNegInf;
-        sacc[kg][i] = sv;
-        cmax = fmaxf(cmax, sv);
       }
-    }
-    cmax = fmaxf(cmax, shfl_xor32(cmax));
-    const float m_new = fmaxf(m_run, cmax);
-    const bool need = m_new > m_run + kLazyRescale;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
-      if (need) m_run = m_new;
-      l_run *= alpha;
+      cmax = fmaxf(cmax, shfl_xor32(cmax));
+      const float m_new = fmaxf(m_run, cmax);
+      const bool need = m_new > m_run + kLazyRescale;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
+        if (need) m_run = m_new;
+        l_run *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+        for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
-    }
-    const float msafe = (m_run == kNegInf) ? 0.f : m_run;
-
-    // ---- P (bf16) as the B operand of O^T += V^T P^T ----
-    bf16x8 pb[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      u32x4 w;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float p0 = fast_exp2(sacc[s >> 1][8 * (s & 1) + 2 * j] - msafe);
-        const float p1 = fast_exp2(sacc[s >> 1][8 * (s & 1) + 2 * j + 1] - msafe);
-        const uint32_t packed = pack_bf16x2(p0, p1);
-        l_run += bf16lo(packed) + bf16hi(packed);
-        w[j] = packed;
+          for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
       }
-      pb[s] = __builtin_bit_cast(bf16x8, w);
-    }
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const int d = 32 * dt + col;
+      const float msafe = (m_run == kNegInf) ? 0.f : m_run;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const bf16x8 va = __builtin_bit_cast(bf16x8, vt[d * 8 + v_swz(d, 2 * s + hl)]);
+        u32x4 w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float p0 = fast_exp2(sacc[s >> 1][8 * (s & 1) + 2 * j] - msafe);
+          const float p1 = fast_exp2(sacc[s >> 1][8 * (s & 1) + 2 * j + 1] - msafe);
+          l_run += p0 + p1;
+          w[j] = cvt_bf16x2(p0, p1);
+        }
+        pb[s] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {  // DT independent accumulation chains
+        const int d = 32 * dt + col;
+        const int c = 2 * s + hl;  // 8-key chunk of the tile
+        const int j = c >> cpb_log2;
+        const int cc = c & (cpb - 1);
+        const bf16x8 va = __builtin_bit_cast(bf16x8, vt[(((j * D + d) << cpb_log2) | (cc ^ v_swz(d, cpb_log2)))]);
         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[s], oacc[dt], 0, 0, 0);
       }
     }
@@ -295,8 +354,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
     for (int g4 = 0; g4 < 4; ++g4) {
       const int d = 32 * dt + 8 * g4 + 4 * hl;
       uint2 w;
-      w.x = pack_bf16x2(oacc[dt][4 * g4 + 0] * inv, oacc[dt][4 * g4 + 1] * inv);
-      w.y = pack_bf16x2(oacc[dt][4 * g4 + 2] * inv, oacc[dt][4 * g4 + 3] * inv);
+      w.x = cvt_bf16x2(oacc[dt][4 * g4 + 0] * inv, oacc[dt][4 * g4 + 1] * inv);
+      w.y = cvt_bf16x2(oacc[dt][4 * g4 + 2] * inv, oacc[dt][4 * g4 + 3] * inv);
       *reinterpret_cast<uint2*>(orow + d * 2) = w;
     }
   }
@@ -309,7 +368,8 @@ int prefill_rows_per_tile(int g) { return kRowsPerWG / g; }
 hipError_t launch_prefill_mfma(const PrefillArgs& a, int D, hipStream_t s) {
   const long long blocks = (long long)a.num_seqs * a.Hkv * a.q_tiles;
   if (blocks <= 0) return hipSuccess;
-  const bool mods = a.softcap > 0.f || a.alibi != nullptr;
+  // the fast path folds a positive scale into the exponent
+  const bool mods = a.softcap > 0.f || a.alibi != nullptr || !(a.scale > 0.f);
   if (D == 64) {
     if (mods) hipLaunchKernelGGL((prefill_mfma_kernel<64, true>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
     else hipLaunchKernelGGL((prefill_mfma_kernel<64, false>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
