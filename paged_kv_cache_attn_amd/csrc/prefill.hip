@@ -127,37 +127,47 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
   const int cpb = 1 << cpb_log2;  // 8-key chunks per block row inside the tile
   const int dcpb_log2 = cpb_log2 + (D == 128 ? 7 : 6);  // log2(D * cpb)
 
-  // Issue the direct-to-LDS loads of the tile starting at key k0 into buffer
-  // `buf`.  Every instruction's 64 lanes fill 64 consecutive LDS slots that
-  // lie in one pool block, so the block id is a scalar (one table entry per
-  // wave-instruction); entries past the sequence's last block are clamped to
-  // it (those keys are masked, their V entries zeroed).
-  auto issue_tile = [&](int k0, int buf) {
+  // Direct-to-LDS loads of a tile.  Wave w fills K rows 16w..16w+15 and V^T
+  // tile-block slots that hold keys of the same pool block (for bs = 16 the
+  // tile-block is w itself), so one table entry per wave per tile -- the block
+  // holding key k0 + 16w -- addresses all of its loads, and each instruction's
+  // 64 lanes read one contiguous run.  Entries past the sequence's last block
+  // are clamped to it (those keys are masked and their V entries zeroed).
+  // Lane-dependent parts of the addresses are fixed for the whole loop.
+  typedef const __attribute__((address_space(4))) int32_t* const_table_ptr;  // scalar loads
+  const const_table_ptr ctable = (const_table_ptr)table;
+  auto wave_block = [&](int k0) { return ctable[min((k0 + 16 * wave) >> a.bs_log2, last_blk)]; };
+  uint32_t k_off[KPIECES], v_off[VPIECES];
+  int v_j[VPIECES];
+#pragma unroll
+  for (int it = 0; it < KPIECES; ++it) {
+    const int rl = it * (64 / KCH) + lane / KCH;  // row - 16w
+    const int c = (lane % KCH) ^ (rl & (KCH - 1) & 15);
+    k_off[it] = (uint32_t)(rl * D + c * 8) * 2u;
+  }
+#pragma unroll
+  for (int it = 0; it < VPIECES; ++it) {
+    const int slot0 = (wave * VPIECES + it) * 64;
+    v_j[it] = slot0 >> dcpb_log2;
+    const int local = (slot0 & ((1 << dcpb_log2) - 1)) + lane;
+    const int d = local >> cpb_log2;
+    const int cc = (local & (cpb - 1)) ^ v_swz(d, cpb_log2);
+    v_off[it] = (uint32_t)(d * bs + cc * 8) * 2u;
+  }
+  auto issue_tile = [&](int k0, int buf, int blk) {
+    const char* kb = kpool + (size_t)blk * blk_stride + (size_t)((k0 + 16 * wave) & (bs - 1)) * D * 2;
+    const char* vb = vpool + (size_t)blk * blk_stride;
     char* lk = reinterpret_cast<char*>(tiles[buf].k);
     char* lv = reinterpret_cast<char*>(tiles[buf].v);
-    const int j0 = k0 >> a.bs_log2;
 #pragma unroll
     for (int it = 0; it < KPIECES; ++it) {
-      const int q = wave * KPIECES + it;              // wave-uniform instruction index
-      const int row0 = q * (64 / KCH);
-      const int blk = table[min((k0 + row0) >> a.bs_log2, last_blk)];
-      const int row = row0 + lane / KCH;
-      const int c = k_swz<KCH>(row, lane % KCH);      // logical chunk of this LDS slot
-      const int tok = k0 + row;
-      const char* src = kpool + (size_t)blk * blk_stride + ((size_t)(tok & (bs - 1)) * D + c * 8) * 2;
-      __builtin_amdgcn_global_load_lds((global_ptr)src, (lds_ptr)(lk + q * 1024), 16, 0, 0);
+      const int q = wave * KPIECES + it;
+      __builtin_amdgcn_global_load_lds((global_ptr)(kb + k_off[it]), (lds_ptr)(lk + q * 1024), 16, 0, 0);
     }
 #pragma unroll
     for (int it = 0; it < VPIECES; ++it) {
       const int q = wave * VPIECES + it;
-      const int slot0 = q * 64;
-      const int j = slot0 >> dcpb_log2;               // tile-block of this instruction
-      const int blk = table[min(j0 + (j << kb_log2 >> a.bs_log2), last_blk)];
-      const int local = slot0 - (j << dcpb_log2) + lane;
-      const int d = local >> cpb_log2;
-      const int cc = (local & (cpb - 1)) ^ v_swz(d, cpb_log2);  // logical chunk of this LDS slot
-      const int off = ((k0 + (j << kb_log2)) & (bs - 1)) + cc * 8;
-      const char* src = vpool + (size_t)blk * blk_stride + ((size_t)d * bs + off) * 2;
+      const char* src = vb + (size_t)((k0 + (v_j[it] << kb_log2)) & (bs - 1)) * 2 + v_off[it];
       __builtin_amdgcn_global_load_lds((global_ptr)src, (lds_ptr)(lv + q * 1024), 16, 0, 0);
     }
   };
@@ -188,11 +198,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
 
   const int k_begin = wg_lo & ~(kTileKeys - 1);
   const int ntiles = wg_hi > k_begin ? (wg_hi - k_begin + kTileKeys - 1) / kTileKeys : 0;
-  if (ntiles > 0) issue_tile(k_begin, 0);
+  int blk_next = 0;
+  if (ntiles > 0) {
+    issue_tile(k_begin, 0, wave_block(k_begin));
+    blk_next = wave_block(ntiles > 1 ? k_begin + kTileKeys : k_begin);
+  }
 
   for (int t = 0; t < ntiles; ++t) {
     const int k0 = k_begin + t * kTileKeys;
     const int buf = t & 1;
+    const int blk_issue = blk_next;  // block of tile t+1 for this wave (loaded one tile ahead)
+    blk_next = wave_block(t + 2 < ntiles ? k0 + 2 * kTileKeys : k0);
     // tile t has landed in every wave's LDS slots; every wave is done with tile t-1
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
@@ -219,7 +235,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
       }
       __syncthreads();
     }
-    if (t + 1 < ntiles) issue_tile(k0 + kTileKeys, buf ^ 1);
+    if (t + 1 < ntiles) issue_tile(k0 + kTileKeys, buf ^ 1, blk_issue);
 
     const u32x4* kt = tiles[buf].k;
     const u32x4* vt = tiles[buf].v;
