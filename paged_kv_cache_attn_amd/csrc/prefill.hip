@@ -49,6 +49,11 @@ __device__ __forceinline__ int key_of_slot(int u) {
 }
 
 // 16-byte chunk position inside an LDS row (bank-conflict-free reads)
+template <int P>
+struct Par {
+  static constexpr int value = P;
+};
+
 template <int KCH>
 __device__ __forceinline__ int k_swz(int row, int c) { return c ^ (row & (KCH - 1) & 15); }
 // The V^T tile is stored per tile-block j (the keys of one pool block, at
@@ -59,20 +64,23 @@ __device__ __forceinline__ int v_swz(int d, int cpb_log2) {
   return ((d << cpb_log2) >> 4) & ((1 << cpb_log2) - 1);
 }
 
-template <int D>
-struct Tile {
-  u32x4 k[kTileKeys * (D / 8)];   // row-major [key][16-byte chunk], swizzled
-  u32x4 v[D * (kTileKeys / 8)];   // [tile-block][dim][8-key chunk], swizzled
-};
-
-template <int D, bool kMods>
+// KBL = log2(min(block_size, 64)): keys of one pool block inside a 64-key tile.
+template <int D, bool kMods, int KBL>
 __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const PrefillArgs a) {
   constexpr int KCH = D / 8;   // 16-byte chunks per K row
   constexpr int KSTEPS = D / 16;
   constexpr int DT = D / 32;   // output 32-dim tiles
   constexpr int KPIECES = kTileKeys * KCH / kThreads;       // K pieces per thread per tile
   constexpr int VPIECES = D * (kTileKeys / 8) / kThreads;   // V^T pieces per thread per tile
-  __shared__ Tile<D> tiles[2];
+  // Two K and two V tile buffers, each its own LDS object: the compiler can
+  // then see that LDS reads of one buffer do not wait for the direct-to-LDS
+  // loads in flight into the other.
+  __shared__ u32x4 ktile0[kTileKeys * (D / 8)];  // [key][16-byte chunk], swizzled
+  __shared__ u32x4 ktile1[kTileKeys * (D / 8)];
+  __shared__ u32x4 vtile0[D * (kTileKeys / 8)];  // [tile-block][dim][8-key chunk], swizzled
+  __shared__ u32x4 vtile1[D * (kTileKeys / 8)];
+  auto kbuf = [&](auto P) -> u32x4* { if constexpr (decltype(P)::value == 0) return ktile0; else return ktile1; };
+  auto vbuf = [&](auto P) -> u32x4* { if constexpr (decltype(P)::value == 0) return vtile0; else return vtile1; };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -122,10 +130,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
   const int last_blk = (n - 1) >> a.bs_log2;
 
   // Tile geometry: a 64-key tile covers nbt = 64/kb pool blocks of kb keys.
-  const int kb_log2 = min(a.bs_log2, 6);
-  const int cpb_log2 = kb_log2 - 3;
-  const int cpb = 1 << cpb_log2;  // 8-key chunks per block row inside the tile
-  const int dcpb_log2 = cpb_log2 + (D == 128 ? 7 : 6);  // log2(D * cpb)
+  constexpr int kb_log2 = KBL;
+  constexpr int cpb_log2 = kb_log2 - 3;
+  constexpr int cpb = 1 << cpb_log2;  // 8-key chunks per block row inside the tile
+  constexpr int dcpb_log2 = cpb_log2 + (D == 128 ? 7 : 6);  // log2(D * cpb)
 
   // Direct-to-LDS loads of a tile.  Wave w fills K rows 16w..16w+15 and V^T
   // tile-block slots that hold keys of the same pool block (for bs = 16 the
@@ -154,16 +162,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
     const int cc = (local & (cpb - 1)) ^ v_swz(d, cpb_log2);
     v_off[it] = (uint32_t)(d * bs + cc * 8) * 2u;
   }
-  auto issue_tile = [&](int k0, int buf, int blk) {
+  auto issue_k = [&](int k0, auto buf, int blk) {
     const char* kb = kpool + (size_t)blk * blk_stride + (size_t)((k0 + 16 * wave) & (bs - 1)) * D * 2;
-    const char* vb = vpool + (size_t)blk * blk_stride;
-    char* lk = reinterpret_cast<char*>(tiles[buf].k);
-    char* lv = reinterpret_cast<char*>(tiles[buf].v);
+    char* lk = reinterpret_cast<char*>(kbuf(buf));
 #pragma unroll
     for (int it = 0; it < KPIECES; ++it) {
       const int q = wave * KPIECES + it;
       __builtin_amdgcn_global_load_lds((global_ptr)(kb + k_off[it]), (lds_ptr)(lk + q * 1024), 16, 0, 0);
     }
+  };
+  auto issue_v = [&](int k0, auto buf, int blk) {
+    const char* vb = vpool + (size_t)blk * blk_stride;
+    char* lv = reinterpret_cast<char*>(vbuf(buf));
 #pragma unroll
     for (int it = 0; it < VPIECES; ++it) {
       const int q = wave * VPIECES + it;
@@ -198,83 +208,177 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
 
   const int k_begin = wg_lo & ~(kTileKeys - 1);
   const int ntiles = wg_hi > k_begin ? (wg_hi - k_begin + kTileKeys - 1) / kTileKeys : 0;
-  int blk_next = 0;
-  if (ntiles > 0) {
-    issue_tile(k_begin, 0, wave_block(k_begin));
-    blk_next = wave_block(ntiles > 1 ? k_begin + kTileKeys : k_begin);
-  }
+  auto tile_k0 = [&](int t) { return k_begin + min(t, ntiles - 1) * kTileKeys; };
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int k0 = k_begin + t * kTileKeys;
-    const int buf = t & 1;
-    const int blk_issue = blk_next;  // block of tile t+1 for this wave (loaded one tile ahead)
-    blk_next = wave_block(t + 2 < ntiles ? k0 + 2 * kTileKeys : k0);
-    // tile t has landed in every wave's LDS slots; every wave is done with tile t-1
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
-    __asm__ volatile("" ::: "memory");
-    if (k0 + kTileKeys > n) {
-      // V^T entries of keys >= n hold whatever the pool had: zero them (P is 0 there)
-#pragma unroll
-      for (int it = 0; it < VPIECES; ++it) {
-        const int p = it * kThreads + tid;
-        const int j = p >> dcpb_log2;
-        const int local = p - (j << dcpb_log2);
-        const int d = local >> cpb_log2;
-        const int cc = (local & (cpb - 1)) ^ v_swz(d, cpb_log2);
-        const int tok = k0 + (j << kb_log2) + 8 * cc;
-        if (tok + 8 > n) {
-          u32x4 x = tiles[buf].v[p];
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const int j = tok + 2 * w;
-            x[w] &= (j < n ? 0xffffu : 0u) | (j + 1 < n ? 0xffff0000u : 0u);
-          }
-          tiles[buf].v[p] = x;
-        }
-      }
-      __syncthreads();
-    }
-    if (t + 1 < ntiles) issue_tile(k0 + kTileKeys, buf ^ 1, blk_issue);
-
-    const u32x4* kt = tiles[buf].k;
-    const u32x4* vt = tiles[buf].v;
-
-    // ---- S^T = K Q^T : two 32-key groups ----
-    f32x16 sacc[2];
+  // S^T of one tile: 16 MFMAs, two independent accumulation chains.
+  auto compute_s = [&](f32x16 (&S)[2], const u32x4* kt) {
 #pragma unroll
     for (int kg = 0; kg < 2; ++kg)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[kg][i] = 0.f;
+      for (int i = 0; i < 16; ++i) S[kg][i] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
 #pragma unroll
-      for (int kg = 0; kg < 2; ++kg) {  // two independent accumulation chains
+      for (int kg = 0; kg < 2; ++kg) {
         const int krow = 32 * kg + key_of_slot(col);
         const bf16x8 ka = __builtin_bit_cast(bf16x8, kt[krow * KCH + k_swz<KCH>(krow, 2 * ks + hl)]);
-        sacc[kg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[ks], sacc[kg], 0, 0, 0);
+        S[kg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[ks], S[kg], 0, 0, 0);
       }
     }
+  };
 
-    // ---- scores, masks, online softmax; P (bf16) as the B operand of O^T += V^T P^T ----
+  // Masks, online softmax update and P (bf16) as the B operand of O^T += V^T P^T
+  // (score-mod path; the plain path is inlined into the pipelined step).
+  auto softmax_mods = [&](f32x16 (&S)[2], const int k0, bf16x8 (&pb)[4]) {
     const bool full = (k0 >= safe_lo) && (k0 + kTileKeys <= safe_hi);
+    float cmax = kNegInf;
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = k0 + 32 * kg + key_of_slot(8 * (i >> 2) + 4 * hl + (i & 3));
+        float x = S[kg][i] * a.scale;
+        if (a.softcap > 0.f) {
+          const float ez = fast_exp2(2.f * kLog2e * (x / a.softcap));
+          x = a.softcap * (1.f - 2.f / (ez + 1.f));
+        }
+        x += alibi_slope * (float)(key - pos);
+        float sv = x * kLog2e;
+        if (!full) sv = (key >= row_lo && key < row_hi) ? sv : kNegInf;
+        S[kg][i] = sv;
+        cmax = fmaxf(cmax, sv);
+      }
+    }
+    cmax = fmaxf(cmax, shfl_xor32(cmax));
+    const float m_new = fmaxf(m_run, cmax);
+    const bool need = m_new > m_run + kLazyRescale;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
+      if (need) m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+    }
+    const float msafe = (m_run == kNegInf) ? 0.f : m_run;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      u32x4 w;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p0 = fast_exp2(S[s >> 1][8 * (s & 1) + 2 * j] - msafe);
+        const float p1 = fast_exp2(S[s >> 1][8 * (s & 1) + 2 * j + 1] - msafe);
+        l_run += p0 + p1;
+        w[j] = cvt_bf16x2(p0, p1);
+      }
+      pb[s] = __builtin_bit_cast(bf16x8, w);
+    }
+  };
+
+  // O^T += V^T P^T: 16 MFMAs, DT independent accumulation chains.
+  auto pv = [&](const u32x4* vt, const bf16x8 (&pb)[4]) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int d = 32 * dt + col;
+        const int c = 2 * s + hl;  // 8-key chunk of the tile
+        const int j = c >> cpb_log2;
+        const int cc = c & (cpb - 1);
+        const bf16x8 va = __builtin_bit_cast(bf16x8, vt[(((j * D + d) << cpb_log2) | (cc ^ v_swz(d, cpb_log2)))]);
+        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[s], oacc[dt], 0, 0, 0);
+      }
+    }
+    // keep three V^T reads in flight ahead of the MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+    for (int i = 0; i < 4 * DT; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+
+  // V^T entries of keys >= n hold whatever the pool had: zero them (P is 0 there)
+  auto fixup_v = [&](const int k0, auto buf) {
+#pragma unroll
+    for (int it = 0; it < VPIECES; ++it) {
+      const int p = it * kThreads + tid;
+      const int j = p >> dcpb_log2;
+      const int local = p - (j << dcpb_log2);
+      const int d = local >> cpb_log2;
+      const int cc = (local & (cpb - 1)) ^ v_swz(d, cpb_log2);
+      const int tok = k0 + (j << kb_log2) + 8 * cc;
+      if (tok + 8 > n) {
+        u32x4 x = vbuf(buf)[p];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int jj = tok + 2 * w;
+          x[w] &= (jj < n ? 0xffffu : 0u) | (jj + 1 < n ? 0xffff0000u : 0u);
+        }
+        vbuf(buf)[p] = x;
+      }
+    }
+  };
+
+  auto wait_tiles = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's direct-to-LDS loads landed
+    __syncthreads();                      // ... and every other wave's
+    __asm__ volatile("" ::: "memory");
+  };
+
+  // Software pipeline over tiles (per wave): iteration t computes S of tile
+  // t+1 on the matrix cores while the vector ALUs run the softmax of tile t,
+  // then O += V_t P_t.  LDS rings: K holds tiles t+1 (read) and t+2
+  // (landing), V holds tiles t (read) and t+1 (landing).
+  // Per-wave block ids: b1 = tile t+1, b2 = tile t+2 (scalar, one tile ahead).
+  f32x16 sA[2], sB[2];
+  int b1 = 0, b2 = 0;
+  if (ntiles > 0) {
+    const int b0 = wave_block(tile_k0(0));
+    b1 = wave_block(tile_k0(1));
+    b2 = wave_block(tile_k0(2));
+    issue_k(tile_k0(0), Par<0>{}, b0);
+    issue_v(tile_k0(0), Par<0>{}, b0);
+    if (ntiles > 1) issue_k(tile_k0(1), Par<1>{}, b1);
+    wait_tiles();
+    compute_s(sA, ktile0);
+  }
+  // P = t & 1 (compile time): K buffer 1-P is read, P receives tile t+2;
+  // V buffer P is read, 1-P receives tile t+1.
+  auto step = [&](auto P, f32x16 (&Scur)[2], f32x16 (&Snext)[2], const int t) {
+    constexpr Par<1 - decltype(P)::value> Q{};
+    const int k0 = tile_k0(t);
+    wait_tiles();  // K_{t+1}, V_t landed; all waves are past iteration t-1
+    if (k0 + kTileKeys > n) {
+      fixup_v(k0, P);
+      __syncthreads();
+    }
+    if (t + 2 < ntiles) issue_k(tile_k0(t + 2), P, b2);
+    if (t + 1 < ntiles) issue_v(tile_k0(t + 1), Q, b1);
+    b1 = b2;
+    b2 = wave_block(tile_k0(t + 3));
     bf16x8 pb[4];
-    if constexpr (!kMods) {
-      // s * scale * log2(e) is folded into the exp argument; scale > 0 here
+    if constexpr (kMods) {
+      if (t + 1 < ntiles) compute_s(Snext, kbuf(Q));
+      softmax_mods(Scur, k0, pb);
+      pv(vbuf(P), pb);
+    } else {
+      const bool full = (k0 >= safe_lo) && (k0 + kTileKeys <= safe_hi);
       if (!full) {
 #pragma unroll
         for (int kg = 0; kg < 2; ++kg)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = k0 + 32 * kg + key_of_slot(8 * (i >> 2) + 4 * hl + (i & 3));
-            if (!(key >= row_lo && key < row_hi)) sacc[kg][i] = kNegInf;
+            if (!(key >= row_lo && key < row_hi)) Scur[kg][i] = kNegInf;
           }
       }
       float cmax = kNegInf;
 #pragma unroll
       for (int kg = 0; kg < 2; ++kg)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) cmax = fmaxf(cmax, sacc[kg][i]);
+        for (int i = 0; i < 16; ++i) cmax = fmaxf(cmax, Scur[kg][i]);
       cmax = fmaxf(cmax, shfl_xor32(cmax)) * scale_log2;
       const float m_new = fmaxf(m_run, cmax);
       const bool need = m_new > m_run + kLazyRescale;
@@ -287,76 +391,39 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
 #pragma unroll
           for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
       }
+      // One basic block: the S_{t+1} MFMAs run while the vector ALUs turn
+      // S_t into P.  On the last tile S_{t+1} reads a stale K buffer and is
+      // never used.  s * scale * log2(e) is folded into the exp argument
+      // (scale > 0 on this path).
+      compute_s(Snext, kbuf(Q));
       const float nm = (m_run == kNegInf) ? 0.f : -m_run;
+      float psum = 0.f;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         u32x4 w;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float p0 = fast_exp2(fmaf(sacc[s >> 1][8 * (s & 1) + 2 * j], scale_log2, nm));
-          const float p1 = fast_exp2(fmaf(sacc[s >> 1][8 * (s & 1) + 2 * j + 1], scale_log2, nm));
-          l_run += p0 + p1;
+          const float p0 = fast_exp2(fmaf(Scur[s >> 1][8 * (s & 1) + 2 * j], scale_log2, nm));
+          const float p1 = fast_exp2(fmaf(Scur[s >> 1][8 * (s & 1) + 2 * j + 1], scale_log2, nm));
+          psum += p0 + p1;
           w[j] = cvt_bf16x2(p0, p1);
         }
         pb[s] = __builtin_bit_cast(bf16x8, w);
       }
-    } else {
-      float cmax = kNegInf;
+      l_run += psum;
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads ahead
 #pragma unroll
-      for (int kg = 0; kg < 2; ++kg) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = k0 + 32 * kg + key_of_slot(8 * (i >> 2) + 4 * hl + (i & 3));
-          float x = sacc[kg][i] * a.scale;
-          if (a.softcap > 0.f) {
-            const float ez = fast_exp2(2.f * kLog2e * (x / a.softcap));
-            x = a.softcap * (1.f - 2.f / (ez + 1.f));
-          }
-          x += alibi_slope * (float)(key - pos);
-          float sv = x * kLog2e;
-          if (!full) sv = (key >= row_lo && key < row_hi) ? sv : kNegInf;
-          sacc[kg][i] = sv;
-          cmax = fmaxf(cmax, sv);
-        }
+      for (int i = 0; i < 2 * KSTEPS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 96 / (2 * KSTEPS), 0);  // VALU
       }
-      cmax = fmaxf(cmax, shfl_xor32(cmax));
-      const float m_new = fmaxf(m_run, cmax);
-      const bool need = m_new > m_run + kLazyRescale;
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
-        if (need) m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
-      }
-      const float msafe = (m_run == kNegInf) ? 0.f : m_run;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        u32x4 w;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float p0 = fast_exp2(sacc[s >> 1][8 * (s & 1) + 2 * j] - msafe);
-          const float p1 = fast_exp2(sacc[s >> 1][8 * (s & 1) + 2 * j + 1] - msafe);
-          l_run += p0 + p1;
-          w[j] = cvt_bf16x2(p0, p1);
-        }
-        pb[s] = __builtin_bit_cast(bf16x8, w);
-      }
+      pv(vbuf(P), pb);
     }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {  // DT independent accumulation chains
-        const int d = 32 * dt + col;
-        const int c = 2 * s + hl;  // 8-key chunk of the tile
-        const int j = c >> cpb_log2;
-        const int cc = c & (cpb - 1);
-        const bf16x8 va = __builtin_bit_cast(bf16x8, vt[(((j * D + d) << cpb_log2) | (cc ^ v_swz(d, cpb_log2)))]);
-        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[s], oacc[dt], 0, 0, 0);
-      }
-    }
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    step(Par<0>{}, sA, sB, t);
+    if (t + 1 < ntiles) step(Par<1>{}, sB, sA, t + 1);
   }
 
   // ---- normalise and store: lane holds row `r`, dims 32dt + 8(i/4) + 4hl + i%4 ----
@@ -386,13 +453,22 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, int D, hipStream_t s) {
   if (blocks <= 0) return hipSuccess;
   // the fast path folds a positive scale into the exponent
   const bool mods = a.softcap > 0.f || a.alibi != nullptr || !(a.scale > 0.f);
-  if (D == 64) {
-    if (mods) hipLaunchKernelGGL((prefill_mfma_kernel<64, true>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((prefill_mfma_kernel<64, false>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
-  } else {
-    if (mods) hipLaunchKernelGGL((prefill_mfma_kernel<128, true>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((prefill_mfma_kernel<128, false>), dim3((unsigned)blocks), dim3(kThreads), 0, s, a);
+  const int kbl = a.bs_log2 < 6 ? a.bs_log2 : 6;
+  const dim3 grid((unsigned)blocks), block(kThreads);
+#define PA_PREFILL_LAUNCH(DD, MM, KK) hipLaunchKernelGGL((prefill_mfma_kernel<DD, MM, KK>), grid, block, 0, s, a)
+#define PA_PREFILL_KBL(DD, MM)                    \
+  switch (kbl) {                                  \
+    case 4: PA_PREFILL_LAUNCH(DD, MM, 4); break;  \
+    case 5: PA_PREFILL_LAUNCH(DD, MM, 5); break;  \
+    default: PA_PREFILL_LAUNCH(DD, MM, 6); break; \
   }
+  if (D == 64) {
+    if (mods) { PA_PREFILL_KBL(64, true) } else { PA_PREFILL_KBL(64, false) }
+  } else {
+    if (mods) { PA_PREFILL_KBL(128, true) } else { PA_PREFILL_KBL(128, false) }
+  }
+#undef PA_PREFILL_KBL
+#undef PA_PREFILL_LAUNCH
   return hipGetLastError();
 }
 
