@@ -48,7 +48,13 @@ __device__ __forceinline__ int key_of_slot(int u) {
   return (u & 16) | (qs << 2) | (u & 3);
 }
 
-// 16-byte chunk position inside an LDS row (bank-conflict-free reads)
+// Offset (from k0 + 8*hl) of the key that accumulator element i of the
+// S^T tile for key group kg holds: key_of_slot(8*(i/4) + 4*hl + i%4) + 32*kg
+// with the hl term taken out.  A compile-time constant once unrolled.
+__device__ __forceinline__ constexpr int key_off(int kg, int i) {
+  return 32 * kg + 16 * ((i >> 3) & 1) + 4 * ((i >> 2) & 1) + (i & 3);
+}
+
 template <int P>
 struct Par {
   static constexpr int value = P;
@@ -142,9 +148,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
   // 64 lanes read one contiguous run.  Entries past the sequence's last block
   // are clamped to it (those keys are masked and their V entries zeroed).
   // Lane-dependent parts of the addresses are fixed for the whole loop.
-  typedef const __attribute__((address_space(4))) int32_t* const_table_ptr;  // scalar loads
-  const const_table_ptr ctable = (const_table_ptr)table;
-  auto wave_block = [&](int k0) { return ctable[min((k0 + 16 * wave) >> a.bs_log2, last_blk)]; };
   uint32_t k_off[KPIECES], v_off[VPIECES];
   int v_j[VPIECES];
 #pragma unroll
@@ -209,6 +212,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
   const int k_begin = wg_lo & ~(kTileKeys - 1);
   const int ntiles = wg_hi > k_begin ? (wg_hi - k_begin + kTileKeys - 1) / kTileKeys : 0;
   auto tile_k0 = [&](int t) { return k_begin + min(t, ntiles - 1) * kTileKeys; };
+  auto tile_full = [&](int k0) { return (k0 >= safe_lo) && (k0 + kTileKeys <= safe_hi); };
 
   // S^T of one tile: 16 MFMAs, two independent accumulation chains.
   auto compute_s = [&](f32x16 (&S)[2], const u32x4* kt) {
@@ -236,7 +240,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
     for (int kg = 0; kg < 2; ++kg) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int key = k0 + 32 * kg + key_of_slot(8 * (i >> 2) + 4 * hl + (i & 3));
+        const int key = k0 + 8 * hl + key_off(kg, i);
         float x = S[kg][i] * a.scale;
         if (a.softcap > 0.f) {
           const float ez = fast_exp2(2.f * kLog2e * (x / a.softcap));
@@ -290,13 +294,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
         oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[s], oacc[dt], 0, 0, 0);
       }
     }
-    // keep three V^T reads in flight ahead of the MFMAs
-    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-#pragma unroll
-    for (int i = 0; i < 4 * DT; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
   };
 
   // V^T entries of keys >= n hold whatever the pool had: zero them (P is 0 there)
@@ -327,74 +324,110 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
     __asm__ volatile("" ::: "memory");
   };
 
-  // Software pipeline over tiles (per wave): iteration t computes S of tile
-  // t+1 on the matrix cores while the vector ALUs run the softmax of tile t,
-  // then O += V_t P_t.  LDS rings: K holds tiles t+1 (read) and t+2
-  // (landing), V holds tiles t (read) and t+1 (landing).
-  // Per-wave block ids: b1 = tile t+1, b2 = tile t+2 (scalar, one tile ahead).
+  // Row maximum of a tile's raw scores (log2 units after the scale).
+  auto row_max = [&](const f32x16 (&S)[2]) {
+    float c = kNegInf;
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) c = fmaxf(c, S[kg][i]);
+    return fmaxf(c, shfl_xor32(c)) * scale_log2;
+  };
+  // Keys outside this row's admissible range -> -inf (raw scores).
+  auto mask_s = [&](f32x16 (&S)[2], const int k0) {
+    const int kb = k0 + 8 * hl;
+    const int lo = row_lo - kb, hi = row_hi - kb;
+#pragma unroll
+    for (int kg = 0; kg < 2; ++kg)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int c = key_off(kg, i);
+        if (c < lo || c >= hi) S[kg][i] = kNegInf;
+      }
+  };
+  // Lazy running-max update: the max moves only when a tile exceeds it by
+  // kLazyRescale (log2 units); then O and l are rescaled.
+  auto update_max = [&](const float cmax) {
+    const float m_new = fmaxf(m_run, cmax);
+    const bool need = m_new > m_run + kLazyRescale;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
+      if (need) m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+    }
+  };
+  // Table entry of the block wave `wave` loads for tile t, read with a vector
+  // load (all lanes, one address) so that waiting for it joins the wait for
+  // the tile loads instead of the LDS counter.
+  auto table_load = [&](int t) {
+    const int j = min((tile_k0(t) + 16 * wave) >> a.bs_log2, last_blk);
+    return __builtin_nontemporal_load(table + j);
+  };
+
+  // Software pipeline over tiles (per wave).  Plain path, iteration t, one
+  // basic block after the barrier: the loads of K_{t+2} and V_{t+1}, the
+  // S_{t+1} MFMAs with the exp/convert of P_t, then the O += V_t P_t MFMAs
+  // with the row maxima of S_{t+1}.  On entry S_t is masked and the running
+  // max covers it.  LDS rings: K holds tiles t+1 (read) and t+2 (landing), V
+  // holds tiles t (read) and t+1 (landing).  Block ids: b1 = tile t+1,
+  // b2 = tile t+2 (scalars), bv = tile t+3 (vector load in flight).
   f32x16 sA[2], sB[2];
-  int b1 = 0, b2 = 0;
+  int b1 = 0, b2 = 0, bv = 0;
   if (ntiles > 0) {
-    const int b0 = wave_block(tile_k0(0));
-    b1 = wave_block(tile_k0(1));
-    b2 = wave_block(tile_k0(2));
+    const int b0 = __builtin_amdgcn_readfirstlane(table_load(0));
+    b1 = __builtin_amdgcn_readfirstlane(table_load(1));
+    b2 = __builtin_amdgcn_readfirstlane(table_load(2));
     issue_k(tile_k0(0), Par<0>{}, b0);
     issue_v(tile_k0(0), Par<0>{}, b0);
     if (ntiles > 1) issue_k(tile_k0(1), Par<1>{}, b1);
+    bv = table_load(3);
     wait_tiles();
     compute_s(sA, ktile0);
+    if constexpr (kMods) {
+      // mods path: scores are modded inside its softmax
+    } else {
+      if (!tile_full(tile_k0(0))) mask_s(sA, tile_k0(0));
+      update_max(row_max(sA));
+    }
   }
   // P = t & 1 (compile time): K buffer 1-P is read, P receives tile t+2;
   // V buffer P is read, 1-P receives tile t+1.
   auto step = [&](auto P, f32x16 (&Scur)[2], f32x16 (&Snext)[2], const int t) {
     constexpr Par<1 - decltype(P)::value> Q{};
     const int k0 = tile_k0(t);
-    wait_tiles();  // K_{t+1}, V_t landed; all waves are past iteration t-1
+    const int k1 = tile_k0(t + 1);
+    wait_tiles();  // K_{t+1}, V_t and the table entry bv landed; all waves are past iteration t-1
+    const int b3 = __builtin_amdgcn_readfirstlane(bv);
     if (k0 + kTileKeys > n) {
       fixup_v(k0, P);
       __syncthreads();
     }
-    if (t + 2 < ntiles) issue_k(tile_k0(t + 2), P, b2);
-    if (t + 1 < ntiles) issue_v(tile_k0(t + 1), Q, b1);
-    b1 = b2;
-    b2 = wave_block(tile_k0(t + 3));
     bf16x8 pb[4];
     if constexpr (kMods) {
+      if (t + 2 < ntiles) issue_k(tile_k0(t + 2), P, b2);
+      if (t + 1 < ntiles) issue_v(k1, Q, b1);
+      b1 = b2;
+      b2 = b3;
+      bv = table_load(t + 4);
       if (t + 1 < ntiles) compute_s(Snext, kbuf(Q));
       softmax_mods(Scur, k0, pb);
       pv(vbuf(P), pb);
     } else {
-      const bool full = (k0 >= safe_lo) && (k0 + kTileKeys <= safe_hi);
-      if (!full) {
-#pragma unroll
-        for (int kg = 0; kg < 2; ++kg)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = k0 + 32 * kg + key_of_slot(8 * (i >> 2) + 4 * hl + (i & 3));
-            if (!(key >= row_lo && key < row_hi)) Scur[kg][i] = kNegInf;
-          }
-      }
-      float cmax = kNegInf;
-#pragma unroll
-      for (int kg = 0; kg < 2; ++kg)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) cmax = fmaxf(cmax, Scur[kg][i]);
-      cmax = fmaxf(cmax, shfl_xor32(cmax)) * scale_log2;
-      const float m_new = fmaxf(m_run, cmax);
-      const bool need = m_new > m_run + kLazyRescale;
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
-        if (need) m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
-      }
-      // One basic block: the S_{t+1} MFMAs run while the vector ALUs turn
-      // S_t into P.  On the last tile S_{t+1} reads a stale K buffer and is
-      // never used.  s * scale * log2(e) is folded into the exp argument
-      // (scale > 0 on this path).
+      // Loads of K_{t+2} and V_{t+1}, unconditional so that they join this
+      // block: past the last tile they reload it into buffers nobody reads
+      // any more.  S_{t+1} (on the last tile from a stale K buffer, never
+      // used) and P_t.  s * scale * log2(e) is folded into the exp argument
+      // (scale > 0 on this path); the row sum adds the bf16-rounded weights
+      // that also enter the P V product.
+      issue_k(tile_k0(t + 2), P, b2);
+      issue_v(k1, Q, b1);
+      b1 = b2;
+      b2 = b3;
+      bv = table_load(t + 4);
       compute_s(Snext, kbuf(Q));
       const float nm = (m_run == kNegInf) ? 0.f : -m_run;
       float psum = 0.f;
@@ -405,26 +438,43 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
         for (int j = 0; j < 4; ++j) {
           const float p0 = fast_exp2(fmaf(Scur[s >> 1][8 * (s & 1) + 2 * j], scale_log2, nm));
           const float p1 = fast_exp2(fmaf(Scur[s >> 1][8 * (s & 1) + 2 * j + 1], scale_log2, nm));
-          psum += p0 + p1;
           w[j] = cvt_bf16x2(p0, p1);
+          psum = dot2_bf16(w[j], 0x3f803f80u, psum);
         }
         pb[s] = __builtin_bit_cast(bf16x8, w);
       }
       l_run += psum;
+      pv(vbuf(P), pb);
+      float cmax = row_max(Snext);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads ahead
 #pragma unroll
       for (int i = 0; i < 2 * KSTEPS; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA (S)
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-        __builtin_amdgcn_sched_group_barrier(0x002, 96 / (2 * KSTEPS), 0);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU (P)
+        if (i < KPIECES + VPIECES + 1)
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (tile loads, table)
       }
-      pv(vbuf(P), pb);
+#pragma unroll
+      for (int i = 0; i < 4 * DT; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA (PV)
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU (row max)
+      }
+      if (t + 1 < ntiles) {  // (S_{t+1} of the last tile is stale: no update)
+        if (!tile_full(k1)) {  // rare: maxima over admissible keys only
+          mask_s(Snext, k1);
+          cmax = row_max(Snext);
+        }
+        update_max(cmax);
+      }
     }
   };
   for (int t = 0; t < ntiles; t += 2) {
     step(Par<0>{}, sA, sB, t);
     if (t + 1 < ntiles) step(Par<1>{}, sB, sA, t + 1);
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // no direct-to-LDS load outlives the loop
 
   // ---- normalise and store: lane holds row `r`, dims 32dt + 8(i/4) + 4hl + i%4 ----
   const float l_tot = l_run + shfl_xor32(l_run);
