@@ -39,7 +39,17 @@ constexpr int kRowsPerWG = 128;
 constexpr int kThreads = 256;
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
-typedef __attribute__((address_space(1))) const void* global_ptr;
+// Word 3 of a raw buffer resource (dword data, no swizzle) on this family.
+constexpr int kBufferFlags = 0x00020000;
+
+// 16 bytes per lane from base + voff + soff straight into LDS (lane i lands
+// at dst + 16*i).  A buffer load rather than a global one: it counts only on
+// the vector-memory counter, so waits for LDS reads issued while tile loads
+// are in flight stay precise.  base and soff are wave-uniform.
+__device__ __forceinline__ void buffer_load_lds16(const void* base, uint32_t voff, uint32_t soff, lds_ptr dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, kBufferFlags), dst, 16, voff, soff, 0, 0);
+}
 
 // key slot (0..31) of a 32-key group -> key offset inside the group
 __device__ __forceinline__ int key_of_slot(int u) {
@@ -171,7 +181,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
 #pragma unroll
     for (int it = 0; it < KPIECES; ++it) {
       const int q = wave * KPIECES + it;
-      __builtin_amdgcn_global_load_lds((global_ptr)(kb + k_off[it]), (lds_ptr)(lk + q * 1024), 16, 0, 0);
+      buffer_load_lds16(kb, k_off[it], 0, (lds_ptr)(lk + q * 1024));
     }
   };
   auto issue_v = [&](int k0, auto buf, int blk) {
@@ -180,8 +190,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
 #pragma unroll
     for (int it = 0; it < VPIECES; ++it) {
       const int q = wave * VPIECES + it;
-      const char* src = vb + (size_t)((k0 + (v_j[it] << kb_log2)) & (bs - 1)) * 2 + v_off[it];
-      __builtin_amdgcn_global_load_lds((global_ptr)src, (lds_ptr)(lv + q * 1024), 16, 0, 0);
+      const uint32_t soff = (uint32_t)((k0 + (v_j[it] << kb_log2)) & (bs - 1)) * 2u;
+      buffer_load_lds16(vb, v_off[it], soff, (lds_ptr)(lv + q * 1024));
     }
   };
 
