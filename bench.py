@@ -17,9 +17,16 @@ The headline ``value`` is the decode KV-read bandwidth: bytes of K and V the
 decode batch must read (sum of context lengths x 8 kv-heads x 128 x 2 x 2)
 divided by the measured time of the decode call (both kernels).  The prefill
 throughput is reported beside it.  Inputs are resident in HBM before timing.
-Per-kernel times come from HIP events recorded on the stream the kernels run
-on.  ``cpu_baseline`` times the fp64 CPU oracle on a bounded sample of the
-same workload.
+Before every step a 512 MiB buffer is overwritten (evicting L2 and the
+last-level cache; not part of any phase).  Per-kernel times come from HIP
+events recorded on the stream the kernels run on.  ``cpu_baseline`` times the
+fp64 CPU oracle on a bounded sample of the same workload.
+
+Beside the step it reports: the achievable HBM read bandwidth of a plain
+streaming-read kernel (a second denominator), the decode of the other
+workloads (GQA batch, shared-prefix batch with logical and unique bytes), a
+context sweep of the GQA shape, and the pool's internal fragmentation per
+workload and page size (arithmetic only).
 
 Prints one JSON line.
 """
@@ -130,6 +137,107 @@ def cpu_baseline(w5, w3, budget_s):
     }
 
 
+PAGE_SIZES = (16, 32, 64, 128, 256)
+
+
+def fragmentation(context_lens):
+    """Internal fragmentation of a paged pool: unused slots of every sequence's
+    last block over all slots it holds, per page size (pure arithmetic)."""
+    n = np.asarray(context_lens, dtype=np.int64)
+    out = {}
+    for bs in PAGE_SIZES:
+        held = ((n + bs - 1) // bs) * bs
+        out[str(bs)] = round(float((held - n).sum() / held.sum()), 5)
+    return out
+
+
+def time_calls(torch, fn, flush, reps, warm=3):
+    """Median GPU time (ms) of ``fn``, each call after a cache-evicting flush;
+    events bracket only the call, and the flush keeps the GPU busy while the
+    host enqueues it."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warm):
+        flush()
+        fn()
+    evs = []
+    for _ in range(reps):
+        flush()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in evs]))
+
+
+def extra_measurements(pa, torch, dev, flush, args):
+    from workloads import build_workload, named_workload
+    from workloads.device import upload
+
+    res = {}
+    # achievable HBM read bandwidth: one streaming read of 4 GiB (16x the last-level cache)
+    src = torch.ones(1 << 30, dtype=torch.int32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    ms = time_calls(torch, lambda: pa.bench_stream_read(src, sink), flush, reps=7)
+    res["achievable_hbm"] = {"value": round(src.numel() * 4 / (ms * 1e-3) / 1e9, 2), "unit": "GB/s",
+                             "kernel": "stream_read_kernel (measurement support), 4 GiB, 16-byte non-temporal loads",
+                             "ms": round(ms, 5)}
+    del src, sink
+    log(f"achievable HBM read: {res['achievable_hbm']['value']} GB/s")
+
+    def decode_fn(w, t, out, ws):
+        def f():
+            pa.paged_attn_decode(out, t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                                 w.scale, w.max_context_len, 0, workspace=ws)
+        return f
+
+    def prepared(w):
+        t = upload(w, dev)
+        if len(w.slot_mapping):
+            pa.kv_append(t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], t["slot_mapping"])
+        out = torch.empty_like(t["q"])
+        ws = pa.decode_workspace(t["q"], w.Hkv, w.max_context_len, 0)
+        return t, out, ws
+
+    workloads = {}
+    frag = {}
+    for name in ("single_decode_f32", "gqa_decode_bf16", "shared_prefix_decode_bf16"):
+        w = named_workload(name)
+        frag[name] = fragmentation(w.context_lens)
+        t, out, ws = prepared(w)
+        ms = time_calls(torch, decode_fn(w, t, out, ws), flush, reps=20)
+        logical = w.kv_bytes()
+        entry = {"ms": round(ms, 5), "kv_bytes": int(logical), "gbs": round(logical / (ms * 1e-3) / 1e9, 2)}
+        if name == "shared_prefix_decode_bf16":
+            unique = w.unique_kv_bytes()
+            entry.update({"unique_kv_bytes": int(unique),
+                          "unique_gbs": round(unique / (ms * 1e-3) / 1e9, 2),
+                          "pct_hbm_peak_unique": round(100.0 * unique / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)})
+        workloads[name] = entry
+        del t, out, ws
+    res["decode_workloads"] = workloads
+    res["fragmentation"] = frag
+    log("other workloads measured")
+
+    # context sweep of the GQA decode shape (8 sequences, 32/8 heads, d128, bf16, block 16)
+    sweep = {}
+    base = None
+    for ctx in (128, 256, 512, 1024, 2048):
+        w = build_workload(name=f"sweep{ctx}", seed=200 + ctx, kind="decode", dtype="bf16", Hq=32, Hkv=8, D=128,
+                           bs=16, context_lens=[ctx] * 8, append_lens=[1] * 8)
+        t, out, ws = prepared(w)
+        ms = time_calls(torch, decode_fn(w, t, out, ws), flush, reps=20)
+        base = base or ms
+        sweep[str(ctx)] = {"us": round(ms * 1e3, 2), "vs_128": round(ms / base, 3),
+                           "gbs": round(w.kv_bytes() / (ms * 1e-3) / 1e9, 2)}
+        del t, out, ws
+    res["context_sweep_gqa_decode"] = sweep
+    log("context sweep measured")
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -145,6 +253,10 @@ def main():
                          "HBM traffic counters)")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
                     help="time budget of the oracle baseline (0: skip it)")
+    ap.add_argument("--flush-mib", type=int, default=512,
+                    help="cache-evicting write before every timed call (0: none)")
+    ap.add_argument("--extras", type=int, default=1,
+                    help="1: also measure achievable HBM, the other workloads and the context sweep")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -179,8 +291,15 @@ def main():
     log("inputs resident on the GPU")
 
     stream = torch.cuda.current_stream()
+    flush_buf = (torch.empty(args.flush_mib << 18, dtype=torch.int32, device=dev)
+                 if args.flush_mib > 0 else None)
+
+    def flush():
+        if flush_buf is not None:
+            pa.bench_fill(flush_buf, 0)
 
     def step(ev=None):
+        flush()
         if ev is not None:
             ev[0].record(stream)
         pa.kv_append(t5["k_new"], t5["v_new"], t5["k_cache"], t5["v_cache"], t5["slot_mapping"])
@@ -348,6 +467,13 @@ def main():
             "prefill_chunks": round(append_bytes3 / (ms_append3 * 1e-3) / 1e9, 2),
         },
     }
+    if args.extras:
+        extra = extra_measurements(pa, torch, dev, flush, args)
+        result["roofline"]["achievable_peak"] = extra["achievable_hbm"]["value"]
+        result["roofline"]["frac_of_achievable"] = round(partials_gbs / extra["achievable_hbm"]["value"], 4)
+        result.update(extra)
+        result["fragmentation"]["long_decode_bf16"] = fragmentation(w5.context_lens)
+        result["fragmentation"]["chunked_prefill_bf16"] = fragmentation(w3.context_lens)
     if args.cpu_baseline_seconds > 0:
         log("timing the fp64 oracle on the host")
         result["cpu_baseline"] = cpu_baseline(w5, w3, args.cpu_baseline_seconds)

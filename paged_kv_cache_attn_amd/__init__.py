@@ -7,6 +7,8 @@ The compute lives in ``libpagedattn.so`` (hand-written HIP kernels, C ABI in
 from .binding import (  # noqa: F401
     PA_BF16,
     PA_F32,
+    bench_fill,
+    bench_stream_read,
     decode_split_tokens,
     decode_workspace,
     decode_workspace_size,

@@ -49,6 +49,9 @@ SIGNATURES = {
     "paged_attn_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                   _i64, _f32, _i32, _mods_p, _i32, _vp]),
     "paged_attn_status_string": (ctypes.c_char_p, [_i32]),
+    # include/pagedattn_bench.h (measurement support)
+    "pa_bench_stream_read": (_i32, [_vp, _sz, _vp, _vp]),
+    "pa_bench_fill": (_i32, [_vp, _sz, ctypes.c_uint32, _vp]),
 }
 
 _lib = None
@@ -155,6 +158,7 @@ def decode_split_tokens(num_seqs, num_kv_heads, max_context_len, split_tokens=0)
 
 
 def decode_workspace(q, num_kv_heads, max_context_len, split_tokens=0):
+    """A decode workspace for these sizes."""
     B, Hq, D = q.shape
     n = decode_workspace_size(B, Hq, num_kv_heads, D, max_context_len, split_tokens)
     return torch.empty(max(n, 4) // 4, dtype=torch.float32, device=q.device)
@@ -220,3 +224,19 @@ def paged_attn_prefill(out, q, cu_q_lens, k_cache, v_cache, block_tables, contex
                                     _stream())
     _check(code, "paged_attn_prefill")
     return out
+
+
+def bench_stream_read(src: torch.Tensor, sink: torch.Tensor):
+    """Measurement support: read every byte of ``src`` once (streaming, non-temporal);
+    the XOR of its 32-bit words is XOR-ed into ``sink`` (one int32, caller-zeroed)."""
+    _need(src, "src")
+    _need(sink, "sink", torch.int32, 1)
+    code = lib().pa_bench_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream())
+    _check(code, "pa_bench_stream_read")
+
+
+def bench_fill(dst: torch.Tensor, value: int = 0):
+    """Measurement support: overwrite ``dst`` with a 32-bit pattern (evicts the caches)."""
+    _need(dst, "dst")
+    code = lib().pa_bench_fill(_ptr(dst), dst.numel() * dst.element_size(), int(value) & 0xFFFFFFFF, _stream())
+    _check(code, "pa_bench_fill")

@@ -11,16 +11,19 @@ import pytest
 from paged_kv_cache_attn_amd import binding
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "pagedattn.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
 NULL = None
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"^(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    names = []
+    for h in HEADERS:
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
     return sorted(set(n for n in names if n not in ("if", "defined")))
 
 
@@ -28,7 +31,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ["kv_append", "paged_attn_decode", "paged_attn_prefill", "paged_attn_decode_partials",
               "paged_attn_decode_merge", "paged_attn_decode_workspace_size", "paged_attn_decode_split_tokens",
-              "paged_attn_status_string"]:
+              "paged_attn_status_string", "pa_bench_stream_read", "pa_bench_fill"]:
         assert n in names, n
     assert set(names) == set(binding.SIGNATURES), names
 
@@ -162,3 +165,16 @@ def test_split_resolution_and_workspace_size():
     # (ceil(max_ctx/16) + 1); no device is visible here, so CUs = 256
     assert binding.decode_workspace_size(64, 64, 8, 128, 32768, 0) == (2048 + 512) * 8 * 130 * 4 + 512 * 8
     assert binding.decode_workspace_size(8, 32, 8, 128, 2048, 0) == (1032 + 64) * 4 * 130 * 4 + 64 * 8
+
+
+def test_bench_util_validation():
+    L = binding.lib()
+    sink = ctypes.c_void_p(0x2000)
+    assert L.pa_bench_stream_read(NULL, 16, sink, None) == -1
+    assert L.pa_bench_stream_read(FAKE, 16, NULL, None) == -1
+    assert L.pa_bench_stream_read(FAKE, 17, sink, None) == -2          # size not a multiple of 16
+    assert L.pa_bench_stream_read(ctypes.c_void_p(0x1004), 16, sink, None) == -2  # misaligned
+    assert L.pa_bench_stream_read(FAKE, 0, sink, None) == 0             # nothing to do
+    assert L.pa_bench_fill(NULL, 16, 0, None) == -1
+    assert L.pa_bench_fill(FAKE, 24, 0, None) == -2
+    assert L.pa_bench_fill(FAKE, 0, 0, None) == 0

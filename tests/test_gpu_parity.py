@@ -340,3 +340,22 @@ def test_poisoned_table_tail_entries_ignored(gpu_lib):
     w.block_table = np.concatenate([w.block_table, np.full((w.B, 8), 2 ** 30, np.int32)], axis=1)
     w.block_table[w.block_table == -1] = 2 ** 30
     assert_close(gpu_decode(gpu_lib, w), oracle_out(w), "bf16")
+
+
+def test_balanced_split_workspace_reuse_across_batches(gpu_lib):
+    """One workspace buffer, sized for the larger batch, serves decode calls
+    of different batches in turn; every result matches the oracle."""
+    import torch
+
+    big = named_workload("long_decode_bf16", batch=6)
+    small_w = small(ctx=(37, 300, 1000, 2500), append=[1, 1, 1, 1])
+    sizes = [gpu_lib.decode_workspace_size(w.B, w.Hq, w.Hkv, w.D, w.max_context_len, 0) for w in (big, small_w)]
+    ws = torch.empty(max(sizes) // 4 + 64, dtype=torch.float32, device="cuda")
+    for w in (big, small_w, big, small_w):
+        t = upload(w)
+        gpu_lib.kv_append(t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], t["slot_mapping"])
+        out = torch.empty_like(t["q"])
+        gpu_lib.paged_attn_decode(out, t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                                  w.scale, w.max_context_len, 0, workspace=ws)
+        torch.cuda.synchronize()
+        assert_close(to_numpy_bits(out), oracle_out(w), "bf16")
