@@ -431,8 +431,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
       // block: past the last tile they reload it into buffers nobody reads
       // any more.  S_{t+1} (on the last tile from a stale K buffer, never
       // used) and P_t.  s * scale * log2(e) is folded into the exp argument
-      // (scale > 0 on this path); the row sum adds the bf16-rounded weights
-      // that also enter the P V product.
+      // (scale > 0 on this path).  The row sum adds the fp32 weights with
+      // plain adds (a v_dot2 per bf16 pair would be a slow instruction).
       issue_k(tile_k0(t + 2), P, b2);
       issue_v(k1, Q, b1);
       b1 = b2;
@@ -448,8 +448,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
         for (int j = 0; j < 4; ++j) {
           const float p0 = fast_exp2(fmaf(Scur[s >> 1][8 * (s & 1) + 2 * j], scale_log2, nm));
           const float p1 = fast_exp2(fmaf(Scur[s >> 1][8 * (s & 1) + 2 * j + 1], scale_log2, nm));
+          psum += p0 + p1;
           w[j] = cvt_bf16x2(p0, p1);
-          psum = dot2_bf16(w[j], 0x3f803f80u, psum);
         }
         pb[s] = __builtin_bit_cast(bf16x8, w);
       }
