@@ -63,14 +63,22 @@ class ScoreMods:
       alibi_slopes    : s <- s + slope[h] * (kv_pos - q_pos)
     then masks (a key is admissible only if all hold):
       kv_pos < n      (the sequence's keys; always)
-      causal          : kv_pos <= q_pos
+      causal          : kv_pos <= q_pos, or kv_pos < prefix_lens[b] when
+                        prefix lengths are given (prefix-LM: the prefix is
+                        seen by every row of the sequence)
       window > 0      : q_pos - kv_pos < window
+      doc_starts      : kv_pos >= doc_starts[row] (document masking of packed
+                        sequences: a row sees nothing before its document)
+    ``prefix_lens`` is per sequence ``[B]``; ``doc_starts`` per query row
+    ``[sum Lq]`` (decode: one per sequence).
     """
 
     causal: bool = False
     window: int = 0
     softcap: float = 0.0
     alibi_slopes: np.ndarray | None = None
+    prefix_lens: np.ndarray | None = None
+    doc_starts: np.ndarray | None = None
 
 
 def kv_append(k_pool, v_pool, k_new, v_new, slot_mapping, bs):
@@ -114,11 +122,14 @@ def gather_sequence(k_pool, v_pool, table_row, n, bs):
     return K, V
 
 
-def attention_dense(Q, K, V, scale, q_pos, mods: ScoreMods | None = None):
+def attention_dense(Q, K, V, scale, q_pos, mods: ScoreMods | None = None, prefix_len=0, doc_start=None):
     """Exact attention of query rows at logical positions ``q_pos``.
 
     ``Q`` ``[Lq, Hq, D]``, ``K``/``V`` ``[Hkv, n, D]`` (fp64), key ``j`` sits at
     logical position ``j``.  Query head ``h`` uses kv-head ``h // (Hq/Hkv)``.
+    ``prefix_len`` (this sequence's prefix-LM length) and ``doc_start``
+    (``[Lq]``, each row's document start) are the per-sequence and per-row
+    values of ``mods.prefix_lens`` / ``mods.doc_starts``.
     Returns fp64 ``[Lq, Hq, D]``; rows with no admissible key are zero.
     """
     mods = mods or ScoreMods()
@@ -132,9 +143,11 @@ def attention_dense(Q, K, V, scale, q_pos, mods: ScoreMods | None = None):
     kp = np.arange(n, dtype=np.int64)[None, :]
     allowed = np.ones((Lq, n), dtype=bool)
     if mods.causal:
-        allowed &= kp <= qp
+        allowed &= (kp <= qp) | (kp < int(prefix_len))
     if mods.window > 0:
         allowed &= (qp - kp) < mods.window
+    if doc_start is not None:
+        allowed &= kp >= np.asarray(doc_start, dtype=np.int64)[:, None]
     for h in range(Hq):
         kvh = h // g
         S = (Q[:, h, :] @ K[kvh].T) * float(scale)
@@ -175,7 +188,9 @@ def paged_attention(q, k_pool, v_pool, block_table, context_lens, cu_q_lens, sca
         Vb = bits_to_f64(Vb, dtype)
         Lq = r1 - r0
         q_pos = np.arange(n - Lq, n)
-        out[r0:r1] = attention_dense(q64[r0:r1], Kb, Vb, float(np.float32(scale)), q_pos, mods)
+        prefix = 0 if mods is None or mods.prefix_lens is None else int(mods.prefix_lens[b])
+        docs = None if mods is None or mods.doc_starts is None else np.asarray(mods.doc_starts)[r0:r1]
+        out[r0:r1] = attention_dense(q64[r0:r1], Kb, Vb, float(np.float32(scale)), q_pos, mods, prefix, docs)
     return out
 
 

@@ -122,10 +122,14 @@ def brute_force(w, mods):
             for h in range(w.Hq):
                 c = h // g
                 scores = []
+                prefix = 0 if mods.prefix_lens is None else int(mods.prefix_lens[b])
+                doc = 0 if mods.doc_starts is None else int(mods.doc_starts[r])
                 for j in range(n):
-                    if mods.causal and j > pos:
+                    if mods.causal and j > pos and j >= prefix:
                         continue
                     if mods.window and pos - j >= mods.window:
+                        continue
+                    if j < doc:
                         continue
                     blk = int(w.block_table[b][j // w.bs])
                     off = j % w.bs
@@ -172,6 +176,44 @@ def test_brute_force_with_mods():
     got = oracle.paged_attention(w.q, w.k_pool, w.v_pool, w.block_table, w.context_lens, w.cu_q_lens,
                                  w.scale, w.bs, w.dtype, mods)
     np.testing.assert_allclose(got, brute_force(w, mods), rtol=0, atol=1e-12)
+
+
+def test_brute_force_with_prefix_and_documents():
+    w = _tiny("prefill", 13, ctx=(11, 30), q_lens=[6, 9], causal=True)
+    mods = oracle.ScoreMods(causal=True, window=7, prefix_lens=np.array([8, 25]),
+                            doc_starts=np.array([0, 0, 3, 3, 6, 6, 0, 12, 12, 21, 21, 21, 25, 25, 27]))
+    got = _run(w, mods)
+    np.testing.assert_allclose(got, brute_force(w, mods), rtol=0, atol=1e-12)
+
+
+def test_prefix_lm_limits():
+    """prefix 0 is plain causal; a prefix covering the context is no mask."""
+    w = _tiny("prefill", 14, ctx=(17, 26), q_lens=[7, 10], causal=True)
+    causal = _run(w, oracle.ScoreMods(causal=True))
+    full = _run(w, oracle.ScoreMods(causal=False))
+    np.testing.assert_allclose(_run(w, oracle.ScoreMods(causal=True, prefix_lens=np.array([0, 0]))), causal,
+                               rtol=0, atol=0)
+    np.testing.assert_allclose(_run(w, oracle.ScoreMods(causal=True, prefix_lens=w.context_lens)), full,
+                               rtol=0, atol=0)
+
+
+def test_document_rows_equal_the_document_alone():
+    """A packed sequence of documents [0, a) and [a, n): a row of the second
+    document with doc_start a gives what that document alone gives, its keys
+    re-based to position 0 (causal holds relative positions)."""
+    rng = np.random.default_rng(15)
+    n, a, Lq, Hq, Hkv, D = 29, 12, 9, 4, 2, 8
+    Q = rng.standard_normal((Lq, Hq, D))
+    K = rng.standard_normal((Hkv, n, D))
+    V = rng.standard_normal((Hkv, n, D))
+    q_pos = np.arange(n - Lq, n)
+    mods = oracle.ScoreMods(causal=True)
+    packed = opa.attention_dense(Q, K, V, 0.3, q_pos, mods, doc_start=np.full(Lq, a))
+    alone = opa.attention_dense(Q, K[:, a:], V[:, a:], 0.3, q_pos - a, mods)
+    np.testing.assert_allclose(packed, alone, rtol=0, atol=1e-13)
+    # doc_start 0 everywhere is no document mask
+    np.testing.assert_allclose(opa.attention_dense(Q, K, V, 0.3, q_pos, mods, doc_start=np.zeros(Lq, int)),
+                               opa.attention_dense(Q, K, V, 0.3, q_pos, mods), rtol=0, atol=0)
 
 
 # --------------------------------------------------------------------------------------
@@ -401,6 +443,7 @@ def _all_pins():
     w = _tiny("prefill", 11, q_lens=[5, 7], causal=True)
     mods = oracle.ScoreMods(causal=True)
     np.testing.assert_allclose(_run(w, mods), brute_force(w, mods), rtol=0, atol=1e-12)
+    test_brute_force_with_prefix_and_documents()
 
 
 def _mutant_gather_v_not_transposed(k_pool, v_pool, table_row, n, bs):
@@ -419,27 +462,31 @@ def _mutant_gather_ignores_table(k_pool, v_pool, table_row, n, bs):
 def _make_attention_mutant(kind):
     orig = opa.__dict__["_orig_attention"]
 
-    def mutant(Q, K, V, scale, q_pos, mods=None):
+    def mutant(Q, K, V, scale, q_pos, mods=None, prefix_len=0, doc_start=None):
         mods = mods or oracle.ScoreMods()
         if kind == "no_scale":
-            return orig(Q, K, V, 1.0, q_pos, mods)
+            return orig(Q, K, V, 1.0, q_pos, mods, prefix_len, doc_start)
         if kind == "top_left_causal":
-            return orig(Q, K, V, scale, np.arange(len(q_pos)), mods)
+            return orig(Q, K, V, scale, np.arange(len(q_pos)), mods, prefix_len, doc_start)
         if kind == "gqa_modulo":
             Hq, Hkv = Q.shape[1], K.shape[0]
             idx = np.arange(Hq) % Hkv  # wrong grouping
             Kx = K[idx]
             Vx = V[idx]
-            return orig(Q, Kx, Vx, scale, q_pos, mods)
+            return orig(Q, Kx, Vx, scale, q_pos, mods, prefix_len, doc_start)
         if kind == "no_max_sub_sign":
-            return orig(Q, K, V, -scale, q_pos, mods)
+            return orig(Q, K, V, -scale, q_pos, mods, prefix_len, doc_start)
+        if kind == "prefix_inclusive":  # key == prefix wrongly visible
+            return orig(Q, K, V, scale, q_pos, mods, prefix_len + 1 if prefix_len else 0, doc_start)
+        if kind == "doc_exclusive":  # the document's first key wrongly hidden
+            return orig(Q, K, V, scale, q_pos, mods, prefix_len, None if doc_start is None else doc_start + 1)
         raise AssertionError(kind)
 
     return mutant
 
 
 @pytest.mark.parametrize("mutant", ["v_layout", "ignore_table", "no_scale", "top_left_causal",
-                                    "gqa_modulo", "sign"])
+                                    "gqa_modulo", "sign", "prefix_inclusive", "doc_exclusive"])
 def test_planted_mistakes_are_caught(monkeypatch, mutant):
     monkeypatch.setitem(opa.__dict__, "_orig_gather", opa.gather_sequence)
     monkeypatch.setitem(opa.__dict__, "_orig_attention", opa.attention_dense)
@@ -449,7 +496,8 @@ def test_planted_mistakes_are_caught(monkeypatch, mutant):
         monkeypatch.setattr(opa, "gather_sequence", _mutant_gather_ignores_table)
     else:
         kind = {"no_scale": "no_scale", "top_left_causal": "top_left_causal",
-                "gqa_modulo": "gqa_modulo", "sign": "no_max_sub_sign"}[mutant]
+                "gqa_modulo": "gqa_modulo", "sign": "no_max_sub_sign",
+                "prefix_inclusive": "prefix_inclusive", "doc_exclusive": "doc_exclusive"}[mutant]
         monkeypatch.setattr(opa, "attention_dense", _make_attention_mutant(kind))
     with pytest.raises(AssertionError):
         _all_pins()
