@@ -83,13 +83,23 @@ enum {
  *   alibi_slopes  : s = s + alibi_slopes[h] * (key_pos - query_pos)
  *                   (device pointer to num_heads floats; NULL = none)
  *   window > 0    : keys with query_pos - key_pos >= window are masked out
- * Passing NULL for the struct means none of them.  The struct itself is read
- * on the host during the call and may be freed on return.
+ *   prefix_lens   : prefix-LM; with causal masking, keys at positions below
+ *                   prefix_lens[b] are seen by every row of sequence b
+ *                   (device pointer to num_seqs int32; NULL = none)
+ *   doc_starts    : document masking of packed sequences; keys before
+ *                   doc_starts[row] are masked out for that query row
+ *                   (device pointer, one int32 per query row -- num_seqs for
+ *                   decode, total_q for prefill; NULL = none)
+ * Masks only shrink a row's key range, so fully masked key tiles are never
+ * read.  Passing NULL for the struct means none of them.  The struct itself
+ * is read on the host during the call and may be freed on return.
  */
 typedef struct {
   int32_t window;
   float softcap;
   const float* alibi_slopes;
+  const int32_t* prefix_lens;
+  const int32_t* doc_starts;
 } pa_score_mods;
 
 /*

@@ -22,10 +22,12 @@ _DTYPES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16}
 
 
 class ScoreMods(ctypes.Structure):
-    """``pa_score_mods``: window (0 = none), softcap (0 = none), alibi slopes."""
+    """``pa_score_mods``: window (0 = none), softcap (0 = none), alibi slopes,
+    prefix-LM lengths per sequence, document starts per query row."""
 
     _fields_ = [("window", ctypes.c_int32), ("softcap", ctypes.c_float),
-                ("alibi_slopes", ctypes.c_void_p)]
+                ("alibi_slopes", ctypes.c_void_p), ("prefix_lens", ctypes.c_void_p),
+                ("doc_starts", ctypes.c_void_p)]
 
 
 _i32 = ctypes.c_int32
@@ -116,12 +118,17 @@ def _dtype_code(t: torch.Tensor) -> int:
     return _DTYPES[t.dtype]
 
 
-def _mods(window=0, softcap=0.0, alibi_slopes=None):
-    if not window and not softcap and alibi_slopes is None:
+def _mods(window=0, softcap=0.0, alibi_slopes=None, prefix_lens=None, doc_starts=None):
+    if not window and not softcap and alibi_slopes is None and prefix_lens is None and doc_starts is None:
         return None, None
     if alibi_slopes is not None:
         _need(alibi_slopes, "alibi_slopes", torch.float32, 1)
-    m = ScoreMods(int(window), float(softcap), None if alibi_slopes is None else alibi_slopes.data_ptr())
+    if prefix_lens is not None:
+        _need(prefix_lens, "prefix_lens", torch.int32, 1)
+    if doc_starts is not None:
+        _need(doc_starts, "doc_starts", torch.int32, 1)
+    ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    m = ScoreMods(int(window), float(softcap), ptr(alibi_slopes), ptr(prefix_lens), ptr(doc_starts))
     return ctypes.pointer(m), m
 
 
@@ -177,7 +184,8 @@ def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens):
 
 
 def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
-                      split_tokens=0, workspace=None, window=0, softcap=0.0, alibi_slopes=None, phase="both"):
+                      split_tokens=0, workspace=None, window=0, softcap=0.0, alibi_slopes=None, phase="both",
+                      prefix_lens=None, doc_starts=None):
     """One query row per sequence; writes ``out [B, Hq, D]``.
 
     ``phase`` selects ``paged_attn_decode`` ("both"), ``..._partials`` or
@@ -188,7 +196,7 @@ def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens, scal
     if workspace is None:
         workspace = decode_workspace(q, Hkv, max_context_len, split_tokens)
     _need(workspace, "workspace")
-    mp, _keep = _mods(window, softcap, alibi_slopes)
+    mp, _keep = _mods(window, softcap, alibi_slopes, prefix_lens, doc_starts)
     ws_bytes = workspace.numel() * workspace.element_size()
     L = lib()
     if phase == "merge":
@@ -205,7 +213,7 @@ def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens, scal
 
 
 def paged_attn_prefill(out, q, cu_q_lens, k_cache, v_cache, block_tables, context_lens, scale, max_q_len,
-                       causal=True, window=0, softcap=0.0, alibi_slopes=None):
+                       causal=True, window=0, softcap=0.0, alibi_slopes=None, prefix_lens=None, doc_starts=None):
     """Query rows ``q [total_q, Hq, D]`` grouped by ``cu_q_lens [B+1]``; writes ``out``."""
     NB, Hkv, bs, D = _pool_dims(k_cache, v_cache)
     _need(q, "q", k_cache.dtype, 3)
@@ -217,7 +225,7 @@ def paged_attn_prefill(out, q, cu_q_lens, k_cache, v_cache, block_tables, contex
     if cu_q_lens.shape[0] != B + 1 or block_tables.shape[0] != B or tuple(out.shape) != tuple(q.shape) \
             or q.shape[2] != D:
         raise ValueError("shape mismatch between q/out/cu_q_lens/block_tables/context_lens/pools")
-    mp, _keep = _mods(window, softcap, alibi_slopes)
+    mp, _keep = _mods(window, softcap, alibi_slopes, prefix_lens, doc_starts)
     code = lib().paged_attn_prefill(_ptr(out), _ptr(q), _ptr(cu_q_lens), _ptr(k_cache), _ptr(v_cache),
                                     _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, int(max_q_len),
                                     q.shape[1], Hkv, D, bs, NB, float(scale), int(bool(causal)), mp, _dtype_code(q),

@@ -146,6 +146,8 @@ void fill_row_args(pa::RowAttnArgs& a, void* out, const void* q, const void* kc,
   a.scale = scale;
   a.softcap = mods ? mods->softcap : 0.f;
   a.alibi = mods ? mods->alibi_slopes : nullptr;
+  a.prefix_lens = mods ? mods->prefix_lens : nullptr;
+  a.doc_starts = mods ? mods->doc_starts : nullptr;
   float* w = static_cast<float*>(ws);
   const size_t units = s.W > 0 ? ((size_t)s.W + (size_t)B * Hkv * s.NG) * s.GP
                                : (size_t)B * max_q * Hkv * s.NG * s.GP * (size_t)s.P;
@@ -304,6 +306,8 @@ int paged_attn_prefill(void* out, const void* q, const int32_t* cu_q_lens, const
     a.context_lens = context_lens;
     a.cu_q_lens = cu_q_lens;
     a.alibi = mods ? mods->alibi_slopes : nullptr;
+    a.prefix_lens = mods ? mods->prefix_lens : nullptr;
+    a.doc_starts = mods ? mods->doc_starts : nullptr;
     a.bt_stride = block_table_stride;
     a.num_seqs = num_seqs;
     a.Hq = num_heads;

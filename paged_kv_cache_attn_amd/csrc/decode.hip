@@ -126,7 +126,9 @@ __device__ __forceinline__ bool row_range(const RowAttnArgs& a, int slot, RowRan
   r.qrow = q0 + i;
   r.pos = n - Lq + i;
   r.hi = a.causal ? min(n, r.pos + 1) : n;
+  if (a.causal && a.prefix_lens) r.hi = min(n, max(r.hi, a.prefix_lens[b]));
   r.lo = a.window > 0 ? max(0, r.pos - a.window + 1) : 0;
+  if (a.doc_starts) r.lo = max(r.lo, a.doc_starts[r.qrow]);
   if (r.hi < 0) r.hi = 0;
   if (r.lo > r.hi) r.lo = r.hi;
   r.start = r.lo & ~15;
@@ -455,9 +457,9 @@ __global__ __launch_bounds__(64) void row_partials_kernel(const RowAttnArgs a) {
 // 16-token chunks a decode row's admissible range spans (>= 1, so that an
 // empty context still gets a (fully masked) chunk and a zero output).
 __device__ __forceinline__ int decode_chunks(const RowAttnArgs& a, int b) {
-  const int n = a.context_lens[b];
-  const int lo = a.window > 0 ? max(0, n - a.window) : 0;
-  const int c = (n - (lo & ~15) + 15) >> 4;
+  RowRange rr;
+  row_range(a, b, rr);  // decode: slot b is sequence b's only row
+  const int c = (rr.hi - rr.start + 15) >> 4;
   return c > 1 ? c : 1;
 }
 

@@ -20,6 +20,8 @@ struct RowAttnArgs {
   float* ws_ml;              // [row_slots, head_groups, P, GP, 2]
   int32_t* ws_meta;          // balanced split: per item (first partial unit, count)
   const float* alibi;        // [Hq] or nullptr
+  const int32_t* prefix_lens;  // [num_seqs] or nullptr (prefix-LM, with causal)
+  const int32_t* doc_starts;   // [rows] or nullptr (first admissible key per row)
   int32_t bt_stride;
   int32_t max_q_len;
   int32_t num_seqs;
@@ -52,6 +54,8 @@ struct PrefillArgs {
   const int32_t* context_lens;
   const int32_t* cu_q_lens;
   const float* alibi;
+  const int32_t* prefix_lens;  // [num_seqs] or nullptr
+  const int32_t* doc_starts;   // [total_q] or nullptr
   int32_t bt_stride;
   int32_t num_seqs;
   int32_t Hq, Hkv, g;

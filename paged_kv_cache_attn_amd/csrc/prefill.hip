@@ -124,18 +124,42 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
   const bool row_ok = qi < Lq;
   const int pos = n - Lq + qi;
   int row_hi = row_ok ? (a.causal ? min(n, pos + 1) : n) : 0;
+  if (row_ok && a.causal && a.prefix_lens) row_hi = min(n, max(row_hi, a.prefix_lens[b]));
   int row_lo = (row_ok && a.window > 0) ? max(0, pos - a.window + 1) : 0;
+  if (row_ok && a.doc_starts) row_lo = max(row_lo, a.doc_starts[q0 + qi]);
   if (row_lo > row_hi) row_lo = row_hi;
   const int head = kvh * a.g + head_in;
 
-  // key range of the whole work-group (uniform)
-  const int q_last = min(Lq, q_start + QT) - 1;
-  const int pos_first = n - Lq + q_start;
-  const int pos_last = n - Lq + q_last;
-  const int wg_hi = a.causal ? min(n, pos_last + 1) : n;
-  const int wg_lo = a.window > 0 ? max(0, pos_first - a.window + 1) : 0;
-  const int safe_hi = a.causal ? min(n, pos_first + 1) : n;                // every row admits keys < safe_hi
-  const int safe_lo = a.window > 0 ? max(0, pos_last - a.window + 1) : 0;  // ... and >= safe_lo
+  // Key range of the whole work-group (uniform): keys [wg_lo, wg_hi) are
+  // admissible for some row, keys [safe_lo, safe_hi) for every row.
+  __shared__ int wg_bounds[4][4];
+  int wg_lo, wg_hi, safe_lo, safe_hi;
+  {
+    int b0 = row_ok ? row_lo : 0x7fffffff, b1 = row_ok ? row_hi : 0;   // min lo, max hi
+    int b2 = row_ok ? row_lo : 0, b3 = row_ok ? row_hi : 0x7fffffff;   // max lo, min hi
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      b0 = min(b0, __shfl_xor(b0, off, 64));
+      b1 = max(b1, __shfl_xor(b1, off, 64));
+      b2 = max(b2, __shfl_xor(b2, off, 64));
+      b3 = min(b3, __shfl_xor(b3, off, 64));
+    }
+    if (lane == 0) {
+      wg_bounds[wave][0] = b0;
+      wg_bounds[wave][1] = b1;
+      wg_bounds[wave][2] = b2;
+      wg_bounds[wave][3] = b3;
+    }
+    __syncthreads();
+    wg_lo = min(min(wg_bounds[0][0], wg_bounds[1][0]), min(wg_bounds[2][0], wg_bounds[3][0]));
+    wg_hi = max(max(wg_bounds[0][1], wg_bounds[1][1]), max(wg_bounds[2][1], wg_bounds[3][1]));
+    safe_lo = max(max(wg_bounds[0][2], wg_bounds[1][2]), max(wg_bounds[2][2], wg_bounds[3][2]));
+    safe_hi = min(min(wg_bounds[0][3], wg_bounds[1][3]), min(wg_bounds[2][3], wg_bounds[3][3]));
+    wg_lo = __builtin_amdgcn_readfirstlane(wg_lo);
+    wg_hi = __builtin_amdgcn_readfirstlane(wg_hi);
+    safe_lo = __builtin_amdgcn_readfirstlane(safe_lo);
+    safe_hi = __builtin_amdgcn_readfirstlane(safe_hi);
+  }
 
   const int32_t* table = a.block_tables + (size_t)b * a.bt_stride;
   const int bs = 1 << a.bs_log2;

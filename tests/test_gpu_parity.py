@@ -6,6 +6,7 @@ over the whole pool.  Invariances that the pages state (scattered placement
 and shared blocks give the same result) are checked bit for bit.
 """
 
+import dataclasses
 import math
 
 import numpy as np
@@ -36,7 +37,7 @@ def oracle_out(w, mods=None, seqs=None, causal=None):
     kp, vp = appended_pools(w)
     m = mods or oracle.ScoreMods()
     if causal is not None:
-        m = oracle.ScoreMods(causal=causal, window=m.window, softcap=m.softcap, alibi_slopes=m.alibi_slopes)
+        m = dataclasses.replace(m, causal=causal)
     return oracle.paged_attention(w.q, kp, vp, w.block_table, w.context_lens, w.cu_q_lens, w.scale, w.bs,
                                   w.dtype, m, seqs=seqs)
 
@@ -359,3 +360,50 @@ def test_balanced_split_workspace_reuse_across_batches(gpu_lib):
                                   w.scale, w.max_context_len, 0, workspace=ws)
         torch.cuda.synchronize()
         assert_close(to_numpy_bits(out), oracle_out(w), "bf16")
+
+
+def _doc_starts(w, rng, docs_per_seq=3):
+    """Per query row: the start of its document, for `docs_per_seq` documents
+    cut at random points of each sequence (rows at positions n - Lq + i)."""
+    out = []
+    for b in range(w.B):
+        n = int(w.context_lens[b])
+        L = int(w.q_lens[b]) if w.kind == "prefill" else 1
+        cuts = np.sort(rng.choice(np.arange(1, n), size=min(docs_per_seq - 1, max(n - 1, 0)), replace=False))
+        starts = np.concatenate([[0], cuts])
+        for pos in range(n - L, n):
+            out.append(int(starts[np.searchsorted(starts, pos, side="right") - 1]))
+    return np.array(out, dtype=np.int32)
+
+
+@pytest.mark.parametrize("case", ["prefix", "docs", "prefix_docs_window", "docs_mods"])
+def test_prefix_lm_and_document_masks(gpu_lib, case):
+    rng = np.random.default_rng(77)
+    Hq, Hkv = 16, 4
+    wp = small("prefill", ctx=(150, 400, 700), q_lens=[150, 170, 300], Hq=Hq, Hkv=Hkv, causal=True)
+    wd = small(ctx=(90, 700, 1300), Hq=Hq, Hkv=Hkv, append=[1, 1, 1])
+    for w, is_prefill in ((wp, True), (wd, False)):
+        kw, om = {}, {}
+        if "prefix" in case:
+            pl = np.array([min(int(n), 64 + 97 * i) for i, n in enumerate(w.context_lens)], dtype=np.int32)
+            kw["prefix_lens"] = torch.from_numpy(pl).cuda()
+            om["prefix_lens"] = pl
+        if "docs" in case:
+            ds = _doc_starts(w, rng)
+            kw["doc_starts"] = torch.from_numpy(ds).cuda()
+            om["doc_starts"] = ds
+        if "window" in case:
+            kw["window"] = om["window"] = 200
+        if case == "docs_mods":
+            kw["softcap"] = om["softcap"] = 0.5
+        if is_prefill:
+            ref = oracle_out(w, oracle.ScoreMods(causal=True, **om))
+            assert_close(gpu_prefill(gpu_lib, w, **kw), ref, "bf16")
+        else:
+            ref = oracle_out(w, oracle.ScoreMods(**om))
+            for split in (0, 64, -1):
+                assert_close(gpu_decode(gpu_lib, w, split=split, **kw), ref, "bf16")
+    wf = small("prefill", dtype="f32", ctx=(150, 400), q_lens=[150, 170], Hq=Hq, Hkv=Hkv, causal=True)
+    ds = _doc_starts(wf, rng)
+    assert_close(gpu_prefill(gpu_lib, wf, doc_starts=torch.from_numpy(ds).cuda()),
+                 oracle_out(wf, oracle.ScoreMods(causal=True, doc_starts=ds)), "f32")
