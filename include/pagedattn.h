@@ -72,7 +72,9 @@ enum {
   PA_ERR_DTYPE = -8,         /* dtype not PA_F32 / PA_BF16                      */
   PA_ERR_FLAG = -9,          /* causal not 0 or 1                               */
   PA_ERR_MODS = -10,         /* window < 0, softcap < 0 or not finite           */
-  PA_ERR_TABLE_STRIDE = -11  /* block_table_stride < 1                          */
+  PA_ERR_TABLE_STRIDE = -11, /* block_table_stride < 1                          */
+  PA_ERR_NO_BLOCKS = -12,    /* block manager: the pool is exhausted            */
+  PA_ERR_SEQ = -13           /* block manager: unknown or freed sequence id     */
 };
 
 /*
@@ -118,6 +120,21 @@ int kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache
               const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
               int32_t head_dim, int32_t block_size, int64_t num_blocks, int32_t dtype,
               void* stream);
+
+/*
+ * kv_copy_blocks -- copy whole physical blocks (copy-on-write, fork).
+ *
+ * For every i < num_pairs and every kv-head, the K slab and the V slab of
+ * block src_blocks[i] are copied bit for bit onto block dst_blocks[i]
+ * ("Ultimate Guide to PagedAttention": copy-on-write when a shared block is
+ * written).  src_blocks / dst_blocks: device int32 [num_pairs].  Caller
+ * contract (not checked on the device): ids in [0, num_blocks), no
+ * destination listed twice and no destination that is also a source.
+ * num_pairs == 0 is a no-op.
+ */
+int kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_blocks, const int32_t* dst_blocks,
+                   int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                   int64_t num_blocks, int32_t dtype, void* stream);
 
 /*
  * Bytes of workspace paged_attn_decode needs for these sizes.  Split-KV --

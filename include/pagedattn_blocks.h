@@ -1,0 +1,76 @@
+/*
+ * pagedattn_blocks.h -- host-side block manager for the paged KV cache.
+ *
+ * The pool of physical blocks is handed out to sequences on demand; a
+ * sequence's block table maps its logical blocks to physical ones, sequences
+ * that share a prefix (a forked beam, a common prompt) share physical blocks
+ * through reference counts, and a write into a shared, partially filled block
+ * first copies it (copy-on-write) ("Ultimate Guide to PagedAttention":
+ * block table, dynamic allocation, memory sharing and copy-on-write; Kwon et
+ * al., "Efficient Memory Management for Large Language Model Serving with
+ * PagedAttention", abstract: near-zero waste and flexible sharing).
+ *
+ * This is bookkeeping on the host only: it produces the slot_mapping that
+ * kv_append consumes, the block-table rows the attention calls read, and the
+ * (src, dst) block pairs that kv_copy_blocks must copy before the append.
+ * It never touches device memory.  Every call is thread-safe (one lock per
+ * manager).  Status codes are those of pagedattn.h; the manager adds
+ * PA_ERR_NO_BLOCKS (the pool is exhausted; the call changed nothing) and
+ * PA_ERR_SEQ (unknown or freed sequence id).
+ */
+#ifndef PAGEDATTN_BLOCKS_H_
+#define PAGEDATTN_BLOCKS_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct pa_block_manager pa_block_manager;
+
+/* A manager for num_blocks physical blocks of block_size tokens (a power of
+ * two in [16, 256]).  *out receives the handle; NULL on failure. */
+int pa_bm_create(int64_t num_blocks, int32_t block_size, pa_block_manager** out);
+void pa_bm_destroy(pa_block_manager* bm);
+
+/* A new, empty sequence; its id goes to *seq. */
+int pa_bm_new_sequence(pa_block_manager* bm, int32_t* seq);
+
+/* A new sequence that shares every block (and the length) of `parent`
+ * (reference counts rise; nothing is copied yet). */
+int pa_bm_fork(pa_block_manager* bm, int32_t parent, int32_t* child);
+
+/* Drop a sequence; blocks whose count falls to zero return to the pool. */
+int pa_bm_free_sequence(pa_block_manager* bm, int32_t seq);
+
+/*
+ * Reserve slots for ntok new tokens at the end of `seq`.  slots_out[i]
+ * (ntok entries) is the pool slot of logical position len + i, as kv_append
+ * expects.  If the last block is shared and not full, it is first replaced
+ * by a fresh block and the pair (old, new) is appended to copy_src/copy_dst
+ * (room for copy_cap pairs; *ncopy receives the count): the caller runs
+ * kv_copy_blocks on those pairs before kv_append.  PA_ERR_NO_BLOCKS leaves
+ * everything unchanged; PA_ERR_SIZE if ntok < 0 or copy_cap is too small.
+ */
+int pa_bm_append(pa_block_manager* bm, int32_t seq, int32_t ntok, int32_t* slots_out,
+                 int32_t* copy_src, int32_t* copy_dst, int32_t copy_cap, int32_t* ncopy);
+
+/* The sequence's token count (*len) and block-table row: the first
+ * min(cap, nblocks) entries go to row, the total to *nblocks. */
+int pa_bm_table(const pa_block_manager* bm, int32_t seq, int32_t* row, int32_t cap, int32_t* nblocks,
+                int64_t* len);
+
+/* Pool accounting: free blocks, blocks in use, and the slots of blocks in
+ * use that hold no token (internal fragmentation = waste / (used * bs)). */
+int pa_bm_stats(const pa_block_manager* bm, int64_t* free_blocks, int64_t* used_blocks, int64_t* waste_slots);
+
+/* Reference count of one physical block (0 = free). */
+int pa_bm_block_refcount(const pa_block_manager* bm, int32_t block, int32_t* count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_BLOCKS_H_ */

@@ -5,6 +5,7 @@ The compute lives in ``libpagedattn.so`` (hand-written HIP kernels, C ABI in
 """
 
 from .binding import (  # noqa: F401
+    BlockManager,
     PA_BF16,
     PA_F32,
     bench_fill,
@@ -13,6 +14,7 @@ from .binding import (  # noqa: F401
     decode_workspace,
     decode_workspace_size,
     kv_append,
+    kv_copy_blocks,
     lib,
     lib_path,
     paged_attn_decode,

@@ -51,6 +51,18 @@ SIGNATURES = {
     "paged_attn_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                   _i64, _f32, _i32, _mods_p, _i32, _vp]),
     "paged_attn_status_string": (ctypes.c_char_p, [_i32]),
+    "kv_copy_blocks": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _i32, _vp]),
+    # include/pagedattn_blocks.h (host block manager)
+    "pa_bm_create": (_i32, [_i64, _i32, ctypes.POINTER(_vp)]),
+    "pa_bm_destroy": (None, [_vp]),
+    "pa_bm_new_sequence": (_i32, [_vp, ctypes.POINTER(_i32)]),
+    "pa_bm_fork": (_i32, [_vp, _i32, ctypes.POINTER(_i32)]),
+    "pa_bm_free_sequence": (_i32, [_vp, _i32]),
+    "pa_bm_append": (_i32, [_vp, _i32, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32), ctypes.POINTER(_i32), _i32,
+                            ctypes.POINTER(_i32)]),
+    "pa_bm_table": (_i32, [_vp, _i32, ctypes.POINTER(_i32), _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i64)]),
+    "pa_bm_stats": (_i32, [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
+    "pa_bm_block_refcount": (_i32, [_vp, _i32, ctypes.POINTER(_i32)]),
     # include/pagedattn_bench.h (measurement support)
     "pa_bench_stream_read": (_i32, [_vp, _sz, _vp, _vp]),
     "pa_bench_fill": (_i32, [_vp, _sz, ctypes.c_uint32, _vp]),
@@ -248,3 +260,81 @@ def bench_fill(dst: torch.Tensor, value: int = 0):
     _need(dst, "dst")
     code = lib().pa_bench_fill(_ptr(dst), dst.numel() * dst.element_size(), int(value) & 0xFFFFFFFF, _stream())
     _check(code, "pa_bench_fill")
+
+
+def kv_copy_blocks(k_cache, v_cache, src_blocks, dst_blocks):
+    """Copy whole physical blocks ``src_blocks[i] -> dst_blocks[i]`` (int32 device tensors) in both pools."""
+    NB, Hkv, bs, D = _pool_dims(k_cache, v_cache)
+    _need(src_blocks, "src_blocks", torch.int32, 1)
+    _need(dst_blocks, "dst_blocks", torch.int32, 1)
+    if src_blocks.shape != dst_blocks.shape:
+        raise ValueError("src_blocks and dst_blocks must have the same length")
+    code = lib().kv_copy_blocks(_ptr(k_cache), _ptr(v_cache), _ptr(src_blocks), _ptr(dst_blocks),
+                                src_blocks.shape[0], Hkv, D, bs, NB, _dtype_code(k_cache), _stream())
+    _check(code, "kv_copy_blocks")
+
+
+class BlockManager:
+    """Host block manager (``include/pagedattn_blocks.h``): allocation, fork by
+    sharing, copy-on-write.  Thin wrapper; all bookkeeping is in the library."""
+
+    def __init__(self, num_blocks: int, block_size: int):
+        h = ctypes.c_void_p()
+        _check(lib().pa_bm_create(int(num_blocks), int(block_size), ctypes.byref(h)), "pa_bm_create")
+        self._h = h
+        self.block_size = int(block_size)
+
+    def close(self):
+        if self._h:
+            lib().pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def new_sequence(self) -> int:
+        s = ctypes.c_int32()
+        _check(lib().pa_bm_new_sequence(self._h, ctypes.byref(s)), "pa_bm_new_sequence")
+        return s.value
+
+    def fork(self, parent: int) -> int:
+        c = ctypes.c_int32()
+        _check(lib().pa_bm_fork(self._h, int(parent), ctypes.byref(c)), "pa_bm_fork")
+        return c.value
+
+    def free(self, seq: int):
+        _check(lib().pa_bm_free_sequence(self._h, int(seq)), "pa_bm_free_sequence")
+
+    def append(self, seq: int, ntok: int):
+        """Slots for ``ntok`` new tokens and the (src, dst) block copies to run first."""
+        slots = (ctypes.c_int32 * max(1, ntok))()
+        src = (ctypes.c_int32 * 1)()
+        dst = (ctypes.c_int32 * 1)()
+        n = ctypes.c_int32()
+        _check(lib().pa_bm_append(self._h, int(seq), int(ntok), slots, src, dst, 1, ctypes.byref(n)),
+               "pa_bm_append")
+        return list(slots[:ntok]), [(src[i], dst[i]) for i in range(n.value)]
+
+    def table(self, seq: int):
+        """(block-table row, token count) of a sequence."""
+        nb = ctypes.c_int32()
+        ln = ctypes.c_int64()
+        _check(lib().pa_bm_table(self._h, int(seq), None, 0, ctypes.byref(nb), ctypes.byref(ln)), "pa_bm_table")
+        row = (ctypes.c_int32 * max(1, nb.value))()
+        _check(lib().pa_bm_table(self._h, int(seq), row, nb.value, ctypes.byref(nb), ctypes.byref(ln)),
+               "pa_bm_table")
+        return list(row[:nb.value]), ln.value
+
+    def stats(self):
+        """(free blocks, used blocks, empty slots in used blocks)."""
+        f, u, w = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        _check(lib().pa_bm_stats(self._h, ctypes.byref(f), ctypes.byref(u), ctypes.byref(w)), "pa_bm_stats")
+        return f.value, u.value, w.value
+
+    def refcount(self, block: int) -> int:
+        c = ctypes.c_int32()
+        _check(lib().pa_bm_block_refcount(self._h, int(block), ctypes.byref(c)), "pa_bm_block_refcount")
+        return c.value

@@ -15,7 +15,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libpagedattn.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "kv_append.hip", "decode.hip", "prefill.hip", "bench_util.hip"]
+SOURCES = ["api.hip", "kv_append.hip", "decode.hip", "prefill.hip", "bench_util.hip", "block_manager.cpp"]
 
 CXXFLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

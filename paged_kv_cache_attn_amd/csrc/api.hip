@@ -226,6 +226,29 @@ int32_t paged_attn_decode_split_tokens(int32_t num_seqs, int32_t num_kv_heads,
   return l2 >= kUnsplitLog2 ? -1 : (1 << l2);
 }
 
+int kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_blocks, const int32_t* dst_blocks,
+                   int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                   int64_t num_blocks, int32_t dtype, void* stream) {
+  int st;
+  if ((st = check_dtype(dtype))) return st;
+  if (num_pairs < 0 || num_blocks < 0) return PA_ERR_SIZE;
+  if (num_kv_heads <= 0) return PA_ERR_HEADS;
+  if ((st = check_dim(head_dim))) return st;
+  if ((st = check_bs(block_size))) return st;
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !src_blocks || !dst_blocks) return PA_ERR_NULL;
+  pa::CopyArgs a;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.src = src_blocks;
+  a.dst = dst_blocks;
+  a.pairs = num_pairs;
+  a.slab16 = (int32_t)((size_t)block_size * head_dim * (dtype == PA_BF16 ? 2 : 4) / 16);
+  a.Hkv = num_kv_heads;
+  if ((long long)num_pairs * num_kv_heads * 2 > 0x7fffffffll) return PA_ERR_SIZE;
+  return launch_status(pa::launch_copy_blocks(a, static_cast<hipStream_t>(stream)));
+}
+
 size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_heads,
                                         int32_t num_kv_heads, int32_t head_dim,
                                         int32_t max_context_len, int32_t split_tokens) {
@@ -354,6 +377,8 @@ const char* paged_attn_status_string(int status) {
     case PA_ERR_FLAG: return "causal must be 0 or 1";
     case PA_ERR_MODS: return "score mods: window and softcap must be finite and >= 0";
     case PA_ERR_TABLE_STRIDE: return "block_table_stride must be >= 1";
+    case PA_ERR_NO_BLOCKS: return "block manager: no free block left in the pool";
+    case PA_ERR_SEQ: return "block manager: unknown or freed sequence id";
     default: break;
   }
   if (status > 0) return hipGetErrorString(static_cast<hipError_t>(status));

@@ -4,7 +4,8 @@
 // freshly allocated ones) and nothing already stored moves ("Ultimate Guide
 // to PagedAttention", newline: KV cache and dynamic growth).  Token t goes to
 // slot s = slot_mapping[t]: block s >> log2(bs), offset s & (bs - 1).  The
-// copy is of raw bits.  One wavefront per (token, kv-head).
+// copy is of raw bits.  One wavefront per (token, kv-head).  Also the
+// whole-block copy that copy-on-write needs.
 #include "pa_device.h"
 #include "pa_kernels.h"
 
@@ -33,7 +34,28 @@ __global__ __launch_bounds__(64) void kv_append_kernel(const AppendArgs a) {
   }
 }
 
+// Copy-on-write: whole (block, kv-head) slabs of K and V, bit for bit.  One
+// work-group per (pair, kv-head, K or V); 16-byte loads and stores.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(const CopyArgs a) {
+  const int which = blockIdx.x & 1;  // 0: K, 1: V
+  const int rest = blockIdx.x >> 1;
+  const int h = rest % a.Hkv;
+  const int i = rest / a.Hkv;
+  const size_t slab = (size_t)a.slab16;
+  const size_t src = ((size_t)a.src[i] * a.Hkv + h) * slab;
+  const size_t dst = ((size_t)a.dst[i] * a.Hkv + h) * slab;
+  u32x4* pool = static_cast<u32x4*>(which ? a.v_cache : a.k_cache);
+  for (size_t u = threadIdx.x; u < slab; u += 256) pool[dst + u] = pool[src + u];
+}
+
 }  // namespace
+
+hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t s) {
+  const long long blocks = (long long)a.pairs * a.Hkv * 2;
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_kv_append(const AppendArgs& a, int dtype, hipStream_t s) {
   const long long blocks = (long long)a.T * a.Hkv;

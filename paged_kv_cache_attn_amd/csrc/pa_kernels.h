@@ -67,7 +67,18 @@ struct PrefillArgs {
   float softcap;
 };
 
+struct CopyArgs {
+  void* k_cache;
+  void* v_cache;
+  const int32_t* src;        // [pairs] physical blocks
+  const int32_t* dst;        // [pairs]
+  int32_t pairs;
+  int32_t slab16;            // 16-byte units in one (block, kv-head) slab
+  int32_t Hkv;
+};
+
 hipError_t launch_kv_append(const AppendArgs& a, int dtype, hipStream_t s);
+hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t s);
 hipError_t launch_row_partials(const RowAttnArgs& a, int dtype, int D, hipStream_t s);
 hipError_t launch_row_merge(const RowAttnArgs& a, int dtype, int D, hipStream_t s);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, int D, hipStream_t s);

@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     assert binding.status_string(0) == "ok"
-    for code in range(-11, 0):
+    for code in range(-13, 0):
         s = binding.status_string(code)
         assert s and s != "unknown status", code
     assert binding.status_string(-99) == "unknown status"
@@ -178,3 +178,24 @@ def test_bench_util_validation():
     assert L.pa_bench_fill(NULL, 16, 0, None) == -1
     assert L.pa_bench_fill(FAKE, 24, 0, None) == -2
     assert L.pa_bench_fill(FAKE, 0, 0, None) == 0
+
+
+def test_copy_blocks_validation():
+    L = binding.lib()
+    assert L.kv_copy_blocks(FAKE, FAKE, FAKE, FAKE, -1, 8, 128, 16, 10, 1, None) == -2
+    assert L.kv_copy_blocks(FAKE, FAKE, FAKE, FAKE, 2, 0, 128, 16, 10, 1, None) == -3
+    assert L.kv_copy_blocks(FAKE, FAKE, FAKE, FAKE, 2, 8, 96, 16, 10, 1, None) == -4
+    assert L.kv_copy_blocks(FAKE, FAKE, FAKE, FAKE, 2, 8, 128, 24, 10, 1, None) == -5
+    assert L.kv_copy_blocks(FAKE, FAKE, FAKE, FAKE, 2, 8, 128, 16, 10, 7, None) == -8
+    assert L.kv_copy_blocks(NULL, FAKE, FAKE, FAKE, 2, 8, 128, 16, 10, 1, None) == -1
+    assert L.kv_copy_blocks(NULL, NULL, NULL, NULL, 0, 8, 128, 16, 10, 1, None) == 0  # nothing to do
+
+
+def test_block_manager_argument_checks():
+    L = binding.lib()
+    h = ctypes.c_void_p()
+    assert L.pa_bm_create(10, 24, ctypes.byref(h)) == -5
+    assert L.pa_bm_create(-1, 16, ctypes.byref(h)) == -2
+    assert L.pa_bm_create(10, 16, None) == -1
+    assert binding.status_string(-12).startswith("block manager")
+    assert binding.status_string(-13).startswith("block manager")
