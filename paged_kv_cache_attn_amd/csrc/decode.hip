@@ -217,7 +217,11 @@ __device__ __forceinline__ void attend_segment(const RowAttnArgs& a, const RowRa
     for (int r = 0; r < C::RPL; ++r)
 #pragma unroll
       for (int w = 0; w < C::VPR; ++w)
-        ch.v[r][w] = load16_stream(vs + ((size_t)(vr + 32 * r) * bs + vh * 8) * C::ES + w * 16);
+        // V rows of a 16-token chunk are 32-byte pieces of rows bs tokens long:
+        // for bs > 16 the next chunks reuse the same cache lines, so those
+        // loads keep the normal (temporal) cache policy
+        ch.v[r][w] = (bs == 16) ? load16_stream(vs + ((size_t)(vr + 32 * r) * bs + vh * 8) * C::ES + w * 16)
+                                : load16(vs + ((size_t)(vr + 32 * r) * bs + vh * 8) * C::ES + w * 16);
   };
 
   // one 16-token chunk: scores, online softmax, P.V.  A chunk that starts at
