@@ -45,7 +45,9 @@
  * block ids must lie in [0, num_blocks), context_lens[b] must not exceed
  * block_table_stride * block_size, a prefill sequence must have
  * q_len <= context_len, and the slots of one kv_append must be distinct.
- * Breaking these is undefined behaviour.
+ * Breaking these is undefined behaviour in the release library; the same
+ * library built with PA_DEBUG_CHECKS (libpagedattn_debug.so) checks block
+ * ids and lengths on the device and traps instead.
  * ---------------------------------------------------------------------------
  */
 #ifndef PAGEDATTN_H_

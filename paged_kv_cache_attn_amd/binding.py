@@ -14,7 +14,11 @@ import os
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedattn.so")
+# PAGEDATTN_DEBUG_CHECKS=1 selects the build whose kernels trap on a broken
+# device-side caller contract (block ids out of range, lengths past the table).
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                         "libpagedattn_debug.so" if os.environ.get("PAGEDATTN_DEBUG_CHECKS") == "1"
+                         else "libpagedattn.so")
 
 PA_F32 = 0
 PA_BF16 = 1

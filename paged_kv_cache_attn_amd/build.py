@@ -44,22 +44,34 @@ def _run(cmd, verbose):
         print(out, flush=True)
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    """Compile every HIP source for gfx950 and link ``libpagedattn.so``; returns its path."""
+DEBUG_LIB_PATH = os.path.join(PKG, "libpagedattn_debug.so")
+
+
+def build(verbose: bool = False, jobs: int = 8, debug_checks: bool = True) -> str:
+    """Compile every HIP source for gfx950 and link ``libpagedattn.so`` (and,
+    with ``debug_checks``, ``libpagedattn_debug.so``: the same code built with
+    PA_DEBUG_CHECKS, whose kernels trap on a broken device-side contract);
+    returns the release library's path."""
     hipcc = _hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    objs = []
-    cmds = []
-    for src in SOURCES:
-        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-        objs.append(obj)
-        cmds.append([hipcc, *CXXFLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+    variants = [(LIB_PATH, BUILD_DIR, [])]
+    if debug_checks:
+        variants.append((DEBUG_LIB_PATH, os.path.join(BUILD_DIR, "debug"), ["-DPA_DEBUG_CHECKS"]))
+    cmds, links = [], []
+    for lib_path, bdir, extra in variants:
+        os.makedirs(bdir, exist_ok=True)
+        objs = []
+        for src in SOURCES:
+            obj = os.path.join(bdir, os.path.splitext(src)[0] + ".o")
+            objs.append(obj)
+            cmds.append([hipcc, *CXXFLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj])
+        links.append((lib_path, objs))
     with ThreadPoolExecutor(max(1, min(jobs, len(cmds)))) as ex:
         for f in [ex.submit(_run, c, verbose) for c in cmds]:
             f.result()
-    tmp = LIB_PATH + ".tmp"
-    _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-fPIC", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB_PATH)
+    for lib_path, objs in links:
+        tmp = lib_path + ".tmp"
+        _run([hipcc, "-shared", f"--offload-arch={ARCH}", "-fPIC", *objs, "-o", tmp], verbose)
+        os.replace(tmp, lib_path)
     return LIB_PATH
 
 

@@ -138,6 +138,7 @@ void fill_row_args(pa::RowAttnArgs& a, void* out, const void* q, const void* kc,
   a.g = s.g;
   a.NG = s.NG;
   a.bs_log2 = ilog2(bs);
+  a.num_blocks = 0;  // set by the caller
   a.split_log2 = s.split_log2;
   a.P = s.P;
   a.stream_waves = s.W;
@@ -178,6 +179,7 @@ int decode_impl(bool do_partials, bool do_merge, void* out, const void* q, const
   pa::RowAttnArgs a;
   fill_row_args(a, out, q, k_cache, v_cache, block_tables, bt_stride, context_lens, nullptr, B, 1,
                 Hq, Hkv, bs, s, scale, 1, mods, need > 0 ? workspace : nullptr, D);
+  a.num_blocks = NB;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   if (do_partials) {
     if ((st = launch_status(pa::launch_row_partials(a, dtype, D, hs)))) return st;
@@ -211,6 +213,7 @@ int kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache
   a.k_cache = k_cache;
   a.v_cache = v_cache;
   a.slots = slot_mapping;
+  a.num_blocks = num_blocks;
   a.T = num_tokens;
   a.Hkv = num_kv_heads;
   a.D = head_dim;
@@ -243,6 +246,7 @@ int kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_blocks, cons
   a.src = src_blocks;
   a.dst = dst_blocks;
   a.pairs = num_pairs;
+  a.num_blocks = num_blocks;
   a.slab16 = (int32_t)((size_t)block_size * head_dim * (dtype == PA_BF16 ? 2 : 4) / 16);
   a.Hkv = num_kv_heads;
   if ((long long)num_pairs * num_kv_heads * 2 > 0x7fffffffll) return PA_ERR_SIZE;
@@ -332,6 +336,7 @@ int paged_attn_prefill(void* out, const void* q, const int32_t* cu_q_lens, const
     a.prefix_lens = mods ? mods->prefix_lens : nullptr;
     a.doc_starts = mods ? mods->doc_starts : nullptr;
     a.bt_stride = block_table_stride;
+    a.num_blocks = num_blocks;
     a.num_seqs = num_seqs;
     a.Hq = num_heads;
     a.Hkv = num_kv_heads;
@@ -360,6 +365,7 @@ int paged_attn_prefill(void* out, const void* q, const int32_t* cu_q_lens, const
   fill_row_args(a, out, q, k_cache, v_cache, block_tables, block_table_stride, context_lens,
                 cu_q_lens, num_seqs, max_q_len, num_heads, num_kv_heads, block_size, s, scale,
                 causal, mods, nullptr, head_dim);
+  a.num_blocks = num_blocks;
   return launch_status(pa::launch_row_partials(a, dtype, head_dim, hs));
 }
 

@@ -123,6 +123,7 @@ __device__ __forceinline__ bool row_range(const RowAttnArgs& a, int slot, RowRan
     Lq = a.cu_q_lens[b + 1] - q0;
   }
   if (i >= Lq) return false;
+  PA_DEVICE_CHECK(n >= 0 && (long long)n <= (long long)a.bt_stride << a.bs_log2 && Lq <= n);
   r.qrow = q0 + i;
   r.pos = n - Lq + i;
   r.hi = a.causal ? min(n, r.pos + 1) : n;
@@ -204,6 +205,7 @@ __device__ __forceinline__ void attend_segment(const RowAttnArgs& a, const RowRa
 
   auto load_chunk = [&](Chunk<E, D, GP>& ch, int tok0) {
     const int blk = table[tok0 >> a.bs_log2];
+    PA_DEVICE_CHECK(blk >= 0 && blk < a.num_blocks);
     const int off = tok0 & (bs - 1);
     const size_t slab = ((size_t)blk * a.Hkv + kvh) * kslab_bytes;
     const char* ks = kpool + slab + (size_t)off * C::kRowBytes;

@@ -18,6 +18,7 @@ __global__ __launch_bounds__(64) void kv_append_kernel(const AppendArgs a) {
   const int h = blockIdx.x - t * a.Hkv;
   const int slot = a.slots[t];
   if (slot < 0) return;
+  PA_DEVICE_CHECK((slot >> a.bs_log2) < a.num_blocks);
   const int bs = 1 << a.bs_log2;
   const int blk = slot >> a.bs_log2;
   const int off = slot & (bs - 1);
@@ -42,6 +43,7 @@ __global__ __launch_bounds__(256) void copy_blocks_kernel(const CopyArgs a) {
   const int h = rest % a.Hkv;
   const int i = rest / a.Hkv;
   const size_t slab = (size_t)a.slab16;
+  PA_DEVICE_CHECK(a.src[i] >= 0 && a.src[i] < a.num_blocks && a.dst[i] >= 0 && a.dst[i] < a.num_blocks);
   const size_t src = ((size_t)a.src[i] * a.Hkv + h) * slab;
   const size_t dst = ((size_t)a.dst[i] * a.Hkv + h) * slab;
   u32x4* pool = static_cast<u32x4*>(which ? a.v_cache : a.k_cache);

@@ -4,6 +4,20 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Debug builds (PA_DEBUG_CHECKS) check the device-side caller contracts the
+// host cannot see (block ids in range, lengths within the table) and trap on
+// a violation; release builds compile the checks away.
+#ifdef PA_DEBUG_CHECKS
+#define PA_DEVICE_CHECK(cond) \
+  do {                         \
+    if (!(cond)) __builtin_trap(); \
+  } while (0)
+#else
+#define PA_DEVICE_CHECK(cond) \
+  do {                         \
+  } while (0)
+#endif
+
 namespace pa {
 
 // Everything one decode-style launch needs.  A "row slot" is (sequence b,
@@ -22,6 +36,7 @@ struct RowAttnArgs {
   const float* alibi;        // [Hq] or nullptr
   const int32_t* prefix_lens;  // [num_seqs] or nullptr (prefix-LM, with causal)
   const int32_t* doc_starts;   // [rows] or nullptr (first admissible key per row)
+  int64_t num_blocks;        // pool size (debug checks only)
   int32_t bt_stride;
   int32_t max_q_len;
   int32_t num_seqs;
@@ -42,6 +57,7 @@ struct AppendArgs {
   void* k_cache;
   void* v_cache;
   const int32_t* slots;
+  int64_t num_blocks;        // pool size (debug checks only)
   int32_t T, Hkv, D, bs_log2;
 };
 
@@ -56,6 +72,7 @@ struct PrefillArgs {
   const float* alibi;
   const int32_t* prefix_lens;  // [num_seqs] or nullptr
   const int32_t* doc_starts;   // [total_q] or nullptr
+  int64_t num_blocks;          // pool size (debug checks only)
   int32_t bt_stride;
   int32_t num_seqs;
   int32_t Hq, Hkv, g;
@@ -72,6 +89,7 @@ struct CopyArgs {
   void* v_cache;
   const int32_t* src;        // [pairs] physical blocks
   const int32_t* dst;        // [pairs]
+  int64_t num_blocks;        // pool size (debug checks only)
   int32_t pairs;
   int32_t slab16;            // 16-byte units in one (block, kv-head) slab
   int32_t Hkv;

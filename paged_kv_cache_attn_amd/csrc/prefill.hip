@@ -116,6 +116,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
   const int Lq = a.cu_q_lens[b + 1] - q0;
   const int q_start = qtile * QT;
   if (q_start >= Lq) return;
+  PA_DEVICE_CHECK(Lq <= n && (long long)n <= (long long)a.bt_stride << a.bs_log2);
 
   // this lane's query row (column of S^T / O^T)
   const int r = wave * 32 + col;
@@ -399,7 +400,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
   // the tile loads instead of the LDS counter.
   auto table_load = [&](int t) {
     const int j = min((tile_k0(t) + 16 * wave) >> a.bs_log2, last_blk);
-    return __builtin_nontemporal_load(table + j);
+    const int blk = __builtin_nontemporal_load(table + j);
+    PA_DEVICE_CHECK(blk >= 0 && blk < a.num_blocks);
+    return blk;
   };
 
   // Software pipeline over tiles (per wave).  Plain path, iteration t, one

@@ -1,0 +1,61 @@
+"""Run with PAGEDATTN_DEBUG_CHECKS=1: append, block copy, decode (three
+splits) and prefill through the debug-check build on valid inputs; every
+result must match the oracle (the checks never fire).  Exit status 0 = pass."""
+
+import os
+import sys
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import oracle  # noqa: E402
+from oracle.paged import bits_to_f64  # noqa: E402
+from paged_kv_cache_attn_amd import binding  # noqa: E402
+from workloads import build_workload  # noqa: E402
+from workloads.device import to_numpy_bits, upload  # noqa: E402
+
+
+def main():
+    assert binding.lib_path().endswith("libpagedattn_debug.so"), binding.lib_path()
+    worst = 0.0
+    w = build_workload(name="dbg", seed=31, kind="decode", dtype="bf16", Hq=32, Hkv=8, D=128, bs=16,
+                       context_lens=[37, 300, 1000], append_lens=[1, 1, 1], threads=1)
+    kp, vp = oracle.kv_append(w.k_pool, w.v_pool, w.k_new, w.v_new, w.slot_mapping, w.bs)
+    ref = oracle.paged_attention(w.q, kp, vp, w.block_table, w.context_lens, w.cu_q_lens, w.scale, w.bs,
+                                 w.dtype)
+    for split in (0, 64, -1):
+        t = upload(w)
+        binding.kv_append(t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], t["slot_mapping"])
+        out = torch.empty_like(t["q"])
+        binding.paged_attn_decode(out, t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                                  w.scale, w.max_context_len, split)
+        torch.cuda.synchronize()
+        worst = max(worst, float(np.max(np.abs(bits_to_f64(to_numpy_bits(out), "bf16") - ref))))
+        # block copy of two unused blocks onto two others, then nothing referenced changed
+        used = set(np.asarray(w.block_table[w.block_table >= 0]).tolist())
+        free = [b for b in range(w.NB) if b not in used][:4]
+        binding.kv_copy_blocks(t["k_cache"], t["v_cache"], torch.tensor(free[:2], dtype=torch.int32, device="cuda"),
+                               torch.tensor(free[2:], dtype=torch.int32, device="cuda"))
+        torch.cuda.synchronize()
+    wp = build_workload(name="dbgp", seed=32, kind="prefill", dtype="bf16", Hq=32, Hkv=8, D=128, bs=16,
+                        context_lens=[150, 400], q_lens=[150, 170], append_lens=[150, 170], causal=True,
+                        threads=1)
+    kp, vp = oracle.kv_append(wp.k_pool, wp.v_pool, wp.k_new, wp.v_new, wp.slot_mapping, wp.bs)
+    ref = oracle.paged_attention(wp.q, kp, vp, wp.block_table, wp.context_lens, wp.cu_q_lens, wp.scale, wp.bs,
+                                 wp.dtype, oracle.ScoreMods(causal=True))
+    t = upload(wp)
+    binding.kv_append(t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], t["slot_mapping"])
+    out = torch.empty_like(t["q"])
+    binding.paged_attn_prefill(out, t["q"], t["cu_q_lens"], t["k_cache"], t["v_cache"], t["block_tables"],
+                               t["context_lens"], wp.scale, wp.max_q_len, True)
+    torch.cuda.synchronize()
+    worst = max(worst, float(np.max(np.abs(bits_to_f64(to_numpy_bits(out), "bf16") - ref))))
+    print(f"debug-check build: max abs err {worst:.3e}", flush=True)
+    return 0 if worst <= 2e-2 else 1
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -199,3 +199,11 @@ def test_block_manager_argument_checks():
     assert L.pa_bm_create(10, 16, None) == -1
     assert binding.status_string(-12).startswith("block manager")
     assert binding.status_string(-13).startswith("block manager")
+
+
+def test_debug_check_build_exports_the_same_symbols():
+    debug = os.path.join(os.path.dirname(binding.lib_path()), "libpagedattn_debug.so")
+    assert os.path.exists(debug), "build() also builds the PA_DEBUG_CHECKS library"
+    out = os.popen(f"nm -D --defined-only {debug}").read()
+    exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
+    assert set(declared_functions()) <= exported
