@@ -10,6 +10,8 @@ from .binding import (  # noqa: F401
     PA_F32,
     bench_fill,
     bench_stream_read,
+    decode_cascade_workspace,
+    decode_cascade_workspace_size,
     decode_split_tokens,
     decode_workspace,
     decode_workspace_size,
@@ -18,6 +20,7 @@ from .binding import (  # noqa: F401
     lib,
     lib_path,
     paged_attn_decode,
+    paged_attn_decode_cascade,
     paged_attn_prefill,
     status_string,
 )

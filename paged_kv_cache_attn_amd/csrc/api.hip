@@ -149,6 +149,8 @@ void fill_row_args(pa::RowAttnArgs& a, void* out, const void* q, const void* kc,
   a.alibi = mods ? mods->alibi_slopes : nullptr;
   a.prefix_lens = mods ? mods->prefix_lens : nullptr;
   a.doc_starts = mods ? mods->doc_starts : nullptr;
+  a.state_o = nullptr;
+  a.state_lse = nullptr;
   float* w = static_cast<float*>(ws);
   const size_t units = s.W > 0 ? ((size_t)s.W + (size_t)B * Hkv * s.NG) * s.GP
                                : (size_t)B * max_q * Hkv * s.NG * s.GP * (size_t)s.P;
@@ -158,6 +160,54 @@ void fill_row_args(pa::RowAttnArgs& a, void* out, const void* q, const void* kc,
 }
 
 int launch_status(hipError_t e) { return e == hipSuccess ? PA_OK : (int)e; }
+
+// ---- two-phase (shared-prefix) decode ----
+constexpr int kCascadeMinTiles = 4;  // 64-key tiles per prefix key range, at least
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct CascadeShape {
+  int q_tiles, key_split, nsplit;
+  Shape dec;  // the suffix decode
+  size_t off_part_lse, off_state_o, off_state_lse, off_key_start, off_dec, total;
+};
+
+// Prefix phase: num_groups x kv-heads x query tiles work-groups per key
+// range; enough ranges for two work-groups per compute unit, each range at
+// least kCascadeMinTiles tiles.
+void cascade_shape(int32_t B, int32_t G, int32_t max_group, int32_t Hq, int32_t Hkv, int32_t D,
+                   int32_t max_ctx, int32_t max_prefix, CascadeShape& c) {
+  const int qt = pa::prefill_rows_per_tile(Hq / Hkv);
+  c.q_tiles = (int)(((long long)max_group + qt - 1) / qt);
+  const long long tiles = ((long long)max_prefix + 63) / 64;
+  const long long base = std::max(1ll, (long long)G * Hkv * c.q_tiles);
+  long long ns = (2ll * device_cus() + base - 1) / base;
+  ns = std::max(1ll, std::min(ns, tiles / kCascadeMinTiles));
+  const long long per = tiles > 0 ? (tiles + ns - 1) / ns : 1;
+  c.key_split = (int)(per * 64);
+  c.nsplit = (int)std::max(1ll, ((long long)max_prefix + c.key_split - 1) / c.key_split);
+  decode_shape(B, Hq, Hkv, max_ctx, 0, c.dec);
+  const size_t rows = (size_t)B * Hq;
+  size_t off = align_up((size_t)c.nsplit * rows * D * sizeof(float));
+  c.off_part_lse = off;
+  off += align_up((size_t)c.nsplit * rows * sizeof(float));
+  c.off_state_o = off;
+  off += align_up(rows * D * sizeof(float));
+  c.off_state_lse = off;
+  off += align_up(rows * sizeof(float));
+  c.off_key_start = off;
+  off += align_up((size_t)B * sizeof(int32_t));
+  c.off_dec = off;
+  off += align_up(workspace_bytes_for(B, Hkv, D, c.dec));
+  c.total = off;
+}
+
+int check_cascade_sizes(int32_t B, int32_t G, int32_t max_group, int32_t max_prefix) {
+  if (G < 0 || max_group < 0 || max_prefix < 0) return PA_ERR_SIZE;
+  if (B > 0 && (G < 1 || max_group < 1)) return PA_ERR_SIZE;
+  return PA_OK;
+}
 
 int decode_impl(bool do_partials, bool do_merge, void* out, const void* q, const void* k_cache,
                 const void* v_cache, const int32_t* block_tables, int32_t bt_stride,
@@ -335,6 +385,13 @@ int paged_attn_prefill(void* out, const void* q, const int32_t* cu_q_lens, const
     a.alibi = mods ? mods->alibi_slopes : nullptr;
     a.prefix_lens = mods ? mods->prefix_lens : nullptr;
     a.doc_starts = mods ? mods->doc_starts : nullptr;
+    a.table_rows = nullptr;
+    a.part_o = nullptr;
+    a.part_lse = nullptr;
+    a.row_key_start = nullptr;
+    a.key_split = 0;
+    a.nsplit = 1;
+    a.total_q = 0;
     a.bt_stride = block_table_stride;
     a.num_blocks = num_blocks;
     a.num_seqs = num_seqs;
@@ -369,6 +426,127 @@ int paged_attn_prefill(void* out, const void* q, const int32_t* cu_q_lens, const
   return launch_status(pa::launch_row_partials(a, dtype, head_dim, hs));
 }
 
+size_t paged_attn_decode_cascade_workspace_size(int32_t num_seqs, int32_t num_groups,
+                                                int32_t max_group_size, int32_t num_heads,
+                                                int32_t num_kv_heads, int32_t head_dim,
+                                                int32_t max_context_len, int32_t max_prefix_len) {
+  if (num_seqs < 0 || max_context_len < 0 || check_heads(num_heads, num_kv_heads) ||
+      check_dim(head_dim) || check_cascade_sizes(num_seqs, num_groups, max_group_size, max_prefix_len) ||
+      128 % (num_heads / num_kv_heads) != 0)
+    return 0;
+  if (num_seqs == 0) return 0;
+  CascadeShape c;
+  cascade_shape(num_seqs, num_groups, max_group_size, num_heads, num_kv_heads, head_dim,
+                max_context_len, max_prefix_len, c);
+  return c.total;
+}
+
+int paged_attn_decode_cascade(void* out, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, int32_t block_table_stride,
+                              const int32_t* context_lens, int32_t num_seqs,
+                              const int32_t* group_starts, const int32_t* prefix_lens,
+                              int32_t num_groups, int32_t max_group_size, int32_t max_prefix_len,
+                              int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, int64_t num_blocks, int32_t max_context_len,
+                              float scale, const pa_score_mods* mods, void* workspace,
+                              size_t workspace_bytes, int32_t dtype, void* stream) {
+  int st = common_decode_checks(num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                                block_table_stride, max_context_len, 0, dtype, mods);
+  if (st) return st;
+  if (dtype != PA_BF16) return PA_ERR_DTYPE;
+  if ((st = check_cascade_sizes(num_seqs, num_groups, max_group_size, max_prefix_len))) return st;
+  if (mods && (mods->window != 0 || mods->alibi_slopes || mods->prefix_lens || mods->doc_starts))
+    return PA_ERR_UNSUPPORTED;
+  const int g = num_heads / num_kv_heads;
+  if (128 % g != 0) return PA_ERR_HEADS;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !group_starts ||
+      !prefix_lens)
+    return PA_ERR_NULL;
+  CascadeShape c;
+  cascade_shape(num_seqs, num_groups, max_group_size, num_heads, num_kv_heads, head_dim,
+                max_context_len, max_prefix_len, c);
+  if (!workspace || workspace_bytes < c.total || reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+    return PA_ERR_WORKSPACE;
+  if ((long long)num_groups * num_kv_heads * c.q_tiles * c.nsplit > 0x7fffffffll ||
+      (long long)num_seqs * num_heads > 0x7fffffffll)
+    return PA_ERR_SIZE;
+  char* ws = static_cast<char*>(workspace);
+  float* part_o = reinterpret_cast<float*>(ws);
+  float* part_lse = reinterpret_cast<float*>(ws + c.off_part_lse);
+  float* state_o = reinterpret_cast<float*>(ws + c.off_state_o);
+  float* state_lse = reinterpret_cast<float*>(ws + c.off_state_lse);
+  int32_t* key_start = reinterpret_cast<int32_t*>(ws + c.off_key_start);
+  void* dec_ws = ws + c.off_dec;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  const float softcap = mods ? mods->softcap : 0.f;
+
+  // 1) shared prefixes: the rows of a group are the query rows of one
+  //    "sequence" whose keys are the prefix, read from the group's first
+  //    member's table row, split into key ranges
+  pa::PrefillArgs p;
+  p.out = nullptr;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.context_lens = prefix_lens;
+  p.cu_q_lens = group_starts;
+  p.alibi = nullptr;
+  p.prefix_lens = nullptr;
+  p.doc_starts = nullptr;
+  p.table_rows = group_starts;
+  p.part_o = part_o;
+  p.part_lse = part_lse;
+  p.row_key_start = key_start;
+  p.key_split = c.key_split;
+  p.nsplit = c.nsplit;
+  p.num_blocks = num_blocks;
+  p.bt_stride = block_table_stride;
+  p.num_seqs = num_groups;
+  p.total_q = num_seqs;
+  p.Hq = num_heads;
+  p.Hkv = num_kv_heads;
+  p.g = g;
+  p.bs_log2 = ilog2(block_size);
+  p.q_tiles = c.q_tiles;
+  p.causal = 0;
+  p.window = 0;
+  p.scale = scale;
+  p.softcap = softcap;
+  if ((st = launch_status(pa::launch_prefill_mfma(p, head_dim, hs)))) return st;
+
+  // 2) each sequence's own keys [prefix, n): the balanced decode with the
+  //    prefix end as every row's first admissible key, leaving fp32 states
+  pa_score_mods dm = {0, softcap, nullptr, nullptr, key_start};
+  pa::RowAttnArgs a;
+  fill_row_args(a, nullptr, q, k_cache, v_cache, block_tables, block_table_stride, context_lens,
+                nullptr, num_seqs, 1, num_heads, num_kv_heads, block_size, c.dec, scale, 1, &dm,
+                workspace_bytes_for(num_seqs, num_kv_heads, head_dim, c.dec) > 0 ? dec_ws : nullptr,
+                head_dim);
+  a.num_blocks = num_blocks;
+  a.state_o = state_o;
+  a.state_lse = state_lse;
+  if ((st = launch_status(pa::launch_row_partials(a, dtype, head_dim, hs)))) return st;
+  if (c.dec.P > 1 || c.dec.W > 0) {
+    if ((st = launch_status(pa::launch_row_merge(a, dtype, head_dim, hs)))) return st;
+  }
+
+  // 3) combine prefix and suffix states into out
+  pa::CascadeMergeArgs m;
+  m.out = out;
+  m.part_o = part_o;
+  m.part_lse = part_lse;
+  m.state_o = state_o;
+  m.state_lse = state_lse;
+  m.row_key_start = key_start;
+  m.context_lens = context_lens;
+  m.rows = num_seqs;
+  m.Hq = num_heads;
+  m.nsplit = c.nsplit;
+  return launch_status(pa::launch_cascade_merge(m, head_dim, hs));
+}
+
 const char* paged_attn_status_string(int status) {
   switch (status) {
     case PA_OK: return "ok";
@@ -385,6 +563,7 @@ const char* paged_attn_status_string(int status) {
     case PA_ERR_TABLE_STRIDE: return "block_table_stride must be >= 1";
     case PA_ERR_NO_BLOCKS: return "block manager: no free block left in the pool";
     case PA_ERR_SEQ: return "block manager: unknown or freed sequence id";
+    case PA_ERR_UNSUPPORTED: return "two-phase decode: only the softcap score mod is supported";
     default: break;
   }
   if (status > 0) return hipGetErrorString(static_cast<hipError_t>(status));

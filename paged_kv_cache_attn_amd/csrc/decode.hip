@@ -123,7 +123,8 @@ __device__ __forceinline__ bool row_range(const RowAttnArgs& a, int slot, RowRan
     Lq = a.cu_q_lens[b + 1] - q0;
   }
   if (i >= Lq) return false;
-  PA_DEVICE_CHECK(n >= 0 && (long long)n <= (long long)a.bt_stride << a.bs_log2 && Lq <= n);
+  // (a decode row may have no key at all; prefill rows sit inside the context)
+  PA_DEVICE_CHECK(n >= 0 && (long long)n <= (long long)a.bt_stride << a.bs_log2 && (!a.cu_q_lens || Lq <= n));
   r.qrow = q0 + i;
   r.pos = n - Lq + i;
   r.hi = a.causal ? min(n, r.pos + 1) : n;
@@ -408,7 +409,19 @@ __device__ __forceinline__ void attend_segment(const RowAttnArgs& a, const RowRa
     lh[h] = stat_lds[2 * h + 1];
   }
 
-  if (whole) {
+  if (whole && a.state_o) {
+    // two-phase decode: the row's state (normalised output, log-sum-exp), fp32
+#pragma unroll
+    for (int h = 0; h < GP; ++h) {
+      if (h >= nvalid) continue;
+      const float inv = lh[h] > 0.f ? 1.f / lh[h] : 0.f;
+      const size_t srow = (size_t)rr.qrow * a.Hq + head0 + h;
+#pragma unroll
+      for (int r = 0; r < C::RPL; ++r)
+        if ((r & 1) == vh) a.state_o[srow * D + vr + 32 * r] = o[h][r] * inv;
+      if (lane == 0) a.state_lse[srow] = state_lse2(mh[h], lh[h]);
+    }
+  } else if (whole) {
 #pragma unroll
     for (int h = 0; h < GP; ++h) {
       if (h >= nvalid) continue;
@@ -587,6 +600,14 @@ __device__ __forceinline__ void merge_units(const RowAttnArgs& a, const size_t u
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
+  if (a.state_o) {
+    // two-phase decode: the row's state (normalised output, log-sum-exp), fp32
+    const size_t srow = (size_t)qrow * a.Hq + h;
+#pragma unroll
+    for (int r = 0; r < R; ++r) a.state_o[srow * D + lane + 64 * r] = acc[r] * inv;
+    if (lane == 0) a.state_lse[srow] = state_lse2(M, L);
+    return;
+  }
   char* orow = static_cast<char*>(a.out) + ((size_t)qrow * a.Hq + h) * D * ES;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -627,6 +648,52 @@ __global__ __launch_bounds__(64) void row_merge_kernel(const RowAttnArgs a) {
   const int hg = kvh * a.NG + hin / GP;
   const int HG = a.Hkv * a.NG;
   merge_units<E, D, GP>(a, ((size_t)slot * HG + hg) * a.P, rr.nparts, hin % GP, rr.qrow, h);
+}
+
+// Two-phase decode, last step: one wavefront per (row, query head) combines
+// the prefix states of every key range with the suffix state.  Weights are
+// 2^(lse_i - max lse); a row with no key at all gets zeros.
+template <int D>
+__global__ __launch_bounds__(64) void cascade_merge_kernel(const CascadeMergeArgs a) {
+  constexpr int R = D / 64;
+  const int lane = threadIdx.x;
+  const size_t rh = blockIdx.x;  // row * Hq + head
+  const size_t plane = (size_t)a.rows * a.Hq;
+  PA_DEVICE_CHECK(a.row_key_start[rh / a.Hq] <= a.context_lens[rh / a.Hq]);
+  const int ns = a.nsplit + 1;  // prefix ranges, then the suffix
+  auto lse_of = [&](int i) { return i < a.nsplit ? a.part_lse[(size_t)i * plane + rh] : a.state_lse[rh]; };
+  auto o_of = [&](int i) { return i < a.nsplit ? a.part_o + ((size_t)i * plane + rh) * D : a.state_o + rh * D; };
+  float M = kNegInf;
+  for (int i = lane; i < ns; i += 64) M = fmaxf(M, lse_of(i));
+  M = wave_max(M);
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.f;
+  float L = 0.f;
+  if (M != kNegInf) {
+    for (int i = lane; i < ns; i += 64) L += fast_exp2(lse_of(i) - M);
+    L = wave_sum(L);
+    constexpr int U = 4;  // states whose loads are in flight together
+    for (int i0 = 0; i0 < ns; i0 += U) {
+      float w[U], x[U][R];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int i = min(i0 + u, ns - 1);
+        w[u] = (i0 + u < ns) ? fast_exp2(lse_of(i) - M) : 0.f;
+        const float* op = o_of(i);
+#pragma unroll
+        for (int r = 0; r < R; ++r) x[u][r] = op[lane + 64 * r];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = fmaf(w[u], x[u][r], acc[r]);
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  uint16_t* orow = static_cast<uint16_t*>(a.out) + rh * D;
+#pragma unroll
+  for (int r = 0; r < R; ++r) orow[lane + 64 * r] = (uint16_t)f32_to_bf16_bits(acc[r] * inv);
 }
 
 template <typename E, int D, int GP>
@@ -686,6 +753,17 @@ hipError_t launch_row_partials(const RowAttnArgs& a, int dtype, int D, hipStream
 
 hipError_t launch_row_merge(const RowAttnArgs& a, int dtype, int D, hipStream_t s) {
   return dtype == 1 ? dispatch_d<BF16>(a, D, true, false, s) : dispatch_d<F32>(a, D, true, false, s);
+}
+
+hipError_t launch_cascade_merge(const CascadeMergeArgs& a, int D, hipStream_t s) {
+  const long long blocks = (long long)a.rows * a.Hq;
+  if (blocks <= 0) return hipSuccess;
+  if (D == 64) {
+    hipLaunchKernelGGL((cascade_merge_kernel<64>), dim3((unsigned)blocks), dim3(64), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((cascade_merge_kernel<128>), dim3((unsigned)blocks), dim3(64), 0, s, a);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace pa

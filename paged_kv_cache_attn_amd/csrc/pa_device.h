@@ -53,6 +53,13 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// log2 of sum_j 2^(s_j) for a softmax state with running max m (log2 units)
+// and sum l = sum_j 2^(s_j - m); -inf for an empty state.
+__device__ __forceinline__ float state_lse2(float m, float l) {
+  return l > 0.f ? m + fast_log2(l) : -__builtin_inff();
+}
 
 // ---- cross-lane moves -------------------------------------------------------
 // DPP controls (gfx9 encoding).

@@ -36,6 +36,11 @@ struct RowAttnArgs {
   const float* alibi;        // [Hq] or nullptr
   const int32_t* prefix_lens;  // [num_seqs] or nullptr (prefix-LM, with causal)
   const int32_t* doc_starts;   // [rows] or nullptr (first admissible key per row)
+  // nullptr: final rows go to out.  Else (two-phase decode) each row's
+  // normalised output goes to state_o [rows, Hq, D] and its log-sum-exp
+  // (log2 units of the scaled scores) to state_lse [rows, Hq], in fp32.
+  float* state_o;
+  float* state_lse;
   int64_t num_blocks;        // pool size (debug checks only)
   int32_t bt_stride;
   int32_t max_q_len;
@@ -72,9 +77,24 @@ struct PrefillArgs {
   const float* alibi;
   const int32_t* prefix_lens;  // [num_seqs] or nullptr
   const int32_t* doc_starts;   // [total_q] or nullptr
+  // Key-split mode (key_split > 0, non-causal, no mods but softcap): the grid
+  // also runs over nsplit key ranges of key_split keys; the work-group of
+  // range s writes each row's output over keys [s*key_split, (s+1)*key_split)
+  // normalised to part_o [nsplit, total_q, Hq, D] and its log-sum-exp (log2
+  // units) to part_lse [nsplit, total_q, Hq], fp32; an empty range gives 0 and
+  // -inf.  Sequence b reads table row table_rows[b] (nullptr: row b), and the
+  // work-groups of range 0 and kv-head 0 store context_lens[b] into
+  // row_key_start[row] for each of its rows (nullptr: not stored).
+  const int32_t* table_rows;
+  float* part_o;
+  float* part_lse;
+  int32_t* row_key_start;
+  int32_t key_split;
+  int32_t nsplit;
   int64_t num_blocks;          // pool size (debug checks only)
   int32_t bt_stride;
   int32_t num_seqs;
+  int32_t total_q;
   int32_t Hq, Hkv, g;
   int32_t bs_log2;
   int32_t q_tiles;           // query tiles per (sequence, kv-head) in the grid
@@ -95,11 +115,27 @@ struct CopyArgs {
   int32_t Hkv;
 };
 
+// Two-phase decode, last step: for each (row b, query head h), the nsplit
+// prefix states part_o/part_lse [nsplit, rows, Hq, (D)] and the suffix state
+// state_o/state_lse [rows, Hq, (D)] (fp32, log2-unit log-sum-exps) are
+// combined with log-sum-exp weights into out [rows, Hq, D] (bf16).
+struct CascadeMergeArgs {
+  void* out;
+  const float* part_o;
+  const float* part_lse;
+  const float* state_o;
+  const float* state_lse;
+  const int32_t* row_key_start;  // debug checks only
+  const int32_t* context_lens;   // debug checks only
+  int32_t rows, Hq, nsplit;
+};
+
 hipError_t launch_kv_append(const AppendArgs& a, int dtype, hipStream_t s);
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t s);
 hipError_t launch_row_partials(const RowAttnArgs& a, int dtype, int D, hipStream_t s);
 hipError_t launch_row_merge(const RowAttnArgs& a, int dtype, int D, hipStream_t s);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, int D, hipStream_t s);
+hipError_t launch_cascade_merge(const CascadeMergeArgs& a, int D, hipStream_t s);
 int prefill_rows_per_tile(int g);
 
 }  // namespace pa

@@ -81,7 +81,9 @@ __device__ __forceinline__ int v_swz(int d, int cpb_log2) {
 }
 
 // KBL = log2(min(block_size, 64)): keys of one pool block inside a 64-key tile.
-template <int D, bool kMods, int KBL>
+// kSplit: key-split mode (a.key_split > 0), a separate instance so that the
+// plain prefill keeps its registers.
+template <int D, bool kMods, int KBL, bool kSplit>
 __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const PrefillArgs a) {
   constexpr int KCH = D / 8;   // 16-byte chunks per K row
   constexpr int KSTEPS = D / 16;
@@ -106,7 +108,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
 
   const int QT = kRowsPerWG / a.g;
   const int BH = a.num_seqs * a.Hkv;
-  const int flat = blockIdx.x;
+  constexpr bool ksplit = kSplit;
+  const int split = ksplit ? blockIdx.x / (BH * a.q_tiles) : 0;  // key range
+  const int flat = blockIdx.x - split * (BH * a.q_tiles);
   const int qtile = a.q_tiles - 1 - flat / BH;
   const int b = (flat % BH) / a.Hkv;
   const int kvh = flat % a.Hkv;
@@ -114,9 +118,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
   const int n = a.context_lens[b];
   const int q0 = a.cu_q_lens[b];
   const int Lq = a.cu_q_lens[b + 1] - q0;
+  // (key-split mode: the sequences' rows must cover all total_q rows)
+  PA_DEVICE_CHECK(!ksplit || ((b > 0 || q0 == 0) && (b + 1 < a.num_seqs || q0 + Lq == a.total_q) && Lq >= 0));
   const int q_start = qtile * QT;
   if (q_start >= Lq) return;
-  PA_DEVICE_CHECK(Lq <= n && (long long)n <= (long long)a.bt_stride << a.bs_log2);
+  PA_DEVICE_CHECK((ksplit || Lq <= n) && n >= 0 && (long long)n <= (long long)a.bt_stride << a.bs_log2);
+  PA_DEVICE_CHECK(!ksplit || ((long long)n <= (long long)a.key_split * a.nsplit && Lq <= a.q_tiles * QT));
 
   // this lane's query row (column of S^T / O^T)
   const int r = wave * 32 + col;
@@ -128,6 +135,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
   if (row_ok && a.causal && a.prefix_lens) row_hi = min(n, max(row_hi, a.prefix_lens[b]));
   int row_lo = (row_ok && a.window > 0) ? max(0, pos - a.window + 1) : 0;
   if (row_ok && a.doc_starts) row_lo = max(row_lo, a.doc_starts[q0 + qi]);
+  if (ksplit) {
+    row_lo = max(row_lo, split * a.key_split);
+    row_hi = min(row_hi, (split + 1) * a.key_split);
+    if (a.row_key_start && split == 0 && kvh == 0 && row_ok && head_in == 0 && hl == 0)
+      a.row_key_start[q0 + qi] = n;
+  }
   if (row_lo > row_hi) row_lo = row_hi;
   const int head = kvh * a.g + head_in;
 
@@ -162,7 +175,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
     safe_hi = __builtin_amdgcn_readfirstlane(safe_hi);
   }
 
-  const int32_t* table = a.block_tables + (size_t)b * a.bt_stride;
+  const int32_t* table = a.block_tables + (size_t)((ksplit && a.table_rows) ? a.table_rows[b] : b) * a.bt_stride;
   const int bs = 1 << a.bs_log2;
   const size_t slab_bytes = (size_t)bs * D * 2;
   const char* kpool = static_cast<const char*>(a.k_cache) + (size_t)kvh * slab_bytes;
@@ -517,6 +530,24 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
   const float l_tot = l_run + shfl_xor32(l_run);
   if (!row_ok) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if constexpr (ksplit) {
+    // this key range's state: normalised output and log-sum-exp, fp32
+    const size_t prow = ((size_t)split * a.total_q + q0 + qi) * a.Hq + head;
+    float* po = a.part_o + prow * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = 32 * dt + 8 * g4 + 4 * hl;
+        f32x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = oacc[dt][4 * g4 + i] * inv;
+        *reinterpret_cast<f32x4*>(po + d) = w;
+      }
+    }
+    if (hl == 0) a.part_lse[prow] = state_lse2(m_run, l_tot);
+    return;
+  }
   char* orow = static_cast<char*>(a.out) + ((size_t)(q0 + qi) * a.Hq + head) * D * 2;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
@@ -536,13 +567,20 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
 int prefill_rows_per_tile(int g) { return kRowsPerWG / g; }
 
 hipError_t launch_prefill_mfma(const PrefillArgs& a, int D, hipStream_t s) {
-  const long long blocks = (long long)a.num_seqs * a.Hkv * a.q_tiles;
+  const long long blocks = (long long)a.num_seqs * a.Hkv * a.q_tiles * (a.key_split > 0 ? a.nsplit : 1);
   if (blocks <= 0) return hipSuccess;
   // the fast path folds a positive scale into the exponent
   const bool mods = a.softcap > 0.f || a.alibi != nullptr || !(a.scale > 0.f);
   const int kbl = a.bs_log2 < 6 ? a.bs_log2 : 6;
+  const bool split = a.key_split > 0;
   const dim3 grid((unsigned)blocks), block(kThreads);
-#define PA_PREFILL_LAUNCH(DD, MM, KK) hipLaunchKernelGGL((prefill_mfma_kernel<DD, MM, KK>), grid, block, 0, s, a)
+#define PA_PREFILL_LAUNCH(DD, MM, KK)                                                         \
+  do {                                                                                        \
+    if (split)                                                                                \
+      hipLaunchKernelGGL((prefill_mfma_kernel<DD, MM, KK, true>), grid, block, 0, s, a);     \
+    else                                                                                      \
+      hipLaunchKernelGGL((prefill_mfma_kernel<DD, MM, KK, false>), grid, block, 0, s, a);    \
+  } while (0)
 #define PA_PREFILL_KBL(DD, MM)                    \
   switch (kbl) {                                  \
     case 4: PA_PREFILL_LAUNCH(DD, MM, 4); break;  \

@@ -1,5 +1,5 @@
 """Run with PAGEDATTN_DEBUG_CHECKS=1: append, block copy, decode (three
-splits) and prefill through the debug-check build on valid inputs; every
+splits), prefill and the two-phase decode through the debug-check build on valid inputs; every
 result must match the oracle (the checks never fire).  Exit status 0 = pass."""
 
 import os
@@ -51,6 +51,23 @@ def main():
     out = torch.empty_like(t["q"])
     binding.paged_attn_prefill(out, t["q"], t["cu_q_lens"], t["k_cache"], t["v_cache"], t["block_tables"],
                                t["context_lens"], wp.scale, wp.max_q_len, True)
+    torch.cuda.synchronize()
+    worst = max(worst, float(np.max(np.abs(bits_to_f64(to_numpy_bits(out), "bf16") - ref))))
+    # two-phase decode: three groups (one of a single empty sequence), a
+    # prefix that ends inside a block, a sequence with no own keys
+    wc = build_workload(name="dbgc", seed=33, kind="decode", dtype="bf16", Hq=32, Hkv=8, D=128, bs=16,
+                        context_lens=[16 * 6 + 9, 16 * 6, 16 * 6 + 300, 0, 16 * 2 + 1, 16 * 2 + 40],
+                        append_lens=[1, 0, 1, 0, 1, 1], prefix_groups=[(3, 6), (1, 0), (2, 2)], threads=1)
+    kp, vp = oracle.kv_append(wc.k_pool, wc.v_pool, wc.k_new, wc.v_new, wc.slot_mapping, wc.bs)
+    ref = oracle.paged_attention(wc.q, kp, vp, wc.block_table, wc.context_lens, wc.cu_q_lens, wc.scale, wc.bs,
+                                 wc.dtype)
+    t = upload(wc)
+    binding.kv_append(t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], t["slot_mapping"])
+    out = torch.empty_like(t["q"])
+    starts = torch.tensor([0, 3, 4, 6], dtype=torch.int32, device="cuda")
+    prefix = torch.tensor([16 * 6 - 5, 0, 32], dtype=torch.int32, device="cuda")
+    binding.paged_attn_decode_cascade(out, t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
+                                      t["context_lens"], starts, prefix, wc.scale, wc.max_context_len, 3, 96)
     torch.cuda.synchronize()
     worst = max(worst, float(np.max(np.abs(bits_to_f64(to_numpy_bits(out), "bf16") - ref))))
     print(f"debug-check build: max abs err {worst:.3e}", flush=True)

@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     assert binding.status_string(0) == "ok"
-    for code in range(-13, 0):
+    for code in range(-14, 0):
         s = binding.status_string(code)
         assert s and s != "unknown status", code
     assert binding.status_string(-99) == "unknown status"
@@ -165,6 +165,60 @@ def test_split_resolution_and_workspace_size():
     # (ceil(max_ctx/16) + 1); no device is visible here, so CUs = 256
     assert binding.decode_workspace_size(64, 64, 8, 128, 32768, 0) == (2048 + 512) * 8 * 130 * 4 + 512 * 8
     assert binding.decode_workspace_size(8, 32, 8, 128, 2048, 0) == (1032 + 64) * 4 * 130 * 4 + 64 * 8
+
+
+def _cascade(**over):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, stride=4, ctx=FAKE, B=8, gs=FAKE, pl=FAKE, G=2, maxg=4,
+             maxp=512, Hq=32, Hkv=8, D=128, bs=16, NB=100, max_ctx=1024, scale=0.1, mods=None, ws=FAKE,
+             ws_bytes=1 << 40, dtype=1)
+    a.update(over)
+    return binding.lib().paged_attn_decode_cascade(
+        a["out"], a["q"], a["k"], a["v"], a["bt"], a["stride"], a["ctx"], a["B"], a["gs"], a["pl"], a["G"], a["maxg"],
+        a["maxp"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["NB"], a["max_ctx"], a["scale"], a["mods"], a["ws"],
+        a["ws_bytes"], a["dtype"], None)
+
+
+def test_cascade_validation():
+    assert _cascade(dtype=0) == -8          # bf16 only
+    assert _cascade(dtype=4) == -8
+    assert _cascade(B=-1) == -2
+    assert _cascade(G=0) == -2               # a non-empty batch needs a group
+    assert _cascade(maxg=0) == -2
+    assert _cascade(maxp=-1) == -2
+    assert _cascade(Hq=24, Hkv=8) == -3      # group of 3 does not divide 128
+    assert _cascade(D=96) == -4
+    assert _cascade(bs=8) == -5
+    assert _cascade(stride=0) == -11
+    assert _cascade(gs=NULL) == -1
+    assert _cascade(pl=NULL) == -1
+    assert _cascade(ws=NULL) == -7
+    assert _cascade(ws_bytes=1024) == -7
+    assert _cascade(ws=ctypes.c_void_p(0x1008)) == -7  # not 16-byte aligned
+    for m in [binding.ScoreMods(64, 0.0, None), binding.ScoreMods(0, 0.0, 0x1000),
+              binding.ScoreMods(0, 0.0, None, 0x1000), binding.ScoreMods(0, 0.0, None, None, 0x1000)]:
+        assert _cascade(mods=ctypes.pointer(m)) == -14
+    assert _cascade(mods=ctypes.pointer(binding.ScoreMods(0, -2.0, None))) == -10
+    assert _cascade(B=0, G=0, maxg=0) == 0   # nothing to do, nothing launched
+
+
+def test_cascade_workspace_size():
+    # prefix states [nsplit, B*Hq, D + 1] fp32, suffix state [B*Hq, D + 1], B key
+    # starts, then the balanced decode's workspace; each piece 256-byte aligned
+    al = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    B, G, maxg, Hq, Hkv, D, ctx, pre = 64, 1, 64, 64, 8, 128, 17408, 16384
+    # 1 group x 8 kv-heads x 4 query tiles = 32 work-groups per key range; 512
+    # wanted (2 per compute unit, 256 units) -> 16 ranges of 16 tiles
+    nsplit = 16
+    dec = binding.decode_workspace_size(B, Hq, Hkv, D, ctx, 0)
+    want = (al(nsplit * B * Hq * D * 4) + al(nsplit * B * Hq * 4) + al(B * Hq * D * 4) + al(B * Hq * 4) + al(B * 4)
+            + al(dec))
+    assert binding.decode_cascade_workspace_size(B, G, maxg, Hq, Hkv, D, ctx, pre) == want
+    # a short prefix keeps at least 4 tiles per range: 300 keys -> 5 tiles -> 1 range
+    want1 = (al(B * Hq * D * 4) + al(B * Hq * 4) + al(B * Hq * D * 4) + al(B * Hq * 4) + al(B * 4) + al(dec))
+    assert binding.decode_cascade_workspace_size(B, G, maxg, Hq, Hkv, D, ctx, 300) == want1
+    assert binding.decode_cascade_workspace_size(B, 0, maxg, Hq, Hkv, D, ctx, pre) == 0  # invalid
+    assert binding.decode_cascade_workspace_size(B, G, maxg, 24, 8, D, ctx, pre) == 0
+    assert binding.decode_cascade_workspace_size(0, 0, 0, Hq, Hkv, D, ctx, pre) == 0
 
 
 def test_bench_util_validation():

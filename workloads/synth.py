@@ -185,6 +185,7 @@ def build_workload(
     NB: int | None = None,
     pool_slack: float = 2.0,
     shared_prefix_blocks: int = 0,
+    prefix_groups=None,
     causal: bool = False,
     scale: float | None = None,
     table_width: int | None = None,
@@ -198,7 +199,9 @@ def build_workload(
     arrive through ``k_new``/``v_new``/``slot_mapping``.  ``q_lens[b]`` query
     rows sit at the last ``q_lens[b]`` positions of the sequence.  The first
     ``shared_prefix_blocks`` logical blocks of every sequence map to the same
-    physical blocks.
+    physical blocks.  ``prefix_groups`` -- a list of (members, blocks) that
+    covers the batch in order -- instead makes each run of ``members``
+    consecutive sequences share their first ``blocks`` physical blocks.
     """
     ss = np.random.SeedSequence(seed)
     c_struct, c_q, c_new, c_pool = ss.spawn(4)
@@ -217,12 +220,17 @@ def build_workload(
         assert np.all(q_lens == 1)
 
     nblk = (ctx + bs - 1) // bs
-    S = shared_prefix_blocks
-    assert np.all(nblk >= S)
-    if S:
-        # shared blocks must be full and present in every sequence
-        assert np.all(ctx - append_lens >= S * bs)
-    unique_needed = int(S + (nblk - S).sum())
+    if prefix_groups is None:
+        groups = [(B, int(shared_prefix_blocks))]
+    else:
+        assert shared_prefix_blocks == 0
+        groups = [(int(m), int(s)) for m, s in prefix_groups]
+        assert sum(m for m, _ in groups) == B
+    S_b = np.repeat(np.array([s for _, s in groups], np.int64), [m for m, _ in groups])
+    assert np.all(nblk >= S_b)
+    # shared blocks must be full and present in every sequence
+    assert np.all((S_b == 0) | (ctx - append_lens >= S_b * bs))
+    unique_needed = int(sum(s for _, s in groups) + (nblk - S_b).sum())
     if NB is None:
         NB = max(1, int(math.ceil(pool_slack * unique_needed)))
     assert NB >= unique_needed
@@ -231,12 +239,17 @@ def build_workload(
 
     table = np.full((B, W), -1, dtype=np.int32)
     live = np.full(NB, -1, dtype=np.int64)
-    shared_ids = perm[:S]
-    cursor = S
+    cursor = 0
+    shared_ids = []
+    for _, s in groups:
+        shared_ids.append(perm[cursor:cursor + s])
+        cursor += s
+    group_of = np.repeat(np.arange(len(groups)), [m for m, _ in groups])
     for b in range(B):
+        S = int(S_b[b])
         priv = perm[cursor:cursor + nblk[b] - S]
         cursor += nblk[b] - S
-        ids = np.concatenate([shared_ids, priv])
+        ids = np.concatenate([shared_ids[group_of[b]], priv])
         table[b, :nblk[b]] = ids
         present = ctx[b] - append_lens[b]
         for j, pb in enumerate(ids):
@@ -268,7 +281,8 @@ def build_workload(
         context_lens=ctx.astype(np.int32), block_table=table, q=q,
         q_lens=q_lens.astype(np.int32), cu_q_lens=cu, k_pool=k_pool, v_pool=v_pool,
         k_new=k_new, v_new=v_new, slot_mapping=slots,
-        meta={"seed": seed, "unique_blocks": unique_needed, "shared_prefix_blocks": S},
+        meta={"seed": seed, "unique_blocks": unique_needed, "shared_prefix_blocks": int(shared_prefix_blocks),
+              "prefix_groups": groups},
     )
 
 
