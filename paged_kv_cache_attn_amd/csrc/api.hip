@@ -528,7 +528,8 @@ int paged_attn_decode_cascade(void* out, const void* q, const void* k_cache, con
   a.state_o = state_o;
   a.state_lse = state_lse;
   if ((st = launch_status(pa::launch_row_partials(a, dtype, head_dim, hs)))) return st;
-  if (c.dec.P > 1 || c.dec.W > 0) {
+  // (the balanced split's partials are merged by step 3 directly)
+  if (c.dec.P > 1 && c.dec.W == 0) {
     if ((st = launch_status(pa::launch_row_merge(a, dtype, head_dim, hs)))) return st;
   }
 
@@ -539,11 +540,18 @@ int paged_attn_decode_cascade(void* out, const void* q, const void* k_cache, con
   m.part_lse = part_lse;
   m.state_o = state_o;
   m.state_lse = state_lse;
+  m.ws_o = a.ws_o;
+  m.ws_ml = a.ws_ml;
+  m.ws_meta = c.dec.W > 0 ? a.ws_meta : nullptr;
   m.row_key_start = key_start;
   m.context_lens = context_lens;
   m.rows = num_seqs;
   m.Hq = num_heads;
   m.nsplit = c.nsplit;
+  m.Hkv = num_kv_heads;
+  m.g = c.dec.g;
+  m.NG = c.dec.NG;
+  m.GP = c.dec.GP;
   return launch_status(pa::launch_cascade_merge(m, head_dim, hs));
 }
 

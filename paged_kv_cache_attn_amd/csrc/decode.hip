@@ -651,27 +651,53 @@ __global__ __launch_bounds__(64) void row_merge_kernel(const RowAttnArgs a) {
 }
 
 // Two-phase decode, last step: one wavefront per (row, query head) combines
-// the prefix states of every key range with the suffix state.  Weights are
-// 2^(lse_i - max lse); a row with no key at all gets zeros.
-template <int D>
+// the prefix states of every key range with the suffix: its whole state, or
+// the balanced decode's partials of it.  Every state is (m, l, o) with o
+// summed relative to 2^m: a normalised state with log-sum-exp lse is
+// (lse, 1, o).  Weights are 2^(m_i - max m); a row with no key gets zeros.
+template <int D, int GP>
 __global__ __launch_bounds__(64) void cascade_merge_kernel(const CascadeMergeArgs a) {
   constexpr int R = D / 64;
   const int lane = threadIdx.x;
+  const int h = blockIdx.x % a.Hq;
+  const int b = blockIdx.x / a.Hq;
   const size_t rh = blockIdx.x;  // row * Hq + head
   const size_t plane = (size_t)a.rows * a.Hq;
-  PA_DEVICE_CHECK(a.row_key_start[rh / a.Hq] <= a.context_lens[rh / a.Hq]);
-  const int ns = a.nsplit + 1;  // prefix ranges, then the suffix
-  auto lse_of = [&](int i) { return i < a.nsplit ? a.part_lse[(size_t)i * plane + rh] : a.state_lse[rh]; };
-  auto o_of = [&](int i) { return i < a.nsplit ? a.part_o + ((size_t)i * plane + rh) * D : a.state_o + rh * D; };
+  PA_DEVICE_CHECK(a.row_key_start[b] <= a.context_lens[b]);
+  // suffix: whole state, or np decode partials from unit unit0
+  int unit0 = 0, np = 0;
+  if (a.ws_meta) {
+    const int kvh = h / a.g;
+    const int hin = h - kvh * a.g;
+    const size_t item = (size_t)b * a.Hkv * a.NG + kvh * a.NG + hin / GP;
+    unit0 = a.ws_meta[2 * item];
+    np = a.ws_meta[2 * item + 1];
+    if (np <= 1) np = 0;
+    unit0 = unit0 * GP + hin % GP;  // (unit, head slot) index
+  }
+  const int ns = a.nsplit + (np > 0 ? np : 1);
+  auto m_of = [&](int i) {
+    if (i < a.nsplit) return a.part_lse[(size_t)i * plane + rh];
+    if (np == 0) return a.state_lse[rh];
+    return a.ws_ml[(size_t)(unit0 + (i - a.nsplit) * GP) * 2];
+  };
+  auto l_of = [&](int i) {
+    return (i < a.nsplit || np == 0) ? 1.f : a.ws_ml[(size_t)(unit0 + (i - a.nsplit) * GP) * 2 + 1];
+  };
+  auto o_of = [&](int i) {
+    if (i < a.nsplit) return a.part_o + ((size_t)i * plane + rh) * D;
+    if (np == 0) return a.state_o + rh * D;
+    return a.ws_o + (size_t)(unit0 + (i - a.nsplit) * GP) * D;
+  };
   float M = kNegInf;
-  for (int i = lane; i < ns; i += 64) M = fmaxf(M, lse_of(i));
+  for (int i = lane; i < ns; i += 64) M = fmaxf(M, m_of(i));
   M = wave_max(M);
   float acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = 0.f;
   float L = 0.f;
   if (M != kNegInf) {
-    for (int i = lane; i < ns; i += 64) L += fast_exp2(lse_of(i) - M);
+    for (int i = lane; i < ns; i += 64) L += fast_exp2(m_of(i) - M) * l_of(i);
     L = wave_sum(L);
     constexpr int U = 4;  // states whose loads are in flight together
     for (int i0 = 0; i0 < ns; i0 += U) {
@@ -679,7 +705,7 @@ __global__ __launch_bounds__(64) void cascade_merge_kernel(const CascadeMergeArg
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int i = min(i0 + u, ns - 1);
-        w[u] = (i0 + u < ns) ? fast_exp2(lse_of(i) - M) : 0.f;
+        w[u] = (i0 + u < ns) ? fast_exp2(m_of(i) - M) : 0.f;
         const float* op = o_of(i);
 #pragma unroll
         for (int r = 0; r < R; ++r) x[u][r] = op[lane + 64 * r];
@@ -758,10 +784,13 @@ hipError_t launch_row_merge(const RowAttnArgs& a, int dtype, int D, hipStream_t 
 hipError_t launch_cascade_merge(const CascadeMergeArgs& a, int D, hipStream_t s) {
   const long long blocks = (long long)a.rows * a.Hq;
   if (blocks <= 0) return hipSuccess;
+  const dim3 grid((unsigned)blocks), block(64);
   if (D == 64) {
-    hipLaunchKernelGGL((cascade_merge_kernel<64>), dim3((unsigned)blocks), dim3(64), 0, s, a);
+    if (a.GP == 4) hipLaunchKernelGGL((cascade_merge_kernel<64, 4>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((cascade_merge_kernel<64, 8>), grid, block, 0, s, a);
   } else {
-    hipLaunchKernelGGL((cascade_merge_kernel<128>), dim3((unsigned)blocks), dim3(64), 0, s, a);
+    if (a.GP == 4) hipLaunchKernelGGL((cascade_merge_kernel<128, 4>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((cascade_merge_kernel<128, 8>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }

@@ -116,18 +116,25 @@ struct CopyArgs {
 };
 
 // Two-phase decode, last step: for each (row b, query head h), the nsplit
-// prefix states part_o/part_lse [nsplit, rows, Hq, (D)] and the suffix state
-// state_o/state_lse [rows, Hq, (D)] (fp32, log2-unit log-sum-exps) are
-// combined with log-sum-exp weights into out [rows, Hq, D] (bf16).
+// prefix states part_o/part_lse [nsplit, rows, Hq, (D)] and the suffix's
+// state are combined with log-sum-exp weights into out [rows, Hq, D] (bf16).
+// The suffix state is state_o/state_lse [rows, Hq, (D)] (fp32, log2-unit
+// log-sum-exps) -- or, when ws_meta is set (balanced decode split) and the
+// row's item was split, the decode's partials (ws_o, ws_ml at the units
+// ws_meta names), merged here instead of by the decode's own merge.
 struct CascadeMergeArgs {
   void* out;
   const float* part_o;
   const float* part_lse;
   const float* state_o;
   const float* state_lse;
+  const float* ws_o;
+  const float* ws_ml;
+  const int32_t* ws_meta;
   const int32_t* row_key_start;  // debug checks only
   const int32_t* context_lens;   // debug checks only
   int32_t rows, Hq, nsplit;
+  int32_t Hkv, g, NG, GP;        // decode item geometry (head groups of GP heads)
 };
 
 hipError_t launch_kv_append(const AppendArgs& a, int dtype, hipStream_t s);
