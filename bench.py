@@ -24,7 +24,8 @@ fp64 CPU oracle on a bounded sample of the same workload.
 
 Beside the step it reports: the achievable HBM read bandwidth of a plain
 streaming-read kernel (a second denominator), the decode of the other
-workloads (GQA batch, shared-prefix batch with logical and unique bytes), a
+workloads (GQA batch, shared-prefix batch with logical and unique bytes), the
+two-phase decode of two shared-prefix batches beside their plain decode, a
 context sweep of the GQA shape, and the pool's internal fragmentation per
 workload and page size (arithmetic only).
 
@@ -172,6 +173,68 @@ def time_calls(torch, fn, flush, reps, warm=3):
     return float(np.median([a.elapsed_time(b) for a, b in evs]))
 
 
+def shared_prefix_long():
+    """64 sequences behind one 16384-token prompt (1024 shared 16-token
+    blocks) with 1024 own tokens each (the last appended this step), 64/8
+    heads, d128, bf16."""
+    from workloads import build_workload
+    return build_workload(name="shared_prefix_16k_b64", seed=6, kind="decode", dtype="bf16", Hq=64, Hkv=8, D=128,
+                          bs=16, context_lens=[16384 + 1024] * 64, append_lens=[1] * 64,
+                          shared_prefix_blocks=16384 // 16, pool_slack=1.05)
+
+
+def two_phase_call(pa, torch, dev, w, t, out, pre):
+    """(workspace, call) of the two-phase decode of a batch that is one group
+    sharing its first ``pre`` tokens."""
+    gs = torch.tensor([0, w.B], dtype=torch.int32, device=dev)
+    pl = torch.tensor([pre], dtype=torch.int32, device=dev)
+    ws2 = pa.decode_cascade_workspace(t["q"], w.Hkv, 1, w.B, w.max_context_len, pre)
+
+    def call():
+        pa.paged_attn_decode_cascade(out, t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
+                                     t["context_lens"], gs, pl, w.scale, w.max_context_len, w.B, pre,
+                                     workspace=ws2)
+    call.keep = (gs, pl)
+    return ws2, call
+
+
+def two_phase_main(args, pa, torch, dev):
+    """``--path two_phase``: the two-phase decode of the long shared-prompt
+    batch as the step (its own JSON line; the plain decode of the same batch
+    is timed beside it)."""
+    from workloads.device import upload
+    w = shared_prefix_long()
+    t = upload(w, dev)
+    pa.kv_append(t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], t["slot_mapping"])
+    out = torch.empty_like(t["q"])
+    flush_buf = torch.empty(max(1, args.flush_mib) << 18, dtype=torch.int32, device=dev)
+
+    def flush():
+        if args.flush_mib > 0:
+            pa.bench_fill(flush_buf, 0)
+    ws2, call = two_phase_call(pa, torch, dev, w, t, out, 16384)
+    ws = pa.decode_workspace(t["q"], w.Hkv, w.max_context_len, 0)
+
+    def plain():
+        pa.paged_attn_decode(out, t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                             w.scale, w.max_context_len, 0, workspace=ws)
+    ms_plain = time_calls(torch, plain, flush, reps=5)
+    for _ in range(args.warmup):
+        flush()
+        call()
+    ms = time_calls(torch, call, flush, reps=args.steps, warm=0)
+    unique = w.unique_kv_bytes()
+    print(json.dumps({
+        "metric": "two-phase shared-prefix decode: unique KV-read GB/s, 1 MI355X", "value": round(
+            unique / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "shared_prefix_16k_b64: 64 sequences, 16384 shared + 1024 own tokens, h64x8, d128, "
+                               "block 16, one group", "kv_bytes": int(w.kv_bytes()), "unique_kv_bytes": int(unique),
+                   "prefix_flops": 4.0 * w.B * w.Hq * 16384 * w.D},
+        "plain_decode_ms": round(ms_plain, 5), "speedup_vs_plain_decode": round(ms_plain / ms, 3)}), flush=True)
+
+
 def extra_measurements(pa, torch, dev, flush, args):
     from workloads import build_workload, named_workload
     from workloads.device import upload
@@ -221,6 +284,28 @@ def extra_measurements(pa, torch, dev, flush, args):
     res["fragmentation"] = frag
     log("other workloads measured")
 
+    # two-phase decode of batches that share a prefix, beside the plain decode
+    # of the same batch: the shared-prefix workload (16 sequences, 1024 shared
+    # + 256 own tokens, 32/8 heads) and a long shared prompt (64 sequences,
+    # 16384 shared + 1024 own tokens, 64/8 heads), d128, bf16, block 16
+    two = {}
+    for name, w, pre in (("shared_prefix_decode_bf16", named_workload("shared_prefix_decode_bf16"), 1024),
+                         ("shared_prefix_16k_b64", shared_prefix_long(), 16384)):
+        t, out, ws = prepared(w)
+        ms_plain = time_calls(torch, decode_fn(w, t, out, ws), flush, reps=20)
+        ws2, two_phase = two_phase_call(pa, torch, dev, w, t, out, pre)
+        ms_two = time_calls(torch, two_phase, flush, reps=20)
+        unique = w.unique_kv_bytes()
+        prefix_flops = 4.0 * w.B * w.Hq * pre * w.D
+        two[name] = {"plain_ms": round(ms_plain, 5), "two_phase_ms": round(ms_two, 5),
+                     "speedup": round(ms_plain / ms_two, 3), "kv_bytes": int(w.kv_bytes()),
+                     "unique_kv_bytes": int(unique),
+                     "two_phase_unique_gbs": round(unique / (ms_two * 1e-3) / 1e9, 2),
+                     "prefix_flops": prefix_flops}
+        del t, out, ws, ws2
+    res["shared_prefix_two_phase"] = two
+    log("two-phase decode measured")
+
     # context sweep of the GQA decode shape (8 sequences, 32/8 heads, d128, bf16, block 16)
     sweep = {}
     base = None
@@ -255,6 +340,9 @@ def main():
                     help="time budget of the oracle baseline (0: skip it)")
     ap.add_argument("--flush-mib", type=int, default=512,
                     help="cache-evicting write before every timed call (0: none)")
+    ap.add_argument("--path", choices=("step", "two_phase"), default="step",
+                    help="step: the hot-path step (default); two_phase: the two-phase decode of a "
+                         "long shared-prompt batch")
     ap.add_argument("--extras", type=int, default=1,
                     help="1: also measure achievable HBM, the other workloads and the context sweep")
     args = ap.parse_args()
@@ -276,6 +364,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     pa.lib()
+    if args.path == "two_phase":
+        two_phase_main(args, pa, torch, dev)
+        return
 
     log("generating long-context decode batch")
     t0 = time.time()
