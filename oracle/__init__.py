@@ -15,4 +15,5 @@ from .paged import (  # noqa: F401
     gather_sequence,
     kv_append,
     paged_attention,
+    v_group,
 )

@@ -33,8 +33,10 @@ Readings where the pages are silent (each is listed in the design notes):
 query row ``i`` of a sequence with ``n`` keys and ``Lq`` query rows sits at
 logical position ``n - Lq + i`` (bottom-right causal alignment; decode is
 ``Lq = 1``); query head ``h`` reads kv-head ``h // (Hq / Hkv)``; a row with no
-admissible key outputs zeros; K slabs are token-major ``[bs, D]`` and V slabs
-dimension-major ``[D, bs]`` inside a (block, kv-head).
+admissible key outputs zeros; inside a (block, kv-head) the K slab is
+token-major ``[bs, D]`` and the V slab is ``bs / S`` dimension-major sub-slabs
+``[D, S]`` of ``S = min(bs, 16)`` tokens each (:func:`v_group`), so the V pool
+is ``[NB, Hkv, bs / S, D, S]``.
 """
 
 from __future__ import annotations
@@ -81,15 +83,30 @@ class ScoreMods:
     doc_starts: np.ndarray | None = None
 
 
+def v_group(bs):
+    """Tokens per V sub-slab: ``min(bs, 16)``."""
+    return min(int(bs), 16)
+
+
+def _check_pools(k_pool, v_pool, bs):
+    S = v_group(bs)
+    NB, Hkv, kbs, D = k_pool.shape
+    if kbs != bs or tuple(v_pool.shape) != (NB, Hkv, bs // S, D, S):
+        raise ValueError(f"pools {k_pool.shape} / {v_pool.shape} do not match block size {bs}")
+
+
 def kv_append(k_pool, v_pool, k_new, v_new, slot_mapping, bs):
     """Write token ``t``'s rows into slot ``slot_mapping[t]``; return new pools.
 
-    Slot ``s`` is block ``s // bs``, offset ``s % bs``.  K goes to
-    ``k_pool[block, :, offset, :]``, V to ``v_pool[block, :, :, offset]``.
+    Slot ``s`` is block ``s // bs``, offset ``o = s % bs``.  K goes to
+    ``k_pool[block, :, o, :]``, V to ``v_pool[block, :, o // S, :, o % S]``
+    (``S = v_group(bs)``).
     Negative slots are skipped.  The copy is of raw bits (no conversion).
     Duplicate non-negative slots within one call have no defined result and
     are rejected here.
     """
+    _check_pools(k_pool, v_pool, bs)
+    S = v_group(bs)
     kp = np.array(k_pool, copy=True)
     vp = np.array(v_pool, copy=True)
     seen = set()
@@ -101,7 +118,7 @@ def kv_append(k_pool, v_pool, k_new, v_new, slot_mapping, bs):
         seen.add(s)
         blk, off = divmod(s, bs)
         kp[blk, :, off, :] = k_new[t]
-        vp[blk, :, :, off] = v_new[t]
+        vp[blk, :, off // S, :, off % S] = v_new[t]
     return kp, vp
 
 
@@ -112,13 +129,14 @@ def gather_sequence(k_pool, v_pool, table_row, n, bs):
     only the first ``ceil(n / bs)`` entries are read and only the first ``n``
     token rows are kept.
     """
+    _check_pools(k_pool, v_pool, bs)
     nb = (n + bs - 1) // bs
     phys = np.asarray(table_row[:nb], dtype=np.int64)
     Hkv, D = k_pool.shape[1], k_pool.shape[3]
     K = k_pool[phys]  # [nb, Hkv, bs, D]
-    V = v_pool[phys]  # [nb, Hkv, D, bs]
+    V = v_pool[phys]  # [nb, Hkv, bs/S, D, S]
     K = K.transpose(1, 0, 2, 3).reshape(Hkv, nb * bs, D)[:, :n]
-    V = V.transpose(1, 0, 3, 2).reshape(Hkv, nb * bs, D)[:, :n]
+    V = V.transpose(1, 0, 2, 4, 3).reshape(Hkv, nb * bs, D)[:, :n]  # token = sub-slab * S + column
     return K, V
 
 

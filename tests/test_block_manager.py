@@ -28,7 +28,7 @@ class Replay:
         self.bm = binding.BlockManager(nb, BS)
         self.nb = nb
         self.k = np.full((nb, HKV, BS, D), np.nan, np.float32)
-        self.v = np.full((nb, HKV, D, BS), np.nan, np.float32)
+        self.v = np.full((nb, HKV, BS // min(BS, 16), D, min(BS, 16)), np.nan, np.float32)
         self.hist = {}
 
     def new(self):

@@ -39,16 +39,18 @@ def contiguous_to_pool(K, V, bs):
     """Contiguous per-kv-head K/V ``[Hkv, n, D]`` -> pools with an identity table.
 
     The pool formats are the storage contract: K ``[NB, Hkv, bs, D]``, V
-    ``[NB, Hkv, D, bs]``; tail slots are NaN.
+    ``[NB, Hkv, bs/S, D, S]`` (sub-slabs of ``S = min(bs, 16)`` tokens);
+    tail slots are NaN.
     """
     Hkv, n, D = K.shape
     NB = max(1, (n + bs - 1) // bs)
+    S = min(bs, 16)
     Kp = np.full((Hkv, NB * bs, D), NAN, np.float32)
     Vp = np.full((Hkv, NB * bs, D), NAN, np.float32)
     Kp[:, :n] = K
     Vp[:, :n] = V
     k_pool = Kp.reshape(Hkv, NB, bs, D).transpose(1, 0, 2, 3).copy()
-    v_pool = Vp.reshape(Hkv, NB, bs, D).transpose(1, 0, 3, 2).copy()
+    v_pool = Vp.reshape(Hkv, NB, bs // S, S, D).transpose(1, 0, 2, 4, 3).copy()
     table = np.arange(NB, dtype=np.int32)[None, :]
     return k_pool, v_pool, table
 
@@ -84,19 +86,19 @@ def check_golden():
     np.testing.assert_allclose(out[:, 0], c["expected"], rtol=0, atol=1e-12)
     c = g["paged_scattered_blocks"]
     k_pool = _nanify(c["k_pool"]).astype(np.float32)
-    v_pool = _nanify(c["v_pool"]).astype(np.float32)
+    v_pool = _nanify(c["v_pool"]).astype(np.float32)[:, :, None]  # bs <= 16: one [D, bs] sub-slab
     out = oracle.paged_attention(np.array(c["q"], np.float32)[None, None], k_pool, v_pool,
                                  np.array([c["table"]], np.int32), [c["n"]], [0, 1],
                                  np.float32(c["scale"]), c["bs"], "f32")
     np.testing.assert_allclose(out[0, 0], c["expected"], rtol=0, atol=1e-12)
     c = g["kv_append_bs4"]
     shape_k = (c["NB"], c["Hkv"], c["bs"], c["D"])
-    shape_v = (c["NB"], c["Hkv"], c["D"], c["bs"])
+    shape_v = (c["NB"], c["Hkv"], 1, c["D"], c["bs"])  # bs <= 16: one [D, bs] sub-slab
     kp, vp = oracle.kv_append(np.zeros(shape_k, np.float32), np.zeros(shape_v, np.float32),
                               np.array(c["k_new"], np.float32), np.array(c["v_new"], np.float32),
                               np.array(c["slot_mapping"], np.int32), c["bs"])
     np.testing.assert_array_equal(kp, np.array(c["expected_k_pool"], np.float32))
-    np.testing.assert_array_equal(vp, np.array(c["expected_v_pool"], np.float32))
+    np.testing.assert_array_equal(vp[:, :, 0], np.array(c["expected_v_pool"], np.float32))
 
 
 def test_golden_worked_examples():
@@ -112,6 +114,7 @@ def brute_force(w, mods):
     q = opa.bits_to_f64(w.q, w.dtype)
     kp = opa.bits_to_f64(w.k_pool, w.dtype)
     vp = opa.bits_to_f64(w.v_pool, w.dtype)
+    S = min(w.bs, 16)  # V: token o of a block is column o % S of sub-slab o // S
     g = w.Hq // w.Hkv
     out = np.zeros(q.shape)
     for b in range(w.B):
@@ -149,7 +152,7 @@ def brute_force(w, mods):
                 for d in range(w.D):
                     acc = 0.0
                     for _, blk, off, s in scores:
-                        acc += math.exp(s - m) * vp[blk, c, d, off]
+                        acc += math.exp(s - m) * vp[blk, c, off // S, d, off % S]
                     out[r, h, d] = acc / den
     return out
 
@@ -157,6 +160,18 @@ def brute_force(w, mods):
 def _tiny(kind, seed, bs=4, dtype="f32", ctx=(13, 40), q_lens=None, Hq=4, Hkv=2, D=8, causal=False):
     return build_workload(name="tiny", seed=seed, kind=kind, dtype=dtype, Hq=Hq, Hkv=Hkv, D=D, bs=bs,
                           context_lens=list(ctx), q_lens=q_lens, causal=causal, threads=1)
+
+
+def check_brute_force_large_pages(bs):
+    """Pages of several V sub-slabs (bs 32, 48-token contexts end inside one)."""
+    w = _tiny("prefill", 12, bs=bs, ctx=(45, 77), q_lens=[3, 9], causal=True)
+    mods = oracle.ScoreMods(causal=True)
+    np.testing.assert_allclose(_run(w, mods), brute_force(w, mods), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("bs", [32, 64])
+def test_brute_force_large_pages(bs):
+    check_brute_force_large_pages(bs)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -314,7 +329,7 @@ def test_one_token_context_returns_v_row():
     got = _run(w)
     for b in range(w.B):
         pb = w.block_table[b, 0]
-        v = opa.bits_to_f64(w.v_pool[pb, :, :, 0], "bf16")  # [Hkv, D]
+        v = opa.bits_to_f64(w.v_pool[pb, :, 0, :, 0], "bf16")  # token 0: sub-slab 0, column 0 -> [Hkv, D]
         assert np.array_equal(got[b], np.repeat(v, w.Hq // w.Hkv, axis=0))
 
 
@@ -420,9 +435,33 @@ def test_kv_append_roundtrip_through_block_table():
     assert set(changed.tolist()) <= set(w.block_table[w.block_table >= 0].tolist())
 
 
+def test_v_sub_slab_layout_by_hand():
+    """V of a 48-token block sits in three [D, 16] sub-slabs: token o of the
+    block is column o % 16 of sub-slab o // 16 (indices written out by hand),
+    K stays token-major, and gather reads the tokens back in logical order."""
+    bs, D = 48, 3
+    kp = np.zeros((2, 1, bs, D), np.float32)
+    vp = np.zeros((2, 1, 3, D, 16), np.float32)
+    slots = np.array([48 + 0, 48 + 15, 48 + 16, 48 + 33, 48 + 47], np.int32)  # block 1
+    vals = np.arange(1, 6, dtype=np.float32)
+    new = (vals[:, None, None] * np.array([1.0, 10.0, 100.0], np.float32)).astype(np.float32)
+    kp2, vp2 = oracle.kv_append(kp, vp, new, new, slots, bs)
+    expect = {(0, 0): 1, (0, 15): 2, (1, 0): 3, (2, 1): 4, (2, 15): 5}
+    for (sub, col), v in expect.items():
+        np.testing.assert_array_equal(vp2[1, 0, sub, :, col], [v, 10 * v, 100 * v])
+    assert np.count_nonzero(vp2) == 3 * len(expect)
+    np.testing.assert_array_equal(kp2[1, 0, [0, 15, 16, 33, 47], 0], vals)
+    K, V = oracle.gather_sequence(kp2, vp2, np.array([1]), bs, bs)
+    for o, v in zip([0, 15, 16, 33, 47], vals):
+        np.testing.assert_array_equal(V[0, o], [v, 10 * v, 100 * v])
+        np.testing.assert_array_equal(K[0, o], [v, 10 * v, 100 * v])
+    with pytest.raises(ValueError):  # a [D, bs] V pool is not the format for bs > 16
+        oracle.kv_append(kp, np.zeros((2, 1, D, bs), np.float32), new, new, slots, bs)
+
+
 def test_kv_append_rejects_duplicates_and_skips_negative():
     z = np.zeros((2, 1, 4, 2), np.float32)
-    zv = np.zeros((2, 1, 2, 4), np.float32)
+    zv = np.zeros((2, 1, 1, 2, 4), np.float32)
     new = np.ones((2, 1, 2), np.float32)
     with pytest.raises(ValueError):
         oracle.kv_append(z, zv, new, new, np.array([3, 3]), 4)
@@ -444,6 +483,7 @@ def _all_pins():
     mods = oracle.ScoreMods(causal=True)
     np.testing.assert_allclose(_run(w, mods), brute_force(w, mods), rtol=0, atol=1e-12)
     test_brute_force_with_prefix_and_documents()
+    check_brute_force_large_pages(32)
 
 
 def _mutant_gather_v_not_transposed(k_pool, v_pool, table_row, n, bs):
@@ -451,7 +491,17 @@ def _mutant_gather_v_not_transposed(k_pool, v_pool, table_row, n, bs):
     phys = np.asarray(table_row[:nb], dtype=np.int64)
     Hkv, D = k_pool.shape[1], k_pool.shape[3]
     K = k_pool[phys].transpose(1, 0, 2, 3).reshape(Hkv, nb * bs, D)[:, :n]
-    V = v_pool[phys].transpose(1, 0, 2, 3).reshape(Hkv, nb * bs, D)[:, :n]  # wrong: V slab is [D, bs]
+    V = v_pool[phys].transpose(1, 0, 2, 3, 4).reshape(Hkv, nb * bs, D)[:, :n]  # wrong: sub-slabs are [D, S]
+    return K, V
+
+
+def _mutant_gather_v_whole_slab(k_pool, v_pool, table_row, n, bs):
+    nb = (n + bs - 1) // bs
+    phys = np.asarray(table_row[:nb], dtype=np.int64)
+    Hkv, D = k_pool.shape[1], k_pool.shape[3]
+    K = k_pool[phys].transpose(1, 0, 2, 3).reshape(Hkv, nb * bs, D)[:, :n]
+    # wrong: reads the block's V as one [D, bs] slab instead of [D, 16] sub-slabs
+    V = v_pool[phys].reshape(nb, Hkv, D, bs).transpose(1, 0, 3, 2).reshape(Hkv, nb * bs, D)[:, :n]
     return K, V
 
 
@@ -485,13 +535,15 @@ def _make_attention_mutant(kind):
     return mutant
 
 
-@pytest.mark.parametrize("mutant", ["v_layout", "ignore_table", "no_scale", "top_left_causal",
+@pytest.mark.parametrize("mutant", ["v_layout", "v_whole_slab", "ignore_table", "no_scale", "top_left_causal",
                                     "gqa_modulo", "sign", "prefix_inclusive", "doc_exclusive"])
 def test_planted_mistakes_are_caught(monkeypatch, mutant):
     monkeypatch.setitem(opa.__dict__, "_orig_gather", opa.gather_sequence)
     monkeypatch.setitem(opa.__dict__, "_orig_attention", opa.attention_dense)
     if mutant == "v_layout":
         monkeypatch.setattr(opa, "gather_sequence", _mutant_gather_v_not_transposed)
+    elif mutant == "v_whole_slab":
+        monkeypatch.setattr(opa, "gather_sequence", _mutant_gather_v_whole_slab)
     elif mutant == "ignore_table":
         monkeypatch.setattr(opa, "gather_sequence", _mutant_gather_ignores_table)
     else:

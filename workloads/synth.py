@@ -10,8 +10,10 @@ share):
 
 * ``k_pool``: ``[NB, Hkv, bs, D]`` -- one (block, kv-head) slab holds ``bs``
   key rows of ``D`` elements each (token-major).
-* ``v_pool``: ``[NB, Hkv, D, bs]`` -- one (block, kv-head) slab holds ``D``
-  rows of ``bs`` tokens each (dimension-major, token-minor).
+* ``v_pool``: ``[NB, Hkv, bs/S, D, S]`` with ``S = min(bs, 16)`` -- one
+  (block, kv-head) slab holds ``bs/S`` sub-slabs of ``S`` tokens, each ``D``
+  rows of ``S`` tokens (dimension-major, token-minor); token ``o`` of a block
+  is column ``o % S`` of sub-slab ``o // S``.
 * ``block_table``: int32 ``[B, W]``; entry ``[b, j]`` is the physical block
   that holds logical tokens ``[j*bs, (j+1)*bs)`` of sequence ``b``; entries
   past ``ceil(context_lens[b] / bs)`` are -1 and never read.
@@ -131,12 +133,14 @@ def _fill_pools(ss: np.random.SeedSequence, NB, Hkv, D, bs, live, dtype, threads
     result does not depend on the thread count); inside a range the
     referenced blocks are drawn in ascending physical order.
     """
+    S = min(bs, 16)
+    vshape = (Hkv, bs // S, D, S)
     if dtype == "bf16":
         k_pool = np.empty((NB, Hkv, bs, D), np.uint16)
-        v_pool = np.empty((NB, Hkv, D, bs), np.uint16)
+        v_pool = np.empty((NB,) + vshape, np.uint16)
     else:
         k_pool = np.empty((NB, Hkv, bs, D), np.float32)
-        v_pool = np.empty((NB, Hkv, D, bs), np.float32)
+        v_pool = np.empty((NB,) + vshape, np.float32)
     ranges = [(i, min(NB, i + _POOL_GROUP_BLOCKS)) for i in range(0, NB, _POOL_GROUP_BLOCKS)]
     children = ss.spawn(len(ranges))
     nan = _nan_value(dtype)
@@ -151,11 +155,12 @@ def _fill_pools(ss: np.random.SeedSequence, NB, Hkv, D, bs, live, dtype, threads
             return
         rng = np.random.default_rng(children[ri])
         kv = _normal(rng, (len(ref), Hkv, bs, D), dtype)
-        vv = _normal(rng, (len(ref), Hkv, D, bs), dtype)
+        vv = _normal(rng, (len(ref),) + vshape, dtype)
         lr = lv[ref]
         for i in np.nonzero(lr < bs)[0]:
             kv[i, :, lr[i]:, :] = nan
-            vv[i, :, :, lr[i]:] = nan
+            tail = np.arange(lr[i], bs)
+            vv[i, :, tail // S, :, tail % S] = nan
         k_pool[c0 + ref] = kv
         v_pool[c0 + ref] = vv
 
