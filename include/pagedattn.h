@@ -20,8 +20,10 @@
  *                  accumulates in fp32.
  *   k_cache        [num_blocks, num_kv_heads, block_size, head_dim]
  *                  (token-major rows inside each (block, kv-head) slab)
- *   v_cache        [num_blocks, num_kv_heads, head_dim, block_size]
- *                  (dimension-major: each row holds block_size tokens)
+ *   v_cache        [num_blocks, num_kv_heads, block_size / 16, head_dim, 16]
+ *                  (dimension-major sub-slabs of 16 tokens: token o of a
+ *                  block is column o % 16 of sub-slab o / 16, so any 16-token
+ *                  chunk's values are one contiguous run for every page size)
  *   block_tables   int32 [num_seqs, block_table_stride]; entry [b, j] is the
  *                  physical block of logical tokens [j*bs, (j+1)*bs) of
  *                  sequence b.  Only entries j < ceil(context_lens[b]/bs) are
@@ -114,7 +116,8 @@ typedef struct {
  * existing data never moves ("Ultimate Guide to PagedAttention": KV cache,
  * dynamic growth).  For every t < num_tokens with s = slot_mapping[t] >= 0:
  *   k_cache[s / bs][h][s % bs][:] = k_new[t][h][:]
- *   v_cache[s / bs][h][:][s % bs] = v_new[t][h][:]     for every kv-head h.
+ *   v_cache[s / bs][h][(s % bs) / 16][:][s % 16] = v_new[t][h][:]
+ * for every kv-head h.
  * Tokens with a negative slot are skipped.  The copy is bit-exact (no
  * conversion).  k_new / v_new: [num_tokens, num_kv_heads, head_dim].
  * num_tokens == 0 is a no-op.

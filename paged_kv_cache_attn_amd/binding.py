@@ -152,11 +152,14 @@ def _mods(window=0, softcap=0.0, alibi_slopes=None, prefix_lens=None, doc_starts
 
 
 def _pool_dims(k_cache, v_cache):
+    """K pool ``[NB, Hkv, bs, D]``; V pool ``[NB, Hkv, bs/S, D, S]``, S = min(bs, 16)."""
     _need(k_cache, "k_cache", ndim=4)
-    _need(v_cache, "v_cache", ndim=4)
+    _need(v_cache, "v_cache", ndim=5)
     NB, Hkv, bs, D = k_cache.shape
-    if tuple(v_cache.shape) != (NB, Hkv, D, bs) or v_cache.dtype != k_cache.dtype:
-        raise ValueError("v_cache must be [num_blocks, num_kv_heads, head_dim, block_size] of k_cache's dtype")
+    S = min(bs, 16)
+    if tuple(v_cache.shape) != (NB, Hkv, bs // S, D, S) or v_cache.dtype != k_cache.dtype:
+        raise ValueError("v_cache must be [num_blocks, num_kv_heads, block_size/S, head_dim, S], "
+                         "S = min(block_size, 16), of k_cache's dtype")
     return NB, Hkv, bs, D
 
 

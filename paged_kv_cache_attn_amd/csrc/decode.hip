@@ -23,9 +23,11 @@
 //   * online softmax in the log2 domain; the running max is raised lazily
 //     (only when a new score exceeds it by more than 2^8), so rescaling of
 //     the accumulators is rare after the first chunk.
-//   * P.V with lanes over head_dim: V slabs are dimension-major, so one dword
-//     holds two consecutive tokens of one dimension -- exactly the bf16 pair
-//     v_dot2 wants against a (p_j, p_j+1) pair read from LDS.
+//   * P.V with lanes over head_dim: V is stored in dimension-major sub-slabs
+//     of 16 tokens, so one dword holds two consecutive tokens of one
+//     dimension -- exactly the bf16 pair v_dot2 wants against a (p_j, p_j+1)
+//     pair read from LDS -- and a chunk's V is one contiguous run whatever
+//     the page size.
 #include "pa_device.h"
 #include "pa_kernels.h"
 
@@ -210,7 +212,7 @@ __device__ __forceinline__ void attend_segment(const RowAttnArgs& a, const RowRa
     const int off = tok0 & (bs - 1);
     const size_t slab = ((size_t)blk * a.Hkv + kvh) * kslab_bytes;
     const char* ks = kpool + slab + (size_t)off * C::kRowBytes;
-    const char* vs = vpool + slab + (size_t)off * C::ES;
+    const char* vs = vpool + slab + (size_t)(off >> 4) * (D * 16 * C::ES);  // the chunk's V sub-slab
 #pragma unroll
     for (int ps = 0; ps < C::NPASS; ++ps)
 #pragma unroll
@@ -220,11 +222,7 @@ __device__ __forceinline__ void attend_segment(const RowAttnArgs& a, const RowRa
     for (int r = 0; r < C::RPL; ++r)
 #pragma unroll
       for (int w = 0; w < C::VPR; ++w)
-        // V rows of a 16-token chunk are 32-byte pieces of rows bs tokens long:
-        // for bs > 16 the next chunks reuse the same cache lines, so those
-        // loads keep the normal (temporal) cache policy
-        ch.v[r][w] = (bs == 16) ? load16_stream(vs + ((size_t)(vr + 32 * r) * bs + vh * 8) * C::ES + w * 16)
-                                : load16(vs + ((size_t)(vr + 32 * r) * bs + vh * 8) * C::ES + w * 16);
+        ch.v[r][w] = load16_stream(vs + ((size_t)(vr + 32 * r) * 16 + vh * 8) * C::ES + w * 16);
   };
 
   // one 16-token chunk: scores, online softmax, P.V.  A chunk that starts at

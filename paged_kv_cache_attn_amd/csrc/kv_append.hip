@@ -3,8 +3,9 @@
 // A growing sequence writes its new tokens into the blocks it owns (possibly
 // freshly allocated ones) and nothing already stored moves ("Ultimate Guide
 // to PagedAttention", newline: KV cache and dynamic growth).  Token t goes to
-// slot s = slot_mapping[t]: block s >> log2(bs), offset s & (bs - 1).  The
-// copy is of raw bits.  One wavefront per (token, kv-head).  Also the
+// slot s = slot_mapping[t]: block s >> log2(bs), offset s & (bs - 1); K is a
+// token-major row of the (block, kv-head) slab, V a column of its 16-token
+// dimension-major sub-slab.  The copy is of raw bits.  One wavefront per (token, kv-head).  Also the
 // whole-block copy that copy-on-write needs.
 #include "pa_device.h"
 #include "pa_kernels.h"
@@ -27,11 +28,12 @@ __global__ __launch_bounds__(64) void kv_append_kernel(const AppendArgs a) {
   const size_t src = ((size_t)t * a.Hkv + h) * D;
   const W* kn = static_cast<const W*>(a.k_new) + src;
   const W* vn = static_cast<const W*>(a.v_new) + src;
-  W* kc = static_cast<W*>(a.k_cache) + slab + (size_t)off * D;  // row of bs x D slab
-  W* vc = static_cast<W*>(a.v_cache) + slab + off;              // column of D x bs slab
+  W* kc = static_cast<W*>(a.k_cache) + slab + (size_t)off * D;  // row of the bs x D slab
+  // column off % 16 of the D x 16 sub-slab off / 16
+  W* vc = static_cast<W*>(a.v_cache) + slab + (size_t)(off >> 4) * D * 16 + (off & 15);
   for (int d = threadIdx.x; d < D; d += 64) {
     kc[d] = kn[d];
-    vc[(size_t)d * bs] = vn[d];
+    vc[(size_t)d * 16] = vn[d];
   }
 }
 

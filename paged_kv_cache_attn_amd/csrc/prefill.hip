@@ -20,9 +20,9 @@
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q^T
 //     kept in registers); each lane then owns one query row's scores, so
 //     softmax statistics are per-lane scalars;
-//   * O^T += V^T P^T with the same MFMA (A = V^T rows from LDS -- V slabs are
-//     dimension-major in the pool, so no transpose is needed -- B = P^T
-//     straight from the S^T accumulators, rounded to bf16).
+//   * O^T += V^T P^T with the same MFMA (A = V^T rows from LDS -- V is
+//     stored in dimension-major sub-slabs of 16 keys, so no transpose is
+//     needed -- B = P^T straight from the S^T accumulators, rounded to bf16).
 // The K rows of the S^T product are read in a permuted order inside each
 // 16-key group (quarters 1 and 2 swapped) so that the accumulator registers
 // a lane holds are exactly the 8 consecutive keys the next MFMA's B operand
@@ -211,7 +211,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
     const int local = (slot0 & ((1 << dcpb_log2) - 1)) + lane;
     const int d = local >> cpb_log2;
     const int cc = (local & (cpb - 1)) ^ v_swz(d, cpb_log2);
-    v_off[it] = (uint32_t)(d * bs + cc * 8) * 2u;
+    // keys 8cc..8cc+7 of the tile-block: sub-slab cc/2 (of 16 keys), row d, half cc%2
+    v_off[it] = (uint32_t)(((cc >> 1) * D + d) * 16 + (cc & 1) * 8) * 2u;
   }
   auto issue_k = [&](int k0, auto buf, int blk) {
     const char* kb = kpool + (size_t)blk * blk_stride + (size_t)((k0 + 16 * wave) & (bs - 1)) * D * 2;
@@ -228,7 +229,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
 #pragma unroll
     for (int it = 0; it < VPIECES; ++it) {
       const int q = wave * VPIECES + it;
-      const uint32_t soff = (uint32_t)((k0 + (v_j[it] << kb_log2)) & (bs - 1)) * 2u;
+      // the tile-block's first key o sits at sub-slab o/16: o * D * 2 bytes in
+      const uint32_t soff = (uint32_t)((k0 + (v_j[it] << kb_log2)) & (bs - 1)) * (uint32_t)(D * 2);
       buffer_load_lds16(vb, v_off[it], soff, (lds_ptr)(lv + q * 1024));
     }
   };

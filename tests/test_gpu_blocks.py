@@ -20,11 +20,11 @@ def test_copy_blocks_bit_exact(gpu_lib, dtype, D, bs):
     NB, Hkv = 40, 4
     if dtype == "bf16":
         k = bf16_round_bits(rng.standard_normal((NB, Hkv, bs, D)).astype(np.float32))
-        v = bf16_round_bits(rng.standard_normal((NB, Hkv, D, bs)).astype(np.float32))
+        v = bf16_round_bits(rng.standard_normal((NB, Hkv, bs // 16, D, 16)).astype(np.float32))
         tk, tv = (torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda() for x in (k, v))
     else:
         k = rng.standard_normal((NB, Hkv, bs, D)).astype(np.float32)
-        v = rng.standard_normal((NB, Hkv, D, bs)).astype(np.float32)
+        v = rng.standard_normal((NB, Hkv, bs // 16, D, 16)).astype(np.float32)
         tk, tv = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
     pairs = [(3, 17), (0, 39), (25, 2), (11, 8)]
     src = torch.tensor([p[0] for p in pairs], dtype=torch.int32, device="cuda")

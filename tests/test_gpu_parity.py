@@ -321,7 +321,7 @@ def test_pool_beyond_4gib(gpu_lib):
     remap[used] = new_ids
     t = upload(w)
     kb = torch.full((NB_big, w.Hkv, w.bs, w.D), float("nan"), dtype=torch.bfloat16, device="cuda")
-    vb = torch.full((NB_big, w.Hkv, w.D, w.bs), float("nan"), dtype=torch.bfloat16, device="cuda")
+    vb = torch.full((NB_big,) + tuple(t["v_cache"].shape[1:]), float("nan"), dtype=torch.bfloat16, device="cuda")
     idx_new = torch.from_numpy(new_ids).cuda()
     idx_old = torch.from_numpy(used.astype(np.int64)).cuda()
     kb[idx_new] = t["k_cache"][idx_old]
