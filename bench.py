@@ -173,6 +173,20 @@ def time_calls(torch, fn, flush, reps, warm=3):
     return float(np.median([a.elapsed_time(b) for a, b in evs]))
 
 
+def calibration_copy(args, torch, dev):
+    """One plain device copy of --calibration-copy-mib MiB: a known-size
+    reference for the HBM traffic counters."""
+    if args.calibration_copy_mib > 0:
+        nbytes = args.calibration_copy_mib << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"calibration copy of {args.calibration_copy_mib} MiB done")
+
+
 def shared_prefix_long():
     """64 sequences behind one 16384-token prompt (1024 shared 16-token
     blocks) with 1024 own tokens each (the last appended this step), 64/8
@@ -212,6 +226,7 @@ def two_phase_main(args, pa, torch, dev):
     def flush():
         if args.flush_mib > 0:
             pa.bench_fill(flush_buf, 0)
+    calibration_copy(args, torch, dev)
     ws2, call = two_phase_call(pa, torch, dev, w, t, out, 16384)
     ws = pa.decode_workspace(t["q"], w.Hkv, w.max_context_len, 0)
 
@@ -412,15 +427,7 @@ def main():
         if ev is not None:
             ev[5].record(stream)
 
-    if args.calibration_copy_mib > 0:
-        nbytes = args.calibration_copy_mib << 20
-        src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-        log(f"calibration copy of {args.calibration_copy_mib} MiB done")
+    calibration_copy(args, torch, dev)
 
     for _ in range(args.warmup):
         step()
