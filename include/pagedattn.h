@@ -151,7 +151,8 @@ int kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_blocks, cons
  *    0  balanced split: 8 wavefronts per compute unit of the current device
  *       (256 units if none is visible) each take an equal share of the
  *       batch's 16-token chunks, so the pieces follow the work, not a fixed
- *       length;
+ *       length -- except when max_context_len <= 256, where no row is split
+ *       (one wavefront per row and head group, and no merge launch);
  *   -1  never split;
  *  > 0  fixed pieces of split_tokens keys (a power of two >= 16).
  * Returns 0 for invalid arguments.

@@ -16,6 +16,7 @@ constexpr long long kAutoTargetUnits = 2048;  // ~8 wavefronts per compute unit
 constexpr int kStreamWavesPerCU = 8;          // resident decode wavefronts per compute unit
 constexpr int kStreamMinChunks = 8;           // 16-token chunks per wavefront, at least
 constexpr int kStreamMaxSeqs = 4096;          // chunk prefix of all rows fits in 16 KB of LDS
+constexpr int kUnsplitMaxCtx = 256;           // rows this short are never split (no merge launch)
 constexpr int kDefaultCUs = 256;              // MI355X, when no device is visible
 
 int ilog2(long long x) {
@@ -79,6 +80,13 @@ int decode_shape(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_ctx, int32_t sp
   s.GP = group_pad(s.g);
   s.NG = (s.g + s.GP - 1) / s.GP;
   s.W = 0;
+  if (split == 0 && max_ctx <= kUnsplitMaxCtx) {
+    // every row fits a few chunks: one wavefront per (row, head group)
+    // finishes it faster than a split plus the merge launch would
+    s.split_log2 = kUnsplitLog2;
+    s.P = 1;
+    return PA_OK;
+  }
   if (split == 0 && B <= kStreamMaxSeqs) {
     // balanced split: as many wavefronts as stay resident, but at least
     // kStreamMinChunks chunks of work each for the largest possible batch
@@ -274,6 +282,7 @@ int kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache
 int32_t paged_attn_decode_split_tokens(int32_t num_seqs, int32_t num_kv_heads,
                                        int32_t max_context_len, int32_t split_tokens) {
   if (check_split(split_tokens) || num_seqs < 0 || num_kv_heads <= 0 || max_context_len < 0) return 0;
+  if (split_tokens == 0 && max_context_len <= kUnsplitMaxCtx) return -1;  // short rows: unsplit
   if (split_tokens == 0 && num_seqs <= kStreamMaxSeqs) return 0;  // balanced split
   const int l2 = resolve_split_log2(num_seqs, num_kv_heads, max_context_len, split_tokens);
   return l2 >= kUnsplitLog2 ? -1 : (1 << l2);

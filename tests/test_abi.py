@@ -153,6 +153,10 @@ def test_split_resolution_and_workspace_size():
     assert binding.decode_split_tokens(64, 8, 32768, 100) == 0  # invalid
     assert binding.decode_split_tokens(64, 8, 32768) == 0
     assert binding.decode_split_tokens(8, 8, 2048) == 0
+    # rows of at most 256 keys are never split by the balanced mode: no workspace, no merge
+    assert binding.decode_split_tokens(8, 8, 256) == -1
+    assert binding.decode_split_tokens(8, 8, 257) == 0
+    assert binding.decode_workspace_size(8, 32, 8, 128, 256, 0) == 0
     # fixed partitions: B * Hkv * ceil(g/GP)*GP * P * (D + 2) * 4 bytes, 0 when unsplit
     assert binding.decode_workspace_size(64, 64, 8, 128, 32768, 512) == 64 * 8 * 8 * 64 * 130 * 4
     assert binding.decode_workspace_size(8, 32, 8, 128, 2048, 512) == 8 * 8 * 4 * 4 * 130 * 4
