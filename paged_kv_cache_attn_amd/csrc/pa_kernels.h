@@ -26,7 +26,7 @@ struct RowAttnArgs {
   void* out;                 // [rows, Hq, D]
   const void* q;             // [rows, Hq, D]
   const void* k_cache;       // [NB, Hkv, bs, D]
-  const void* v_cache;       // [NB, Hkv, D, bs]
+  const void* v_cache;       // [NB, Hkv, bs/16, D, 16]
   const int32_t* block_tables;
   const int32_t* context_lens;
   const int32_t* cu_q_lens;  // nullptr: one row per sequence, row index b

@@ -91,7 +91,7 @@ class Workload:
     q_lens: np.ndarray  # int32 [B]
     cu_q_lens: np.ndarray  # int32 [B + 1]
     k_pool: np.ndarray  # [NB, Hkv, bs, D]   (state before kv_append)
-    v_pool: np.ndarray  # [NB, Hkv, D, bs]   (state before kv_append)
+    v_pool: np.ndarray  # [NB, Hkv, bs/S, D, S], S = min(bs, 16)   (state before kv_append)
     k_new: np.ndarray  # [T, Hkv, D]
     v_new: np.ndarray  # [T, Hkv, D]
     slot_mapping: np.ndarray  # int32 [T]
