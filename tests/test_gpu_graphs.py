@@ -1,0 +1,95 @@
+"""The C-ABI calls on other streams and inside captured HIP graphs.
+
+No call allocates or clears memory, so an append + decode + prefill step can
+be captured once and replayed.  Each replay runs after eager work that
+changes the inputs, and must give exactly the eager calls' result on the same
+inputs.  The calls also take a non-default stream (default priority) and give
+bit-identical results there.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from workloads import build_workload
+from workloads.device import to_numpy_bits, upload
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode_batch():
+    return build_workload(name="graph_decode", seed=901, kind="decode", dtype="bf16", Hq=32, Hkv=8, D=128, bs=16,
+                          context_lens=[40, 700, 1500, 3000], append_lens=[1, 1, 1, 1])
+
+
+def _prefill_batch():
+    return build_workload(name="graph_prefill", seed=902, kind="prefill", dtype="bf16", Hq=32, Hkv=8, D=128, bs=16,
+                          context_lens=[300, 520], q_lens=[100, 200], append_lens=[100, 200], causal=True)
+
+
+def test_graph_replays_match_eager_calls(gpu_lib):
+    wd, wp = _decode_batch(), _prefill_batch()
+    td, tp = upload(wd), upload(wp)
+    k0, v0 = td["k_cache"].clone(), td["v_cache"].clone()
+    kp0, vp0 = tp["k_cache"].clone(), tp["v_cache"].clone()
+    out_d = torch.empty_like(td["q"])
+    out_p = torch.empty_like(tp["q"])
+    ws = gpu_lib.decode_workspace(td["q"], wd.Hkv, wd.max_context_len, 0)
+
+    def step():
+        gpu_lib.kv_append(td["k_new"], td["v_new"], td["k_cache"], td["v_cache"], td["slot_mapping"])
+        gpu_lib.paged_attn_decode(out_d, td["q"], td["k_cache"], td["v_cache"], td["block_tables"],
+                                  td["context_lens"], wd.scale, wd.max_context_len, 0, workspace=ws)
+        gpu_lib.kv_append(tp["k_new"], tp["v_new"], tp["k_cache"], tp["v_cache"], tp["slot_mapping"])
+        gpu_lib.paged_attn_prefill(out_p, tp["q"], tp["cu_q_lens"], tp["k_cache"], tp["v_cache"],
+                                   tp["block_tables"], tp["context_lens"], wp.scale, wp.max_q_len, True)
+
+    def reset(seed):
+        # eager work between replays: fresh pools and new queries
+        td["k_cache"].copy_(k0)
+        td["v_cache"].copy_(v0)
+        tp["k_cache"].copy_(kp0)
+        tp["v_cache"].copy_(vp0)
+        g = torch.Generator(device="cuda").manual_seed(seed)
+        td["q"].copy_(torch.randn(td["q"].shape, generator=g, device="cuda").to(td["q"].dtype))
+        tp["q"].copy_(torch.randn(tp["q"].shape, generator=g, device="cuda").to(tp["q"].dtype))
+        torch.cuda.synchronize()
+
+    step()  # warm-up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    reset(0)
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for seed in (1, 2, 3):
+        reset(seed)
+        step()
+        torch.cuda.synchronize()
+        want_d, want_p = to_numpy_bits(out_d).copy(), to_numpy_bits(out_p).copy()
+        reset(seed)
+        out_d.zero_()
+        out_p.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_numpy_bits(out_d), want_d), f"decode replay {seed}"
+        assert np.array_equal(to_numpy_bits(out_p), want_p), f"prefill replay {seed}"
+
+
+def test_calls_on_a_side_stream(gpu_lib):
+    w = _decode_batch()
+    t = upload(w)
+    gpu_lib.kv_append(t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], t["slot_mapping"])
+    ref = torch.empty_like(t["q"])
+    gpu_lib.paged_attn_decode(ref, t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                              w.scale, w.max_context_len, 0)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()  # default priority
+    out = torch.empty_like(t["q"])
+    ws = gpu_lib.decode_workspace(t["q"], w.Hkv, w.max_context_len, 0)
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        gpu_lib.paged_attn_decode(out, t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                                  w.scale, w.max_context_len, 0, workspace=ws)
+    side.synchronize()
+    assert np.array_equal(to_numpy_bits(out), to_numpy_bits(ref))
