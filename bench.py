@@ -202,13 +202,12 @@ def two_phase_call(pa, torch, dev, w, t, out, pre):
     sharing its first ``pre`` tokens."""
     gs = torch.tensor([0, w.B], dtype=torch.int32, device=dev)
     pl = torch.tensor([pre], dtype=torch.int32, device=dev)
-    ws2 = pa.decode_cascade_workspace(t["q"], w.Hkv, 1, w.B, w.max_context_len, pre)
+    levels = [pa.prefix_level(gs, pl, w.B, pre)]
+    ws2 = pa.decode_cascade_workspace(t["q"], w.Hkv, levels, w.max_context_len)
 
     def call():
         pa.paged_attn_decode_cascade(out, t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
-                                     t["context_lens"], gs, pl, w.scale, w.max_context_len, w.B, pre,
-                                     workspace=ws2)
-    call.keep = (gs, pl)
+                                     t["context_lens"], levels, w.scale, w.max_context_len, workspace=ws2)
     return ws2, call
 
 

@@ -219,49 +219,66 @@ int paged_attn_decode_merge(void* out, const int32_t* context_lens, int32_t num_
  * Requests that start with the same prompt share the prefix's physical
  * blocks ("Ultimate Guide to PagedAttention": block table and scheduler,
  * memory sharing), so a decode step over such a batch reads the same keys once
- * per sequence.  This call instead computes the prefix part once per group of
- * sharing sequences, with all the group's query rows against the prefix keys
- * on the matrix cores, then each sequence's own keys with the paged decode,
- * and combines the two softmax states by their log-sum-exps -- the
- * prefix-first, then sequence-first split that the related-paper list of
- * "Paged Attention Meets FlexAttention" (fugumt.com) describes for
- * ChunkAttention.  The result is the same attention as paged_attn_decode
- * (up to rounding order; the prefix's softmax weights are rounded to bf16
- * before the P.V product, as in paged_attn_prefill).
+ * per sequence.  This call instead computes each shared part once per group
+ * of sharing sequences, with all the group's query rows against those keys on
+ * the matrix cores, then each sequence's own keys with the paged decode, and
+ * combines the softmax states by their log-sum-exps -- the prefix-first, then
+ * sequence-first split that the related-paper list of "Paged Attention Meets
+ * FlexAttention" (fugumt.com) describes for ChunkAttention.  Shared parts may
+ * be nested (a system prompt shared by all, then a conversation shared by its
+ * beams: the hierarchical prefixes the vAttention page's decode snippets
+ * speak of), one level per nesting depth.  The result is the same attention
+ * as paged_attn_decode (up to rounding order; the shared parts' softmax
+ * weights are rounded to bf16 before the P.V product, as in
+ * paged_attn_prefill).
  *
- * Arguments as paged_attn_decode, plus (device int32):
- *   group_starts  [num_groups + 1]: sequences group_starts[g] ..
+ * One pa_prefix_level per depth, levels[0] outermost.  At every level the
+ * groups partition the batch into runs of consecutive sequences:
+ *   group_starts  device int32 [num_groups + 1]: sequences group_starts[g] ..
  *                 group_starts[g+1]-1 form group g; group_starts[0] = 0,
- *                 non-decreasing, group_starts[num_groups] = num_seqs (every
- *                 sequence in exactly one group; a group may have one member
- *                 or none).
- *   prefix_lens   [num_groups]: the first prefix_lens[g] keys (0 allowed) of
- *                 every member of group g hold the same key/value vectors;
- *                 they are read through the table row of the group's first
- *                 member.  prefix_lens[g] <= context_lens[b] of each member.
- * and host-side upper bounds that size the launch: max_group_size (members
- * of any group, >= 1) and max_prefix_len (>= every prefix_lens[g]).
- * bf16 only, num_heads / num_kv_heads must divide 128; of the score mods only
- * softcap is taken (window, ALiBi, prefix-LM and document masks depend on each
- * row's position and return PA_ERR_UNSUPPORTED).  The workspace is device
- * memory of at least paged_attn_decode_cascade_workspace_size(...) bytes,
- * 16-byte aligned.  Breaking the device-side contract (groups, prefix
- * lengths) is undefined behaviour; the debug library traps.
+ *                 non-decreasing, group_starts[num_groups] = num_seqs (a
+ *                 group may have one member or none).
+ *   prefix_starts device int32 [num_groups], or NULL for all 0;
+ *   prefix_ends   device int32 [num_groups]: group g shares keys
+ *                 [prefix_starts[g], prefix_ends[g]) -- the same key/value
+ *                 vectors for every member, read through the table row of
+ *                 the group's first member.
+ *   num_groups (>= 1), max_group_size (host bound on members per group,
+ *   >= 1), max_prefix_len (host bound on prefix_ends[g] - prefix_starts[g]).
+ * For every sequence the ranges of its groups must follow each other: level
+ * 0 starts at key 0, level l + 1 starts where level l ended, and the last end
+ * is at most the sequence's context length; its own keys are the rest.  An
+ * empty range (start == end) is allowed.  1 <= num_levels <= 8.
+ *
+ * Other arguments as paged_attn_decode.  bf16 only, num_heads / num_kv_heads
+ * must divide 128; of the score mods only softcap is taken (window, ALiBi,
+ * prefix-LM and document masks depend on each row's position and return
+ * PA_ERR_UNSUPPORTED).  The workspace is device memory of at least
+ * paged_attn_decode_cascade_workspace_size(...) bytes, 16-byte aligned (the
+ * size function reads only the levels' host fields).  Breaking the
+ * device-side contract (groups, ranges) is undefined behaviour; the debug
+ * library traps.
  */
-size_t paged_attn_decode_cascade_workspace_size(int32_t num_seqs, int32_t num_groups,
-                                                int32_t max_group_size, int32_t num_heads,
-                                                int32_t num_kv_heads, int32_t head_dim,
-                                                int32_t max_context_len, int32_t max_prefix_len);
+typedef struct {
+  const int32_t* group_starts;
+  const int32_t* prefix_starts;
+  const int32_t* prefix_ends;
+  int32_t num_groups;
+  int32_t max_group_size;
+  int32_t max_prefix_len;
+} pa_prefix_level;
+
+size_t paged_attn_decode_cascade_workspace_size(int32_t num_seqs, const pa_prefix_level* levels,
+                                                int32_t num_levels, int32_t num_heads, int32_t num_kv_heads,
+                                                int32_t head_dim, int32_t max_context_len);
 
 int paged_attn_decode_cascade(void* out, const void* q, const void* k_cache, const void* v_cache,
                               const int32_t* block_tables, int32_t block_table_stride,
-                              const int32_t* context_lens, int32_t num_seqs,
-                              const int32_t* group_starts, const int32_t* prefix_lens,
-                              int32_t num_groups, int32_t max_group_size, int32_t max_prefix_len,
-                              int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
-                              int32_t block_size, int64_t num_blocks, int32_t max_context_len,
-                              float scale, const pa_score_mods* mods, void* workspace,
-                              size_t workspace_bytes, int32_t dtype, void* stream);
+                              const int32_t* context_lens, int32_t num_seqs, const pa_prefix_level* levels,
+                              int32_t num_levels, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, int64_t num_blocks, int32_t max_context_len, float scale,
+                              const pa_score_mods* mods, void* workspace, size_t workspace_bytes, int32_t dtype,
+                              void* stream);
 
 /*
  * paged_attn_prefill -- several query rows per sequence (prefill, or a

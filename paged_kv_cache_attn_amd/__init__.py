@@ -6,6 +6,7 @@ The compute lives in ``libpagedattn.so`` (hand-written HIP kernels, C ABI in
 
 from .binding import (  # noqa: F401
     BlockManager,
+    PrefixLevel,
     PA_BF16,
     PA_F32,
     bench_fill,
@@ -22,5 +23,6 @@ from .binding import (  # noqa: F401
     paged_attn_decode,
     paged_attn_decode_cascade,
     paged_attn_prefill,
+    prefix_level,
     status_string,
 )

@@ -34,6 +34,14 @@ class ScoreMods(ctypes.Structure):
                 ("doc_starts", ctypes.c_void_p)]
 
 
+class PrefixLevel(ctypes.Structure):
+    """``pa_prefix_level``: one depth of shared prefixes for the two-phase decode."""
+
+    _fields_ = [("group_starts", ctypes.c_void_p), ("prefix_starts", ctypes.c_void_p),
+                ("prefix_ends", ctypes.c_void_p), ("num_groups", ctypes.c_int32),
+                ("max_group_size", ctypes.c_int32), ("max_prefix_len", ctypes.c_int32)]
+
+
 _i32 = ctypes.c_int32
 _i64 = ctypes.c_int64
 _vp = ctypes.c_void_p
@@ -54,8 +62,9 @@ SIGNATURES = {
                                        _vp]),
     "paged_attn_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                   _i64, _f32, _i32, _mods_p, _i32, _vp]),
-    "paged_attn_decode_cascade_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
-    "paged_attn_decode_cascade": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _i32, _i32,
+    "paged_attn_decode_cascade_workspace_size": (_sz, [_i32, ctypes.POINTER(PrefixLevel), _i32, _i32, _i32, _i32,
+                                                        _i32]),
+    "paged_attn_decode_cascade": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, ctypes.POINTER(PrefixLevel), _i32,
                                          _i32, _i32, _i32, _i32, _i64, _i32, _f32, _mods_p, _vp, _sz, _i32, _vp]),
     "paged_attn_status_string": (ctypes.c_char_p, [_i32]),
     "kv_copy_blocks": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _i32, _vp]),
@@ -234,45 +243,61 @@ def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens, scal
     return out
 
 
-def decode_cascade_workspace_size(num_seqs, num_groups, max_group_size, num_heads, num_kv_heads, head_dim,
-                                  max_context_len, max_prefix_len) -> int:
-    return int(lib().paged_attn_decode_cascade_workspace_size(num_seqs, num_groups, max_group_size, num_heads,
-                                                              num_kv_heads, head_dim, max_context_len,
-                                                              max_prefix_len))
+def prefix_level(group_starts, prefix_ends, max_group_size, max_prefix_len, prefix_starts=None):
+    """One depth of shared prefixes: int32 device tensors ``group_starts [G+1]``,
+    ``prefix_ends [G]`` and optionally ``prefix_starts [G]`` (None: all 0),
+    with host bounds on group members and range lengths."""
+    _need(group_starts, "group_starts", torch.int32, 1)
+    _need(prefix_ends, "prefix_ends", torch.int32, 1)
+    G = prefix_ends.shape[0]
+    if group_starts.shape[0] != G + 1:
+        raise ValueError("group_starts must hold num_groups + 1 entries")
+    if prefix_starts is not None:
+        _need(prefix_starts, "prefix_starts", torch.int32, 1)
+        if prefix_starts.shape[0] != G:
+            raise ValueError("prefix_starts must hold num_groups entries")
+    return {"group_starts": group_starts, "prefix_starts": prefix_starts, "prefix_ends": prefix_ends,
+            "num_groups": G, "max_group_size": int(max_group_size), "max_prefix_len": int(max_prefix_len)}
 
 
-def decode_cascade_workspace(q, num_kv_heads, num_groups, max_group_size, max_context_len, max_prefix_len):
+def _levels_array(levels):
+    arr = (PrefixLevel * max(1, len(levels)))()
+    for i, v in enumerate(levels):
+        arr[i] = PrefixLevel(v["group_starts"].data_ptr(),
+                             None if v["prefix_starts"] is None else v["prefix_starts"].data_ptr(),
+                             v["prefix_ends"].data_ptr(), v["num_groups"], v["max_group_size"], v["max_prefix_len"])
+    return arr
+
+
+def decode_cascade_workspace_size(num_seqs, levels, num_heads, num_kv_heads, head_dim, max_context_len) -> int:
+    return int(lib().paged_attn_decode_cascade_workspace_size(num_seqs, _levels_array(levels), len(levels),
+                                                              num_heads, num_kv_heads, head_dim, max_context_len))
+
+
+def decode_cascade_workspace(q, num_kv_heads, levels, max_context_len):
     """A two-phase decode workspace for these sizes."""
     B, Hq, D = q.shape
-    n = decode_cascade_workspace_size(B, num_groups, max_group_size, Hq, num_kv_heads, D, max_context_len,
-                                      max_prefix_len)
+    n = decode_cascade_workspace_size(B, levels, Hq, num_kv_heads, D, max_context_len)
     return torch.empty(max(n, 4) // 4, dtype=torch.float32, device=q.device)
 
 
-def paged_attn_decode_cascade(out, q, k_cache, v_cache, block_tables, context_lens, group_starts, prefix_lens,
-                              scale, max_context_len, max_group_size, max_prefix_len, workspace=None,
-                              softcap=0.0, window=0, alibi_slopes=None):
-    """Decode where groups of sequences share a prefix (``paged_attn_decode_cascade``).
+def paged_attn_decode_cascade(out, q, k_cache, v_cache, block_tables, context_lens, levels, scale,
+                              max_context_len, workspace=None, softcap=0.0, window=0, alibi_slopes=None):
+    """Decode where sequences share (possibly nested) prefixes (``paged_attn_decode_cascade``).
 
-    ``group_starts [G+1]`` and ``prefix_lens [G]`` are int32 device tensors;
-    ``max_group_size`` / ``max_prefix_len`` are host-side bounds.  Writes
+    ``levels``: a list of :func:`prefix_level`, outermost first.  Writes
     ``out [B, Hq, D]``.
     """
     NB, Hkv, bs, D, B, Hq = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens)
-    _need(group_starts, "group_starts", torch.int32, 1)
-    _need(prefix_lens, "prefix_lens", torch.int32, 1)
-    G = prefix_lens.shape[0]
-    if group_starts.shape[0] != G + 1:
-        raise ValueError("group_starts must hold num_groups + 1 entries")
     if workspace is None:
-        workspace = decode_cascade_workspace(q, Hkv, G, max_group_size, max_context_len, max_prefix_len)
+        workspace = decode_cascade_workspace(q, Hkv, levels, max_context_len)
     _need(workspace, "workspace")
     mp, _keep = _mods(window, softcap, alibi_slopes)
+    arr = _levels_array(levels)
     code = lib().paged_attn_decode_cascade(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1],
-        _ptr(context_lens), B, _ptr(group_starts), _ptr(prefix_lens), G, int(max_group_size), int(max_prefix_len),
-        Hq, Hkv, D, bs, NB, int(max_context_len), float(scale), mp, _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _dtype_code(q), _stream())
+        _ptr(context_lens), B, arr, len(levels), Hq, Hkv, D, bs, NB, int(max_context_len), float(scale), mp,
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _dtype_code(q), _stream())
     _check(code, "paged_attn_decode_cascade")
     return out
 

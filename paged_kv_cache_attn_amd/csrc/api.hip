@@ -170,36 +170,51 @@ void fill_row_args(pa::RowAttnArgs& a, void* out, const void* q, const void* kc,
 int launch_status(hipError_t e) { return e == hipSuccess ? PA_OK : (int)e; }
 
 // ---- two-phase (shared-prefix) decode ----
-constexpr int kCascadeMinTiles = 4;  // 64-key tiles per prefix key range, at least
+constexpr int kCascadeMinTiles = 4;   // 64-key tiles per prefix key range, at least
+constexpr int kCascadeMaxLevels = 8;  // prefix levels per call
 constexpr size_t kAlign = 256;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+struct CascadeLevel {
+  int q_tiles, key_split, nsplit, range0;  // range0: index of the level's first key range
+};
+
 struct CascadeShape {
-  int q_tiles, key_split, nsplit;
-  Shape dec;  // the suffix decode
+  CascadeLevel lv[kCascadeMaxLevels];
+  int nranges;  // key ranges over all levels
+  Shape dec;    // the suffix decode
   size_t off_part_lse, off_state_o, off_state_lse, off_key_start, off_dec, total;
 };
 
-// Prefix phase: num_groups x kv-heads x query tiles work-groups per key
-// range; enough ranges for two work-groups per compute unit, each range at
+// Prefix phase of one level: groups x kv-heads x query tiles work-groups per
+// key range; enough ranges for two work-groups per compute unit, each range at
 // least kCascadeMinTiles tiles.
-void cascade_shape(int32_t B, int32_t G, int32_t max_group, int32_t Hq, int32_t Hkv, int32_t D,
-                   int32_t max_ctx, int32_t max_prefix, CascadeShape& c) {
+void cascade_level(int32_t G, int32_t max_group, int32_t Hq, int32_t Hkv, int32_t max_range, CascadeLevel& l) {
   const int qt = pa::prefill_rows_per_tile(Hq / Hkv);
-  c.q_tiles = (int)(((long long)max_group + qt - 1) / qt);
-  const long long tiles = ((long long)max_prefix + 63) / 64;
-  const long long base = std::max(1ll, (long long)G * Hkv * c.q_tiles);
+  l.q_tiles = (int)(((long long)max_group + qt - 1) / qt);
+  const long long tiles = ((long long)max_range + 63) / 64;
+  const long long base = std::max(1ll, (long long)G * Hkv * l.q_tiles);
   long long ns = (2ll * device_cus() + base - 1) / base;
   ns = std::max(1ll, std::min(ns, tiles / kCascadeMinTiles));
   const long long per = tiles > 0 ? (tiles + ns - 1) / ns : 1;
-  c.key_split = (int)(per * 64);
-  c.nsplit = (int)std::max(1ll, ((long long)max_prefix + c.key_split - 1) / c.key_split);
+  l.key_split = (int)(per * 64);
+  l.nsplit = (int)std::max(1ll, ((long long)max_range + l.key_split - 1) / l.key_split);
+}
+
+void cascade_shape(int32_t B, const pa_prefix_level* levels, int32_t L, int32_t Hq, int32_t Hkv, int32_t D,
+                   int32_t max_ctx, CascadeShape& c) {
+  c.nranges = 0;
+  for (int i = 0; i < L; ++i) {
+    cascade_level(levels[i].num_groups, levels[i].max_group_size, Hq, Hkv, levels[i].max_prefix_len, c.lv[i]);
+    c.lv[i].range0 = c.nranges;
+    c.nranges += c.lv[i].nsplit;
+  }
   decode_shape(B, Hq, Hkv, max_ctx, 0, c.dec);
   const size_t rows = (size_t)B * Hq;
-  size_t off = align_up((size_t)c.nsplit * rows * D * sizeof(float));
+  size_t off = align_up((size_t)c.nranges * rows * D * sizeof(float));
   c.off_part_lse = off;
-  off += align_up((size_t)c.nsplit * rows * sizeof(float));
+  off += align_up((size_t)c.nranges * rows * sizeof(float));
   c.off_state_o = off;
   off += align_up(rows * D * sizeof(float));
   c.off_state_lse = off;
@@ -211,9 +226,16 @@ void cascade_shape(int32_t B, int32_t G, int32_t max_group, int32_t Hq, int32_t 
   c.total = off;
 }
 
-int check_cascade_sizes(int32_t B, int32_t G, int32_t max_group, int32_t max_prefix) {
-  if (G < 0 || max_group < 0 || max_prefix < 0) return PA_ERR_SIZE;
-  if (B > 0 && (G < 1 || max_group < 1)) return PA_ERR_SIZE;
+// Host-visible parts of the levels (the device arrays are checked for NULL
+// by the call itself).
+int check_cascade_levels(int32_t B, const pa_prefix_level* levels, int32_t L) {
+  if (B == 0) return (L >= 0 && L <= kCascadeMaxLevels) ? PA_OK : PA_ERR_SIZE;
+  if (!levels) return PA_ERR_NULL;
+  if (L < 1 || L > kCascadeMaxLevels) return PA_ERR_SIZE;
+  for (int i = 0; i < L; ++i) {
+    const pa_prefix_level& v = levels[i];
+    if (v.num_groups < 1 || v.max_group_size < 1 || v.max_prefix_len < 0) return PA_ERR_SIZE;
+  }
   return PA_OK;
 }
 
@@ -398,6 +420,8 @@ int paged_attn_prefill(void* out, const void* q, const int32_t* cu_q_lens, const
     a.part_o = nullptr;
     a.part_lse = nullptr;
     a.row_key_start = nullptr;
+    a.key_starts = nullptr;
+    a.chain = 0;
     a.key_split = 0;
     a.nsplit = 1;
     a.total_q = 0;
@@ -435,51 +459,45 @@ int paged_attn_prefill(void* out, const void* q, const int32_t* cu_q_lens, const
   return launch_status(pa::launch_row_partials(a, dtype, head_dim, hs));
 }
 
-size_t paged_attn_decode_cascade_workspace_size(int32_t num_seqs, int32_t num_groups,
-                                                int32_t max_group_size, int32_t num_heads,
-                                                int32_t num_kv_heads, int32_t head_dim,
-                                                int32_t max_context_len, int32_t max_prefix_len) {
-  if (num_seqs < 0 || max_context_len < 0 || check_heads(num_heads, num_kv_heads) ||
-      check_dim(head_dim) || check_cascade_sizes(num_seqs, num_groups, max_group_size, max_prefix_len) ||
-      128 % (num_heads / num_kv_heads) != 0)
+size_t paged_attn_decode_cascade_workspace_size(int32_t num_seqs, const pa_prefix_level* levels,
+                                                int32_t num_levels, int32_t num_heads, int32_t num_kv_heads,
+                                                int32_t head_dim, int32_t max_context_len) {
+  if (num_seqs <= 0 || max_context_len < 0 || check_heads(num_heads, num_kv_heads) || check_dim(head_dim) ||
+      check_cascade_levels(num_seqs, levels, num_levels) || 128 % (num_heads / num_kv_heads) != 0)
     return 0;
-  if (num_seqs == 0) return 0;
   CascadeShape c;
-  cascade_shape(num_seqs, num_groups, max_group_size, num_heads, num_kv_heads, head_dim,
-                max_context_len, max_prefix_len, c);
+  cascade_shape(num_seqs, levels, num_levels, num_heads, num_kv_heads, head_dim, max_context_len, c);
   return c.total;
 }
 
 int paged_attn_decode_cascade(void* out, const void* q, const void* k_cache, const void* v_cache,
                               const int32_t* block_tables, int32_t block_table_stride,
-                              const int32_t* context_lens, int32_t num_seqs,
-                              const int32_t* group_starts, const int32_t* prefix_lens,
-                              int32_t num_groups, int32_t max_group_size, int32_t max_prefix_len,
-                              int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
-                              int32_t block_size, int64_t num_blocks, int32_t max_context_len,
-                              float scale, const pa_score_mods* mods, void* workspace,
-                              size_t workspace_bytes, int32_t dtype, void* stream) {
+                              const int32_t* context_lens, int32_t num_seqs, const pa_prefix_level* levels,
+                              int32_t num_levels, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, int64_t num_blocks, int32_t max_context_len, float scale,
+                              const pa_score_mods* mods, void* workspace, size_t workspace_bytes, int32_t dtype,
+                              void* stream) {
   int st = common_decode_checks(num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                                 block_table_stride, max_context_len, 0, dtype, mods);
   if (st) return st;
   if (dtype != PA_BF16) return PA_ERR_DTYPE;
-  if ((st = check_cascade_sizes(num_seqs, num_groups, max_group_size, max_prefix_len))) return st;
+  if ((st = check_cascade_levels(num_seqs, levels, num_levels))) return st;
   if (mods && (mods->window != 0 || mods->alibi_slopes || mods->prefix_lens || mods->doc_starts))
     return PA_ERR_UNSUPPORTED;
   const int g = num_heads / num_kv_heads;
   if (128 % g != 0) return PA_ERR_HEADS;
   if (num_seqs == 0) return PA_OK;
-  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !group_starts ||
-      !prefix_lens)
-    return PA_ERR_NULL;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
+  for (int i = 0; i < num_levels; ++i)
+    if (!levels[i].group_starts || !levels[i].prefix_ends) return PA_ERR_NULL;
   CascadeShape c;
-  cascade_shape(num_seqs, num_groups, max_group_size, num_heads, num_kv_heads, head_dim,
-                max_context_len, max_prefix_len, c);
+  cascade_shape(num_seqs, levels, num_levels, num_heads, num_kv_heads, head_dim, max_context_len, c);
   if (!workspace || workspace_bytes < c.total || reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
     return PA_ERR_WORKSPACE;
-  if ((long long)num_groups * num_kv_heads * c.q_tiles * c.nsplit > 0x7fffffffll ||
-      (long long)num_seqs * num_heads > 0x7fffffffll)
-    return PA_ERR_SIZE;
+  for (int i = 0; i < num_levels; ++i)
+    if ((long long)levels[i].num_groups * num_kv_heads * c.lv[i].q_tiles * c.lv[i].nsplit > 0x7fffffffll)
+      return PA_ERR_SIZE;
+  if ((long long)num_seqs * num_heads > 0x7fffffffll) return PA_ERR_SIZE;
   char* ws = static_cast<char*>(workspace);
   float* part_o = reinterpret_cast<float*>(ws);
   float* part_lse = reinterpret_cast<float*>(ws + c.off_part_lse);
@@ -489,44 +507,53 @@ int paged_attn_decode_cascade(void* out, const void* q, const void* k_cache, con
   void* dec_ws = ws + c.off_dec;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const float softcap = mods ? mods->softcap : 0.f;
+  const size_t plane = (size_t)num_seqs * num_heads;
 
-  // 1) shared prefixes: the rows of a group are the query rows of one
-  //    "sequence" whose keys are the prefix, read from the group's first
-  //    member's table row, split into key ranges
-  pa::PrefillArgs p;
-  p.out = nullptr;
-  p.q = q;
-  p.k_cache = k_cache;
-  p.v_cache = v_cache;
-  p.block_tables = block_tables;
-  p.context_lens = prefix_lens;
-  p.cu_q_lens = group_starts;
-  p.alibi = nullptr;
-  p.prefix_lens = nullptr;
-  p.doc_starts = nullptr;
-  p.table_rows = group_starts;
-  p.part_o = part_o;
-  p.part_lse = part_lse;
-  p.row_key_start = key_start;
-  p.key_split = c.key_split;
-  p.nsplit = c.nsplit;
-  p.num_blocks = num_blocks;
-  p.bt_stride = block_table_stride;
-  p.num_seqs = num_groups;
-  p.total_q = num_seqs;
-  p.Hq = num_heads;
-  p.Hkv = num_kv_heads;
-  p.g = g;
-  p.bs_log2 = ilog2(block_size);
-  p.q_tiles = c.q_tiles;
-  p.causal = 0;
-  p.window = 0;
-  p.scale = scale;
-  p.softcap = softcap;
-  if ((st = launch_status(pa::launch_prefill_mfma(p, head_dim, hs)))) return st;
+  // 1) shared prefixes, level by level: the rows of a group are the query
+  //    rows of one "sequence" whose keys are the group's range, read from the
+  //    group's first member's table row, split into key ranges.  Each level
+  //    leaves every row's range end as the next level's (and finally the
+  //    suffix's) first key.
+  for (int i = 0; i < num_levels; ++i) {
+    const pa_prefix_level& v = levels[i];
+    const CascadeLevel& l = c.lv[i];
+    pa::PrefillArgs p;
+    p.out = nullptr;
+    p.q = q;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.block_tables = block_tables;
+    p.context_lens = v.prefix_ends;
+    p.cu_q_lens = v.group_starts;
+    p.alibi = nullptr;
+    p.prefix_lens = nullptr;
+    p.doc_starts = nullptr;
+    p.table_rows = v.group_starts;
+    p.key_starts = v.prefix_starts;
+    p.part_o = part_o + (size_t)l.range0 * plane * head_dim;
+    p.part_lse = part_lse + (size_t)l.range0 * plane;
+    p.row_key_start = key_start;
+    p.chain = i > 0;
+    p.key_split = l.key_split;
+    p.nsplit = l.nsplit;
+    p.num_blocks = num_blocks;
+    p.bt_stride = block_table_stride;
+    p.num_seqs = v.num_groups;
+    p.total_q = num_seqs;
+    p.Hq = num_heads;
+    p.Hkv = num_kv_heads;
+    p.g = g;
+    p.bs_log2 = ilog2(block_size);
+    p.q_tiles = l.q_tiles;
+    p.causal = 0;
+    p.window = 0;
+    p.scale = scale;
+    p.softcap = softcap;
+    if ((st = launch_status(pa::launch_prefill_mfma(p, head_dim, hs)))) return st;
+  }
 
-  // 2) each sequence's own keys [prefix, n): the balanced decode with the
-  //    prefix end as every row's first admissible key, leaving fp32 states
+  // 2) each sequence's own keys [last range end, n): the balanced decode with
+  //    that end as every row's first admissible key, leaving fp32 states
   pa_score_mods dm = {0, softcap, nullptr, nullptr, key_start};
   pa::RowAttnArgs a;
   fill_row_args(a, nullptr, q, k_cache, v_cache, block_tables, block_table_stride, context_lens,
@@ -542,7 +569,7 @@ int paged_attn_decode_cascade(void* out, const void* q, const void* k_cache, con
     if ((st = launch_status(pa::launch_row_merge(a, dtype, head_dim, hs)))) return st;
   }
 
-  // 3) combine prefix and suffix states into out
+  // 3) combine the key ranges' and the suffix's states into out
   pa::CascadeMergeArgs m;
   m.out = out;
   m.part_o = part_o;
@@ -556,7 +583,7 @@ int paged_attn_decode_cascade(void* out, const void* q, const void* k_cache, con
   m.context_lens = context_lens;
   m.rows = num_seqs;
   m.Hq = num_heads;
-  m.nsplit = c.nsplit;
+  m.nsplit = c.nranges;
   m.Hkv = num_kv_heads;
   m.g = c.dec.g;
   m.NG = c.dec.NG;

@@ -82,10 +82,15 @@ struct PrefillArgs {
   // range s writes each row's output over keys [s*key_split, (s+1)*key_split)
   // normalised to part_o [nsplit, total_q, Hq, D] and its log-sum-exp (log2
   // units) to part_lse [nsplit, total_q, Hq], fp32; an empty range gives 0 and
-  // -inf.  Sequence b reads table row table_rows[b] (nullptr: row b), and the
-  // work-groups of range 0 and kv-head 0 store context_lens[b] into
-  // row_key_start[row] for each of its rows (nullptr: not stored).
+  // -inf.  With key_starts, sequence b's keys are [key_starts[b],
+  // context_lens[b]) and range s is counted from key_starts[b].  Sequence b
+  // reads table row table_rows[b] (nullptr: row b), and the work-groups of
+  // range 0 and kv-head 0 store context_lens[b] into row_key_start[row] for
+  // each of its rows (nullptr: not stored); with chain set, the value found
+  // there must be key_starts[b] (checked in debug builds).
   const int32_t* table_rows;
+  const int32_t* key_starts;
+  int32_t chain;
   float* part_o;
   float* part_lse;
   int32_t* row_key_start;

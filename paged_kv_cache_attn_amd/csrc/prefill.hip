@@ -118,12 +118,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
   const int n = a.context_lens[b];
   const int q0 = a.cu_q_lens[b];
   const int Lq = a.cu_q_lens[b + 1] - q0;
+  const int kstart = (ksplit && a.key_starts) ? a.key_starts[b] : 0;  // first key (key-split mode)
   // (key-split mode: the sequences' rows must cover all total_q rows)
   PA_DEVICE_CHECK(!ksplit || ((b > 0 || q0 == 0) && (b + 1 < a.num_seqs || q0 + Lq == a.total_q) && Lq >= 0));
   const int q_start = qtile * QT;
   if (q_start >= Lq) return;
   PA_DEVICE_CHECK((ksplit || Lq <= n) && n >= 0 && (long long)n <= (long long)a.bt_stride << a.bs_log2);
-  PA_DEVICE_CHECK(!ksplit || ((long long)n <= (long long)a.key_split * a.nsplit && Lq <= a.q_tiles * QT));
+  PA_DEVICE_CHECK(!ksplit || (kstart >= 0 && kstart <= n && (long long)(n - kstart) <= (long long)a.key_split * a.nsplit &&
+                              Lq <= a.q_tiles * QT));
 
   // this lane's query row (column of S^T / O^T)
   const int r = wave * 32 + col;
@@ -136,10 +138,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
   int row_lo = (row_ok && a.window > 0) ? max(0, pos - a.window + 1) : 0;
   if (row_ok && a.doc_starts) row_lo = max(row_lo, a.doc_starts[q0 + qi]);
   if (ksplit) {
-    row_lo = max(row_lo, split * a.key_split);
-    row_hi = min(row_hi, (split + 1) * a.key_split);
-    if (a.row_key_start && split == 0 && kvh == 0 && row_ok && head_in == 0 && hl == 0)
+    row_lo = max(row_lo, kstart + split * a.key_split);
+    row_hi = min(row_hi, kstart + (split + 1) * a.key_split);
+    if (a.row_key_start && split == 0 && kvh == 0 && row_ok && head_in == 0 && hl == 0) {
+      PA_DEVICE_CHECK(!a.chain || a.row_key_start[q0 + qi] == kstart);
       a.row_key_start[q0 + qi] = n;
+    }
   }
   if (row_lo > row_hi) row_lo = row_hi;
   const int head = kvh * a.g + head_in;

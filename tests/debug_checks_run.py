@@ -64,10 +64,16 @@ def main():
     t = upload(wc)
     binding.kv_append(t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], t["slot_mapping"])
     out = torch.empty_like(t["q"])
+    # two levels: the groups above, then the first group split in (2, 1) with
+    # 3 more shared keys for the pair (inside the shared sixth block)
     starts = torch.tensor([0, 3, 4, 6], dtype=torch.int32, device="cuda")
     prefix = torch.tensor([16 * 6 - 5, 0, 32], dtype=torch.int32, device="cuda")
+    starts2 = torch.tensor([0, 2, 3, 4, 6], dtype=torch.int32, device="cuda")
+    lo2 = torch.tensor([16 * 6 - 5, 16 * 6 - 5, 0, 32], dtype=torch.int32, device="cuda")
+    hi2 = torch.tensor([16 * 6 - 2, 16 * 6 - 5, 0, 32], dtype=torch.int32, device="cuda")
+    levels = [binding.prefix_level(starts, prefix, 3, 96), binding.prefix_level(starts2, hi2, 2, 3, lo2)]
     binding.paged_attn_decode_cascade(out, t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
-                                      t["context_lens"], starts, prefix, wc.scale, wc.max_context_len, 3, 96)
+                                      t["context_lens"], levels, wc.scale, wc.max_context_len)
     torch.cuda.synchronize()
     worst = max(worst, float(np.max(np.abs(bits_to_f64(to_numpy_bits(out), "bf16") - ref))))
     print(f"debug-check build: max abs err {worst:.3e}", flush=True)

@@ -171,30 +171,39 @@ def test_split_resolution_and_workspace_size():
     assert binding.decode_workspace_size(8, 32, 8, 128, 2048, 0) == (1032 + 64) * 4 * 130 * 4 + 64 * 8
 
 
-def _cascade(**over):
-    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, stride=4, ctx=FAKE, B=8, gs=FAKE, pl=FAKE, G=2, maxg=4,
-             maxp=512, Hq=32, Hkv=8, D=128, bs=16, NB=100, max_ctx=1024, scale=0.1, mods=None, ws=FAKE,
-             ws_bytes=1 << 40, dtype=1)
+def _lv(G=2, maxg=4, maxp=512, gs=FAKE, pe=FAKE, ps=None):
+    return binding.PrefixLevel(gs, ps, pe, G, maxg, maxp)
+
+
+def _cascade(levels=None, **over):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, stride=4, ctx=FAKE, B=8, L=None, Hq=32, Hkv=8, D=128, bs=16,
+             NB=100, max_ctx=1024, scale=0.1, mods=None, ws=FAKE, ws_bytes=1 << 40, dtype=1)
     a.update(over)
+    lv = [_lv()] if levels is None else levels
+    arr = (binding.PrefixLevel * max(1, len(lv)))(*lv)
     return binding.lib().paged_attn_decode_cascade(
-        a["out"], a["q"], a["k"], a["v"], a["bt"], a["stride"], a["ctx"], a["B"], a["gs"], a["pl"], a["G"], a["maxg"],
-        a["maxp"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["NB"], a["max_ctx"], a["scale"], a["mods"], a["ws"],
-        a["ws_bytes"], a["dtype"], None)
+        a["out"], a["q"], a["k"], a["v"], a["bt"], a["stride"], a["ctx"], a["B"], arr,
+        len(lv) if a["L"] is None else a["L"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["NB"], a["max_ctx"], a["scale"],
+        a["mods"], a["ws"], a["ws_bytes"], a["dtype"], None)
 
 
 def test_cascade_validation():
     assert _cascade(dtype=0) == -8          # bf16 only
     assert _cascade(dtype=4) == -8
     assert _cascade(B=-1) == -2
-    assert _cascade(G=0) == -2               # a non-empty batch needs a group
-    assert _cascade(maxg=0) == -2
-    assert _cascade(maxp=-1) == -2
+    assert _cascade(levels=[_lv(G=0)]) == -2           # a non-empty batch needs a group per level
+    assert _cascade(levels=[_lv(maxg=0)]) == -2
+    assert _cascade(levels=[_lv(maxp=-1)]) == -2
+    assert _cascade(levels=[_lv(), _lv(G=0)]) == -2
+    assert _cascade(L=0) == -2                          # at least one level
+    assert _cascade(levels=[_lv()] * 9) == -2           # at most eight
     assert _cascade(Hq=24, Hkv=8) == -3      # group of 3 does not divide 128
     assert _cascade(D=96) == -4
     assert _cascade(bs=8) == -5
     assert _cascade(stride=0) == -11
-    assert _cascade(gs=NULL) == -1
-    assert _cascade(pl=NULL) == -1
+    assert _cascade(levels=[_lv(gs=NULL)]) == -1
+    assert _cascade(levels=[_lv(), _lv(pe=NULL)]) == -1
+    assert _cascade(q=NULL) == -1
     assert _cascade(ws=NULL) == -7
     assert _cascade(ws_bytes=1024) == -7
     assert _cascade(ws=ctypes.c_void_p(0x1008)) == -7  # not 16-byte aligned
@@ -202,27 +211,36 @@ def test_cascade_validation():
               binding.ScoreMods(0, 0.0, None, 0x1000), binding.ScoreMods(0, 0.0, None, None, 0x1000)]:
         assert _cascade(mods=ctypes.pointer(m)) == -14
     assert _cascade(mods=ctypes.pointer(binding.ScoreMods(0, -2.0, None))) == -10
-    assert _cascade(B=0, G=0, maxg=0) == 0   # nothing to do, nothing launched
+    assert _cascade(B=0, L=0) == 0   # nothing to do, nothing launched
+
+
+def _ws(B, levels, Hq, Hkv, D, ctx):
+    arr = (binding.PrefixLevel * max(1, len(levels)))(*levels)
+    return binding.lib().paged_attn_decode_cascade_workspace_size(B, arr, len(levels), Hq, Hkv, D, ctx)
 
 
 def test_cascade_workspace_size():
-    # prefix states [nsplit, B*Hq, D + 1] fp32, suffix state [B*Hq, D + 1], B key
-    # starts, then the balanced decode's workspace; each piece 256-byte aligned
+    # key-range states [ranges, B*Hq, D + 1] fp32 over all levels, the suffix
+    # state [B*Hq, D + 1], B key starts, then the balanced decode's workspace;
+    # each piece 256-byte aligned
     al = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    B, G, maxg, Hq, Hkv, D, ctx, pre = 64, 1, 64, 64, 8, 128, 17408, 16384
-    # 1 group x 8 kv-heads x 4 query tiles = 32 work-groups per key range; 512
-    # wanted (2 per compute unit, 256 units) -> 16 ranges of 16 tiles
-    nsplit = 16
+    B, Hq, Hkv, D, ctx = 64, 64, 8, 128, 17408
     dec = binding.decode_workspace_size(B, Hq, Hkv, D, ctx, 0)
-    want = (al(nsplit * B * Hq * D * 4) + al(nsplit * B * Hq * 4) + al(B * Hq * D * 4) + al(B * Hq * 4) + al(B * 4)
-            + al(dec))
-    assert binding.decode_cascade_workspace_size(B, G, maxg, Hq, Hkv, D, ctx, pre) == want
+
+    def want(ranges):
+        return (al(ranges * B * Hq * D * 4) + al(ranges * B * Hq * 4) + al(B * Hq * D * 4) + al(B * Hq * 4)
+                + al(B * 4) + al(dec))
+    # one group of 64: 1 group x 8 kv-heads x 4 query tiles = 32 work-groups per
+    # key range; 512 wanted (2 per compute unit, 256 units) -> 16 ranges of 16 tiles
+    assert _ws(B, [_lv(G=1, maxg=64, maxp=16384)], Hq, Hkv, D, ctx) == want(16)
     # a short prefix keeps at least 4 tiles per range: 300 keys -> 5 tiles -> 1 range
-    want1 = (al(B * Hq * D * 4) + al(B * Hq * 4) + al(B * Hq * D * 4) + al(B * Hq * 4) + al(B * 4) + al(dec))
-    assert binding.decode_cascade_workspace_size(B, G, maxg, Hq, Hkv, D, ctx, 300) == want1
-    assert binding.decode_cascade_workspace_size(B, 0, maxg, Hq, Hkv, D, ctx, pre) == 0  # invalid
-    assert binding.decode_cascade_workspace_size(B, G, maxg, 24, 8, D, ctx, pre) == 0
-    assert binding.decode_cascade_workspace_size(0, 0, 0, Hq, Hkv, D, ctx, pre) == 0
+    assert _ws(B, [_lv(G=1, maxg=64, maxp=300)], Hq, Hkv, D, ctx) == want(1)
+    # two levels add their ranges: 16 + (8 groups of 8 -> 64 work-groups -> 8 ranges of 4096/8)
+    assert _ws(B, [_lv(G=1, maxg=64, maxp=16384), _lv(G=8, maxg=8, maxp=4096)], Hq, Hkv, D, ctx) == want(16 + 8)
+    assert _ws(B, [_lv(G=0, maxg=64, maxp=16384)], Hq, Hkv, D, ctx) == 0  # invalid
+    assert _ws(B, [], Hq, Hkv, D, ctx) == 0
+    assert _ws(B, [_lv(G=1, maxg=64, maxp=16384)], 24, 8, D, ctx) == 0
+    assert _ws(0, [_lv(G=1, maxg=64, maxp=16384)], Hq, Hkv, D, ctx) == 0
 
 
 def test_bench_util_validation():

@@ -36,19 +36,29 @@ def grouped(seed, groups, private, cuts=None, Hq=32, Hkv=8, D=128, bs=16):
     return w, starts, prefix
 
 
-def gpu_cascade(lib, w, starts, prefix, t=None, workspace=None, **mods):
+def device_level(lib, starts, ends, prefix_starts=None):
+    """One prefix level from host arrays (group starts, range ends, range starts)."""
+    starts = np.asarray(starts, np.int32)
+    ends = np.asarray(ends, np.int32)
+    lo = np.zeros_like(ends) if prefix_starts is None else np.asarray(prefix_starts, np.int32)
+    return lib.prefix_level(torch.from_numpy(starts).cuda(), torch.from_numpy(ends).cuda(),
+                            max(1, int(np.max(np.diff(starts), initial=1))), int(np.max(ends - lo, initial=0)),
+                            None if prefix_starts is None else torch.from_numpy(lo).cuda())
+
+
+def gpu_cascade_levels(lib, w, levels, t=None, workspace=None, **mods):
     t = t or upload(w)
     if len(w.slot_mapping):
         lib.kv_append(t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], t["slot_mapping"])
     out = torch.empty_like(t["q"])
-    gs = torch.from_numpy(starts).cuda()
-    pl = torch.from_numpy(prefix).cuda()
-    max_group = int(np.max(np.diff(starts))) if len(starts) > 1 else 1
     lib.paged_attn_decode_cascade(out, t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
-                                  gs, pl, w.scale, w.max_context_len, max(1, max_group),
-                                  int(prefix.max(initial=0)), workspace=workspace, **mods)
+                                  levels, w.scale, w.max_context_len, workspace=workspace, **mods)
     torch.cuda.synchronize()
     return to_numpy_bits(out)
+
+
+def gpu_cascade(lib, w, starts, prefix, t=None, workspace=None, **mods):
+    return gpu_cascade_levels(lib, w, [device_level(lib, starts, prefix)], t=t, workspace=workspace, **mods)
 
 
 CASES = {
@@ -120,6 +130,90 @@ def test_cascade_workspace_reuse(gpu_lib):
     w1, s1, p1 = grouped(714, [(6, 12), (2, 5)], [3, 0, 50, 1, 7, 200, 9, 1], [0, 4])
     w2, s2, p2 = grouped(715, [(3, 2)], [1, 2, 3], [5])
     t1 = upload(w1)
-    ws = gpu_lib.decode_cascade_workspace(t1["q"], w1.Hkv, len(p1), 6, w1.max_context_len, int(p1.max()))
+    ws = gpu_lib.decode_cascade_workspace(t1["q"], w1.Hkv, [device_level(gpu_lib, s1, p1)], w1.max_context_len)
     assert_close(gpu_cascade(gpu_lib, w1, s1, p1, t=t1, workspace=ws), oracle_out(w1), "bf16")
     assert_close(gpu_cascade(gpu_lib, w2, s2, p2, workspace=ws), oracle_out(w2), "bf16")
+
+
+# ------------------------------------------------------------------------------------------
+# nested prefixes (several levels)
+# ------------------------------------------------------------------------------------------
+
+def nested(seed, specs, private, cuts, Hq=32, Hkv=8, D=128, bs=16):
+    """Decode batch with nested shared prefixes.  ``specs[l]`` lists level l's
+    groups as (members, blocks): the members share ``blocks`` more blocks
+    after the previous levels' (groups nest: each level refines the one
+    before).  The tables of the members are pointed at the group leader's
+    blocks; the prefix ranges end ``cuts[l][g]`` keys before the shared
+    blocks do (a range may end inside a block)."""
+    B = len(private)
+    cum = np.zeros(B, np.int64)
+    for spec in specs:
+        assert sum(m for m, _ in spec) == B
+        cum += np.repeat([nb for _, nb in spec], [m for m, _ in spec])
+    private = np.asarray(private, np.int64)
+    ctx = cum * bs + private
+    w = build_workload(name="nested", seed=seed, kind="decode", dtype="bf16", Hq=Hq, Hkv=Hkv, D=D, bs=bs,
+                       context_lens=ctx, append_lens=(private > 0).astype(np.int64))
+    table = w.block_table
+    levels = []
+    off_blocks = np.zeros(B, np.int64)
+    prev_end = np.zeros(B, np.int64)
+    for spec, cut in zip(specs, cuts):
+        starts = np.concatenate([[0], np.cumsum([m for m, _ in spec])]).astype(np.int32)
+        lo, hi = [], []
+        for g, (m, nb) in enumerate(spec):
+            mem = range(starts[g], starts[g + 1])
+            if m == 0:
+                lo.append(0)
+                hi.append(0)
+                continue
+            lead = starts[g]
+            b0 = int(off_blocks[lead])
+            assert all(off_blocks[b] == b0 and prev_end[b] == prev_end[lead] for b in mem)
+            for b in mem:
+                table[b, b0:b0 + nb] = table[lead, b0:b0 + nb]
+            start = int(prev_end[lead])
+            end = max(start, (b0 + nb) * bs - int(cut[g]))
+            lo.append(start)
+            hi.append(end)
+            for b in mem:
+                off_blocks[b] = b0 + nb
+                prev_end[b] = end
+        levels.append((starts, np.array(hi, np.int32), np.array(lo, np.int32)))
+    return w, levels
+
+
+NESTED = {
+    "two_levels": dict(specs=[[(12, 16)], [(4, 8), (4, 0), (3, 20), (1, 2)]],
+                       private=[1, 40, 0, 7, 300, 1, 2, 3, 64, 0, 90, 5], cuts=[[5], [3, 0, 15, 0]]),
+    "three_levels_g8": dict(specs=[[(9, 4)], [(5, 2), (4, 3)], [(2, 1), (3, 0), (4, 5)]],
+                            private=[1, 2, 30, 0, 17, 200, 1, 5, 64], cuts=[[0], [7, 0], [1, 0, 9]],
+                            Hq=64, Hkv=8),
+    "two_groups_per_level_d64": dict(specs=[[(3, 6), (3, 2)], [(1, 1), (2, 4), (3, 0)]],
+                                     private=[5, 1, 300, 0, 33, 2], cuts=[[0, 9], [2, 0, 0]], Hq=16, Hkv=4,
+                                     D=64),
+}
+
+
+@pytest.mark.parametrize("case", sorted(NESTED))
+def test_nested_prefixes_match_oracle(gpu_lib, case):
+    c = dict(NESTED[case])
+    specs, private, cuts = c.pop("specs"), c.pop("private"), c.pop("cuts")
+    w, lv = nested(800 + len(case), specs, private, cuts, **c)
+    levels = [device_level(gpu_lib, st, hi, lo) for st, hi, lo in lv]
+    assert_close(gpu_cascade_levels(gpu_lib, w, levels), oracle_out(w), "bf16")
+
+
+def test_nested_long_prefixes_sampled(gpu_lib):
+    """64 sequences: a 2048-token prompt for all, then 8 conversations of 8
+    sharing 1021 more tokens, then up to 256 own tokens; several key ranges
+    at both levels.  Oracle on a sample of sequences."""
+    rng = np.random.default_rng(830)
+    private = rng.integers(0, 257, size=64)
+    private[5] = 0
+    w, lv = nested(830, [[(64, 128)], [(8, 64)] * 8], private, [[0], [3] * 8], Hq=64, Hkv=8)
+    levels = [device_level(gpu_lib, st, hi, lo) for st, hi, lo in lv]
+    got = gpu_cascade_levels(gpu_lib, w, levels)
+    seqs = [0, 5, 9, 31, 63]
+    assert_close(got, oracle_out(w, seqs=seqs), "bf16", rows=seqs)
