@@ -69,6 +69,31 @@ int pa_bm_stats(const pa_block_manager* bm, int64_t* free_blocks, int64_t* used_
 /* Reference count of one physical block (0 = free). */
 int pa_bm_block_refcount(const pa_block_manager* bm, int32_t block, int32_t* count);
 
+/*
+ * Shared prefixes of a decode batch, as the levels paged_attn_decode_cascade
+ * takes (pagedattn.h).  seqs[0..n) is the batch in the caller's order (put
+ * sequences forked from one another next to each other: only neighbours in
+ * this order are grouped).  Two neighbours share the leading full blocks
+ * that both tables name identically (blocks shared by fork; a partly filled
+ * block is never counted).  Level 0 groups maximal runs of neighbours that
+ * share at least one block, with the run's common part as range [0, end);
+ * each deeper level splits every group the same way over what its members
+ * share beyond the previous end.  A sequence left alone, or a run that shares
+ * nothing more, continues as a group with an empty range, so every level
+ * partitions the batch and ranges chain.
+ *
+ * Host output arrays, one row per level (at most max_levels, 1..8):
+ * group_starts [max_levels][n + 1], prefix_starts and prefix_ends
+ * [max_levels][n], num_groups [max_levels]; *num_levels gets the levels
+ * used -- 0 when no two neighbours share a block (then the plain decode is
+ * the right call).  Sharing deeper than max_levels stays in the sequences'
+ * own keys (still correct, computed per sequence).  PA_ERR_SEQ for an
+ * unknown id, PA_ERR_SIZE for n < 0 or max_levels outside 1..8.
+ */
+int pa_bm_prefix_levels(const pa_block_manager* bm, const int32_t* seqs, int32_t n, int32_t max_levels,
+                        int32_t* group_starts, int32_t* prefix_starts, int32_t* prefix_ends, int32_t* num_groups,
+                        int32_t* num_levels);
+
 #ifdef __cplusplus
 }
 #endif

@@ -12,6 +12,7 @@ from __future__ import annotations
 import ctypes
 import os
 
+import numpy as np
 import torch
 
 # PAGEDATTN_DEBUG_CHECKS=1 selects the build whose kernels trap on a broken
@@ -79,6 +80,9 @@ SIGNATURES = {
     "pa_bm_table": (_i32, [_vp, _i32, ctypes.POINTER(_i32), _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i64)]),
     "pa_bm_stats": (_i32, [_vp, ctypes.POINTER(_i64), ctypes.POINTER(_i64), ctypes.POINTER(_i64)]),
     "pa_bm_block_refcount": (_i32, [_vp, _i32, ctypes.POINTER(_i32)]),
+    "pa_bm_prefix_levels": (_i32, [_vp, ctypes.POINTER(_i32), _i32, _i32, ctypes.POINTER(_i32),
+                                   ctypes.POINTER(_i32), ctypes.POINTER(_i32), ctypes.POINTER(_i32),
+                                   ctypes.POINTER(_i32)]),
     # include/pagedattn_bench.h (measurement support)
     "pa_bench_stream_read": (_i32, [_vp, _sz, _vp, _vp]),
     "pa_bench_fill": (_i32, [_vp, _sz, ctypes.c_uint32, _vp]),
@@ -416,3 +420,24 @@ class BlockManager:
         c = ctypes.c_int32()
         _check(lib().pa_bm_block_refcount(self._h, int(block), ctypes.byref(c)), "pa_bm_block_refcount")
         return c.value
+
+    def prefix_levels(self, seqs, max_levels: int = 8):
+        """Shared prefixes of the batch ``seqs`` (in this order) as a list of
+        (group_starts, prefix_starts, prefix_ends) int32 arrays, outermost
+        level first; empty when neighbours share nothing."""
+        n = len(seqs)
+        ids = (ctypes.c_int32 * max(1, n))(*[int(x) for x in seqs])
+        gs = (ctypes.c_int32 * (max_levels * (n + 1)))()
+        ps = (ctypes.c_int32 * max(1, max_levels * n))()
+        pe = (ctypes.c_int32 * max(1, max_levels * n))()
+        ng = (ctypes.c_int32 * max_levels)()
+        nl = ctypes.c_int32()
+        _check(lib().pa_bm_prefix_levels(self._h, ids, n, int(max_levels), gs, ps, pe, ng, ctypes.byref(nl)),
+               "pa_bm_prefix_levels")
+        out = []
+        for lvl in range(nl.value):
+            G = ng[lvl]
+            out.append((np.array(gs[lvl * (n + 1): lvl * (n + 1) + G + 1], np.int32),
+                        np.array(ps[lvl * n: lvl * n + G], np.int32),
+                        np.array(pe[lvl * n: lvl * n + G], np.int32)))
+        return out

@@ -5,6 +5,7 @@
 // memory sharing and copy-on-write).  Bookkeeping only; the device work it
 // implies (block copies, appends) is the caller's, through kv_copy_blocks and
 // kv_append.
+#include <algorithm>
 #include <cstdint>
 #include <mutex>
 #include <new>
@@ -191,6 +192,75 @@ int pa_bm_block_refcount(const pa_block_manager* bm, int32_t block, int32_t* cou
   std::lock_guard<std::mutex> lk(bm->mu);
   if (block < 0 || (int64_t)block >= bm->num_blocks) return PA_ERR_SIZE;
   *count = bm->refcount[(size_t)block];
+  return PA_OK;
+}
+
+int pa_bm_prefix_levels(const pa_block_manager* bm, const int32_t* seqs, int32_t n, int32_t max_levels,
+                        int32_t* group_starts, int32_t* prefix_starts, int32_t* prefix_ends, int32_t* num_groups,
+                        int32_t* num_levels) {
+  if (!bm || !num_levels) return PA_ERR_NULL;
+  if (n < 0 || max_levels < 1 || max_levels > 8) return PA_ERR_SIZE;
+  if (n > 0 && (!seqs || !group_starts || !prefix_starts || !prefix_ends || !num_groups)) return PA_ERR_NULL;
+  std::lock_guard<std::mutex> lk(bm->mu);
+  *num_levels = 0;
+  for (int32_t i = 0; i < n; ++i)
+    if (!bm->valid(seqs[i])) return PA_ERR_SEQ;
+  if (n == 0) return PA_OK;
+  const int64_t bs = bm->bs;
+  // shared[i]: tokens in the leading full blocks that sequences i and i+1 both name
+  std::vector<int64_t> shared(n > 1 ? n - 1 : 0, 0);
+  for (int32_t i = 0; i + 1 < n; ++i) {
+    const pa_block_manager::Seq& a = bm->seqs[seqs[i]];
+    const pa_block_manager::Seq& b = bm->seqs[seqs[i + 1]];
+    const int64_t full = std::min(a.len, b.len) / bs;
+    int64_t j = 0;
+    while (j < full && a.blocks[(size_t)j] == b.blocks[(size_t)j]) ++j;
+    shared[(size_t)i] = j * bs;
+  }
+  // groups of the current level: (first, last + 1, range end)
+  struct Group {
+    int32_t lo, hi;
+    int64_t end;
+  };
+  std::vector<Group> cur{{0, n, 0}}, next;
+  int32_t levels = 0;
+  for (int32_t lvl = 0; lvl < max_levels; ++lvl) {
+    next.clear();
+    bool any = false;
+    for (const Group& g : cur) {
+      // maximal runs of neighbours sharing more than g.end
+      int32_t a = g.lo;
+      while (a < g.hi) {
+        int32_t b = a + 1;
+        int64_t end = INT64_MAX;
+        while (b < g.hi && shared[(size_t)(b - 1)] > g.end) {
+          end = std::min(end, shared[(size_t)(b - 1)]);
+          ++b;
+        }
+        if (b - a < 2) end = g.end;  // alone: an empty range
+        if (end > g.end) any = true;
+        next.push_back({a, b, end});
+        a = b;
+      }
+    }
+    if (!any) break;
+    int32_t* gs = group_starts + (size_t)lvl * (n + 1);
+    int32_t* ps = prefix_starts + (size_t)lvl * n;
+    int32_t* pe = prefix_ends + (size_t)lvl * n;
+    // the range of a group starts where its members' previous range ended
+    size_t k = 0;
+    for (size_t i = 0; i < next.size(); ++i) {
+      while (cur[k].hi <= next[i].lo) ++k;
+      gs[i] = next[i].lo;
+      ps[i] = (int32_t)cur[k].end;
+      pe[i] = (int32_t)next[i].end;
+    }
+    gs[next.size()] = n;
+    num_groups[lvl] = (int32_t)next.size();
+    levels = lvl + 1;
+    cur.swap(next);
+  }
+  *num_levels = levels;
   return PA_OK;
 }
 

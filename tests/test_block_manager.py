@@ -4,6 +4,8 @@ the oracle's kv_append and a plain block copy; every live sequence must read
 back exactly its own token history through its table, and the counts must
 add up.  Runs on the CPU (the manager never touches device memory)."""
 
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -142,3 +144,107 @@ def test_fragmentation_matches_the_arithmetic():
     free, used, waste = r.bm.stats()
     held = sum((n + BS - 1) // BS * BS for n in lens)
     assert used * BS == held and waste == held - sum(lens)
+
+
+# ------------------------------------------------------------------------------------------
+# shared prefixes of a decode batch (levels for the two-phase decode)
+# ------------------------------------------------------------------------------------------
+
+def _shared_tokens(r, s, t):
+    """Leading full blocks that two sequences' tables both name, in tokens."""
+    (ra, na), (rb, nb) = r.bm.table(s), r.bm.table(t)
+    j = 0
+    while j < min(na, nb) // BS and ra[j] == rb[j]:
+        j += 1
+    return j * BS
+
+
+def check_levels(r, seqs, levels):
+    n = len(seqs)
+    prev = np.zeros(n, np.int64)
+    for starts, lo, hi in levels:
+        assert starts[0] == 0 and starts[-1] == n and np.all(np.diff(starts) >= 1)
+        assert np.any(hi > lo), "a level with nothing shared"
+        for g in range(len(lo)):
+            mem = list(range(starts[g], starts[g + 1]))
+            rows = [r.bm.table(seqs[i]) for i in mem]
+            for i in mem:
+                assert lo[g] == prev[i]                       # ranges chain per sequence
+                prev[i] = hi[g]
+            assert lo[g] <= hi[g] <= min(ln for _, ln in rows)
+            nbk = (int(hi[g]) + BS - 1) // BS                # the range's blocks are the same ids
+            for row, _ in rows:
+                assert list(row[:nbk]) == list(rows[0][0][:nbk])
+    return prev
+
+
+def test_prefix_levels_by_hand():
+    r = Replay(21, nb=64)
+    a = r.new()
+    r.append(a, 48)                      # 3 full blocks
+    b, c = r.fork(a), r.fork(a)
+    r.append(a, 20)
+    r.append(b, 20)
+    r.append(c, 20)                      # c: 4 full blocks + 4 tokens
+    d = r.fork(c)
+    r.append(d, 5)                       # copy-on-write of c's partly filled 5th block
+    e = r.new()
+    r.append(e, 30)
+    seqs = [a, b, c, d, e]
+    levels = r.bm.prefix_levels(seqs)
+    assert len(levels) == 2
+    (s0, lo0, hi0), (s1, lo1, hi1) = levels
+    assert list(s0) == [0, 4, 5] and list(lo0) == [0, 0] and list(hi0) == [48, 0]
+    assert list(s1) == [0, 1, 2, 4, 5] and list(lo1) == [48, 48, 48, 0] and list(hi1) == [48, 48, 64, 0]
+    check_levels(r, seqs, levels)
+    one = r.bm.prefix_levels(seqs, max_levels=1)
+    assert len(one) == 1 and all(np.array_equal(x, y) for x, y in zip(one[0], levels[0]))
+    assert r.bm.prefix_levels([a, e]) == []                 # neighbours that share nothing
+    assert r.bm.prefix_levels([]) == []
+
+
+@pytest.mark.parametrize("seed", [3, 4, 5])
+def test_prefix_levels_of_random_fork_trees(seed):
+    rng = np.random.default_rng(seed)
+    r = Replay(seed, nb=400)
+    roots = [r.new() for _ in range(3)]
+    for s in roots:
+        r.append(s, int(rng.integers(1, 80)))
+    live = list(roots)
+    order = {s: (i,) for i, s in enumerate(roots)}      # fork-tree path: keeps forks adjacent
+    for _ in range(25):
+        p = live[int(rng.integers(len(live)))]
+        c = r.fork(p)
+        order[c] = order[p] + (len(order),)
+        live.append(c)
+        for s in (p, c):
+            r.append(s, int(rng.integers(0, 40)))
+    seqs = sorted(live, key=lambda s: order[s])
+    levels = r.bm.prefix_levels(seqs)
+    ends = check_levels(r, seqs, levels)
+    # with enough levels, every neighbour pair's shared blocks are grouped exactly
+    assert len(levels) < 8
+    for i in range(len(seqs) - 1):
+        want = _shared_tokens(r, seqs[i], seqs[i + 1])
+        got = 0
+        for starts, lo, hi in levels:
+            g = np.searchsorted(starts, i, side="right") - 1
+            if starts[g + 1] > i + 1:
+                got = max(got, int(hi[g]))
+        assert got == want, (i, got, want)
+    assert np.all(ends <= np.array([r.bm.table(s)[1] for s in seqs]))
+
+
+def test_prefix_levels_argument_checks():
+    r = Replay(22)
+    a = r.new()
+    L = binding.lib()
+    ids = (ctypes.c_int32 * 1)(a)
+    buf = (ctypes.c_int32 * 64)()
+    nl = ctypes.c_int32()
+    assert L.pa_bm_prefix_levels(r.bm._h, ids, 1, 0, buf, buf, buf, buf, ctypes.byref(nl)) == -2
+    assert L.pa_bm_prefix_levels(r.bm._h, ids, 1, 9, buf, buf, buf, buf, ctypes.byref(nl)) == -2
+    assert L.pa_bm_prefix_levels(r.bm._h, ids, -1, 1, buf, buf, buf, buf, ctypes.byref(nl)) == -2
+    bad = (ctypes.c_int32 * 1)(12345)
+    assert L.pa_bm_prefix_levels(r.bm._h, bad, 1, 1, buf, buf, buf, buf, ctypes.byref(nl)) == -13
+    assert L.pa_bm_prefix_levels(r.bm._h, ids, 1, 1, None, buf, buf, buf, ctypes.byref(nl)) == -1

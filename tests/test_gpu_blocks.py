@@ -95,3 +95,75 @@ def test_manager_driven_pools_and_decode(gpu_lib):
         assert np.max(np.abs(out.cpu().numpy() - ref)) <= 1e-4
     finally:
         tbm.HKV, tbm.D = old
+
+
+def test_manager_prefix_levels_drive_the_two_phase_decode(gpu_lib):
+    """A fork tree of bf16 sequences (prompt, beams, sub-beams) kept by the
+    manager on GPU pools; the manager's prefix levels of the batch drive the
+    two-phase decode, which must match the oracle over the same tables."""
+    HKV_, D_, HQ_, BS_ = 8, 128, 32, 16
+    rng = np.random.default_rng(77)
+    nb = 600
+    bm = gpu_lib.BlockManager(nb, BS_)
+    kp = np.full((nb, HKV_, BS_, D_), 0x7FC0, np.uint16)
+    vp = np.full((nb, HKV_, BS_ // 16, D_, 16), 0x7FC0, np.uint16)
+    gk = torch.from_numpy(kp.view(np.int16)).cuda().view(torch.bfloat16)
+    gv = torch.from_numpy(vp.view(np.int16)).cuda().view(torch.bfloat16)
+
+    def append(s, n):
+        nonlocal kp, vp
+        slots, copies = bm.append(s, n)
+        copy_blocks_reference(kp, vp, copies)
+        if copies:
+            src = torch.tensor([c[0] for c in copies], dtype=torch.int32, device="cuda")
+            dst = torch.tensor([c[1] for c in copies], dtype=torch.int32, device="cuda")
+            gpu_lib.kv_copy_blocks(gk, gv, src, dst)
+        kn = bf16_round_bits(rng.standard_normal((n, HKV_, D_)).astype(np.float32))
+        vn = bf16_round_bits(rng.standard_normal((n, HKV_, D_)).astype(np.float32))
+        kp, vp = oracle.kv_append(kp, vp, kn, vn, np.array(slots, np.int32), BS_)
+        to_dev = lambda x: torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)  # noqa: E731
+        gpu_lib.kv_append(to_dev(kn), to_dev(vn), gk, gv, torch.tensor(slots, dtype=torch.int32, device="cuda"))
+
+    prompt = bm.new_sequence()
+    append(prompt, 300)                          # shared system prompt (18 full blocks + 12)
+    order = {prompt: (0,)}
+    beams = [prompt]
+    for i in range(3):
+        c = bm.fork(prompt)
+        order[c] = (0, i + 1)
+        beams.append(c)
+    for s in beams:
+        append(s, int(rng.integers(40, 200)))    # each conversation's own history
+    for s in list(beams[1:3]):
+        for j in range(2):
+            c = bm.fork(s)
+            order[c] = order[s] + (j + 1,)
+            beams.append(c)
+    for s in beams:
+        append(s, int(rng.integers(1, 30)))      # the newest tokens (decode step included)
+    other = bm.new_sequence()
+    append(other, 77)
+    order[other] = (9,)
+    beams.append(other)
+    seqs = sorted(beams, key=lambda s: order[s])
+    levels_host = bm.prefix_levels(seqs)
+    assert len(levels_host) >= 2
+    rows = [bm.table(s) for s in seqs]
+    W = max(len(t) for t, _ in rows)
+    table = np.zeros((len(seqs), W), np.int32)
+    for i, (t, _) in enumerate(rows):
+        table[i, :len(t)] = t
+    lens = np.array([n for _, n in rows], np.int32)
+    q = bf16_round_bits(rng.standard_normal((len(seqs), HQ_, D_)).astype(np.float32))
+    scale = np.float32(1 / np.sqrt(D_))
+    levels = [gpu_lib.prefix_level(torch.from_numpy(st).cuda(), torch.from_numpy(hi).cuda(),
+                                   int(np.max(np.diff(st))), int(np.max(hi - lo)), torch.from_numpy(lo).cuda())
+              for st, lo, hi in levels_host]
+    qd = torch.from_numpy(q.view(np.int16)).cuda().view(torch.bfloat16)
+    out = torch.empty_like(qd)
+    gpu_lib.paged_attn_decode_cascade(out, qd, gk, gv, torch.from_numpy(table).cuda(), torch.from_numpy(lens).cuda(),
+                                      levels, float(scale), int(lens.max()))
+    torch.cuda.synchronize()
+    ref = oracle.paged_attention(q, kp, vp, table, lens, np.arange(len(seqs) + 1), scale, BS_, "bf16")
+    got = oracle.bits_to_f64(out.view(torch.int16).cpu().numpy().view(np.uint16), "bf16")
+    assert np.max(np.abs(got - ref)) <= 2e-2
