@@ -34,8 +34,9 @@
  *   position n - L + i (decode: L = 1, position n - 1).  Query head h reads
  *   kv-head h / (num_heads / num_kv_heads).
  *
- * All calls are asynchronous on `stream` (a hipStream_t; NULL = the null
- * stream).  No call allocates device or host memory, and none keeps state
+ * Tensor pointers (q, out, the pools, new tokens, workspaces) must be 16-byte
+ * aligned: the kernels move 16-byte pieces.  All calls are asynchronous on
+ * `stream` (a hipStream_t; NULL = the null stream).  No call allocates device or host memory, and none keeps state
  * between calls.  Calls are thread-safe.
  *
  * Status: 0 = success.  A negative value is an invalid argument found on the
@@ -79,7 +80,8 @@ enum {
   PA_ERR_TABLE_STRIDE = -11, /* block_table_stride < 1                          */
   PA_ERR_NO_BLOCKS = -12,    /* block manager: the pool is exhausted            */
   PA_ERR_SEQ = -13,          /* block manager: unknown or freed sequence id     */
-  PA_ERR_UNSUPPORTED = -14   /* two-phase decode: a score mod it does not take  */
+  PA_ERR_UNSUPPORTED = -14,  /* two-phase decode: a score mod it does not take  */
+  PA_ERR_ALIGN = -15         /* a tensor pointer is not 16-byte aligned         */
 };
 
 /*

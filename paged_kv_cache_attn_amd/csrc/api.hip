@@ -3,6 +3,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <initializer_list>
 
 #include "pagedattn.h"
 #include "pa_kernels.h"
@@ -169,6 +170,13 @@ void fill_row_args(pa::RowAttnArgs& a, void* out, const void* q, const void* kc,
 
 int launch_status(hipError_t e) { return e == hipSuccess ? PA_OK : (int)e; }
 
+// Every tensor pointer given (NULL ones are checked elsewhere) is 16-byte aligned.
+bool aligned16(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (reinterpret_cast<uintptr_t>(p) % 16 != 0) return false;
+  return true;
+}
+
 // ---- two-phase (shared-prefix) decode ----
 constexpr int kCascadeMinTiles = 4;   // 64-key tiles per prefix key range, at least
 constexpr int kCascadeMaxLevels = 8;  // prefix levels per call
@@ -250,6 +258,7 @@ int decode_impl(bool do_partials, bool do_merge, void* out, const void* q, const
   if (B == 0) return PA_OK;
   if (!out || !context_lens) return PA_ERR_NULL;
   if (do_partials && (!q || !k_cache || !v_cache || !block_tables)) return PA_ERR_NULL;
+  if (!aligned16({out, q, k_cache, v_cache, workspace})) return PA_ERR_ALIGN;
   Shape s;
   decode_shape(B, Hq, Hkv, max_ctx, split, s);
   const size_t need = workspace_bytes_for(B, Hkv, D, s);
@@ -286,6 +295,7 @@ int kv_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache
   if ((st = check_bs(block_size))) return st;
   if (num_tokens == 0) return PA_OK;
   if (!k_new || !v_new || !k_cache || !v_cache || !slot_mapping) return PA_ERR_NULL;
+  if (!aligned16({k_new, v_new, k_cache, v_cache})) return PA_ERR_ALIGN;
   if ((long long)num_tokens * num_kv_heads > 0x7fffffffll) return PA_ERR_SIZE;
   pa::AppendArgs a;
   a.k_new = k_new;
@@ -321,6 +331,7 @@ int kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_blocks, cons
   if ((st = check_bs(block_size))) return st;
   if (num_pairs == 0) return PA_OK;
   if (!k_cache || !v_cache || !src_blocks || !dst_blocks) return PA_ERR_NULL;
+  if (!aligned16({k_cache, v_cache})) return PA_ERR_ALIGN;
   pa::CopyArgs a;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
@@ -402,6 +413,7 @@ int paged_attn_prefill(void* out, const void* q, const int32_t* cu_q_lens, const
   if (num_seqs == 0 || max_q_len == 0) return PA_OK;
   if (!out || !q || !cu_q_lens || !k_cache || !v_cache || !block_tables || !context_lens)
     return PA_ERR_NULL;
+  if (!aligned16({out, q, k_cache, v_cache})) return PA_ERR_ALIGN;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const int g = num_heads / num_kv_heads;
   if (dtype == PA_BF16 && 128 % g == 0) {
@@ -490,6 +502,7 @@ int paged_attn_decode_cascade(void* out, const void* q, const void* k_cache, con
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
   for (int i = 0; i < num_levels; ++i)
     if (!levels[i].group_starts || !levels[i].prefix_ends) return PA_ERR_NULL;
+  if (!aligned16({out, q, k_cache, v_cache})) return PA_ERR_ALIGN;
   CascadeShape c;
   cascade_shape(num_seqs, levels, num_levels, num_heads, num_kv_heads, head_dim, max_context_len, c);
   if (!workspace || workspace_bytes < c.total || reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
@@ -608,6 +621,7 @@ const char* paged_attn_status_string(int status) {
     case PA_ERR_NO_BLOCKS: return "block manager: no free block left in the pool";
     case PA_ERR_SEQ: return "block manager: unknown or freed sequence id";
     case PA_ERR_UNSUPPORTED: return "two-phase decode: only the softcap score mod is supported";
+    case PA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     default: break;
   }
   if (status > 0) return hipGetErrorString(static_cast<hipError_t>(status));

@@ -5,35 +5,90 @@
 // to PagedAttention", newline: KV cache and dynamic growth).  Token t goes to
 // slot s = slot_mapping[t]: block s >> log2(bs), offset s & (bs - 1); K is a
 // token-major row of the (block, kv-head) slab, V a column of its 16-token
-// dimension-major sub-slab.  The copy is of raw bits.  One wavefront per (token, kv-head).  Also the
-// whole-block copy that copy-on-write needs.
+// dimension-major sub-slab.  The copy is of raw bits.  Also the whole-block
+// copy that copy-on-write needs.
 #include "pa_device.h"
 #include "pa_kernels.h"
 
 namespace pa {
 namespace {
 
+// One work-group per (run of 16 consecutive new tokens, kv-head).  K rows
+// are copied with 16-byte pieces.  When the run's slots are the 16 columns of
+// one V sub-slab, in order (a prefill chunk appended to its own blocks), the
+// run's V is transposed through LDS and the whole [D x 16] sub-slab is
+// written with 16-byte stores; otherwise each token's V column is written
+// element by element.
 template <typename W>  // W: uint16_t (bf16) or uint32_t (fp32) -- a raw element
-__global__ __launch_bounds__(64) void kv_append_kernel(const AppendArgs a) {
-  const int t = blockIdx.x / a.Hkv;
-  const int h = blockIdx.x - t * a.Hkv;
-  const int slot = a.slots[t];
-  if (slot < 0) return;
-  PA_DEVICE_CHECK((slot >> a.bs_log2) < a.num_blocks);
-  const int bs = 1 << a.bs_log2;
-  const int blk = slot >> a.bs_log2;
-  const int off = slot & (bs - 1);
+__global__ __launch_bounds__(256) void kv_append_kernel(const AppendArgs a) {
+  constexpr int kRun = 16;
+  constexpr int EPP = 16 / (int)sizeof(W);  // elements per 16-byte piece
+  __shared__ int slot_s[kRun];
+  __shared__ __attribute__((aligned(16))) W vt[kRun * 128];  // [token][d], D <= 128
+  const int h = blockIdx.x % a.Hkv;
+  const int t0 = (blockIdx.x / a.Hkv) * kRun;
+  const int ntok = min(kRun, a.T - t0);
+  const int tid = threadIdx.x;
   const int D = a.D;
-  const size_t slab = ((size_t)blk * a.Hkv + h) * (size_t)bs * D;  // elements
-  const size_t src = ((size_t)t * a.Hkv + h) * D;
-  const W* kn = static_cast<const W*>(a.k_new) + src;
-  const W* vn = static_cast<const W*>(a.v_new) + src;
-  W* kc = static_cast<W*>(a.k_cache) + slab + (size_t)off * D;  // row of the bs x D slab
-  // column off % 16 of the D x 16 sub-slab off / 16
-  W* vc = static_cast<W*>(a.v_cache) + slab + (size_t)(off >> 4) * D * 16 + (off & 15);
-  for (int d = threadIdx.x; d < D; d += 64) {
-    kc[d] = kn[d];
-    vc[(size_t)d * 16] = vn[d];
+  const int bs = 1 << a.bs_log2;
+  if (tid < kRun) slot_s[tid] = tid < ntok ? a.slots[t0 + tid] : -1;
+  __syncthreads();
+  const int s0 = slot_s[0];
+  bool whole = ntok == kRun && s0 >= 0 && (s0 & (kRun - 1)) == 0;
+#pragma unroll
+  for (int i = 1; i < kRun; ++i) whole = whole && slot_s[i] == s0 + i;
+
+  const size_t slab = (size_t)bs * D;  // elements of one (block, kv-head) slab
+  const W* kn = static_cast<const W*>(a.k_new);
+  const W* vn = static_cast<const W*>(a.v_new);
+  W* kc = static_cast<W*>(a.k_cache);
+  W* vc = static_cast<W*>(a.v_cache);
+  // K: 16-byte pieces of each token's row
+  const int ppr = D / EPP;  // pieces per row
+  for (int p = tid; p < kRun * ppr; p += 256) {
+    const int i = p / ppr, c = p - i * ppr;
+    const int slot = slot_s[i];
+    if (slot < 0) continue;
+    PA_DEVICE_CHECK((slot >> a.bs_log2) < a.num_blocks);
+    const int blk = slot >> a.bs_log2, off = slot & (bs - 1);
+    const u32x4 x = *reinterpret_cast<const u32x4*>(kn + ((size_t)(t0 + i) * a.Hkv + h) * D + c * EPP);
+    *reinterpret_cast<u32x4*>(kc + ((size_t)blk * a.Hkv + h) * slab + (size_t)off * D + c * EPP) = x;
+  }
+  if (whole) {
+    // V rows of the run into LDS, then the sub-slab [D][16] with 16-byte stores
+    for (int p = tid; p < kRun * ppr; p += 256) {
+      const int i = p / ppr, c = p - i * ppr;
+      *reinterpret_cast<u32x4*>(&vt[i * D + c * EPP]) =
+          *reinterpret_cast<const u32x4*>(vn + ((size_t)(t0 + i) * a.Hkv + h) * D + c * EPP);
+    }
+    __syncthreads();
+    const int blk = s0 >> a.bs_log2, off = s0 & (bs - 1);
+    PA_DEVICE_CHECK(blk < a.num_blocks);
+    W* sub = vc + ((size_t)blk * a.Hkv + h) * slab + (size_t)(off >> 4) * D * kRun;
+    constexpr int PPD = kRun / EPP;  // pieces per sub-slab row
+    for (int p = tid; p < D * PPD; p += 256) {
+      const int d = p / PPD, c = p - d * PPD;
+      W e[EPP];
+#pragma unroll
+      for (int k = 0; k < EPP; ++k) e[k] = vt[(c * EPP + k) * D + d];
+      *reinterpret_cast<u32x4*>(sub + (size_t)d * kRun + c * EPP) = __builtin_bit_cast(u32x4, e);
+    }
+  } else {
+    // scattered slots: a 16-byte piece of a token's V row per thread, written
+    // element by element down the token's sub-slab column
+    for (int p = tid; p < kRun * ppr; p += 256) {
+      const int i = p / ppr, c = p - i * ppr;
+      const int slot = slot_s[i];
+      if (slot < 0) continue;
+      PA_DEVICE_CHECK((slot >> a.bs_log2) < a.num_blocks);
+      const int blk = slot >> a.bs_log2, off = slot & (bs - 1);
+      const u32x4 x = *reinterpret_cast<const u32x4*>(vn + ((size_t)(t0 + i) * a.Hkv + h) * D + c * EPP);
+      W e[EPP];
+      __builtin_memcpy(e, &x, 16);
+      W* col = vc + ((size_t)blk * a.Hkv + h) * slab + (size_t)(off >> 4) * D * kRun + (off & 15);
+#pragma unroll
+      for (int k = 0; k < EPP; ++k) col[(size_t)(c * EPP + k) * kRun] = e[k];
+    }
   }
 }
 
@@ -62,12 +117,12 @@ hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_kv_append(const AppendArgs& a, int dtype, hipStream_t s) {
-  const long long blocks = (long long)a.T * a.Hkv;
+  const long long blocks = ((long long)a.T + 15) / 16 * a.Hkv;
   if (blocks <= 0) return hipSuccess;
   if (dtype == 1) {
-    hipLaunchKernelGGL(kv_append_kernel<uint16_t>, dim3((unsigned)blocks), dim3(64), 0, s, a);
+    hipLaunchKernelGGL(kv_append_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, s, a);
   } else {
-    hipLaunchKernelGGL(kv_append_kernel<uint32_t>, dim3((unsigned)blocks), dim3(64), 0, s, a);
+    hipLaunchKernelGGL(kv_append_kernel<uint32_t>, dim3((unsigned)blocks), dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -92,10 +92,15 @@ def small(kind="decode", seed=100, dtype="bf16", ctx=(37, 300, 1000), Hq=32, Hkv
 # kv_append
 # ------------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("case", ["gqa_decode", "chunked_prefill", "bs64_f32", "negative_slots"])
+@pytest.mark.parametrize("case", ["gqa_decode", "chunked_prefill", "bs64_f32", "negative_slots",
+                                  "mixed_runs_bf16_d64"])
 def test_kv_append_bit_exact(gpu_lib, case):
     if case == "gqa_decode":
         w = named_workload("gqa_decode_bf16")
+    elif case == "mixed_runs_bf16_d64":
+        # runs of 16 new tokens that are one V sub-slab, that start inside one,
+        # and that straddle two sequences
+        w = small(ctx=(48, 100, 300), append=[40, 100, 37], D=64, Hq=8, Hkv=4, bs=32)
     elif case == "chunked_prefill":
         w = named_workload("chunked_prefill_bf16")
     elif case == "bs64_f32":
