@@ -507,7 +507,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
       for (int i = 0; i < 2 * KSTEPS; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA (S)
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU (P)
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU (P)
         if (i < KPIECES + VPIECES + 1)
           __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM (tile loads, table)
       }
@@ -515,7 +515,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
       for (int i = 0; i < 4 * DT; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA (PV)
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU (row max)
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU (row max)
       }
       if (t + 1 < ntiles) {  // (S_{t+1} of the last tile is stale: no update)
         if (!tile_full(k1)) {  // rare: maxima over admissible keys only
