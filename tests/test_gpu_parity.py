@@ -155,11 +155,13 @@ def test_long_decode_page_size_variants_subset(gpu_lib, bs):
     assert_close(gpu_decode(gpu_lib, w, split=512), oracle_out(w), "bf16")
 
 
-def test_long_decode_full_size_sampled(gpu_lib):
-    """Full 64-sequence workload, split 512 (the benchmarked launch); the oracle
+@pytest.mark.parametrize("split", [0, 512])
+def test_long_decode_full_size_sampled(gpu_lib, split):
+    """Full 64-sequence workload with the benchmarked launch (the balanced
+    split, 0) and the fixed 512-token split measured beside it; the oracle
     checks a sample of sequences: the shortest, the longest and a few others."""
     w = named_workload("long_decode_bf16")
-    got = gpu_decode(gpu_lib, w, split=512)
+    got = gpu_decode(gpu_lib, w, split=split)
     order = np.argsort(w.context_lens)
     seqs = sorted(set([int(order[0]), int(order[-1]), int(order[len(order) // 2]), 3, 17, 42]))
     ref = oracle_out(w, seqs=seqs)
@@ -412,3 +414,39 @@ def test_prefix_lm_and_document_masks(gpu_lib, case):
     ds = _doc_starts(wf, rng)
     assert_close(gpu_prefill(gpu_lib, wf, doc_starts=torch.from_numpy(ds).cuda()),
                  oracle_out(wf, oracle.ScoreMods(causal=True, doc_starts=ds)), "f32")
+
+
+# ------------------------------------------------------------------------------------------
+# large sizes, checked on sampled rows
+# ------------------------------------------------------------------------------------------
+
+def test_decode_of_a_131072_token_row(gpu_lib):
+    """One 128K-token row beside short ones (balanced split: the long row is
+    cut into many pieces); the oracle checks the long row and a short one."""
+    w = build_workload(name="long_row", seed=950, kind="decode", dtype="bf16", Hq=64, Hkv=8, D=128, bs=16,
+                       context_lens=[131072, 40, 3000], append_lens=[1, 1, 1], pool_slack=1.1)
+    got = gpu_decode(gpu_lib, w, split=0)
+    assert_close(got, oracle_out(w, seqs=[0, 1]), "bf16", rows=[0, 1])
+
+
+def test_long_prefill_chunks_sampled_rows(gpu_lib):
+    """Two 2048-row causal chunks after 6144 and 2048 existing tokens, page 64;
+    the oracle (the definition over the gathered keys) checks 96 sampled rows."""
+    w = build_workload(name="long_prefill", seed=951, kind="prefill", dtype="bf16", Hq=32, Hkv=8, D=128,
+                       bs=64, context_lens=[8192, 4096], q_lens=[2048, 2048], append_lens=[2048, 2048],
+                       causal=True, pool_slack=1.1)
+    got = bits_to_f64(gpu_prefill(gpu_lib, w), "bf16")
+    kp, vp = appended_pools(w)
+    rng = np.random.default_rng(951)
+    for b in range(w.B):
+        n = int(w.context_lens[b])
+        r0, r1 = int(w.cu_q_lens[b]), int(w.cu_q_lens[b + 1])
+        rows = np.sort(rng.choice(np.arange(r0, r1), size=48, replace=False))
+        rows[0], rows[-1] = r0, r1 - 1                       # first and last row of the chunk
+        K, V = oracle.gather_sequence(kp, vp, w.block_table[b], n, w.bs)
+        K, V = bits_to_f64(K, "bf16"), bits_to_f64(V, "bf16")
+        Q = bits_to_f64(w.q[rows], "bf16")
+        pos = n - (r1 - r0) + (rows - r0)
+        ref = oracle.attention_dense(Q, K, V, float(w.scale), pos, oracle.ScoreMods(causal=True))
+        err = np.max(np.abs(got[rows] - ref))
+        assert np.all(np.isfinite(got[rows])) and err <= TOL["bf16"], (b, err)
