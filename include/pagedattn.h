@@ -80,8 +80,7 @@ enum {
   PA_ERR_TABLE_STRIDE = -11, /* block_table_stride < 1                          */
   PA_ERR_NO_BLOCKS = -12,    /* block manager: the pool is exhausted            */
   PA_ERR_SEQ = -13,          /* block manager: unknown or freed sequence id     */
-  PA_ERR_UNSUPPORTED = -14,  /* two-phase decode: a score mod it does not take  */
-  PA_ERR_ALIGN = -15         /* a tensor pointer is not 16-byte aligned         */
+  PA_ERR_ALIGN = -14         /* a tensor pointer is not 16-byte aligned         */
 };
 
 /*
@@ -252,10 +251,10 @@ int paged_attn_decode_merge(void* out, const int32_t* context_lens, int32_t num_
  * is at most the sequence's context length; its own keys are the rest.  An
  * empty range (start == end) is allowed.  1 <= num_levels <= 8.
  *
- * Other arguments as paged_attn_decode.  bf16 only, num_heads / num_kv_heads
- * must divide 128; of the score mods only softcap is taken (window, ALiBi,
- * prefix-LM and document masks depend on each row's position and return
- * PA_ERR_UNSUPPORTED).  The workspace is device memory of at least
+ * Other arguments, score mods included, as paged_attn_decode (the shared
+ * parts see each row at its own sequence's position for the window and
+ * ALiBi, and its document start).  bf16 only, num_heads / num_kv_heads must
+ * divide 128.  The workspace is device memory of at least
  * paged_attn_decode_cascade_workspace_size(...) bytes, 16-byte aligned (the
  * size function reads only the levels' host fields).  Breaking the
  * device-side contract (groups, ranges) is undefined behaviour; the debug

@@ -286,7 +286,8 @@ def decode_cascade_workspace(q, num_kv_heads, levels, max_context_len):
 
 
 def paged_attn_decode_cascade(out, q, k_cache, v_cache, block_tables, context_lens, levels, scale,
-                              max_context_len, workspace=None, softcap=0.0, window=0, alibi_slopes=None):
+                              max_context_len, workspace=None, softcap=0.0, window=0, alibi_slopes=None,
+                              prefix_lens=None, doc_starts=None):
     """Decode where sequences share (possibly nested) prefixes (``paged_attn_decode_cascade``).
 
     ``levels``: a list of :func:`prefix_level`, outermost first.  Writes
@@ -296,7 +297,7 @@ def paged_attn_decode_cascade(out, q, k_cache, v_cache, block_tables, context_le
     if workspace is None:
         workspace = decode_cascade_workspace(q, Hkv, levels, max_context_len)
     _need(workspace, "workspace")
-    mp, _keep = _mods(window, softcap, alibi_slopes)
+    mp, _keep = _mods(window, softcap, alibi_slopes, prefix_lens, doc_starts)
     arr = _levels_array(levels)
     code = lib().paged_attn_decode_cascade(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1],

@@ -158,6 +158,7 @@ void fill_row_args(pa::RowAttnArgs& a, void* out, const void* q, const void* kc,
   a.alibi = mods ? mods->alibi_slopes : nullptr;
   a.prefix_lens = mods ? mods->prefix_lens : nullptr;
   a.doc_starts = mods ? mods->doc_starts : nullptr;
+  a.row_floor = nullptr;
   a.state_o = nullptr;
   a.state_lse = nullptr;
   float* w = static_cast<float*>(ws);
@@ -433,6 +434,7 @@ int paged_attn_prefill(void* out, const void* q, const int32_t* cu_q_lens, const
     a.part_lse = nullptr;
     a.row_key_start = nullptr;
     a.key_starts = nullptr;
+    a.q_ctx = nullptr;
     a.chain = 0;
     a.key_split = 0;
     a.nsplit = 1;
@@ -494,8 +496,6 @@ int paged_attn_decode_cascade(void* out, const void* q, const void* k_cache, con
   if (st) return st;
   if (dtype != PA_BF16) return PA_ERR_DTYPE;
   if ((st = check_cascade_levels(num_seqs, levels, num_levels))) return st;
-  if (mods && (mods->window != 0 || mods->alibi_slopes || mods->prefix_lens || mods->doc_starts))
-    return PA_ERR_UNSUPPORTED;
   const int g = num_heads / num_kv_heads;
   if (128 % g != 0) return PA_ERR_HEADS;
   if (num_seqs == 0) return PA_OK;
@@ -520,6 +520,9 @@ int paged_attn_decode_cascade(void* out, const void* q, const void* k_cache, con
   void* dec_ws = ws + c.off_dec;
   hipStream_t hs = static_cast<hipStream_t>(stream);
   const float softcap = mods ? mods->softcap : 0.f;
+  const float* alibi = mods ? mods->alibi_slopes : nullptr;
+  const int32_t window = mods ? mods->window : 0;
+  const int32_t* doc_starts = mods ? mods->doc_starts : nullptr;
   const size_t plane = (size_t)num_seqs * num_heads;
 
   // 1) shared prefixes, level by level: the rows of a group are the query
@@ -538,11 +541,12 @@ int paged_attn_decode_cascade(void* out, const void* q, const void* k_cache, con
     p.block_tables = block_tables;
     p.context_lens = v.prefix_ends;
     p.cu_q_lens = v.group_starts;
-    p.alibi = nullptr;
-    p.prefix_lens = nullptr;
-    p.doc_starts = nullptr;
+    p.alibi = alibi;
+    p.prefix_lens = nullptr;  // (a decode row sees every earlier key anyway)
+    p.doc_starts = doc_starts;
     p.table_rows = v.group_starts;
     p.key_starts = v.prefix_starts;
+    p.q_ctx = context_lens;
     p.part_o = part_o + (size_t)l.range0 * plane * head_dim;
     p.part_lse = part_lse + (size_t)l.range0 * plane;
     p.row_key_start = key_start;
@@ -559,20 +563,21 @@ int paged_attn_decode_cascade(void* out, const void* q, const void* k_cache, con
     p.bs_log2 = ilog2(block_size);
     p.q_tiles = l.q_tiles;
     p.causal = 0;
-    p.window = 0;
+    p.window = window;
     p.scale = scale;
     p.softcap = softcap;
     if ((st = launch_status(pa::launch_prefill_mfma(p, head_dim, hs)))) return st;
   }
 
   // 2) each sequence's own keys [last range end, n): the balanced decode with
-  //    that end as every row's first admissible key, leaving fp32 states
-  pa_score_mods dm = {0, softcap, nullptr, nullptr, key_start};
+  //    that end as a floor on every row's first admissible key (beside the
+  //    caller's mods), leaving fp32 states
   pa::RowAttnArgs a;
   fill_row_args(a, nullptr, q, k_cache, v_cache, block_tables, block_table_stride, context_lens,
-                nullptr, num_seqs, 1, num_heads, num_kv_heads, block_size, c.dec, scale, 1, &dm,
+                nullptr, num_seqs, 1, num_heads, num_kv_heads, block_size, c.dec, scale, 1, mods,
                 workspace_bytes_for(num_seqs, num_kv_heads, head_dim, c.dec) > 0 ? dec_ws : nullptr,
                 head_dim);
+  a.row_floor = key_start;
   a.num_blocks = num_blocks;
   a.state_o = state_o;
   a.state_lse = state_lse;
@@ -620,7 +625,6 @@ const char* paged_attn_status_string(int status) {
     case PA_ERR_TABLE_STRIDE: return "block_table_stride must be >= 1";
     case PA_ERR_NO_BLOCKS: return "block manager: no free block left in the pool";
     case PA_ERR_SEQ: return "block manager: unknown or freed sequence id";
-    case PA_ERR_UNSUPPORTED: return "two-phase decode: only the softcap score mod is supported";
     case PA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
     default: break;
   }

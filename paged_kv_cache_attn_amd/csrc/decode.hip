@@ -133,6 +133,7 @@ __device__ __forceinline__ bool row_range(const RowAttnArgs& a, int slot, RowRan
   if (a.causal && a.prefix_lens) r.hi = min(n, max(r.hi, a.prefix_lens[b]));
   r.lo = a.window > 0 ? max(0, r.pos - a.window + 1) : 0;
   if (a.doc_starts) r.lo = max(r.lo, a.doc_starts[r.qrow]);
+  if (a.row_floor) r.lo = max(r.lo, a.row_floor[r.qrow]);
   if (r.hi < 0) r.hi = 0;
   if (r.lo > r.hi) r.lo = r.hi;
   r.start = r.lo & ~15;

@@ -36,6 +36,7 @@ struct RowAttnArgs {
   const float* alibi;        // [Hq] or nullptr
   const int32_t* prefix_lens;  // [num_seqs] or nullptr (prefix-LM, with causal)
   const int32_t* doc_starts;   // [rows] or nullptr (first admissible key per row)
+  const int32_t* row_floor;    // [rows] or nullptr: a second first-admissible-key bound
   // nullptr: final rows go to out.  Else (two-phase decode) each row's
   // normalised output goes to state_o [rows, Hq, D] and its log-sum-exp
   // (log2 units of the scaled scores) to state_lse [rows, Hq], in fp32.
@@ -90,6 +91,9 @@ struct PrefillArgs {
   // there must be key_starts[b] (checked in debug builds).
   const int32_t* table_rows;
   const int32_t* key_starts;
+  // key-split mode: nullptr, or per row the context length of the decode row
+  // it is (the row sits at position q_ctx[row] - 1, for window and ALiBi)
+  const int32_t* q_ctx;
   int32_t chain;
   float* part_o;
   float* part_lse;

@@ -132,7 +132,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
   const int head_in = r / QT;
   const int qi = q_start + (r - head_in * QT);
   const bool row_ok = qi < Lq;
-  const int pos = n - Lq + qi;
+  // (key-split rows of decode rows sit at their own sequence's last position)
+  const int pos = (ksplit && a.q_ctx) ? (row_ok ? a.q_ctx[q0 + qi] - 1 : 0) : n - Lq + qi;
   int row_hi = row_ok ? (a.causal ? min(n, pos + 1) : n) : 0;
   if (row_ok && a.causal && a.prefix_lens) row_hi = min(n, max(row_hi, a.prefix_lens[b]));
   int row_lo = (row_ok && a.window > 0) ? max(0, pos - a.window + 1) : 0;

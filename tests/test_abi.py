@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     assert binding.status_string(0) == "ok"
-    for code in range(-15, 0):
+    for code in range(-14, 0):
         s = binding.status_string(code)
         assert s and s != "unknown status", code
     assert binding.status_string(-99) == "unknown status"
@@ -73,8 +73,8 @@ def test_kv_append_validation():
     assert _append(k_cache=NULL) == -1
     assert _append(slots=NULL) == -1
     assert _append(T=0, k_new=NULL, v_new=NULL, k_cache=NULL, v_cache=NULL, slots=NULL) == 0  # no-op
-    assert _append(v_cache=ctypes.c_void_p(0x1002)) == -15   # not 16-byte aligned
-    assert _append(k_new=ctypes.c_void_p(0x1008)) == -15
+    assert _append(v_cache=ctypes.c_void_p(0x1002)) == -14   # not 16-byte aligned
+    assert _append(k_new=ctypes.c_void_p(0x1008)) == -14
 
 
 def _decode(fn="paged_attn_decode", **over):
@@ -114,8 +114,8 @@ def test_decode_validation(fn):
     bad = binding.ScoreMods(0, float("inf"), None)
     assert _decode(fn, mods=ctypes.pointer(bad)) == -10
     assert _decode(fn, B=0) == 0  # nothing to do, nothing launched
-    assert _decode(fn, q=ctypes.c_void_p(0x1004)) == -15
-    assert _decode(fn, ws=ctypes.c_void_p(0x1010 + 8)) == -15
+    assert _decode(fn, q=ctypes.c_void_p(0x1004)) == -14
+    assert _decode(fn, ws=ctypes.c_void_p(0x1010 + 8)) == -14
 
 
 def test_merge_validation():
@@ -146,7 +146,7 @@ def test_prefill_validation():
     assert _prefill(v=NULL) == -1
     bad = binding.ScoreMods(0, -1.0, None)
     assert _prefill(mods=ctypes.pointer(bad)) == -10
-    assert _prefill(out=ctypes.c_void_p(0x1001)) == -15
+    assert _prefill(out=ctypes.c_void_p(0x1001)) == -14
     assert _prefill(maxq=0) == 0
     assert _prefill(B=0) == 0
 
@@ -212,11 +212,9 @@ def test_cascade_validation():
     assert _cascade(ws=NULL) == -7
     assert _cascade(ws_bytes=1024) == -7
     assert _cascade(ws=ctypes.c_void_p(0x1008)) == -7  # not 16-byte aligned
-    assert _cascade(k=ctypes.c_void_p(0x1008)) == -15
-    for m in [binding.ScoreMods(64, 0.0, None), binding.ScoreMods(0, 0.0, 0x1000),
-              binding.ScoreMods(0, 0.0, None, 0x1000), binding.ScoreMods(0, 0.0, None, None, 0x1000)]:
-        assert _cascade(mods=ctypes.pointer(m)) == -14
+    assert _cascade(k=ctypes.c_void_p(0x1008)) == -14
     assert _cascade(mods=ctypes.pointer(binding.ScoreMods(0, -2.0, None))) == -10
+    assert _cascade(mods=ctypes.pointer(binding.ScoreMods(-3, 0.0, None))) == -10
     assert _cascade(B=0, L=0) == 0   # nothing to do, nothing launched
 
 
@@ -271,7 +269,7 @@ def test_copy_blocks_validation():
     assert L.kv_copy_blocks(FAKE, FAKE, FAKE, FAKE, 2, 8, 128, 16, 10, 7, None) == -8
     assert L.kv_copy_blocks(NULL, FAKE, FAKE, FAKE, 2, 8, 128, 16, 10, 1, None) == -1
     assert L.kv_copy_blocks(NULL, NULL, NULL, NULL, 0, 8, 128, 16, 10, 1, None) == 0  # nothing to do
-    assert L.kv_copy_blocks(FAKE, ctypes.c_void_p(0x1004), FAKE, FAKE, 2, 8, 128, 16, 10, 1, None) == -15
+    assert L.kv_copy_blocks(FAKE, ctypes.c_void_p(0x1004), FAKE, FAKE, 2, 8, 128, 16, 10, 1, None) == -14
 
 
 def test_block_manager_argument_checks():

@@ -217,3 +217,55 @@ def test_nested_long_prefixes_sampled(gpu_lib):
     got = gpu_cascade_levels(gpu_lib, w, levels)
     seqs = [0, 5, 9, 31, 63]
     assert_close(got, oracle_out(w, seqs=seqs), "bf16", rows=seqs)
+
+
+# ------------------------------------------------------------------------------------------
+# score mods through the two-phase decode
+# ------------------------------------------------------------------------------------------
+
+def _mods_for(w, seed, window=0, softcap=0.0, alibi=False, docs=False):
+    """Device mods and the oracle's ScoreMods for a decode batch."""
+    rng = np.random.default_rng(seed)
+    kw, om = {}, dict(window=window, softcap=softcap)
+    if window:
+        kw["window"] = window
+    if softcap:
+        kw["softcap"] = softcap
+    if alibi:
+        slopes = (2.0 ** (-8.0 * np.arange(1, w.Hq + 1) / w.Hq)).astype(np.float32)
+        kw["alibi_slopes"] = torch.from_numpy(slopes).cuda()
+        om["alibi_slopes"] = slopes
+    if docs:
+        # each row's document starts somewhere in its context (inside a shared range too)
+        starts = np.array([int(rng.integers(0, max(1, n))) for n in w.context_lens], np.int32)
+        kw["doc_starts"] = torch.from_numpy(starts).cuda()
+        om["doc_starts"] = starts
+    return kw, oracle.ScoreMods(**om)
+
+
+MOD_CASES = {
+    "window_cuts_prefix": dict(window=150),
+    "alibi": dict(alibi=True),
+    "documents": dict(docs=True),
+    "all": dict(window=333, softcap=3.0, alibi=True, docs=True),
+}
+
+
+@pytest.mark.parametrize("mods", sorted(MOD_CASES))
+def test_cascade_mods_single_level(gpu_lib, mods):
+    c = dict(CASES["mixed"])
+    groups, private, cuts = c.pop("groups"), c.pop("private"), c.pop("cuts")
+    w, starts, prefix = grouped(760, groups, private, cuts, **c)
+    kw, om = _mods_for(w, 761, **MOD_CASES[mods])
+    got = gpu_cascade(gpu_lib, w, starts, prefix, **kw)
+    assert_close(got, oracle_out(w, om), "bf16")
+
+
+@pytest.mark.parametrize("mods", ["window_cuts_prefix", "all"])
+def test_cascade_mods_nested(gpu_lib, mods):
+    c = dict(NESTED["two_levels"])
+    specs, private, cuts = c.pop("specs"), c.pop("private"), c.pop("cuts")
+    w, lv = nested(770, specs, private, cuts, **c)
+    kw, om = _mods_for(w, 771, **MOD_CASES[mods])
+    levels = [device_level(gpu_lib, st, hi, lo) for st, hi, lo in lv]
+    assert_close(gpu_cascade_levels(gpu_lib, w, levels, **kw), oracle_out(w, om), "bf16")
