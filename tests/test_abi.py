@@ -288,3 +288,13 @@ def test_debug_check_build_exports_the_same_symbols():
     out = os.popen(f"nm -D --defined-only {debug}").read()
     exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
     assert set(declared_functions()) <= exported
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """No fallback: without the built library every call raises."""
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "_LIB_PATH", str(tmp_path / "libpagedattn.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        binding.lib()
+    with pytest.raises(RuntimeError, match="missing"):
+        binding.decode_workspace_size(8, 32, 8, 128, 2048)
