@@ -115,10 +115,27 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
   const int b = (flat % BH) / a.Hkv;
   const int kvh = flat % a.Hkv;
 
+  // The sequence's lengths and the block-table entries of its first three
+  // tiles, read together and waited for once: scalar loads return out of
+  // order, so any use waits for all of them, and reading the entries only
+  // after the work-group's key range is known would add a memory round trip.
+  // Without a window, document starts or a key split every row's range starts
+  // at key 0, and so does the first tile; an entry is used only then, and
+  // only if its block lies within the sequence (see the prologue below).  The
+  // index is clamped to the table row, so the read stays inside the table.
+  const bool spec = !ksplit && a.window <= 0 && a.doc_starts == nullptr;
   const int n = a.context_lens[b];
   const int q0 = a.cu_q_lens[b];
   const int Lq = a.cu_q_lens[b + 1] - q0;
+  int spec_blk[3];
+  {
+    const int32_t* row = a.block_tables + (size_t)b * a.bt_stride;
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+      spec_blk[t] = __builtin_nontemporal_load(row + min((64 * t + 16 * wave) >> a.bs_log2, a.bt_stride - 1));
+  }
   const int kstart = (ksplit && a.key_starts) ? a.key_starts[b] : 0;  // first key (key-split mode)
+  asm volatile("" ::"s"(n), "s"(q0), "s"(Lq), "s"(kstart), "s"(spec_blk[0]), "s"(spec_blk[1]), "s"(spec_blk[2]));
   // (key-split mode: the sequences' rows must cover all total_q rows)
   PA_DEVICE_CHECK(!ksplit || ((b > 0 || q0 == 0) && (b + 1 < a.num_seqs || q0 + Lq == a.total_q) && Lq >= 0));
   const int q_start = qtile * QT;
@@ -148,6 +165,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
   }
   if (row_lo > row_hi) row_lo = row_hi;
   const int head = kvh * a.g + head_in;
+
+  // Q^T operand (B of S^T): this lane's row, dims 16*ks + 8*hl .. +8 (read
+  // here, so that it overlaps the work-group reduction below)
+  bf16x8 qb[KSTEPS];
+  {
+    const char* qrow = static_cast<const char*>(a.q) + ((size_t)(q0 + (row_ok ? qi : 0)) * a.Hq + head) * D * 2;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      u32x4 x = row_ok ? load16(qrow + (16 * ks + 8 * hl) * 2) : u32x4{0, 0, 0, 0};
+      qb[ks] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
 
   // Key range of the whole work-group (uniform): keys [wg_lo, wg_hi) are
   // admissible for some row, keys [safe_lo, safe_hi) for every row.
@@ -239,17 +268,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
       buffer_load_lds16(vb, v_off[it], soff, (lds_ptr)(lv + q * 1024));
     }
   };
-
-  // Q^T operand (B of S^T): this lane's row, dims 16*ks + 8*hl .. +8
-  bf16x8 qb[KSTEPS];
-  {
-    const char* qrow = static_cast<const char*>(a.q) + ((size_t)(q0 + (row_ok ? qi : 0)) * a.Hq + head) * D * 2;
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      u32x4 x = row_ok ? load16(qrow + (16 * ks + 8 * hl) * 2) : u32x4{0, 0, 0, 0};
-      qb[ks] = __builtin_bit_cast(bf16x8, x);
-    }
-  }
 
   const float scale_log2 = a.scale * kLog2e;
   float alibi_slope = 0.f;
@@ -435,9 +453,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
   f32x16 sA[2], sB[2];
   int b1 = 0, b2 = 0, bv = 0;
   if (ntiles > 0) {
-    const int b0 = __builtin_amdgcn_readfirstlane(table_load(0));
-    b1 = __builtin_amdgcn_readfirstlane(table_load(1));
-    b2 = __builtin_amdgcn_readfirstlane(table_load(2));
+    // the entries read at entry hold for tile t if the range starts at key 0,
+    // the tile exists and its block for this wave is within the sequence
+    auto first_entry = [&](int t) {
+      if (spec && k_begin == 0 && t < ntiles && ((64 * t + 16 * wave) >> a.bs_log2) <= last_blk) {
+        PA_DEVICE_CHECK(spec_blk[t] >= 0 && spec_blk[t] < a.num_blocks);
+        return spec_blk[t];
+      }
+      return table_load(t);
+    };
+    const int b0 = __builtin_amdgcn_readfirstlane(first_entry(0));
+    b1 = __builtin_amdgcn_readfirstlane(first_entry(1));
+    b2 = __builtin_amdgcn_readfirstlane(first_entry(2));
     issue_k(tile_k0(0), Par<0>{}, b0);
     issue_v(tile_k0(0), Par<0>{}, b0);
     if (ntiles > 1) issue_k(tile_k0(1), Par<1>{}, b1);

@@ -15,7 +15,7 @@ import torch
 
 import oracle
 from oracle.paged import bits_to_f64
-from workloads import build_workload, named_workload
+from workloads import bf16_round_bits, build_workload, named_workload
 from workloads.device import to_numpy_bits, to_tensor, upload
 
 pytestmark = pytest.mark.gpu
@@ -208,6 +208,30 @@ def test_shared_prefix_equals_private_copies(gpu_lib):
     table[:, :S] = (w.NB + np.arange(w.B * S)).reshape(w.B, S)
     w.k_pool, w.v_pool, w.block_table, w.NB = kp, vp, table.astype(np.int32), kp.shape[0]
     assert np.array_equal(gpu_decode(gpu_lib, w), base)
+
+
+@pytest.mark.parametrize("kind", ["prefill", "decode"])
+def test_running_max_moves_many_times(gpu_lib, kind):
+    """Two fresh sequences (every key arrives through kv_append, in position
+    order) whose key magnitudes grow up to 15-fold along the batch, with the
+    queries doubled: later tiles keep raising each row's maximum past the lazy
+    rescale threshold, so O and l are rescaled many times per row.  V is
+    scaled by 0.4 so that outputs stay below 2 in magnitude, where the
+    absolute bound is not dominated by the bf16 rounding of the output itself
+    (half an ulp is at most 1/256 there, 1/64 at 4)."""
+    prefill = kind == "prefill"
+    w = small(kind, ctx=(1100, 400), q_lens=[1100, 400] if prefill else None, append=[1100, 400], causal=prefill,
+              seed=5)
+    k = bits_to_f64(w.k_new, "bf16")
+    grow = 1.0 + np.arange(k.shape[0], dtype=np.float64) / 100.0
+    w.k_new = bf16_round_bits((k * grow[:, None, None]).astype(np.float32))
+    w.v_new = bf16_round_bits((bits_to_f64(w.v_new, "bf16") * 0.4).astype(np.float32))
+    w.q = bf16_round_bits((bits_to_f64(w.q, "bf16") * 2.0).astype(np.float32))
+    if prefill:
+        assert_close(gpu_prefill(gpu_lib, w), oracle_out(w, causal=True), "bf16")
+    else:
+        for split in (0, 64, -1):
+            assert_close(gpu_decode(gpu_lib, w, split=split), oracle_out(w), "bf16")
 
 
 def test_one_token_context_returns_v_row_exactly(gpu_lib):
