@@ -143,12 +143,20 @@ PAGE_SIZES = (16, 32, 64, 128, 256)
 
 def fragmentation(context_lens):
     """Internal fragmentation of a paged pool: unused slots of every sequence's
-    last block over all slots it holds, per page size (pure arithmetic)."""
+    last page over all slots it holds (pure arithmetic), per fixed page size,
+    and for pages that double along each sequence from 16 to 256 tokens
+    (the block manager's 1..16-block pages on 16-token blocks: power-of-two
+    growth)."""
     n = np.asarray(context_lens, dtype=np.int64)
     out = {}
     for bs in PAGE_SIZES:
         held = ((n + bs - 1) // bs) * bs
         out[str(bs)] = round(float((held - n).sum() / held.sum()), 5)
+    page, held = 16, np.zeros_like(n)
+    while np.any(held < n):
+        held = np.where(held < n, held + page, held)
+        page = min(2 * page, 256)
+    out["doubling_16_256"] = round(float((held - n).sum() / max(held.sum(), 1)), 5)
     return out
 
 

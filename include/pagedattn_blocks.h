@@ -10,6 +10,16 @@
  * al., "Efficient Memory Management for Large Language Model Serving with
  * PagedAttention", abstract: near-zero waste and flexible sharing).
  *
+ * Pages are aligned runs of 1, 2, 4, ... consecutive blocks, handed out by a
+ * buddy allocator (split on demand, merged with a free buddy on release).  A
+ * sequence's pages have one size, or double along the sequence up to a cap:
+ * power-of-two cache growth, as in "Paged Attention Meets FlexAttention"
+ * (abstract: memory grows at power-of-two allocation steps).  One pool can
+ * hold sequences with different page sizes.  Block tables stay at block
+ * resolution (a page of 2^k blocks is 2^k consecutive entries), so the
+ * attention calls read a mixed pool as an ordinary pool of block_size-token
+ * blocks; pa_bm_create / pa_bm_new_sequence are the one-block-page case.
+ *
  * This is bookkeeping on the host only: it produces the slot_mapping that
  * kv_append consumes, the block-table rows the attention calls read, and the
  * (src, dst) block pairs that kv_copy_blocks must copy before the append.
@@ -31,28 +41,46 @@ extern "C" {
 typedef struct pa_block_manager pa_block_manager;
 
 /* A manager for num_blocks physical blocks of block_size tokens (a power of
- * two in [16, 256]).  *out receives the handle; NULL on failure. */
+ * two in [16, 256]), with pages of one block.  *out receives the handle;
+ * NULL on failure. */
 int pa_bm_create(int64_t num_blocks, int32_t block_size, pa_block_manager** out);
+
+/* The same with pages of up to max_page_blocks blocks (a power of two,
+ * 1..4096).  The pool starts as aligned free pages as large as alignment and
+ * num_blocks allow.  PA_ERR_SIZE for a max_page_blocks out of range. */
+int pa_bm_create_paged(int64_t num_blocks, int32_t block_size, int32_t max_page_blocks, pa_block_manager** out);
 void pa_bm_destroy(pa_block_manager* bm);
 
-/* A new, empty sequence; its id goes to *seq. */
+/* A new, empty sequence with one-block pages; its id goes to *seq. */
 int pa_bm_new_sequence(pa_block_manager* bm, int32_t* seq);
 
-/* A new sequence that shares every block (and the length) of `parent`
+/* A new, empty sequence whose page k (k = 0, 1, ...) has
+ * min(min_page_blocks << k, max_page_blocks) blocks: equal bounds give one
+ * page size, different bounds pages that double along the sequence.  Both
+ * are powers of two with min_page_blocks <= max_page_blocks <= the manager's
+ * max_page_blocks (else PA_ERR_SIZE).  If the pool has no free page of the
+ * size due, the largest smaller free page stands in.  Forks keep the
+ * parent's pages and rule. */
+int pa_bm_new_sequence_paged(pa_block_manager* bm, int32_t min_page_blocks, int32_t max_page_blocks, int32_t* seq);
+
+/* A new sequence that shares every page (and the length) of `parent`
  * (reference counts rise; nothing is copied yet). */
 int pa_bm_fork(pa_block_manager* bm, int32_t parent, int32_t* child);
 
-/* Drop a sequence; blocks whose count falls to zero return to the pool. */
+/* Drop a sequence; pages whose count falls to zero return to the pool. */
 int pa_bm_free_sequence(pa_block_manager* bm, int32_t seq);
 
 /*
- * Reserve slots for ntok new tokens at the end of `seq`.  slots_out[i]
- * (ntok entries) is the pool slot of logical position len + i, as kv_append
- * expects.  If the last block is shared and not full, it is first replaced
- * by a fresh block and the pair (old, new) is appended to copy_src/copy_dst
- * (room for copy_cap pairs; *ncopy receives the count): the caller runs
- * kv_copy_blocks on those pairs before kv_append.  PA_ERR_NO_BLOCKS leaves
- * everything unchanged; PA_ERR_SIZE if ntok < 0 or copy_cap is too small.
+ * Reserve slots for ntok new tokens at the end of `seq`, taking new pages
+ * as needed.  slots_out[i] (ntok entries) is the pool slot of logical
+ * position len + i, as kv_append expects.  If the last page is shared and
+ * has free slots (other owners would write into the same slots), it is
+ * first replaced by a fresh page of the same size, and the (old, new) pairs
+ * of its blocks that hold tokens go to copy_src/copy_dst (room for copy_cap
+ * pairs, at most the page's block count; *ncopy receives the count): the
+ * caller runs kv_copy_blocks on those pairs before kv_append.
+ * PA_ERR_NO_BLOCKS leaves everything unchanged; PA_ERR_SIZE if ntok < 0 or
+ * copy_cap is too small.
  */
 int pa_bm_append(pa_block_manager* bm, int32_t seq, int32_t ntok, int32_t* slots_out,
                  int32_t* copy_src, int32_t* copy_dst, int32_t copy_cap, int32_t* ncopy);
@@ -66,7 +94,12 @@ int pa_bm_table(const pa_block_manager* bm, int32_t seq, int32_t* row, int32_t c
  * use that hold no token (internal fragmentation = waste / (used * bs)). */
 int pa_bm_stats(const pa_block_manager* bm, int64_t* free_blocks, int64_t* used_blocks, int64_t* waste_slots);
 
-/* Reference count of one physical block (0 = free). */
+/* The sequence's pages in order: first block (starts) and size in blocks
+ * (blocks) of the first min(cap, npages) pages; the total goes to *npages. */
+int pa_bm_pages(const pa_block_manager* bm, int32_t seq, int32_t* starts, int32_t* blocks, int32_t cap,
+                int32_t* npages);
+
+/* Reference count of one physical block (0 = free; equal over a page). */
 int pa_bm_block_refcount(const pa_block_manager* bm, int32_t block, int32_t* count);
 
 /*

@@ -71,6 +71,9 @@ SIGNATURES = {
     "kv_copy_blocks": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _i32, _vp]),
     # include/pagedattn_blocks.h (host block manager)
     "pa_bm_create": (_i32, [_i64, _i32, ctypes.POINTER(_vp)]),
+    "pa_bm_create_paged": (_i32, [_i64, _i32, _i32, ctypes.POINTER(_vp)]),
+    "pa_bm_new_sequence_paged": (_i32, [_vp, _i32, _i32, ctypes.POINTER(_i32)]),
+    "pa_bm_pages": (_i32, [_vp, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32), _i32, ctypes.POINTER(_i32)]),
     "pa_bm_destroy": (None, [_vp]),
     "pa_bm_new_sequence": (_i32, [_vp, ctypes.POINTER(_i32)]),
     "pa_bm_fork": (_i32, [_vp, _i32, ctypes.POINTER(_i32)]),
@@ -358,14 +361,18 @@ def kv_copy_blocks(k_cache, v_cache, src_blocks, dst_blocks):
 
 
 class BlockManager:
-    """Host block manager (``include/pagedattn_blocks.h``): allocation, fork by
-    sharing, copy-on-write.  Thin wrapper; all bookkeeping is in the library."""
+    """Host block manager (``include/pagedattn_blocks.h``): allocation of
+    power-of-two pages of blocks, fork by sharing, copy-on-write.  Thin
+    wrapper; all bookkeeping is in the library.  ``max_page_blocks`` > 1 lets
+    sequences take pages of several blocks (``new_sequence``'s bounds)."""
 
-    def __init__(self, num_blocks: int, block_size: int):
+    def __init__(self, num_blocks: int, block_size: int, max_page_blocks: int = 1):
         h = ctypes.c_void_p()
-        _check(lib().pa_bm_create(int(num_blocks), int(block_size), ctypes.byref(h)), "pa_bm_create")
+        _check(lib().pa_bm_create_paged(int(num_blocks), int(block_size), int(max_page_blocks), ctypes.byref(h)),
+               "pa_bm_create_paged")
         self._h = h
         self.block_size = int(block_size)
+        self.max_page_blocks = int(max_page_blocks)
 
     def close(self):
         if self._h:
@@ -378,9 +385,14 @@ class BlockManager:
         except Exception:
             pass
 
-    def new_sequence(self) -> int:
+    def new_sequence(self, min_page_blocks: int = 1, max_page_blocks: int | None = None) -> int:
+        """A new sequence whose page k has min(min_page_blocks << k,
+        max_page_blocks) blocks (max_page_blocks defaults to min_page_blocks:
+        one page size)."""
+        hi = min_page_blocks if max_page_blocks is None else max_page_blocks
         s = ctypes.c_int32()
-        _check(lib().pa_bm_new_sequence(self._h, ctypes.byref(s)), "pa_bm_new_sequence")
+        _check(lib().pa_bm_new_sequence_paged(self._h, int(min_page_blocks), int(hi), ctypes.byref(s)),
+               "pa_bm_new_sequence_paged")
         return s.value
 
     def fork(self, parent: int) -> int:
@@ -394,10 +406,11 @@ class BlockManager:
     def append(self, seq: int, ntok: int):
         """Slots for ``ntok`` new tokens and the (src, dst) block copies to run first."""
         slots = (ctypes.c_int32 * max(1, ntok))()
-        src = (ctypes.c_int32 * 1)()
-        dst = (ctypes.c_int32 * 1)()
+        cap = self.max_page_blocks
+        src = (ctypes.c_int32 * cap)()
+        dst = (ctypes.c_int32 * cap)()
         n = ctypes.c_int32()
-        _check(lib().pa_bm_append(self._h, int(seq), int(ntok), slots, src, dst, 1, ctypes.byref(n)),
+        _check(lib().pa_bm_append(self._h, int(seq), int(ntok), slots, src, dst, cap, ctypes.byref(n)),
                "pa_bm_append")
         return list(slots[:ntok]), [(src[i], dst[i]) for i in range(n.value)]
 
@@ -410,6 +423,15 @@ class BlockManager:
         _check(lib().pa_bm_table(self._h, int(seq), row, nb.value, ctypes.byref(nb), ctypes.byref(ln)),
                "pa_bm_table")
         return list(row[:nb.value]), ln.value
+
+    def pages(self, seq: int):
+        """The sequence's pages in order, as (first block, blocks) pairs."""
+        n = ctypes.c_int32()
+        _check(lib().pa_bm_pages(self._h, int(seq), None, None, 0, ctypes.byref(n)), "pa_bm_pages")
+        st = (ctypes.c_int32 * max(1, n.value))()
+        nb = (ctypes.c_int32 * max(1, n.value))()
+        _check(lib().pa_bm_pages(self._h, int(seq), st, nb, n.value, ctypes.byref(n)), "pa_bm_pages")
+        return [(st[i], nb[i]) for i in range(n.value)]
 
     def stats(self):
         """(free blocks, used blocks, empty slots in used blocks)."""

@@ -1,35 +1,97 @@
-// Host-side block manager of the paged KV cache: a free list of physical
-// blocks, per-block reference counts, per-sequence block tables, fork by
-// sharing, and copy-on-write of a shared, partially filled last block
-// ("Ultimate Guide to PagedAttention": block table, on-demand allocation,
-// memory sharing and copy-on-write).  Bookkeeping only; the device work it
-// implies (block copies, appends) is the caller's, through kv_copy_blocks and
-// kv_append.
+// Host-side block manager of the paged KV cache: per-block reference counts,
+// per-sequence block tables, fork by sharing, and copy-on-write of a shared,
+// partially filled last page ("Ultimate Guide to PagedAttention": block
+// table, on-demand allocation, memory sharing and copy-on-write).
+//
+// Pages are aligned runs of 2^k consecutive blocks, handed out by a buddy
+// allocator (split on demand, merged with a free buddy on release); a
+// sequence's pages are all of one size or double along the sequence, which
+// is the power-of-two cache growth that "Paged Attention Meets
+// FlexAttention" (abstract) reports for its memory curves.  Tables stay at
+// block resolution, so the attention kernels see an ordinary pool of
+// block_size-token blocks whatever the page sizes.  Bookkeeping only; the
+// device work it implies (block copies, appends) is the caller's, through
+// kv_copy_blocks and kv_append.
 #include <algorithm>
 #include <cstdint>
 #include <mutex>
 #include <new>
+#include <set>
 #include <vector>
 
 #include "pagedattn.h"
 #include "pagedattn_blocks.h"
 
 struct pa_block_manager {
+  struct Page {
+    int32_t start;  // first block (a multiple of 2^order)
+    int32_t order;  // 2^order blocks
+  };
   struct Seq {
-    std::vector<int32_t> blocks;  // logical block j -> physical block
-    int64_t len = 0;              // tokens
+    std::vector<int32_t> blocks;  // logical block j -> physical block (every page, expanded)
+    std::vector<Page> pages;
+    int32_t min_order = 0, max_order = 0;  // page k has order min(min_order + k, max_order)
+    int64_t len = 0;                       // tokens
     bool live = false;
   };
   int64_t num_blocks = 0;
   int32_t bs = 0;
-  std::vector<int32_t> refcount;  // per physical block
-  std::vector<int32_t> fill;      // tokens stored in a physical block (max over its owners)
-  std::vector<int32_t> free_list; // stack of free physical blocks
+  int32_t max_order = 0;                  // largest page: 2^max_order blocks
+  std::vector<int32_t> refcount;          // per physical block (equal over a page)
+  std::vector<int32_t> fill;              // tokens stored in a physical block (max over its owners)
+  std::vector<std::set<int32_t>> free_pages;  // per order: first blocks of free pages
+  int64_t free_blocks = 0;
   std::vector<Seq> seqs;
   std::vector<int32_t> free_ids;
   mutable std::mutex mu;
 
   bool valid(int32_t s) const { return s >= 0 && (size_t)s < seqs.size() && seqs[s].live; }
+
+  // A free page of 2^k blocks, splitting a larger one if needed; -1 if none.
+  int32_t take_page(int32_t k) {
+    int32_t j = k;
+    while (j <= max_order && free_pages[(size_t)j].empty()) ++j;
+    if (j > max_order) return -1;
+    const int32_t start = *free_pages[(size_t)j].begin();  // lowest first
+    free_pages[(size_t)j].erase(free_pages[(size_t)j].begin());
+    while (j > k) {  // keep the low half, free the high half
+      --j;
+      free_pages[(size_t)j].insert(start + (1 << j));
+    }
+    for (int32_t b = start; b < start + (1 << k); ++b) {
+      refcount[(size_t)b] = 1;
+      fill[(size_t)b] = 0;
+    }
+    free_blocks -= (int64_t)1 << k;
+    return start;
+  }
+
+  // Return a page whose blocks no sequence names any more, merging it with
+  // its free buddy as long as there is one.
+  void give_page(int32_t start, int32_t k) {
+    for (int32_t b = start; b < start + (1 << k); ++b) {
+      refcount[(size_t)b] = 0;
+      fill[(size_t)b] = 0;
+    }
+    free_blocks += (int64_t)1 << k;
+    while (k < max_order) {
+      const int64_t buddy = (int64_t)start ^ ((int64_t)1 << k);
+      if (buddy + ((int64_t)1 << k) > num_blocks) break;
+      auto it = free_pages[(size_t)k].find((int32_t)buddy);
+      if (it == free_pages[(size_t)k].end()) break;
+      free_pages[(size_t)k].erase(it);
+      start = (int32_t)std::min<int64_t>(start, buddy);
+      ++k;
+    }
+    free_pages[(size_t)k].insert(start);
+  }
+
+  // Drop one owner of a page.
+  void release_page(const Page& p) {
+    bool last = false;
+    for (int32_t b = p.start; b < p.start + (1 << p.order); ++b) last = (--refcount[(size_t)b] == 0);
+    if (last) give_page(p.start, p.order);
+  }
 
   int32_t new_id() {
     if (!free_ids.empty()) {
@@ -41,51 +103,72 @@ struct pa_block_manager {
     return (int32_t)(seqs.size() - 1);
   }
 
-  void release(int32_t blk) {
-    if (--refcount[blk] == 0) {
-      fill[blk] = 0;
-      free_list.push_back(blk);
-    }
-  }
 };
 
 namespace {
 
 bool pow2_block(int32_t bs) { return bs >= 16 && bs <= 256 && (bs & (bs - 1)) == 0; }
+bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+int32_t log2i(int64_t x) {
+  int32_t k = 0;
+  while (((int64_t)1 << k) < x) ++k;
+  return k;
+}
+constexpr int32_t kMaxPageBlocks = 4096;
 
 }  // namespace
 
 extern "C" {
 
-int pa_bm_create(int64_t num_blocks, int32_t block_size, pa_block_manager** out) {
+int pa_bm_create_paged(int64_t num_blocks, int32_t block_size, int32_t max_page_blocks, pa_block_manager** out) {
   if (!out) return PA_ERR_NULL;
   *out = nullptr;
   if (num_blocks < 0 || num_blocks > 0x7fffffffll) return PA_ERR_SIZE;
   if (!pow2_block(block_size)) return PA_ERR_BLOCK_SIZE;
+  if (!pow2(max_page_blocks) || max_page_blocks > kMaxPageBlocks) return PA_ERR_SIZE;
   pa_block_manager* bm = new (std::nothrow) pa_block_manager();
   if (!bm) return PA_ERR_SIZE;
   bm->num_blocks = num_blocks;
   bm->bs = block_size;
+  bm->max_order = log2i(max_page_blocks);
   bm->refcount.assign((size_t)num_blocks, 0);
   bm->fill.assign((size_t)num_blocks, 0);
-  bm->free_list.reserve((size_t)num_blocks);
-  // hand out low block ids first
-  for (int64_t b = num_blocks - 1; b >= 0; --b) bm->free_list.push_back((int32_t)b);
+  bm->free_pages.resize((size_t)bm->max_order + 1);
+  // the pool as aligned free pages, each as large as alignment and size allow
+  int64_t b = 0;
+  while (b < num_blocks) {
+    int32_t k = bm->max_order;
+    while (k > 0 && ((b & (((int64_t)1 << k) - 1)) != 0 || b + ((int64_t)1 << k) > num_blocks)) --k;
+    bm->free_pages[(size_t)k].insert((int32_t)b);
+    b += (int64_t)1 << k;
+  }
+  bm->free_blocks = num_blocks;
   *out = bm;
   return PA_OK;
 }
 
+int pa_bm_create(int64_t num_blocks, int32_t block_size, pa_block_manager** out) {
+  return pa_bm_create_paged(num_blocks, block_size, 1, out);
+}
+
 void pa_bm_destroy(pa_block_manager* bm) { delete bm; }
 
-int pa_bm_new_sequence(pa_block_manager* bm, int32_t* seq) {
+int pa_bm_new_sequence_paged(pa_block_manager* bm, int32_t min_page_blocks, int32_t max_page_blocks, int32_t* seq) {
   if (!bm || !seq) return PA_ERR_NULL;
   std::lock_guard<std::mutex> lk(bm->mu);
+  if (!pow2(min_page_blocks) || !pow2(max_page_blocks) || min_page_blocks > max_page_blocks ||
+      log2i(max_page_blocks) > bm->max_order)
+    return PA_ERR_SIZE;
   const int32_t id = bm->new_id();
   bm->seqs[id] = pa_block_manager::Seq();
+  bm->seqs[id].min_order = log2i(min_page_blocks);
+  bm->seqs[id].max_order = log2i(max_page_blocks);
   bm->seqs[id].live = true;
   *seq = id;
   return PA_OK;
 }
+
+int pa_bm_new_sequence(pa_block_manager* bm, int32_t* seq) { return pa_bm_new_sequence_paged(bm, 1, 1, seq); }
 
 int pa_bm_fork(pa_block_manager* bm, int32_t parent, int32_t* child) {
   if (!bm || !child) return PA_ERR_NULL;
@@ -102,7 +185,7 @@ int pa_bm_free_sequence(pa_block_manager* bm, int32_t seq) {
   if (!bm) return PA_ERR_NULL;
   std::lock_guard<std::mutex> lk(bm->mu);
   if (!bm->valid(seq)) return PA_ERR_SEQ;
-  for (int32_t blk : bm->seqs[seq].blocks) bm->release(blk);
+  for (const pa_block_manager::Page& p : bm->seqs[seq].pages) bm->release_page(p);
   bm->seqs[seq] = pa_block_manager::Seq();
   bm->free_ids.push_back(seq);
   return PA_OK;
@@ -119,38 +202,68 @@ int pa_bm_append(pa_block_manager* bm, int32_t seq, int32_t ntok, int32_t* slots
   *ncopy = 0;
   if (ntok == 0) return PA_OK;
   const int64_t bs = bm->bs;
-  const int64_t in_last = s.len % bs;  // tokens already in the last block
-  const bool cow = in_last != 0 && bm->refcount[s.blocks.back()] > 1;
-  const int64_t new_blocks = (s.len + ntok + bs - 1) / bs - (int64_t)s.blocks.size();
-  const int64_t need = new_blocks + (cow ? 1 : 0);
-  if (need > (int64_t)bm->free_list.size()) return PA_ERR_NO_BLOCKS;
-  if (cow && (copy_cap < 1 || !copy_src || !copy_dst)) return PA_ERR_SIZE;
+  const int64_t cap_tokens = (int64_t)s.blocks.size() * bs;
+  // A shared last page with room left: its owners would write into the same
+  // free slots, so this sequence continues in a fresh page of the same size,
+  // after copying the page's blocks that hold tokens.
+  const bool cow = !s.pages.empty() && cap_tokens > s.len && bm->refcount[(size_t)s.pages.back().start] > 1;
+  int32_t ncow = 0;
   if (cow) {
-    // the shared last block keeps its other owners; this sequence writes into a copy
-    const int32_t old = s.blocks.back();
-    const int32_t fresh = bm->free_list.back();
-    bm->free_list.pop_back();
-    bm->refcount[fresh] = 1;
-    bm->fill[fresh] = (int32_t)in_last;
-    bm->release(old);
-    s.blocks.back() = fresh;
-    copy_src[0] = old;
-    copy_dst[0] = fresh;
-    *ncopy = 1;
+    const pa_block_manager::Page& last = s.pages.back();
+    const int64_t page_first = cap_tokens - ((int64_t)bs << last.order);
+    ncow = (int32_t)((s.len - page_first + bs - 1) / bs);
+    if (copy_cap < ncow || !copy_src || !copy_dst) return PA_ERR_SIZE;
   }
-  for (int64_t i = 0; i < new_blocks; ++i) {
-    const int32_t blk = bm->free_list.back();
-    bm->free_list.pop_back();
-    bm->refcount[blk] = 1;
-    bm->fill[blk] = 0;
-    s.blocks.push_back(blk);
+  // every page this call takes, given back if the pool runs out midway
+  std::vector<pa_block_manager::Page> taken;
+  auto undo = [&]() {
+    for (const pa_block_manager::Page& p : taken) bm->give_page(p.start, p.order);
+    return PA_ERR_NO_BLOCKS;
+  };
+  int32_t cow_start = -1;
+  if (cow) {
+    cow_start = bm->take_page(s.pages.back().order);
+    if (cow_start < 0) return PA_ERR_NO_BLOCKS;
+    taken.push_back({cow_start, s.pages.back().order});
+  }
+  // new pages: page k of the sequence has order min(min_order + k, max_order);
+  // a smaller page stands in when the pool has no page of that size left
+  std::vector<pa_block_manager::Page> added;
+  int64_t cap = cap_tokens;
+  while (cap < s.len + ntok) {
+    const int32_t want = std::min(s.min_order + (int32_t)(s.pages.size() + added.size()), s.max_order);
+    int32_t k = want, start = -1;
+    for (; k >= 0 && start < 0; --k) start = bm->take_page(k);
+    if (start < 0) return undo();
+    const int32_t order = k + 1;
+    taken.push_back({start, order});
+    added.push_back({start, order});
+    cap += bs << order;
+  }
+  // commit
+  if (cow) {
+    pa_block_manager::Page& last = s.pages.back();
+    const size_t first_blk = s.blocks.size() - ((size_t)1 << last.order);
+    for (int32_t i = 0; i < ncow; ++i) {
+      copy_src[i] = last.start + i;
+      copy_dst[i] = cow_start + i;
+      bm->fill[(size_t)(cow_start + i)] = bm->fill[(size_t)(last.start + i)];
+    }
+    for (int32_t i = 0; i < (1 << last.order); ++i) s.blocks[first_blk + (size_t)i] = cow_start + i;
+    bm->release_page(last);
+    last.start = cow_start;
+    *ncopy = ncow;
+  }
+  for (const pa_block_manager::Page& p : added) {
+    s.pages.push_back(p);
+    for (int32_t i = 0; i < (1 << p.order); ++i) s.blocks.push_back(p.start + i);
   }
   for (int32_t i = 0; i < ntok; ++i) {
     const int64_t pos = s.len + i;
     const int32_t blk = s.blocks[(size_t)(pos / bs)];
     slots_out[i] = (int32_t)((int64_t)blk * bs + pos % bs);
     const int32_t f = (int32_t)(pos % bs) + 1;
-    if (f > bm->fill[blk]) bm->fill[blk] = f;
+    if (f > bm->fill[(size_t)blk]) bm->fill[(size_t)blk] = f;
   }
   s.len += ntok;
   return PA_OK;
@@ -181,9 +294,25 @@ int pa_bm_stats(const pa_block_manager* bm, int64_t* free_blocks, int64_t* used_
       waste += bm->bs - bm->fill[(size_t)b];
     }
   }
-  *free_blocks = (int64_t)bm->free_list.size();
+  *free_blocks = bm->free_blocks;
   *used_blocks = used;
   *waste_slots = waste;
+  return PA_OK;
+}
+
+int pa_bm_pages(const pa_block_manager* bm, int32_t seq, int32_t* starts, int32_t* blocks, int32_t cap,
+                int32_t* npages) {
+  if (!bm || !npages) return PA_ERR_NULL;
+  if (cap < 0) return PA_ERR_SIZE;
+  if (cap > 0 && (!starts || !blocks)) return PA_ERR_NULL;
+  std::lock_guard<std::mutex> lk(bm->mu);
+  if (!bm->valid(seq)) return PA_ERR_SEQ;
+  const std::vector<pa_block_manager::Page>& p = bm->seqs[seq].pages;
+  for (size_t i = 0; i < p.size() && i < (size_t)cap; ++i) {
+    starts[i] = p[i].start;
+    blocks[i] = 1 << p[i].order;
+  }
+  *npages = (int32_t)p.size();
   return PA_OK;
 }
 

@@ -77,6 +77,24 @@ int main(void) {
   EXPECT(pa_bm_free_sequence(bm, b) == PA_OK && pa_bm_free_sequence(bm, b) == PA_ERR_SEQ);
   pa_bm_destroy(bm);
 
+  /* pages of several blocks: 1, 2, 4 blocks along a sequence, 4-block pages for its fork */
+  EXPECT(pa_bm_create_paged(64, 16, 3, &bm) == PA_ERR_SIZE && bm == NULL);
+  EXPECT(pa_bm_create_paged(64, 16, 4, &bm) == PA_OK && bm != NULL);
+  EXPECT(pa_bm_new_sequence_paged(bm, 1, 8, &a) == PA_ERR_SIZE);
+  EXPECT(pa_bm_new_sequence_paged(bm, 1, 4, &a) == PA_OK);
+  int32_t pslots[128];
+  EXPECT(pa_bm_append(bm, a, 100, pslots, src, dst, 4, &ncopy) == PA_OK && ncopy == 0);
+  int32_t pst[8], pnb[8], np = -1;
+  EXPECT(pa_bm_pages(bm, a, pst, pnb, 8, &np) == PA_OK && np == 3 && pnb[0] == 1 && pnb[1] == 2 && pnb[2] == 4);
+  EXPECT(pst[1] % 2 == 0 && pst[2] % 4 == 0);
+  EXPECT(pa_bm_fork(bm, a, &b) == PA_OK);
+  /* 100 tokens: 48 in the first two pages, 52 in the shared 4-block last page, whose 4 blocks
+     all hold tokens and are copied (room for 2 pairs is too little) */
+  EXPECT(pa_bm_append(bm, b, 1, pslots, src, dst, 2, &ncopy) == PA_ERR_SIZE);
+  EXPECT(pa_bm_append(bm, b, 1, pslots, src, dst, 4, &ncopy) == PA_OK && ncopy == 4 && src[0] == pst[2]);
+  EXPECT(pa_bm_stats(bm, &fr, &used, &waste) == PA_OK && used == 11 && fr == 53);
+  pa_bm_destroy(bm);
+
   if (failures) return 1;
   printf("ok\n");
   return 0;

@@ -37,7 +37,11 @@ def test_fragmentation_arithmetic():
     f = bench.fragmentation(np.array([1, 16, 17]))
     assert f["16"] == round(30 / 64, 5)
     assert f["32"] == round(62 / 96, 5)
-    assert set(f) == {"16", "32", "64", "128", "256"}
+    assert set(f) == {"16", "32", "64", "128", "256", "doubling_16_256"}
+    # pages doubling from 16 to 256 tokens: capacities 16, 48, 112, 240, 496, 752, ...
+    # lengths 1, 16, 17, 500 hold 16, 16, 48, 752 slots, 15 + 0 + 31 + 252 unused
+    g = bench.fragmentation(np.array([1, 16, 17, 500]))
+    assert g["doubling_16_256"] == round(298 / 832, 5)
 
 
 def test_traffic_record_only_for_the_current_kernel_source(tmp_path, monkeypatch):

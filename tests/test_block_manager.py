@@ -25,16 +25,16 @@ def copy_blocks_reference(k_pool, v_pool, pairs):
 class Replay:
     """Manager + numpy pools + each sequence's token history."""
 
-    def __init__(self, seed, nb=NB):
+    def __init__(self, seed, nb=NB, max_page=1):
         self.rng = np.random.default_rng(seed)
-        self.bm = binding.BlockManager(nb, BS)
+        self.bm = binding.BlockManager(nb, BS, max_page)
         self.nb = nb
         self.k = np.full((nb, HKV, BS, D), np.nan, np.float32)
         self.v = np.full((nb, HKV, BS // min(BS, 16), D, min(BS, 16)), np.nan, np.float32)
         self.hist = {}
 
-    def new(self):
-        s = self.bm.new_sequence()
+    def new(self, min_page=1, max_page=None):
+        s = self.bm.new_sequence(min_page, max_page)
         self.hist[s] = (np.zeros((0, HKV, D), np.float32), np.zeros((0, HKV, D), np.float32))
         return s
 
@@ -60,15 +60,26 @@ class Replay:
     def check(self):
         refs = np.zeros(self.nb, np.int64)
         waste = {}
+        pages = {}  # first block -> size, over every live sequence
         for s, (hk, hv) in self.hist.items():
             row, n = self.bm.table(s)
             assert n == len(hk)
-            assert len(row) == (n + BS - 1) // BS
+            # the table is the pages expanded; pages are aligned runs of 2^k blocks,
+            # the last one holding the last token
+            pg = self.bm.pages(s)
+            assert row == [b for st, nb in pg for b in range(st, st + nb)]
+            assert all(nb & (nb - 1) == 0 and st % nb == 0 for st, nb in pg)
+            assert len(row) >= (n + BS - 1) // BS and (not pg or len(row) - pg[-1][1] < max(n, 1) / BS)
+            for st, nb in pg:
+                assert pages.setdefault(st, nb) == nb
             K, V = oracle.gather_sequence(self.k, self.v, np.array(row), n, BS)
             assert np.array_equal(K.transpose(1, 0, 2), hk) and np.array_equal(V.transpose(1, 0, 2), hv)
             for j, b in enumerate(row):
                 refs[b] += 1
-                waste[b] = min(waste.get(b, BS), BS - min(BS, n - j * BS))
+                waste[b] = min(waste.get(b, BS), BS - max(0, min(BS, n - j * BS)))
+        # pages of different sequences are the same page or disjoint
+        spans = sorted(pages.items())
+        assert all(a + na <= b for (a, na), (b, _) in zip(spans, spans[1:]))
         for b in range(self.nb):
             assert self.bm.refcount(b) == refs[b], b
         free, used, w = self.bm.stats()
@@ -134,6 +145,129 @@ def test_exhaustion_changes_nothing_and_ids_are_checked():
     with pytest.raises(ValueError, match="sequence"):
         r.bm.fork(12345)
     r.check()
+
+
+# ---- pages of several blocks (power-of-two sizes, buddy allocation) ----
+
+def test_pages_double_along_a_sequence():
+    r = Replay(7, nb=200, max_page=8)
+    a = r.new(1, 8)
+    for _ in range(53):
+        r.append(a, 7)                   # 371 tokens: capacity 1+2+4+8+8 = 23 blocks = 368 < 371
+    assert [n for _, n in r.bm.pages(a)] == [1, 2, 4, 8, 8, 8]
+    r.check()
+
+
+def test_page_sizes_mix_in_one_pool():
+    r = Replay(8, nb=640, max_page=16)
+    seqs = [r.new(k, k) for k in (1, 2, 4, 8, 16)] + [r.new(1, 16), r.new(2, 4)]
+    for _ in range(25):
+        for q in seqs:
+            r.append(q, int(r.rng.integers(1, 40)))
+    for q, k in zip(seqs, (1, 2, 4, 8, 16)):
+        assert {n for _, n in r.bm.pages(q)} == {k}
+    r.check()
+
+
+def test_copy_on_write_copies_the_filled_blocks_of_a_shared_page():
+    r = Replay(9, nb=64, max_page=4)
+    a = r.new(4, 4)
+    r.append(a, 40)                      # one 4-block page; blocks 0..2 hold tokens
+    b = r.fork(a)
+    _, copies = r.append(b, 5)           # the shared page has room: b continues in a fresh page
+    (pa_start, _), (pb_start, _) = r.bm.pages(a)[0], r.bm.pages(b)[0]
+    assert copies == [(pa_start + i, pb_start + i) for i in range(3)]
+    assert r.bm.refcount(pa_start) == 1 and r.bm.refcount(pb_start + 3) == 1
+    _, copies = r.append(a, 30)          # a's page is its own again: written in place, then a new page
+    assert copies == []
+    r.check()
+    c = r.fork(b)
+    r.append(c, 100)
+    r.free(b)
+    r.check()
+    r.free(a)
+    r.free(c)
+    assert r.bm.stats() == (64, 0, 0)
+
+
+def test_buddies_merge_back_on_release():
+    bm = binding.BlockManager(64, BS, 16)          # four aligned 16-block pages
+    seqs = [bm.new_sequence(1, 16) for _ in range(6)]
+    for q in seqs:
+        bm.append(q, 16 * 5)                      # pages of 1, 2 and 4 blocks each
+    for q in seqs:
+        bm.free(q)
+    big = [bm.new_sequence(16, 16) for _ in range(4)]
+    for q in big:
+        bm.append(q, 16 * 16)
+    assert sorted(st for q in big for st, _ in bm.pages(q)) == [0, 16, 32, 48]
+    assert bm.stats() == (0, 64, 0)
+
+
+def test_smaller_pages_stand_in_when_the_pool_is_fragmented():
+    bm = binding.BlockManager(16, BS, 8)
+    ones = [bm.new_sequence() for _ in range(16)]
+    for q in ones:
+        bm.append(q, 1)
+    for q in ones[1::2]:
+        bm.free(q)                                # every other block free: no 2-block page left
+    big = bm.new_sequence(8, 8)
+    bm.append(big, 16 * 8)
+    assert [n for _, n in bm.pages(big)] == [1] * 8
+    assert bm.stats()[0] == 0
+
+
+def test_paged_exhaustion_changes_nothing_and_arguments_are_checked():
+    r = Replay(10, nb=12, max_page=4)
+    a = r.new(4, 4)
+    r.append(a, 16 * 8)                  # two full 4-block pages
+    b = r.fork(a)
+    r.append(b, 16)                      # a third page for b alone (its last page was full)
+    before = [r.bm.stats(), r.bm.table(a), r.bm.table(b), r.bm.pages(b)]
+    with pytest.raises(ValueError, match="no free block"):
+        r.bm.append(b, 16 * 4)           # needs one more page
+    c = r.fork(b)
+    with pytest.raises(ValueError, match="no free block"):
+        r.bm.append(c, 1)                # copy-on-write of the shared, part-filled page needs a page too
+    r.free(c)
+    assert [r.bm.stats(), r.bm.table(a), r.bm.table(b), r.bm.pages(b)] == before
+    r.check()
+    for lo, hi in ((3, 4), (4, 2), (8, 8), (0, 1)):
+        with pytest.raises(ValueError):
+            r.bm.new_sequence(lo, hi)     # not powers of two, min > max, or beyond the manager's pages
+    with pytest.raises(ValueError):
+        binding.BlockManager(8, BS, 3)
+    with pytest.raises(ValueError):
+        binding.BlockManager(8, BS, 8192)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_paged_workload_replays_exactly(seed):
+    r = Replay(200 + seed, nb=96, max_page=8)
+    policies = [(1, 1), (2, 2), (8, 8), (1, 8), (2, 4)]
+
+    def new():
+        return r.new(*policies[r.rng.integers(len(policies))])
+
+    live = [new()]
+    for _ in range(80):
+        op = r.rng.random()
+        if op < 0.5 and live:
+            q = live[r.rng.integers(len(live))]
+            try:
+                r.append(q, int(r.rng.integers(1, 60)))
+            except ValueError:
+                pass  # pool exhausted: nothing changed
+        elif op < 0.7 and live:
+            live.append(r.fork(live[r.rng.integers(len(live))]))
+        elif op < 0.85 and len(live) > 1:
+            r.free(live.pop(r.rng.integers(len(live))))
+        else:
+            live.append(new())
+        r.check()
+    for q in live:
+        r.free(q)
+    assert r.bm.stats() == (96, 0, 0)
 
 
 def test_fragmentation_matches_the_arithmetic():

@@ -167,3 +167,86 @@ def test_manager_prefix_levels_drive_the_two_phase_decode(gpu_lib):
     ref = oracle.paged_attention(q, kp, vp, table, lens, np.arange(len(seqs) + 1), scale, BS_, "bf16")
     got = oracle.bits_to_f64(out.view(torch.int16).cpu().numpy().view(np.uint16), "bf16")
     assert np.max(np.abs(got - ref)) <= 2e-2
+
+
+def test_mixed_page_sizes_in_one_pool_drive_decode_prefill_and_two_phase(gpu_lib):
+    """One bf16 pool kept by the manager with pages of 1-16 blocks: fixed
+    page sizes, pages doubling along a sequence, forks whose copy-on-write
+    moves multi-block pages.  Decode, chunked prefill and the two-phase
+    decode read the tables (block resolution) and must match the oracle."""
+    HKV_, D_, HQ_, BS_ = 8, 128, 32, 16
+    rng = np.random.default_rng(91)
+    nb = 1024
+    bm = gpu_lib.BlockManager(nb, BS_, 16)
+    kp = np.full((nb, HKV_, BS_, D_), 0x7FC0, np.uint16)
+    vp = np.full((nb, HKV_, BS_ // 16, D_, 16), 0x7FC0, np.uint16)
+    gk = torch.from_numpy(kp.view(np.int16)).cuda().view(torch.bfloat16)
+    gv = torch.from_numpy(vp.view(np.int16)).cuda().view(torch.bfloat16)
+    to_dev = lambda x: torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)  # noqa: E731
+
+    def append(s, n):
+        nonlocal kp, vp
+        slots, copies = bm.append(s, n)
+        copy_blocks_reference(kp, vp, copies)
+        if copies:
+            src = torch.tensor([c[0] for c in copies], dtype=torch.int32, device="cuda")
+            dst = torch.tensor([c[1] for c in copies], dtype=torch.int32, device="cuda")
+            gpu_lib.kv_copy_blocks(gk, gv, src, dst)
+        kn = bf16_round_bits(rng.standard_normal((n, HKV_, D_)).astype(np.float32))
+        vn = bf16_round_bits(rng.standard_normal((n, HKV_, D_)).astype(np.float32))
+        kp, vp = oracle.kv_append(kp, vp, kn, vn, np.array(slots, np.int32), BS_)
+        gpu_lib.kv_append(to_dev(kn), to_dev(vn), gk, gv, torch.tensor(slots, dtype=torch.int32, device="cuda"))
+        return copies
+
+    prompt = bm.new_sequence(4, 4)
+    append(prompt, 700)                              # 4-block pages; the last one part-filled
+    beams = [prompt] + [bm.fork(prompt) for _ in range(3)]
+    moved = [append(s, int(rng.integers(30, 300))) for s in beams[1:]]
+    assert all(len(c) > 1 for c in moved)            # copy-on-write moved a page of several blocks
+    others = [bm.new_sequence(1, 16), bm.new_sequence(16, 16), bm.new_sequence(1, 1), bm.new_sequence(2, 8)]
+    for s in others:
+        append(s, int(rng.integers(200, 1500)))
+    for s in beams + others:
+        append(s, 1)                                 # this step's token
+    seqs = beams + others
+    assert {n for s in seqs for _, n in bm.pages(s)} >= {1, 2, 4, 8, 16}
+    rows = [bm.table(s) for s in seqs]
+    W = max(len(t) for t, _ in rows)
+    table = np.zeros((len(seqs), W), np.int32)
+    for i, (t, _) in enumerate(rows):
+        table[i, :len(t)] = t
+    lens = np.array([n for _, n in rows], np.int32)
+    scale = np.float32(1 / np.sqrt(D_))
+    tt, tl = torch.from_numpy(table).cuda(), torch.from_numpy(lens).cuda()
+
+    # decode, and the two-phase decode over the manager's prefix levels
+    q = bf16_round_bits(rng.standard_normal((len(seqs), HQ_, D_)).astype(np.float32))
+    ref = oracle.paged_attention(q, kp, vp, table, lens, np.arange(len(seqs) + 1), scale, BS_, "bf16")
+    qd = to_dev(q)
+    for split in (0, 64):
+        out = torch.empty_like(qd)
+        gpu_lib.paged_attn_decode(out, qd, gk, gv, tt, tl, float(scale), int(lens.max()), split)
+        torch.cuda.synchronize()
+        got = oracle.bits_to_f64(out.view(torch.int16).cpu().numpy().view(np.uint16), "bf16")
+        assert np.max(np.abs(got - ref)) <= 2e-2, split
+    levels_host = bm.prefix_levels(seqs)
+    assert levels_host
+    levels = [gpu_lib.prefix_level(torch.from_numpy(st).cuda(), torch.from_numpy(hi).cuda(),
+                                   int(np.max(np.diff(st))), int(np.max(hi - lo)), torch.from_numpy(lo).cuda())
+              for st, lo, hi in levels_host]
+    out = torch.empty_like(qd)
+    gpu_lib.paged_attn_decode_cascade(out, qd, gk, gv, tt, tl, levels, float(scale), int(lens.max()))
+    torch.cuda.synchronize()
+    got = oracle.bits_to_f64(out.view(torch.int16).cpu().numpy().view(np.uint16), "bf16")
+    assert np.max(np.abs(got - ref)) <= 2e-2
+
+    # chunked prefill: the last 150 tokens of every sequence as query rows
+    L = 150
+    qp = bf16_round_bits(rng.standard_normal((len(seqs) * L, HQ_, D_)).astype(np.float32))
+    cu = np.arange(len(seqs) + 1, dtype=np.int32) * L
+    refp = oracle.paged_attention(qp, kp, vp, table, lens, cu, scale, BS_, "bf16", oracle.ScoreMods(causal=True))
+    outp = torch.empty((len(seqs) * L, HQ_, D_), dtype=torch.bfloat16, device="cuda")
+    gpu_lib.paged_attn_prefill(outp, to_dev(qp), torch.from_numpy(cu).cuda(), gk, gv, tt, tl, float(scale), L, True)
+    torch.cuda.synchronize()
+    got = oracle.bits_to_f64(outp.view(torch.int16).cpu().numpy().view(np.uint16), "bf16")
+    assert np.max(np.abs(got - refp)) <= 2e-2
