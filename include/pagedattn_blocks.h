@@ -41,8 +41,9 @@ extern "C" {
 typedef struct pa_block_manager pa_block_manager;
 
 /* A manager for num_blocks physical blocks of block_size tokens (a power of
- * two in [16, 256]), with pages of one block.  *out receives the handle;
- * NULL on failure. */
+ * two in [16, 256]), with pages of one block.  Slots are int32, so
+ * num_blocks * block_size must stay below 2^31 (else PA_ERR_SIZE).  *out
+ * receives the handle; NULL on failure. */
 int pa_bm_create(int64_t num_blocks, int32_t block_size, pa_block_manager** out);
 
 /* The same with pages of up to max_page_blocks blocks (a power of two,

@@ -16,7 +16,6 @@
 #include <cstdint>
 #include <mutex>
 #include <new>
-#include <set>
 #include <vector>
 
 #include "pagedattn.h"
@@ -39,8 +38,27 @@ struct pa_block_manager {
   int32_t max_order = 0;                  // largest page: 2^max_order blocks
   std::vector<int32_t> refcount;          // per physical block (equal over a page)
   std::vector<int32_t> fill;              // tokens stored in a physical block (max over its owners)
-  std::vector<std::set<int32_t>> free_pages;  // per order: first blocks of free pages
+  // Free pages: per order a stack of first blocks; free_pos[b] is the index
+  // of the free page starting at block b in its order's stack (-1: none), so
+  // a buddy leaves its stack in O(1) when it merges.
+  std::vector<std::vector<int32_t>> free_pages;
+  std::vector<int32_t> free_pos;
+  std::vector<int8_t> free_ord;
   int64_t free_blocks = 0;
+
+  void push_free(int32_t start, int32_t k) {
+    free_pos[(size_t)start] = (int32_t)free_pages[(size_t)k].size();
+    free_ord[(size_t)start] = (int8_t)k;
+    free_pages[(size_t)k].push_back(start);
+  }
+  void drop_free(int32_t start) {
+    std::vector<int32_t>& st = free_pages[(size_t)free_ord[(size_t)start]];
+    const int32_t i = free_pos[(size_t)start];
+    st[(size_t)i] = st.back();
+    free_pos[(size_t)st[(size_t)i]] = i;
+    st.pop_back();
+    free_pos[(size_t)start] = -1;
+  }
   std::vector<Seq> seqs;
   std::vector<int32_t> free_ids;
   mutable std::mutex mu;
@@ -52,11 +70,11 @@ struct pa_block_manager {
     int32_t j = k;
     while (j <= max_order && free_pages[(size_t)j].empty()) ++j;
     if (j > max_order) return -1;
-    const int32_t start = *free_pages[(size_t)j].begin();  // lowest first
-    free_pages[(size_t)j].erase(free_pages[(size_t)j].begin());
+    const int32_t start = free_pages[(size_t)j].back();
+    drop_free(start);
     while (j > k) {  // keep the low half, free the high half
       --j;
-      free_pages[(size_t)j].insert(start + (1 << j));
+      push_free(start + (1 << j), j);
     }
     for (int32_t b = start; b < start + (1 << k); ++b) {
       refcount[(size_t)b] = 1;
@@ -77,13 +95,12 @@ struct pa_block_manager {
     while (k < max_order) {
       const int64_t buddy = (int64_t)start ^ ((int64_t)1 << k);
       if (buddy + ((int64_t)1 << k) > num_blocks) break;
-      auto it = free_pages[(size_t)k].find((int32_t)buddy);
-      if (it == free_pages[(size_t)k].end()) break;
-      free_pages[(size_t)k].erase(it);
+      if (free_pos[(size_t)buddy] < 0 || free_ord[(size_t)buddy] != k) break;
+      drop_free((int32_t)buddy);
       start = (int32_t)std::min<int64_t>(start, buddy);
       ++k;
     }
-    free_pages[(size_t)k].insert(start);
+    push_free(start, k);
   }
 
   // Drop one owner of a page.
@@ -123,8 +140,9 @@ extern "C" {
 int pa_bm_create_paged(int64_t num_blocks, int32_t block_size, int32_t max_page_blocks, pa_block_manager** out) {
   if (!out) return PA_ERR_NULL;
   *out = nullptr;
-  if (num_blocks < 0 || num_blocks > 0x7fffffffll) return PA_ERR_SIZE;
   if (!pow2_block(block_size)) return PA_ERR_BLOCK_SIZE;
+  // slots are int32 (kv_append's slot mapping): every slot of the pool must fit
+  if (num_blocks < 0 || num_blocks * block_size > 0x7fffffffll) return PA_ERR_SIZE;
   if (!pow2(max_page_blocks) || max_page_blocks > kMaxPageBlocks) return PA_ERR_SIZE;
   pa_block_manager* bm = new (std::nothrow) pa_block_manager();
   if (!bm) return PA_ERR_SIZE;
@@ -134,14 +152,19 @@ int pa_bm_create_paged(int64_t num_blocks, int32_t block_size, int32_t max_page_
   bm->refcount.assign((size_t)num_blocks, 0);
   bm->fill.assign((size_t)num_blocks, 0);
   bm->free_pages.resize((size_t)bm->max_order + 1);
-  // the pool as aligned free pages, each as large as alignment and size allow
+  bm->free_pos.assign((size_t)num_blocks, -1);
+  bm->free_ord.assign((size_t)num_blocks, 0);
+  // the pool as aligned free pages, each as large as alignment and size
+  // allow; pushed from the top so that low block ids go out first
+  std::vector<std::pair<int32_t, int32_t>> init;
   int64_t b = 0;
   while (b < num_blocks) {
     int32_t k = bm->max_order;
     while (k > 0 && ((b & (((int64_t)1 << k) - 1)) != 0 || b + ((int64_t)1 << k) > num_blocks)) --k;
-    bm->free_pages[(size_t)k].insert((int32_t)b);
+    init.push_back({(int32_t)b, k});
     b += (int64_t)1 << k;
   }
+  for (auto it = init.rbegin(); it != init.rend(); ++it) bm->push_free(it->first, it->second);
   bm->free_blocks = num_blocks;
   *out = bm;
   return PA_OK;

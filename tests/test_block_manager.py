@@ -239,6 +239,8 @@ def test_paged_exhaustion_changes_nothing_and_arguments_are_checked():
         binding.BlockManager(8, BS, 3)
     with pytest.raises(ValueError):
         binding.BlockManager(8, BS, 8192)
+    with pytest.raises(ValueError, match="too large"):
+        binding.BlockManager((1 << 31) // BS, BS)   # slots past 2^31 - 1 would not fit kv_append's int32
 
 
 @pytest.mark.parametrize("seed", range(6))
