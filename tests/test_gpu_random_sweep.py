@@ -117,3 +117,94 @@ def test_random_case(gpu_lib, seed):
     else:
         errs = [assert_close(gpu_prefill(gpu_lib, w, t=t, causal=c["causal"], **kw), ref, w.dtype, tol=TOL[w.dtype])]
     print(f"case {seed}: max abs err {max(errs):.3e} (tolerance {TOL[w.dtype]})", flush=True)
+
+
+FORK_SEEDS = list(range(2000, 2016))
+
+
+@pytest.mark.parametrize("seed", FORK_SEEDS)
+def test_random_fork_tree_two_phase(gpu_lib, seed):
+    """Random fork trees kept by the block manager with random page rules
+    (pages of one size or doubling, up to 16 blocks), random appends with the
+    copy-on-write they cause, and a random subset of score mods: the
+    manager's prefix levels drive the two-phase decode, which must match the
+    oracle, as the plain decode must."""
+    from tests.test_block_manager import copy_blocks_reference
+    from workloads import bf16_round_bits
+
+    rng = np.random.default_rng(seed)
+    Hkv = int(rng.choice([2, 4, 8]))
+    g = int(rng.choice([1, 4, 8]))
+    D = int(rng.choice([64, 128]))
+    Hq, BS_, nb = Hkv * g, 16, 1280
+    bm = gpu_lib.BlockManager(nb, BS_, 16)
+    kp = np.full((nb, Hkv, BS_, D), 0x7FC0, np.uint16)
+    vp = np.full((nb, Hkv, 1, D, 16), 0x7FC0, np.uint16)
+    gk = torch.from_numpy(kp.view(np.int16)).cuda().view(torch.bfloat16)
+    gv = torch.from_numpy(vp.view(np.int16)).cuda().view(torch.bfloat16)
+    to_dev = lambda x: torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)  # noqa: E731
+    rules = [(1, 1), (4, 4), (16, 16), (1, 16), (2, 8)]
+
+    def append(s, n):
+        nonlocal kp, vp
+        slots, copies = bm.append(s, n)
+        copy_blocks_reference(kp, vp, copies)
+        if copies:
+            gpu_lib.kv_copy_blocks(gk, gv, torch.tensor([c[0] for c in copies], dtype=torch.int32, device="cuda"),
+                                   torch.tensor([c[1] for c in copies], dtype=torch.int32, device="cuda"))
+        kn = bf16_round_bits(rng.standard_normal((n, Hkv, D)).astype(np.float32))
+        vn = bf16_round_bits(rng.standard_normal((n, Hkv, D)).astype(np.float32))
+        kp, vp = oracle.kv_append(kp, vp, kn, vn, np.array(slots, np.int32), BS_)
+        gpu_lib.kv_append(to_dev(kn), to_dev(vn), gk, gv, torch.tensor(slots, dtype=torch.int32, device="cuda"))
+
+    # a forest: roots with random rules, children forked at random depths; the
+    # batch lists each tree depth-first, so forks sit next to their relatives
+    order = []
+    for _ in range(int(rng.integers(1, 4))):
+        root = bm.new_sequence(*rules[rng.integers(len(rules))])
+        append(root, int(rng.integers(1, 900)))
+        tree = [root]
+        for _ in range(int(rng.integers(0, 7))):
+            parent = tree[rng.integers(len(tree))]
+            child = bm.fork(parent)
+            tree.insert(tree.index(parent) + 1, child)
+            append(child, int(rng.integers(0, 300)) or 1)
+        order += tree
+    for s in order:
+        append(s, 1)                                 # this step's token
+    rows = [bm.table(s) for s in order]
+    W = max(len(t) for t, _ in rows)
+    table = np.zeros((len(order), W), np.int32)
+    for i, (t, _) in enumerate(rows):
+        table[i, :len(t)] = t
+    lens = np.array([n for _, n in rows], np.int32)
+    scale = np.float32(1 / np.sqrt(D))
+    kw, om = {}, {}
+    if rng.random() < 0.3:
+        kw["window"] = om["window"] = int(rng.integers(16, 600))
+    if rng.random() < 0.3:
+        kw["softcap"] = om["softcap"] = float(rng.choice([1.0, 10.0]))
+    if rng.random() < 0.3:
+        slopes = (2.0 ** -np.arange(1, Hq + 1) * 0.25).astype(np.float32)
+        kw["alibi_slopes"] = torch.from_numpy(slopes).cuda()
+        om["alibi_slopes"] = slopes.astype(np.float64)
+    print(f"fork case {seed}: Hkv {Hkv} g {g} D {D} lens {lens.tolist()} mods {sorted(om)}", flush=True)
+    q = bf16_round_bits(rng.standard_normal((len(order), Hq, D)).astype(np.float32))
+    ref = oracle.paged_attention(q, kp, vp, table, lens, np.arange(len(order) + 1), scale, BS_, "bf16",
+                                 oracle.ScoreMods(**om))
+    qd, tt, tl = to_dev(q), torch.from_numpy(table).cuda(), torch.from_numpy(lens).cuda()
+    out = torch.empty_like(qd)
+    gpu_lib.paged_attn_decode(out, qd, gk, gv, tt, tl, float(scale), int(lens.max()), 0, **kw)
+    torch.cuda.synchronize()
+    assert_close(to_numpy_bits(out), ref, "bf16")
+    levels_host = bm.prefix_levels(order)
+    if not levels_host:
+        return  # nothing shared (e.g. one sequence): the plain decode is the call
+    levels = [gpu_lib.prefix_level(torch.from_numpy(st).cuda(), torch.from_numpy(hi).cuda(),
+                                   int(np.max(np.diff(st))), int(max(1, np.max(hi - lo))), torch.from_numpy(lo).cuda())
+              for st, lo, hi in levels_host]
+    out = torch.empty_like(qd)
+    gpu_lib.paged_attn_decode_cascade(out, qd, gk, gv, tt, tl, levels, float(scale), int(lens.max()), **kw)
+    torch.cuda.synchronize()
+    err = assert_close(to_numpy_bits(out), ref, "bf16")
+    print(f"fork case {seed}: {len(levels_host)} levels, two-phase max abs err {err:.3e}", flush=True)
