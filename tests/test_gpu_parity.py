@@ -453,6 +453,20 @@ def test_decode_of_a_131072_token_row(gpu_lib):
     assert_close(got, oracle_out(w, seqs=[0, 1]), "bf16", rows=[0, 1])
 
 
+@pytest.mark.parametrize("B", [4096, 4097])
+def test_batch_size_limit_of_the_balanced_split(gpu_lib, B):
+    """4,096 sequences are the most the balanced split takes (its per-row
+    chunk prefix lives in LDS); one more and the automatic choice falls back
+    to fixed partitions.  Both sides, with rows just past the unsplit cutoff,
+    against the oracle on every row."""
+    rng = np.random.default_rng(B)
+    w = build_workload(name=f"many{B}", seed=B, kind="decode", dtype="bf16", Hq=8, Hkv=1, D=64, bs=16,
+                       context_lens=rng.integers(257, 420, size=B), append_lens=[1] * B, pool_slack=1.1)
+    split = gpu_lib.decode_split_tokens(B, 1, int(w.max_context_len), 0)
+    assert split == 0 if B <= 4096 else split > 0     # balanced split / fixed partitions
+    assert_close(gpu_decode(gpu_lib, w, split=0), oracle_out(w), "bf16")
+
+
 def test_long_prefill_chunks_sampled_rows(gpu_lib):
     """Two 2048-row causal chunks after 6144 and 2048 existing tokens, page 64;
     the oracle (the definition over the gathered keys) checks 96 sampled rows."""
