@@ -37,6 +37,7 @@ constexpr float kLazyRescale = 8.0f;  // log2 units
 constexpr int kTileKeys = 64;
 constexpr int kRowsPerWG = 128;
 constexpr int kThreads = 256;
+constexpr int kWGsPerCU = 2;  // resident work-groups per compute unit (launch bounds)
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 // Word 3 of a raw buffer resource (dword data, no swizzle) on this family.
@@ -84,7 +85,7 @@ __device__ __forceinline__ int v_swz(int d, int cpb_log2) {
 // kSplit: key-split mode (a.key_split > 0), a separate instance so that the
 // plain prefill keeps its registers.
 template <int D, bool kMods, int KBL, bool kSplit>
-__global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const PrefillArgs a, const int pair_tiles) {
   constexpr int KCH = D / 8;   // 16-byte chunks per K row
   constexpr int KSTEPS = D / 16;
   constexpr int DT = D / 32;   // output 32-dim tiles
@@ -111,7 +112,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_mfma_kernel(const Prefill
   constexpr bool ksplit = kSplit;
   const int split = ksplit ? blockIdx.x / (BH * a.q_tiles) : 0;  // key range
   const int flat = blockIdx.x - split * (BH * a.q_tiles);
-  const int qtile = a.q_tiles - 1 - flat / BH;
+  // Longest tiles first (causal rows further down see more keys).  When the
+  // launcher finds the whole grid resident at once (pair_tiles), the second
+  // half runs shortest first instead, so that work-groups i and i + half,
+  // which tend to share a compute unit, hold tiles t and q_tiles - 1 - t.
+  const int tslot = flat / BH;
+  const int thalf = (a.q_tiles + 1) >> 1;
+  const int qtile = (pair_tiles && tslot >= thalf) ? tslot - thalf : a.q_tiles - 1 - tslot;
   const int b = (flat % BH) / a.Hkv;
   const int kvh = flat % a.Hkv;
 
@@ -608,12 +615,17 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, int D, hipStream_t s) {
   const int kbl = a.bs_log2 < 6 ? a.bs_log2 : 6;
   const bool split = a.key_split > 0;
   const dim3 grid((unsigned)blocks), block(kThreads);
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 0;
+  const int pair = !split && blocks <= (long long)kWGsPerCU * cus;
 #define PA_PREFILL_LAUNCH(DD, MM, KK)                                                         \
   do {                                                                                        \
     if (split)                                                                                \
-      hipLaunchKernelGGL((prefill_mfma_kernel<DD, MM, KK, true>), grid, block, 0, s, a);     \
+      hipLaunchKernelGGL((prefill_mfma_kernel<DD, MM, KK, true>), grid, block, 0, s, a, pair); \
     else                                                                                      \
-      hipLaunchKernelGGL((prefill_mfma_kernel<DD, MM, KK, false>), grid, block, 0, s, a);    \
+      hipLaunchKernelGGL((prefill_mfma_kernel<DD, MM, KK, false>), grid, block, 0, s, a, pair); \
   } while (0)
 #define PA_PREFILL_KBL(DD, MM)                    \
   switch (kbl) {                                  \
