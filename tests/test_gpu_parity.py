@@ -453,6 +453,30 @@ def test_decode_of_a_131072_token_row(gpu_lib):
     assert_close(got, oracle_out(w, seqs=[0, 1]), "bf16", rows=[0, 1])
 
 
+@pytest.mark.parametrize("B,max_q", [(16, 1024), (27, 608)])
+def test_prefill_tile_order_at_the_residency_limit(gpu_lib, B, max_q):
+    """The bf16 prefill grid has sequences x kv-heads x query tiles work-groups
+    (one kv-head here, 4 heads per kv-head, so 32 query rows per tile): 16 x 32
+    = 512 fits two per compute unit on a 256-CU chip, and the launcher pairs
+    long and short tiles; 27 x 19 = 513 does not, and the order stays longest
+    first.  Both must cover every (row, head) once: the output starts as NaN,
+    and every row is compared with the oracle.  Chunk lengths are ragged (one
+    chunk of max_q rows, the rest random), contexts extend the chunks."""
+    rng = np.random.default_rng(7000 + B)
+    q = [max_q] + [int(rng.integers(1, max_q + 1)) for _ in range(B - 1)]
+    ctx = [n + int(rng.integers(0, 400)) for n in q]
+    w = build_workload(name=f"order{B}", seed=7000 + B, kind="prefill", dtype="bf16", Hq=4, Hkv=1, D=64, bs=16,
+                       context_lens=ctx, q_lens=q, append_lens=q, causal=True)
+    assert w.B * 1 * -(-w.max_q_len // 32) == {16: 512, 27: 513}[B]
+    t = upload(w)
+    gpu_lib.kv_append(t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], t["slot_mapping"])
+    out = torch.full_like(t["q"], float("nan"))
+    gpu_lib.paged_attn_prefill(out, t["q"], t["cu_q_lens"], t["k_cache"], t["v_cache"], t["block_tables"],
+                               t["context_lens"], w.scale, w.max_q_len, True)
+    torch.cuda.synchronize()
+    assert_close(to_numpy_bits(out), oracle_out(w, causal=True), "bf16")
+
+
 @pytest.mark.parametrize("B", [4096, 4097])
 def test_batch_size_limit_of_the_balanced_split(gpu_lib, B):
     """4,096 sequences are the most the balanced split takes (its per-row
