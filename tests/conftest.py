@@ -8,10 +8,6 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 
-def pytest_configure(config):
-    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
-
-
 @pytest.fixture(scope="session")
 def gpu_lib():
     """The C-ABI library on a GPU; fails (not skips) when the HIP path is missing."""

@@ -109,11 +109,79 @@ def test_golden_worked_examples():
 # brute force: walk the block table token by token in plain Python
 # --------------------------------------------------------------------------------------
 
+def bf16_value(bits):
+    """A bfloat16 bit pattern's value from the format itself: 1 sign bit, 8
+    exponent bits with bias 127, 7 fraction bits; exponent 0 is subnormal
+    (no implicit leading 1), exponent 255 is inf / NaN."""
+    bits = int(bits)
+    sign = -1.0 if bits & 0x8000 else 1.0
+    e = (bits >> 7) & 0xFF
+    f = bits & 0x7F
+    if e == 0xFF:
+        return sign * math.inf if f == 0 else math.nan
+    if e == 0:
+        return sign * math.ldexp(f, -126 - 7)
+    return sign * math.ldexp(128 + f, e - 127 - 7)
+
+
+_BF16_BY_FORMAT = None
+
+
+def decode_storage(a, dtype):
+    """Stored values -> fp64 without the oracle's routine: bf16 through
+    :func:`bf16_value`, fp32 by numpy's exact widening."""
+    global _BF16_BY_FORMAT
+    if dtype == "f32":
+        return np.asarray(a, dtype=np.float32).astype(np.float64)
+    if _BF16_BY_FORMAT is None:
+        _BF16_BY_FORMAT = np.array([bf16_value(i) for i in range(1 << 16)], dtype=np.float64)
+    return _BF16_BY_FORMAT[np.asarray(a, dtype=np.uint16).astype(np.int64)]
+
+
+# (bit pattern, value) written out by hand from the bfloat16 format
+BF16_HAND = [
+    (0x3F80, 1.0), (0xBF80, -1.0), (0xC040, -3.0), (0x3F81, 1.0078125), (0x4049, 3.140625),
+    (0x3F00, 0.5), (0x4300, 128.0), (0x0080, 2.0 ** -126), (0x0001, 2.0 ** -133), (0x007F, 127 * 2.0 ** -133),
+    (0x7F7F, (2 - 2.0 ** -7) * 2.0 ** 127), (0x0000, 0.0), (0x8000, -0.0), (0x7F80, math.inf),
+    (0xFF80, -math.inf),
+]
+
+
+def check_bf16_decode():
+    bits = np.array([b for b, _ in BF16_HAND], dtype=np.uint16)
+    got = opa.bits_to_f64(bits, "bf16")
+    for (b, v), x in zip(BF16_HAND, got.tolist()):
+        assert x == v and math.copysign(1.0, x) == math.copysign(1.0, v), (hex(b), x, v)
+    nan = opa.bits_to_f64(np.array([0x7FC0, 0xFFC1, 0x7F81], dtype=np.uint16), "bf16")
+    assert np.all(np.isnan(nan))
+
+
+def test_bf16_decode_hand_values():
+    check_bf16_decode()
+
+
+def test_bf16_decode_every_pattern():
+    """All 65,536 patterns: the oracle's decode equals the format's definition
+    and torch's own bfloat16 -> float64 conversion, sign of zero and NaNs
+    included."""
+    allbits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    got = opa.bits_to_f64(allbits, "bf16")
+    by_format = decode_storage(allbits, "bf16")
+    by_torch = torch.from_numpy(allbits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    for ref in (by_format, by_torch):
+        nan = np.isnan(ref)
+        assert np.array_equal(np.isnan(got), nan)
+        assert np.array_equal(got[~nan], ref[~nan])
+        assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
 def brute_force(w, mods):
-    """Two-pass softmax with math.exp, reading each key through its table entry."""
-    q = opa.bits_to_f64(w.q, w.dtype)
-    kp = opa.bits_to_f64(w.k_pool, w.dtype)
-    vp = opa.bits_to_f64(w.v_pool, w.dtype)
+    """Two-pass softmax with math.exp, reading each key through its table
+    entry; stored values are decoded by :func:`decode_storage`, not by the
+    oracle."""
+    q = decode_storage(w.q, w.dtype)
+    kp = decode_storage(w.k_pool, w.dtype)
+    vp = decode_storage(w.v_pool, w.dtype)
     S = min(w.bs, 16)  # V: token o of a block is column o % S of sub-slab o // S
     g = w.Hq // w.Hkv
     out = np.zeros(q.shape)
@@ -474,6 +542,7 @@ def test_kv_append_rejects_duplicates_and_skips_negative():
 # --------------------------------------------------------------------------------------
 
 def _all_pins():
+    check_bf16_decode()
     check_golden()
     check_sdpa()
     check_permutation_invariance("f32")
@@ -484,6 +553,8 @@ def _all_pins():
     np.testing.assert_allclose(_run(w, mods), brute_force(w, mods), rtol=0, atol=1e-12)
     test_brute_force_with_prefix_and_documents()
     check_brute_force_large_pages(32)
+    wb = _tiny("prefill", 11, dtype="bf16", q_lens=[5, 7], causal=True)
+    np.testing.assert_allclose(_run(wb, mods), brute_force(wb, mods), rtol=0, atol=1e-12)
 
 
 def _mutant_gather_v_not_transposed(k_pool, v_pool, table_row, n, bs):
@@ -507,6 +578,13 @@ def _mutant_gather_v_whole_slab(k_pool, v_pool, table_row, n, bs):
 
 def _mutant_gather_ignores_table(k_pool, v_pool, table_row, n, bs):
     return opa.__dict__["_orig_gather"](k_pool, v_pool, np.arange(len(table_row)), n, bs)
+
+
+def _mutant_bf16_low_bit_dropped(a, dtype):
+    """bf16 decode that loses the last fraction bit (a plausible masking slip)."""
+    if dtype == "bf16":
+        a = np.asarray(a, dtype=np.uint16) & np.uint16(0xFFFE)
+    return opa.__dict__["_orig_bits"](a, dtype)
 
 
 def _make_attention_mutant(kind):
@@ -535,12 +613,15 @@ def _make_attention_mutant(kind):
     return mutant
 
 
-@pytest.mark.parametrize("mutant", ["v_layout", "v_whole_slab", "ignore_table", "no_scale", "top_left_causal",
+@pytest.mark.parametrize("mutant", ["bf16_low_bit", "v_layout", "v_whole_slab", "ignore_table", "no_scale", "top_left_causal",
                                     "gqa_modulo", "sign", "prefix_inclusive", "doc_exclusive"])
 def test_planted_mistakes_are_caught(monkeypatch, mutant):
     monkeypatch.setitem(opa.__dict__, "_orig_gather", opa.gather_sequence)
     monkeypatch.setitem(opa.__dict__, "_orig_attention", opa.attention_dense)
-    if mutant == "v_layout":
+    monkeypatch.setitem(opa.__dict__, "_orig_bits", opa.bits_to_f64)
+    if mutant == "bf16_low_bit":
+        monkeypatch.setattr(opa, "bits_to_f64", _mutant_bf16_low_bit_dropped)
+    elif mutant == "v_layout":
         monkeypatch.setattr(opa, "gather_sequence", _mutant_gather_v_not_transposed)
     elif mutant == "v_whole_slab":
         monkeypatch.setattr(opa, "gather_sequence", _mutant_gather_v_whole_slab)
