@@ -125,8 +125,10 @@ __device__ __forceinline__ bool row_range(const RowAttnArgs& a, int slot, RowRan
     Lq = a.cu_q_lens[b + 1] - q0;
   }
   if (i >= Lq) return false;
-  // (a decode row may have no key at all; prefill rows sit inside the context)
-  PA_DEVICE_CHECK(n >= 0 && (long long)n <= (long long)a.bt_stride << a.bs_log2 && (!a.cu_q_lens || Lq <= n));
+  // (a decode row may have no key at all; prefill rows sit inside the context;
+  // a merge-only launch has no block table, so no table extent to check)
+  PA_DEVICE_CHECK(n >= 0 && (!a.block_tables || (long long)n <= (long long)a.bt_stride << a.bs_log2) &&
+                  (!a.cu_q_lens || Lq <= n));
   r.qrow = q0 + i;
   r.pos = n - Lq + i;
   r.hi = a.causal ? min(n, r.pos + 1) : n;

@@ -34,6 +34,17 @@ def main():
                                   w.scale, w.max_context_len, split)
         torch.cuda.synchronize()
         worst = max(worst, float(np.max(np.abs(bits_to_f64(to_numpy_bits(out), "bf16") - ref))))
+        if split > 0:
+            # the same decode as two calls: partials, then the merge alone (the
+            # merge-only call has no block table; rows longer than one block)
+            out2 = torch.full_like(t["q"], float("nan"))
+            ws = binding.decode_workspace(t["q"], w.Hkv, w.max_context_len, split)
+            for phase in ("partials", "merge"):
+                binding.paged_attn_decode(out2, t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
+                                          t["context_lens"], w.scale, w.max_context_len, split, workspace=ws,
+                                          phase=phase)
+            torch.cuda.synchronize()
+            worst = max(worst, float(np.max(np.abs(bits_to_f64(to_numpy_bits(out2), "bf16") - ref))))
         # block copy of two unused blocks onto two others, then nothing referenced changed
         used = set(np.asarray(w.block_table[w.block_table >= 0]).tolist())
         free = [b for b in range(w.NB) if b not in used][:4]
