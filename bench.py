@@ -19,8 +19,11 @@ divided by the measured time of the decode call (both kernels).  The prefill
 throughput is reported beside it.  Inputs are resident in HBM before timing.
 Before every step a 512 MiB buffer is overwritten (evicting L2 and the
 last-level cache; not part of any phase).  Per-kernel times come from HIP
-events recorded on the stream the kernels run on.  ``cpu_baseline`` times the
-fp64 CPU oracle on a bounded sample of the same workload.
+events recorded on the stream the kernels run on.  Every output row of the
+timed step (all decode rows, all prefill rows) is compared with the fp64 CPU
+oracle afterwards: the max-abs errors go into ``parity`` and the run fails
+(exit status 3) above 2e-2.  ``cpu_baseline`` times that oracle on a bounded
+sample of the same workload.
 
 Beside the step it reports: the achievable HBM read bandwidth of a plain
 streaming-read kernel (a second denominator), the decode of the other
@@ -49,6 +52,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PARITY_TOL = 2e-2           # max-abs error bar for bf16 inputs, fp32 accumulation
 METRIC = "paged decode KV-read GB/s (% of HBM peak) + paged prefill TFLOP/s, 1 MI355X"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partials_traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "paged_kv_cache_attn_amd", "csrc", f)
@@ -92,10 +96,13 @@ def traffic_record():
     return rec
 
 
-def cpu_baseline(w5, w3, budget_s):
-    """fp64 oracle on a bounded sample: whole decode sequences of the long
-    batch (append + attention, on a compact copy of their blocks), then one
-    sequence of the chunked prefill."""
+def oracle_reference(w5, w3, budget_s):
+    """The fp64 oracle over every row the step computes: all decode rows of
+    the long batch (append + attention, each sequence on a compact copy of
+    its blocks, so the multi-GB pool is never widened) and every chunked-
+    prefill row.  Returns the reference outputs and, as ``cpu_baseline``, the
+    oracle's own speed on the host: the decode sequences done within
+    ``budget_s`` seconds (0: none timed) and the prefill batch."""
     import threadpoolctl
 
     import oracle
@@ -103,7 +110,8 @@ def cpu_baseline(w5, w3, budget_s):
     info = threadpoolctl.threadpool_info()
     cores = max([i.get("num_threads", 1) for i in info] + [1])
 
-    done, t_dec, bytes_dec = [], 0.0, 0
+    ref5 = np.full(w5.q.shape, np.nan, dtype=np.float64)
+    timed, t_dec, bytes_dec = [], 0.0, 0
     for b in range(w5.B):
         nb = (int(w5.context_lens[b]) + w5.bs - 1) // w5.bs
         ids = w5.block_table[b, :nb].astype(np.int64)
@@ -113,29 +121,39 @@ def cpu_baseline(w5, w3, budget_s):
         slot = np.array([int(np.nonzero(ids == s // w5.bs)[0][0]) * w5.bs + s % w5.bs], np.int32)
         t0 = time.perf_counter()
         kp2, vp2 = oracle.kv_append(kp, vp, w5.k_new[b:b + 1], w5.v_new[b:b + 1], slot, w5.bs)
-        oracle.paged_attention(w5.q[b:b + 1], kp2, vp2, table, w5.context_lens[b:b + 1], np.array([0, 1]),
-                               w5.scale, w5.bs, w5.dtype)
-        t_dec += time.perf_counter() - t0
-        done.append(b)
-        bytes_dec += int(w5.context_lens[b]) * w5.Hkv * w5.D * 2 * 2
-        if t_dec >= budget_s * 0.6:
-            break
+        ref5[b:b + 1] = oracle.paged_attention(w5.q[b:b + 1], kp2, vp2, table, w5.context_lens[b:b + 1],
+                                               np.array([0, 1]), w5.scale, w5.bs, w5.dtype)
+        dt = time.perf_counter() - t0
+        if t_dec < budget_s * 0.6:
+            t_dec += dt
+            timed.append(b)
+            bytes_dec += int(w5.context_lens[b]) * w5.Hkv * w5.D * 2 * 2
     t0 = time.perf_counter()
-    kp, vp = oracle.kv_append(w3.k_pool, w3.v_pool, w3.k_new[:512], w3.v_new[:512], w3.slot_mapping[:512], w3.bs)
-    oracle.paged_attention(w3.q[:512], kp, vp, w3.block_table[:1], w3.context_lens[:1], np.array([0, 512]),
-                           w3.scale, w3.bs, w3.dtype, oracle.ScoreMods(causal=True))
+    kp, vp = oracle.kv_append(w3.k_pool, w3.v_pool, w3.k_new, w3.v_new, w3.slot_mapping, w3.bs)
+    ref3 = oracle.paged_attention(w3.q, kp, vp, w3.block_table, w3.context_lens, w3.cu_q_lens,
+                                  w3.scale, w3.bs, w3.dtype, oracle.ScoreMods(causal=True))
     t_pre = time.perf_counter() - t0
-    pre_flops = prefill_flops(w3) / w3.B
-    return {
-        "value": round(bytes_dec / t_dec / 1e9, 4),
-        "unit": "GB/s",
-        "cores": int(cores),
-        "kind": "oracle",
-        "sample": (f"decode: {len(done)} of {w5.B} sequences of the long-context batch "
-                   f"({sum(int(w5.context_lens[b]) for b in done)} tokens, kv_append + fp64 attention) in "
-                   f"{t_dec:.2f} s; prefill: 1 of {w3.B} chunked-prefill sequences in {t_pre:.2f} s"),
-        "prefill_tflops": round(pre_flops / t_pre / 1e12, 6),
-    }
+    base = None
+    if timed:
+        base = {
+            "value": round(bytes_dec / t_dec / 1e9, 4),
+            "unit": "GB/s",
+            "cores": int(cores),
+            "kind": "oracle",
+            "sample": (f"decode: {len(timed)} of {w5.B} sequences of the long-context batch "
+                       f"({sum(int(w5.context_lens[b]) for b in timed)} tokens, kv_append + fp64 attention) in "
+                       f"{t_dec:.2f} s; prefill: all {w3.B} chunked-prefill sequences (append + fp64 attention) "
+                       f"in {t_pre:.2f} s"),
+            "prefill_tflops": round(prefill_flops(w3) / t_pre / 1e12, 6),
+        }
+    return ref5, ref3, base
+
+
+def max_abs_err(out, ref):
+    """Largest |GPU - oracle| over every element (bf16 output read exactly)."""
+    from oracle.paged import bits_to_f64
+    from workloads.device import to_numpy_bits
+    return float(np.max(np.abs(bits_to_f64(to_numpy_bits(out), "bf16") - ref)))
 
 
 PAGE_SIZES = (16, 32, 64, 128, 256)
@@ -359,7 +377,10 @@ def main():
                     help="also run one plain device copy of this many MiB (a known-size reference for "
                          "HBM traffic counters)")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0,
-                    help="time budget of the oracle baseline (0: skip it)")
+                    help="time budget of the oracle baseline's decode sample (0: no baseline)")
+    ap.add_argument("--parity", type=int, default=1,
+                    help="1: check every output row of the timed step against the fp64 oracle and fail "
+                         "above the tolerance (0: skip)")
     ap.add_argument("--flush-mib", type=int, default=512,
                     help="cache-evicting write before every timed call (0: none)")
     ap.add_argument("--path", choices=("step", "two_phase"), default="step",
@@ -449,6 +470,8 @@ def main():
     torch.cuda.synchronize()
     t_end = time.perf_counter()
     log(f"timed {args.steps} steps")
+    # the timed step's outputs, kept for the parity check against the oracle
+    out5_step, out3_step = out5.clone(), out3.clone()
 
     def phase_ms(i, j):
         return float(np.mean([e[i].elapsed_time(e[j]) for e in events]))
@@ -487,6 +510,7 @@ def main():
             if k >= args.warmup:
                 evs.append(e)
         torch.cuda.synchronize()
+        out5_fixed = out5.clone()
         f_part = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
         f_merge = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
         fixed = {
@@ -579,12 +603,29 @@ def main():
         result.update(extra)
         result["fragmentation"]["long_decode_bf16"] = fragmentation(w5.context_lens)
         result["fragmentation"]["chunked_prefill_bf16"] = fragmentation(w3.context_lens)
-    if args.cpu_baseline_seconds > 0:
-        log("timing the fp64 oracle on the host")
-        result["cpu_baseline"] = cpu_baseline(w5, w3, args.cpu_baseline_seconds)
+    failed = False
+    if args.parity:
+        log("fp64 oracle on the host: every decode and prefill row of the step")
+        ref5, ref3, base = oracle_reference(w5, w3, args.cpu_baseline_seconds)
+        result["cpu_baseline"] = base
+        par = {"tolerance": PARITY_TOL, "decode_rows": int(w5.B), "prefill_rows": int(w3.q_lens.sum()),
+               "decode_max_abs_err": max_abs_err(out5_step, ref5),
+               "prefill_max_abs_err": max_abs_err(out3_step, ref3)}
+        if fixed is not None:
+            fixed["max_abs_err"] = max_abs_err(out5_fixed, ref5)
+            par["decode_fixed_split_max_abs_err"] = fixed["max_abs_err"]
+        result["parity"] = par
+        errs = [v for k, v in par.items() if k.endswith("max_abs_err")]
+        failed = not all(e <= PARITY_TOL for e in errs)
+        log(f"parity vs the oracle: {par}")
     else:
         result["cpu_baseline"] = None
+        result["parity"] = None
     print(json.dumps(result), flush=True)
+    if failed:
+        print(f"bench.py: the timed step's outputs differ from the oracle by more than {PARITY_TOL}",
+              file=sys.stderr)
+        sys.exit(3)
 
 
 if __name__ == "__main__":
