@@ -34,6 +34,7 @@ namespace pa {
 namespace {
 
 constexpr float kLazyRescale = 8.0f;  // log2 units
+constexpr uint32_t kBf16One2 = 0x3F803F80u;  // (1.0, 1.0) as a bf16 pair
 constexpr int kTileKeys = 64;
 constexpr int kRowsPerWG = 128;
 constexpr int kThreads = 256;
@@ -353,8 +354,8 @@ __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const
       for (int j = 0; j < 4; ++j) {
         const float p0 = fast_exp2(S[s >> 1][8 * (s & 1) + 2 * j] - msafe);
         const float p1 = fast_exp2(S[s >> 1][8 * (s & 1) + 2 * j + 1] - msafe);
-        l_run += p0 + p1;
         w[j] = cvt_bf16x2(p0, p1);
+        l_run = dot2_bf16(w[j], kBf16One2, l_run);
       }
       pb[s] = __builtin_bit_cast(bf16x8, w);
     }
@@ -512,8 +513,10 @@ __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const
       // block: past the last tile they reload it into buffers nobody reads
       // any more.  S_{t+1} (on the last tile from a stale K buffer, never
       // used) and P_t.  s * scale * log2(e) is folded into the exp argument
-      // (scale > 0 on this path).  The row sum adds the fp32 weights with
-      // plain adds (a v_dot2 per bf16 pair would be a slow instruction).
+      // (scale > 0 on this path).  The row sum adds the bf16-rounded weights
+      // that enter P.V (a dot2 of each packed pair with (1, 1)), so the
+      // weights sum to one and a row whose weight sits on one key returns
+      // that key's V row.
       issue_k(tile_k0(t + 2), P, b2);
       issue_v(k1, Q, b1);
       b1 = b2;
@@ -529,8 +532,8 @@ __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const
         for (int j = 0; j < 4; ++j) {
           const float p0 = fast_exp2(fmaf(Scur[s >> 1][8 * (s & 1) + 2 * j], scale_log2, nm));
           const float p1 = fast_exp2(fmaf(Scur[s >> 1][8 * (s & 1) + 2 * j + 1], scale_log2, nm));
-          psum += p0 + p1;
           w[j] = cvt_bf16x2(p0, p1);
+          psum = dot2_bf16(w[j], kBf16One2, psum);
         }
         pb[s] = __builtin_bit_cast(bf16x8, w);
       }
