@@ -36,8 +36,10 @@
  *
  * Tensor pointers (q, out, the pools, new tokens, workspaces) must be 16-byte
  * aligned: the kernels move 16-byte pieces.  All calls are asynchronous on
- * `stream` (a hipStream_t; NULL = the null stream).  No call allocates device or host memory, and none keeps state
- * between calls.  Calls are thread-safe.
+ * `stream` (a hipStream_t; NULL = the null stream).  No call allocates device
+ * or host memory.  None keeps state between calls, except the per-device
+ * scratch of paged_attn_decode_noalloc, and calls are thread-safe, except
+ * paged_attn_decode_noalloc calls that overlap on one device.
  *
  * Status: 0 = success.  A negative value is an invalid argument found on the
  * host before anything is enqueued (no buffer is touched).  A positive value
@@ -80,7 +82,9 @@ enum {
   PA_ERR_TABLE_STRIDE = -11, /* block_table_stride < 1                          */
   PA_ERR_NO_BLOCKS = -12,    /* block manager: the pool is exhausted            */
   PA_ERR_SEQ = -13,          /* block manager: unknown or freed sequence id     */
-  PA_ERR_ALIGN = -14         /* a tensor pointer is not 16-byte aligned         */
+  PA_ERR_ALIGN = -14,        /* a tensor pointer is not 16-byte aligned         */
+  PA_ERR_SCRATCH = -15       /* paged_attn_decode_noalloc: needs more than
+                                PA_DECODE_SCRATCH_BYTES of workspace            */
 };
 
 /*
@@ -190,6 +194,36 @@ int paged_attn_decode(void* out, const void* q, const void* k_cache, const void*
                       int64_t num_blocks, int32_t max_context_len, float scale,
                       int32_t split_tokens, const pa_score_mods* mods, void* workspace,
                       size_t workspace_bytes, int32_t dtype, void* stream);
+
+/*
+ * paged_attn_decode_noalloc -- paged_attn_decode with no workspace argument,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, serving loops that must not call hipMalloc, harnesses that forbid
+ * it.  Arguments, result and status codes as paged_attn_decode.
+ *
+ * The partial results live in a scratch array the library holds on each
+ * device (PA_DECODE_SCRATCH_BYTES = 16 MiB, allocated with the library's
+ * code on that device and kept until the process ends).  A call whose
+ * workspace would exceed it -- paged_attn_decode_workspace_size() of the
+ * same sizes above PA_DECODE_SCRATCH_BYTES -- returns PA_ERR_SCRATCH and
+ * enqueues nothing (the long-context batch of 64 sequences x 8 kv-heads x
+ * 8 query heads per kv-head, D 128, needs 10.6 MB).  The call allocates
+ * nothing: no hipMalloc, no hipFree, no library routine that allocates.
+ * Every call on a device shares that device's array and leaves its contents
+ * behind; each call writes everything it reads there before reading it.
+ * Calls that overlap on one device (two streams, two threads) race on the
+ * array and give undefined results: order them on one stream, or use
+ * paged_attn_decode with workspaces of your own.
+ */
+#define PA_DECODE_SCRATCH_BYTES (16u << 20)
+
+int paged_attn_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, int32_t block_table_stride,
+                              const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              int64_t num_blocks, int32_t max_context_len, float scale,
+                              int32_t split_tokens, const pa_score_mods* mods, int32_t dtype,
+                              void* stream);
 
 /*
  * The two phases of paged_attn_decode as separate calls (same arguments).

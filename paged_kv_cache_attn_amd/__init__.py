@@ -21,6 +21,7 @@ from .binding import (  # noqa: F401
     lib,
     lib_path,
     paged_attn_decode,
+    paged_attn_decode_noalloc,
     paged_attn_decode_cascade,
     paged_attn_prefill,
     prefix_level,

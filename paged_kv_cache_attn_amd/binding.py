@@ -57,6 +57,8 @@ SIGNATURES = {
     "paged_attn_decode_split_tokens": (_i32, [_i32, _i32, _i32, _i32]),
     "paged_attn_decode": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i64,
                                  _i32, _f32, _i32, _mods_p, _vp, _sz, _i32, _vp]),
+    "paged_attn_decode_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i64,
+                                         _i32, _f32, _i32, _mods_p, _i32, _vp]),
     "paged_attn_decode_partials": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
                                           _i64, _i32, _f32, _i32, _mods_p, _vp, _sz, _i32, _vp]),
     "paged_attn_decode_merge": (_i32, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _mods_p, _vp, _sz, _i32,
@@ -248,6 +250,26 @@ def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens, scal
                   mp, _ptr(workspace), ws_bytes, _dtype_code(q), _stream())
     _check(code, f"paged_attn_decode[{phase}]")
     return out
+
+
+def paged_attn_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+                              split_tokens=0, window=0, softcap=0.0, alibi_slopes=None, prefix_lens=None,
+                              doc_starts=None):
+    """``paged_attn_decode`` on the library's own per-device scratch: takes no
+    workspace and allocates nothing (the call fails with ``ValueError`` when
+    the sizes need more than ``PA_DECODE_SCRATCH_BYTES``).  Calls that overlap
+    on one device race on that scratch."""
+    NB, Hkv, bs, D, B, Hq = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens)
+    mp, _keep = _mods(window, softcap, alibi_slopes, prefix_lens, doc_starts)
+    code = lib().paged_attn_decode_noalloc(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                                           block_tables.shape[1], _ptr(context_lens), B, Hq, Hkv, D, bs, NB,
+                                           int(max_context_len), float(scale), int(split_tokens), mp,
+                                           _dtype_code(q), _stream())
+    _check(code, "paged_attn_decode_noalloc")
+    return out
+
+
+DECODE_SCRATCH_BYTES = 16 << 20  # PA_DECODE_SCRATCH_BYTES
 
 
 def prefix_level(group_starts, prefix_ends, max_group_size, max_prefix_len, prefix_starts=None):

@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <initializer_list>
+#include <mutex>
 
 #include "pagedattn.h"
 #include "pa_kernels.h"
@@ -280,6 +281,37 @@ int decode_impl(bool do_partials, bool do_merge, void* out, const void* q, const
   return PA_OK;
 }
 
+// ---- library-held decode scratch (paged_attn_decode_noalloc) ----
+// One array per device, allocated with the code object when the library is
+// loaded on that device and kept until the process ends.  Host code never
+// uses the array's name as an address: its device address is looked up once
+// per device with hipGetSymbolAddress and cached.
+constexpr size_t kScratchBytes = (size_t)PA_DECODE_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch (looked up on first use), or a
+// positive hipError_t.
+int scratch_for_current_device(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    if (!p) return (int)hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -368,6 +400,33 @@ int paged_attn_decode(void* out, const void* q, const void* k_cache, const void*
                      context_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                      num_blocks, max_context_len, scale, split_tokens, mods, workspace,
                      workspace_bytes, dtype, stream);
+}
+
+int paged_attn_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, int32_t block_table_stride,
+                              const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              int64_t num_blocks, int32_t max_context_len, float scale,
+                              int32_t split_tokens, const pa_score_mods* mods, int32_t dtype,
+                              void* stream) {
+  int st = common_decode_checks(num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                                block_table_stride, max_context_len, split_tokens, dtype, mods);
+  if (st) return st;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return PA_ERR_NULL;
+  if (!aligned16({out, q, k_cache, v_cache})) return PA_ERR_ALIGN;
+  Shape s;
+  decode_shape(num_seqs, num_heads, num_kv_heads, max_context_len, split_tokens, s);
+  const size_t need = workspace_bytes_for(num_seqs, num_kv_heads, head_dim, s);
+  if (need > kScratchBytes) return PA_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (need > 0 && (st = scratch_for_current_device(&ws))) return st;
+  // Every workspace byte the kernels read is written earlier in the same
+  // call (per-item unit records, partials), so nothing is cleared here.
+  return decode_impl(true, true, out, q, k_cache, v_cache, block_tables, block_table_stride,
+                     context_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                     num_blocks, max_context_len, scale, split_tokens, mods, ws, need > 0 ? kScratchBytes : 0,
+                     dtype, stream);
 }
 
 int paged_attn_decode_partials(void* out, const void* q, const void* k_cache,
@@ -626,6 +685,7 @@ const char* paged_attn_status_string(int status) {
     case PA_ERR_NO_BLOCKS: return "block manager: no free block left in the pool";
     case PA_ERR_SEQ: return "block manager: unknown or freed sequence id";
     case PA_ERR_ALIGN: return "a tensor pointer is not 16-byte aligned";
+    case PA_ERR_SCRATCH: return "the call needs more decode scratch than the library holds (16 MiB)";
     default: break;
   }
   if (status > 0) return hipGetErrorString(static_cast<hipError_t>(status));

@@ -24,7 +24,7 @@ int main(void) {
   int32_t* ifake = (int32_t*)0x1000;
 
   EXPECT(strcmp(paged_attn_status_string(PA_OK), "ok") == 0);
-  for (int c = PA_ERR_ALIGN; c < 0; ++c) EXPECT(strcmp(paged_attn_status_string(c), "unknown status") != 0);
+  for (int c = PA_ERR_SCRATCH; c < 0; ++c) EXPECT(strcmp(paged_attn_status_string(c), "unknown status") != 0);
 
   /* kv_append */
   EXPECT(kv_append(fake, fake, fake, fake, ifake, 4, 8, 96, 16, 10, PA_BF16, NULL) == PA_ERR_HEAD_DIM);
@@ -40,6 +40,9 @@ int main(void) {
   pa_score_mods bad = {-1, 0.f, NULL, NULL, NULL};
   EXPECT(paged_attn_decode(fake, fake, fake, fake, ifake, 4, ifake, 2, 32, 8, 128, 16, 100, 64, 0.1f, 0, &bad,
                            fake, (size_t)1 << 40, PA_BF16, NULL) == PA_ERR_MODS);
+  EXPECT(paged_attn_decode_noalloc(fake, fake, fake, fake, ifake, 2048, ifake, 4000, 64, 8, 128, 16, 100, 32768,
+                                   0.1f, 0, NULL, PA_BF16, NULL) == PA_ERR_SCRATCH);
+  EXPECT(paged_attn_decode_workspace_size(64, 64, 8, 128, 32768, 0) <= PA_DECODE_SCRATCH_BYTES);
   EXPECT(paged_attn_decode_workspace_size(8, 32, 8, 128, 256, 0) == 0);   /* short rows: unsplit */
   EXPECT(paged_attn_decode_split_tokens(64, 8, 32768, 512) == 512);
 

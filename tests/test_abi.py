@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     assert binding.status_string(0) == "ok"
-    for code in range(-14, 0):
+    for code in range(-15, 0):
         s = binding.status_string(code)
         assert s and s != "unknown status", code
     assert binding.status_string(-99) == "unknown status"
@@ -88,6 +88,33 @@ def _decode(fn="paged_attn_decode", **over):
     return getattr(L, fn)(a["out"], a["q"], a["k"], a["v"], a["bt"], a["stride"], a["ctx"], a["B"], a["Hq"],
                           a["Hkv"], a["D"], a["bs"], a["NB"], a["max_ctx"], a["scale"], a["split"], a["mods"],
                           a["ws"], a["ws_bytes"], a["dtype"], None)
+
+
+def _decode_noalloc(**over):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, stride=4, ctx=FAKE, B=2, Hq=32, Hkv=8, D=128, bs=16, NB=100,
+             max_ctx=64, scale=0.1, split=0, mods=None, dtype=1)
+    a.update(over)
+    return binding.lib().paged_attn_decode_noalloc(a["out"], a["q"], a["k"], a["v"], a["bt"], a["stride"], a["ctx"],
+                                                   a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["NB"], a["max_ctx"],
+                                                   a["scale"], a["split"], a["mods"], a["dtype"], None)
+
+
+def test_decode_noalloc_validation():
+    """The allocation-free decode checks its arguments like the decode and
+    refuses sizes whose workspace exceeds the library's 16 MiB scratch (all
+    before any device work)."""
+    assert _decode_noalloc(dtype=5) == -8
+    assert _decode_noalloc(D=96) == -4
+    assert _decode_noalloc(split=100) == -6
+    assert _decode_noalloc(q=NULL) == -1
+    assert _decode_noalloc(out=ctypes.c_void_p(0x1008)) == -14
+    assert _decode_noalloc(B=0) == 0
+    big = dict(B=4000, Hq=64, Hkv=8, max_ctx=32768, stride=2048)
+    assert binding.decode_workspace_size(4000, 64, 8, 128, 32768, 0) > binding.DECODE_SCRATCH_BYTES
+    assert _decode_noalloc(**big) == -15
+    assert _decode_noalloc(**big, split=512) == -15
+    # the long-context batch fits
+    assert binding.decode_workspace_size(64, 64, 8, 128, 32768, 0) <= binding.DECODE_SCRATCH_BYTES
 
 
 @pytest.mark.parametrize("fn", ["paged_attn_decode", "paged_attn_decode_partials"])
