@@ -51,7 +51,10 @@ int resolve_split_log2(int32_t B, int32_t Hkv, int32_t max_ctx, int32_t split) {
   if (split == -1) return kUnsplitLog2;
   if (split > 0) return ilog2(split);
   long long s = kAutoSplitMax;
-  auto units = [&](long long sp) { return (long long)B * Hkv * ((max_ctx + sp - 1) / sp); };
+  // (B * Hkv capped at the target: the comparison below is unchanged and the
+  // product cannot overflow)
+  const long long bh = std::min((long long)B * Hkv, kAutoTargetUnits);
+  auto units = [&](long long sp) { return bh * (((long long)max_ctx + sp - 1) / sp); };
   while (s > kAutoSplitMin && units(s) < kAutoTargetUnits) s >>= 1;
   return ilog2(s);
 }
@@ -80,7 +83,7 @@ struct Shape {
 int decode_shape(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_ctx, int32_t split, Shape& s) {
   s.g = Hq / Hkv;
   s.GP = group_pad(s.g);
-  s.NG = (s.g + s.GP - 1) / s.GP;
+  s.NG = (s.g - 1) / s.GP + 1;  // (g >= 1; no overflow for any int32 g)
   s.W = 0;
   if (split == 0 && max_ctx <= kUnsplitMaxCtx) {
     // every row fits a few chunks: one wavefront per (row, head group)
@@ -506,7 +509,7 @@ int paged_attn_prefill(void* out, const void* q, const int32_t* cu_q_lens, const
     a.g = g;
     a.bs_log2 = ilog2(block_size);
     const int qt = pa::prefill_rows_per_tile(g);
-    a.q_tiles = (max_q_len + qt - 1) / qt;
+    a.q_tiles = (max_q_len - 1) / qt + 1;  // (max_q_len >= 1 here)
     a.causal = causal;
     a.window = mods ? mods->window : 0;
     a.scale = scale;
@@ -519,7 +522,7 @@ int paged_attn_prefill(void* out, const void* q, const int32_t* cu_q_lens, const
   Shape s;
   s.g = g;
   s.GP = group_pad(g);
-  s.NG = (g + s.GP - 1) / s.GP;
+  s.NG = (g - 1) / s.GP + 1;
   s.split_log2 = kUnsplitLog2;
   s.P = 1;
   s.W = 0;
