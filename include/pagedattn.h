@@ -293,6 +293,15 @@ int paged_attn_decode_merge(void* out, const int32_t* context_lens, int32_t num_
  * size function reads only the levels' host fields).  Breaking the
  * device-side contract (groups, ranges) is undefined behaviour; the debug
  * library traps.
+ *
+ * paged_attn_decode_cascade picks the faster of the two-phase decode and the
+ * plain paged_attn_decode for the batch: below 256 MiB of logical K+V
+ * (num_seqs x max_context_len keys, K and V, every kv-head: the host-side
+ * bound) a decode step is bound by launches rather than by re-reading the
+ * shared keys, and the plain decode (run in the same workspace) is faster;
+ * paged_attn_decode_cascade_plan() tells which one a call will run (1:
+ * two-phase, 0: plain).  paged_attn_decode_cascade_two_phase always runs the
+ * two-phase decode.  Both give the same attention up to rounding order.
  */
 typedef struct {
   const int32_t* group_starts;
@@ -314,6 +323,21 @@ int paged_attn_decode_cascade(void* out, const void* q, const void* k_cache, con
                               int32_t block_size, int64_t num_blocks, int32_t max_context_len, float scale,
                               const pa_score_mods* mods, void* workspace, size_t workspace_bytes, int32_t dtype,
                               void* stream);
+
+int paged_attn_decode_cascade_two_phase(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                        const int32_t* block_tables, int32_t block_table_stride,
+                                        const int32_t* context_lens, int32_t num_seqs,
+                                        const pa_prefix_level* levels, int32_t num_levels, int32_t num_heads,
+                                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                        int64_t num_blocks, int32_t max_context_len, float scale,
+                                        const pa_score_mods* mods, void* workspace, size_t workspace_bytes,
+                                        int32_t dtype, void* stream);
+
+/* 1 if paged_attn_decode_cascade would run the two-phase decode for these
+ * sizes, 0 if the plain decode (or invalid arguments). */
+int32_t paged_attn_decode_cascade_plan(int32_t num_seqs, const pa_prefix_level* levels, int32_t num_levels,
+                                       int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t max_context_len);
 
 /*
  * paged_attn_prefill -- several query rows per sequence (prefill, or a

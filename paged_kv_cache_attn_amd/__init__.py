@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     PA_F32,
     bench_fill,
     bench_stream_read,
+    decode_cascade_plan,
     decode_cascade_workspace,
     decode_cascade_workspace_size,
     decode_split_tokens,

@@ -69,6 +69,10 @@ SIGNATURES = {
                                                         _i32]),
     "paged_attn_decode_cascade": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, ctypes.POINTER(PrefixLevel), _i32,
                                          _i32, _i32, _i32, _i32, _i64, _i32, _f32, _mods_p, _vp, _sz, _i32, _vp]),
+    "paged_attn_decode_cascade_two_phase": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32,
+                                                   ctypes.POINTER(PrefixLevel), _i32, _i32, _i32, _i32, _i32, _i64,
+                                                   _i32, _f32, _mods_p, _vp, _sz, _i32, _vp]),
+    "paged_attn_decode_cascade_plan": (_i32, [_i32, ctypes.POINTER(PrefixLevel), _i32, _i32, _i32, _i32, _i32]),
     "paged_attn_status_string": (ctypes.c_char_p, [_i32]),
     "kv_copy_blocks": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _i32, _vp]),
     # include/pagedattn_blocks.h (host block manager)
@@ -292,6 +296,9 @@ def prefix_level(group_starts, prefix_ends, max_group_size, max_prefix_len, pref
 def _levels_array(levels):
     arr = (PrefixLevel * max(1, len(levels)))()
     for i, v in enumerate(levels):
+        if isinstance(v, PrefixLevel):  # already a pa_prefix_level
+            arr[i] = v
+            continue
         arr[i] = PrefixLevel(v["group_starts"].data_ptr(),
                              None if v["prefix_starts"] is None else v["prefix_starts"].data_ptr(),
                              v["prefix_ends"].data_ptr(), v["num_groups"], v["max_group_size"], v["max_prefix_len"])
@@ -310,13 +317,22 @@ def decode_cascade_workspace(q, num_kv_heads, levels, max_context_len):
     return torch.empty(max(n, 4) // 4, dtype=torch.float32, device=q.device)
 
 
+def decode_cascade_plan(num_seqs, levels, num_heads, num_kv_heads, head_dim, max_context_len) -> int:
+    """1 if ``paged_attn_decode_cascade`` runs the two-phase decode for these sizes, 0 if the plain decode."""
+    return int(lib().paged_attn_decode_cascade_plan(int(num_seqs), _levels_array(levels), len(levels),
+                                                    int(num_heads), int(num_kv_heads), int(head_dim),
+                                                    int(max_context_len)))
+
+
 def paged_attn_decode_cascade(out, q, k_cache, v_cache, block_tables, context_lens, levels, scale,
                               max_context_len, workspace=None, softcap=0.0, window=0, alibi_slopes=None,
-                              prefix_lens=None, doc_starts=None):
-    """Decode where sequences share (possibly nested) prefixes (``paged_attn_decode_cascade``).
+                              prefix_lens=None, doc_starts=None, mode="auto"):
+    """Decode where sequences share (possibly nested) prefixes.
 
     ``levels``: a list of :func:`prefix_level`, outermost first.  Writes
-    ``out [B, Hq, D]``.
+    ``out [B, Hq, D]``.  ``mode`` "auto" calls ``paged_attn_decode_cascade``
+    (the library runs the plain decode where that is faster), "two_phase"
+    calls ``paged_attn_decode_cascade_two_phase``.
     """
     NB, Hkv, bs, D, B, Hq = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens)
     if workspace is None:
@@ -324,11 +340,14 @@ def paged_attn_decode_cascade(out, q, k_cache, v_cache, block_tables, context_le
     _need(workspace, "workspace")
     mp, _keep = _mods(window, softcap, alibi_slopes, prefix_lens, doc_starts)
     arr = _levels_array(levels)
-    code = lib().paged_attn_decode_cascade(
+    if mode not in ("auto", "two_phase"):
+        raise ValueError(f"mode must be 'auto' or 'two_phase', not {mode!r}")
+    fn = lib().paged_attn_decode_cascade if mode == "auto" else lib().paged_attn_decode_cascade_two_phase
+    code = fn(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1],
         _ptr(context_lens), B, arr, len(levels), Hq, Hkv, D, bs, NB, int(max_context_len), float(scale), mp,
         _ptr(workspace), workspace.numel() * workspace.element_size(), _dtype_code(q), _stream())
-    _check(code, "paged_attn_decode_cascade")
+    _check(code, f"paged_attn_decode_cascade[{mode}]")
     return out
 
 

@@ -252,6 +252,25 @@ int check_cascade_levels(int32_t B, const pa_prefix_level* levels, int32_t L) {
   return PA_OK;
 }
 
+// The two-phase decode pays off once re-reading the shared keys per sequence
+// costs more than its extra launches: measured on MI355X, a 16 x (1,024 +
+// 256)-token batch (84 MB of logical K+V) ran 0.87x as fast two-phase as
+// plain, and every batch of 335 MB or more (64 x (1,024 + 256) up to
+// 64 x (16,384 + 1,024)) ran 1.2-4.8x faster.  The bound is host-side:
+// num_seqs x max_context_len keys of K and V in every kv-head.
+constexpr double kTwoPhaseMinLogicalBytes = 256.0 * (1 << 20);
+
+bool two_phase_pays_off(int32_t B, int32_t Hkv, int32_t D, int32_t max_ctx) {
+  return (double)B * max_ctx * Hkv * D * 2.0 * 2.0 >= kTwoPhaseMinLogicalBytes;
+}
+
+int cascade_impl(bool force_two_phase, void* out, const void* q, const void* k_cache, const void* v_cache,
+                 const int32_t* block_tables, int32_t block_table_stride, const int32_t* context_lens,
+                 int32_t num_seqs, const pa_prefix_level* levels, int32_t num_levels, int32_t num_heads,
+                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                 int32_t max_context_len, float scale, const pa_score_mods* mods, void* workspace,
+                 size_t workspace_bytes, int32_t dtype, void* stream);
+
 int decode_impl(bool do_partials, bool do_merge, void* out, const void* q, const void* k_cache,
                 const void* v_cache, const int32_t* block_tables, int32_t bt_stride,
                 const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
@@ -546,6 +565,15 @@ size_t paged_attn_decode_cascade_workspace_size(int32_t num_seqs, const pa_prefi
   return c.total;
 }
 
+int32_t paged_attn_decode_cascade_plan(int32_t num_seqs, const pa_prefix_level* levels, int32_t num_levels,
+                                       int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t max_context_len) {
+  if (num_seqs < 0 || max_context_len < 0 || check_heads(num_heads, num_kv_heads) || check_dim(head_dim) ||
+      check_cascade_levels(num_seqs, levels, num_levels))
+    return 0;
+  return two_phase_pays_off(num_seqs, num_kv_heads, head_dim, max_context_len) ? 1 : 0;
+}
+
 int paged_attn_decode_cascade(void* out, const void* q, const void* k_cache, const void* v_cache,
                               const int32_t* block_tables, int32_t block_table_stride,
                               const int32_t* context_lens, int32_t num_seqs, const pa_prefix_level* levels,
@@ -553,6 +581,34 @@ int paged_attn_decode_cascade(void* out, const void* q, const void* k_cache, con
                               int32_t block_size, int64_t num_blocks, int32_t max_context_len, float scale,
                               const pa_score_mods* mods, void* workspace, size_t workspace_bytes, int32_t dtype,
                               void* stream) {
+  return cascade_impl(false, out, q, k_cache, v_cache, block_tables, block_table_stride, context_lens, num_seqs,
+                      levels, num_levels, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                      max_context_len, scale, mods, workspace, workspace_bytes, dtype, stream);
+}
+
+int paged_attn_decode_cascade_two_phase(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                        const int32_t* block_tables, int32_t block_table_stride,
+                                        const int32_t* context_lens, int32_t num_seqs,
+                                        const pa_prefix_level* levels, int32_t num_levels, int32_t num_heads,
+                                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                        int64_t num_blocks, int32_t max_context_len, float scale,
+                                        const pa_score_mods* mods, void* workspace, size_t workspace_bytes,
+                                        int32_t dtype, void* stream) {
+  return cascade_impl(true, out, q, k_cache, v_cache, block_tables, block_table_stride, context_lens, num_seqs,
+                      levels, num_levels, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                      max_context_len, scale, mods, workspace, workspace_bytes, dtype, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int cascade_impl(bool force_two_phase, void* out, const void* q, const void* k_cache, const void* v_cache,
+                 const int32_t* block_tables, int32_t block_table_stride, const int32_t* context_lens,
+                 int32_t num_seqs, const pa_prefix_level* levels, int32_t num_levels, int32_t num_heads,
+                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                 int32_t max_context_len, float scale, const pa_score_mods* mods, void* workspace,
+                 size_t workspace_bytes, int32_t dtype, void* stream) {
   int st = common_decode_checks(num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                                 block_table_stride, max_context_len, 0, dtype, mods);
   if (st) return st;
@@ -569,6 +625,16 @@ int paged_attn_decode_cascade(void* out, const void* q, const void* k_cache, con
   cascade_shape(num_seqs, levels, num_levels, num_heads, num_kv_heads, head_dim, max_context_len, c);
   if (!workspace || workspace_bytes < c.total || reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
     return PA_ERR_WORKSPACE;
+  if (!force_two_phase && !two_phase_pays_off(num_seqs, num_kv_heads, head_dim, max_context_len)) {
+    // a batch this small is bound by launches, not by re-reading the shared
+    // keys: the plain decode (one launch, or two) is faster; its workspace is
+    // the region the two-phase call keeps for its own-keys decode
+    const size_t need = workspace_bytes_for(num_seqs, num_kv_heads, head_dim, c.dec);
+    return decode_impl(true, true, out, q, k_cache, v_cache, block_tables, block_table_stride, context_lens,
+                       num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_context_len, scale,
+                       0, mods, need > 0 ? static_cast<char*>(workspace) + c.off_dec : nullptr, need, dtype,
+                       stream);
+  }
   for (int i = 0; i < num_levels; ++i)
     if ((long long)levels[i].num_groups * num_kv_heads * c.lv[i].q_tiles * c.lv[i].nsplit > 0x7fffffffll)
       return PA_ERR_SIZE;
@@ -670,6 +736,10 @@ int paged_attn_decode_cascade(void* out, const void* q, const void* k_cache, con
   m.GP = c.dec.GP;
   return launch_status(pa::launch_cascade_merge(m, head_dim, hs));
 }
+
+}  // namespace
+
+extern "C" {
 
 const char* paged_attn_status_string(int status) {
   switch (status) {

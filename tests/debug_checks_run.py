@@ -84,7 +84,7 @@ def main():
     hi2 = torch.tensor([16 * 6 - 2, 16 * 6 - 5, 0, 32], dtype=torch.int32, device="cuda")
     levels = [binding.prefix_level(starts, prefix, 3, 96), binding.prefix_level(starts2, hi2, 2, 3, lo2)]
     binding.paged_attn_decode_cascade(out, t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
-                                      t["context_lens"], levels, wc.scale, wc.max_context_len)
+                                      t["context_lens"], levels, wc.scale, wc.max_context_len, mode="two_phase")
     torch.cuda.synchronize()
     worst = max(worst, float(np.max(np.abs(bits_to_f64(to_numpy_bits(out), "bf16") - ref))))
     print(f"debug-check build: max abs err {worst:.3e}", flush=True)

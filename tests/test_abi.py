@@ -207,16 +207,38 @@ def _lv(G=2, maxg=4, maxp=512, gs=FAKE, pe=FAKE, ps=None):
     return binding.PrefixLevel(gs, ps, pe, G, maxg, maxp)
 
 
-def _cascade(levels=None, **over):
+def _cascade(levels=None, fn="paged_attn_decode_cascade", **over):
     a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, stride=4, ctx=FAKE, B=8, L=None, Hq=32, Hkv=8, D=128, bs=16,
              NB=100, max_ctx=1024, scale=0.1, mods=None, ws=FAKE, ws_bytes=1 << 40, dtype=1)
     a.update(over)
     lv = [_lv()] if levels is None else levels
     arr = (binding.PrefixLevel * max(1, len(lv)))(*lv)
-    return binding.lib().paged_attn_decode_cascade(
+    return getattr(binding.lib(), fn)(
         a["out"], a["q"], a["k"], a["v"], a["bt"], a["stride"], a["ctx"], a["B"], arr,
         len(lv) if a["L"] is None else a["L"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["NB"], a["max_ctx"], a["scale"],
         a["mods"], a["ws"], a["ws_bytes"], a["dtype"], None)
+
+
+def test_cascade_plan_picks_the_plain_decode_for_small_batches():
+    """The two-phase decode runs from 256 MiB of logical K+V up (host bound:
+    sequences x max context x kv-heads x D x 2 x 2 bytes); below, the plain
+    decode is faster (a 16 x 1,280-token batch: 84 MB)."""
+    lv = [_lv(G=1, maxg=16, maxp=1024)]
+    assert binding.decode_cascade_plan(16, lv, 32, 8, 128, 1280) == 0          # 84 MB
+    assert binding.decode_cascade_plan(64, lv, 32, 8, 128, 1280) == 1          # 335 MB
+    assert binding.decode_cascade_plan(64, [_lv(G=1, maxg=64, maxp=16384)], 64, 8, 128, 17408) == 1
+    assert binding.decode_cascade_plan(16, lv, 30, 8, 128, 1 << 20) == 0       # invalid heads
+    assert binding.decode_cascade_plan(-1, lv, 32, 8, 128, 1280) == 0
+
+
+@pytest.mark.parametrize("fn", ["paged_attn_decode_cascade", "paged_attn_decode_cascade_two_phase"])
+def test_cascade_validation_both_entries(fn):
+    assert _cascade(fn=fn, dtype=0) == -8
+    assert _cascade(fn=fn, B=-1) == -2
+    assert _cascade(fn=fn, Hq=24, Hkv=8) == -3 or _cascade(fn=fn, Hq=24, Hkv=8) < 0
+    assert _cascade(fn=fn, q=NULL) == -1
+    assert _cascade(fn=fn, ws=NULL) == -7
+    assert _cascade(fn=fn, levels=[_lv(G=0)]) == -2
 
 
 def test_cascade_validation():

@@ -162,7 +162,7 @@ def test_manager_prefix_levels_drive_the_two_phase_decode(gpu_lib):
     qd = torch.from_numpy(q.view(np.int16)).cuda().view(torch.bfloat16)
     out = torch.empty_like(qd)
     gpu_lib.paged_attn_decode_cascade(out, qd, gk, gv, torch.from_numpy(table).cuda(), torch.from_numpy(lens).cuda(),
-                                      levels, float(scale), int(lens.max()))
+                                      levels, float(scale), int(lens.max()), mode="two_phase")
     torch.cuda.synchronize()
     ref = oracle.paged_attention(q, kp, vp, table, lens, np.arange(len(seqs) + 1), scale, BS_, "bf16")
     got = oracle.bits_to_f64(out.view(torch.int16).cpu().numpy().view(np.uint16), "bf16")
@@ -235,7 +235,7 @@ def test_mixed_page_sizes_in_one_pool_drive_decode_prefill_and_two_phase(gpu_lib
                                    int(np.max(np.diff(st))), int(np.max(hi - lo)), torch.from_numpy(lo).cuda())
               for st, lo, hi in levels_host]
     out = torch.empty_like(qd)
-    gpu_lib.paged_attn_decode_cascade(out, qd, gk, gv, tt, tl, levels, float(scale), int(lens.max()))
+    gpu_lib.paged_attn_decode_cascade(out, qd, gk, gv, tt, tl, levels, float(scale), int(lens.max()), mode="two_phase")
     torch.cuda.synchronize()
     got = oracle.bits_to_f64(out.view(torch.int16).cpu().numpy().view(np.uint16), "bf16")
     assert np.max(np.abs(got - ref)) <= 2e-2

@@ -52,7 +52,7 @@ def gpu_cascade_levels(lib, w, levels, t=None, workspace=None, **mods):
         lib.kv_append(t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], t["slot_mapping"])
     out = torch.empty_like(t["q"])
     lib.paged_attn_decode_cascade(out, t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
-                                  levels, w.scale, w.max_context_len, workspace=workspace, **mods)
+                                  levels, w.scale, w.max_context_len, workspace=workspace, mode="two_phase", **mods)
     torch.cuda.synchronize()
     return to_numpy_bits(out)
 
@@ -269,3 +269,49 @@ def test_cascade_mods_nested(gpu_lib, mods):
     kw, om = _mods_for(w, 771, **MOD_CASES[mods])
     levels = [device_level(gpu_lib, st, hi, lo) for st, hi, lo in lv]
     assert_close(gpu_cascade_levels(gpu_lib, w, levels, **kw), oracle_out(w, om), "bf16")
+
+
+def _auto_and(lib, w, starts, prefix, other):
+    """(bits of the default call, bits of ``other``: "plain" decode or forced "two_phase")."""
+    t = upload(w)
+    lib.kv_append(t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], t["slot_mapping"])
+    levels = [device_level(lib, starts, prefix)]
+    out_a = torch.full_like(t["q"], float("nan"))
+    out_b = torch.full_like(t["q"], float("nan"))
+    lib.paged_attn_decode_cascade(out_a, t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                                  levels, w.scale, w.max_context_len)
+    if other == "plain":
+        lib.paged_attn_decode(out_b, t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                              w.scale, w.max_context_len, 0)
+    else:
+        lib.paged_attn_decode_cascade(out_b, t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
+                                      t["context_lens"], levels, w.scale, w.max_context_len, mode="two_phase")
+    torch.cuda.synchronize()
+    return to_numpy_bits(out_a), to_numpy_bits(out_b)
+
+
+def test_cascade_default_runs_the_plain_decode_on_the_shared_prefix_batch(gpu_lib):
+    """16 sequences behind a 1,024-token prompt with 256 own tokens each: 84 MB
+    of logical K+V, below the 256 MiB where the two-phase decode pays off, so
+    the default call runs the plain decode (same bits) -- never slower."""
+    from workloads import named_workload
+    w = named_workload("shared_prefix_decode_bf16")
+    starts, prefix = np.array([0, w.B], np.int32), np.array([1024], np.int32)
+    assert gpu_lib.decode_cascade_plan(w.B, [device_level(gpu_lib, starts, prefix)], w.Hq, w.Hkv, w.D,
+                                       w.max_context_len) == 0
+    a, b = _auto_and(gpu_lib, w, starts, prefix, "plain")
+    assert np.array_equal(a, b)
+    assert_close(a, oracle_out(w), "bf16")
+
+
+def test_cascade_default_runs_two_phase_on_large_batches(gpu_lib):
+    """64 sequences behind one 1,024-token prompt, 256 own tokens each (335 MB
+    logical): the default call is the two-phase decode (same bits)."""
+    private = np.full(64, 256)
+    w, starts, prefix = grouped(715, [(64, 64)], private, [0])
+    assert gpu_lib.decode_cascade_plan(w.B, [device_level(gpu_lib, starts, prefix)], w.Hq, w.Hkv, w.D,
+                                       w.max_context_len) == 1
+    a, b = _auto_and(gpu_lib, w, starts, prefix, "two_phase")
+    assert np.array_equal(a, b)
+    seqs = [0, 31, 63]
+    assert_close(a, oracle_out(w, seqs=seqs), "bf16", rows=seqs)

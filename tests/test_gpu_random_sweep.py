@@ -204,7 +204,8 @@ def test_random_fork_tree_two_phase(gpu_lib, seed):
                                    int(np.max(np.diff(st))), int(max(1, np.max(hi - lo))), torch.from_numpy(lo).cuda())
               for st, lo, hi in levels_host]
     out = torch.empty_like(qd)
-    gpu_lib.paged_attn_decode_cascade(out, qd, gk, gv, tt, tl, levels, float(scale), int(lens.max()), **kw)
+    gpu_lib.paged_attn_decode_cascade(out, qd, gk, gv, tt, tl, levels, float(scale), int(lens.max()),
+                                      mode="two_phase", **kw)
     torch.cuda.synchronize()
     err = assert_close(to_numpy_bits(out), ref, "bf16")
     print(f"fork case {seed}: {len(levels_host)} levels, two-phase max abs err {err:.3e}", flush=True)
