@@ -178,6 +178,74 @@ def fragmentation(context_lens):
     return out
 
 
+class _HipTimer:
+    """HIP events made with hipEventDisableSystemFence: recording one writes a
+    timestamp without the system-scope cache write-back and invalidation a
+    default event performs, which adds several microseconds between
+    consecutive kernels (the runtime's own note on the flag: it improves the
+    accuracy of timing).  Bound through ctypes to the HIP runtime torch has
+    already loaded, so the events live on the same runtime and stream as the
+    kernels."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    path = line.split()[-1]
+                    break
+        if path is None:
+            raise RuntimeError("the HIP runtime is not loaded")
+        self.c = ctypes
+        L = ctypes.CDLL(path)
+        L.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        L.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.L = L
+
+    def event(self):
+        return _HipEvent(self)
+
+
+class _HipEvent:
+    def __init__(self, timer):
+        self.t = timer
+        self.h = timer.c.c_void_p()
+        if timer.L.hipEventCreateWithFlags(timer.c.byref(self.h), _HipTimer.DISABLE_SYSTEM_FENCE) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+
+    def record(self, stream):
+        if self.t.L.hipEventRecord(self.h, self.t.c.c_void_p(stream.cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_time(self, other):
+        ms = self.t.c.c_float()
+        if self.t.L.hipEventElapsedTime(self.t.c.byref(ms), self.h, other.h) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def __del__(self):
+        try:
+            self.t.L.hipEventDestroy(self.h)
+        except Exception:
+            pass
+
+
+_TIMER = None
+
+
+def new_event(torch):
+    """A timing event on the kernels' stream: fence-free HIP event by default,
+    torch's (default HIP flags) with --event-fence system."""
+    if _TIMER is None:
+        return torch.cuda.Event(enable_timing=True)
+    return _TIMER.event()
+
+
 def time_calls(torch, fn, flush, reps, warm=3):
     """Median GPU time (ms) of ``fn``, each call after a cache-evicting flush;
     events bracket only the call, and the flush keeps the GPU busy while the
@@ -189,8 +257,8 @@ def time_calls(torch, fn, flush, reps, warm=3):
     evs = []
     for _ in range(reps):
         flush()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
+        a = new_event(torch)
+        b = new_event(torch)
         a.record(stream)
         fn()
         b.record(stream)
@@ -223,9 +291,10 @@ def shared_prefix_long():
                           shared_prefix_blocks=16384 // 16, pool_slack=1.05)
 
 
-def two_phase_call(pa, torch, dev, w, t, out, pre):
-    """(workspace, call) of the two-phase decode of a batch that is one group
-    sharing its first ``pre`` tokens."""
+def two_phase_call(pa, torch, dev, w, t, out, pre, mode="two_phase"):
+    """(workspace, call) of the shared-prefix decode of a batch that is one
+    group sharing its first ``pre`` tokens: forced two-phase, or the library's
+    default choice (``mode="auto"``)."""
     gs = torch.tensor([0, w.B], dtype=torch.int32, device=dev)
     pl = torch.tensor([pre], dtype=torch.int32, device=dev)
     levels = [pa.prefix_level(gs, pl, w.B, pre)]
@@ -233,7 +302,8 @@ def two_phase_call(pa, torch, dev, w, t, out, pre):
 
     def call():
         pa.paged_attn_decode_cascade(out, t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
-                                     t["context_lens"], levels, w.scale, w.max_context_len, workspace=ws2)
+                                     t["context_lens"], levels, w.scale, w.max_context_len, workspace=ws2, mode=mode)
+    call.plan = pa.decode_cascade_plan(w.B, levels, w.Hq, w.Hkv, w.D, w.max_context_len)
     return ws2, call
 
 
@@ -273,6 +343,56 @@ def two_phase_main(args, pa, torch, dev):
                                "block 16, one group", "kv_bytes": int(w.kv_bytes()), "unique_kv_bytes": int(unique),
                    "prefix_flops": 4.0 * w.B * w.Hq * 16384 * w.D},
         "plain_decode_ms": round(ms_plain, 5), "speedup_vs_plain_decode": round(ms_plain / ms, 3)}), flush=True)
+
+
+def small_decode_main(args, pa, torch, dev):
+    """``--path small_decode``: the decode of the three small workloads alone
+    (single-sequence fp32, GQA batch with its append, shared-prefix batch
+    plain, two-phase and default), ``--steps`` calls each after a
+    cache-evicting write; one JSON line.  Made for kernel traces of these
+    workloads."""
+    from workloads import named_workload
+    from workloads.device import upload
+    flush_buf = torch.empty(max(1, args.flush_mib) << 18, dtype=torch.int32, device=dev)
+
+    def flush():
+        if args.flush_mib > 0:
+            pa.bench_fill(flush_buf, 0)
+    res = {}
+    for name in ("single_decode_f32", "gqa_decode_bf16", "shared_prefix_decode_bf16"):
+        w = named_workload(name)
+        t = upload(w, dev)
+        out = torch.empty_like(t["q"])
+        ws = pa.decode_workspace(t["q"], w.Hkv, w.max_context_len, 0)
+        has_append = len(w.slot_mapping) > 0
+
+        def append():
+            if has_append:
+                pa.kv_append(t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], t["slot_mapping"])
+
+        def decode(split=0, ws=ws):
+            pa.paged_attn_decode(out, t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
+                                 w.scale, w.max_context_len, split, workspace=ws)
+        append()
+        entry = {"kv_bytes": int(w.kv_bytes()),
+                 "append_ms": round(time_calls(torch, append, flush, reps=args.steps), 5) if has_append else None,
+                 "decode_ms": round(time_calls(torch, decode, flush, reps=args.steps), 5),
+                 "decode_split": int(pa.decode_split_tokens(w.B, w.Hkv, w.max_context_len, 0))}
+        entry["decode_gbs"] = round(w.kv_bytes() / (entry["decode_ms"] * 1e-3) / 1e9, 2)
+        for split, key in ((-2, "workgroup_split_ms"), (-3, "balanced_split_ms")):
+            ws_s = pa.decode_workspace(t["q"], w.Hkv, w.max_context_len, split)
+            entry[key] = round(time_calls(torch, lambda: decode(split, ws_s), flush, reps=args.steps), 5)
+        if name == "shared_prefix_decode_bf16":
+            for mode in ("two_phase", "auto"):
+                _, call = two_phase_call(pa, torch, dev, w, t, out, 1024, mode=mode)
+                entry[f"{mode}_ms"] = round(time_calls(torch, call, flush, reps=args.steps), 5)
+            entry["unique_kv_bytes"] = int(w.unique_kv_bytes())
+        res[name] = entry
+        log(f"{name}: {entry}")
+        del t, out, ws
+    print(json.dumps({"metric": "small-batch paged decode latency, 1 MI355X", "unit": "ms", "n_gpus": 1,
+                      "steps": args.steps, "higher_is_better": False, "data": "synthetic", "dtype": "bf16/f32",
+                      "workloads": res}), flush=True)
 
 
 def extra_measurements(pa, torch, dev, flush, args):
@@ -335,14 +455,19 @@ def extra_measurements(pa, torch, dev, flush, args):
         ms_plain = time_calls(torch, decode_fn(w, t, out, ws), flush, reps=20)
         ws2, two_phase = two_phase_call(pa, torch, dev, w, t, out, pre)
         ms_two = time_calls(torch, two_phase, flush, reps=20)
+        ws3, auto = two_phase_call(pa, torch, dev, w, t, out, pre, mode="auto")
+        ms_auto = time_calls(torch, auto, flush, reps=20)
         unique = w.unique_kv_bytes()
         prefix_flops = 4.0 * w.B * w.Hq * pre * w.D
         two[name] = {"plain_ms": round(ms_plain, 5), "two_phase_ms": round(ms_two, 5),
-                     "speedup": round(ms_plain / ms_two, 3), "kv_bytes": int(w.kv_bytes()),
+                     "speedup": round(ms_plain / ms_two, 3),
+                     "default_call": "two_phase" if auto.plan else "plain decode",
+                     "default_call_ms": round(ms_auto, 5), "default_speedup": round(ms_plain / ms_auto, 3),
+                     "kv_bytes": int(w.kv_bytes()),
                      "unique_kv_bytes": int(unique),
                      "two_phase_unique_gbs": round(unique / (ms_two * 1e-3) / 1e9, 2),
                      "prefix_flops": prefix_flops}
-        del t, out, ws, ws2
+        del t, out, ws, ws2, ws3
     res["shared_prefix_two_phase"] = two
     log("two-phase decode measured")
 
@@ -383,9 +508,12 @@ def main():
                          "above the tolerance (0: skip)")
     ap.add_argument("--flush-mib", type=int, default=512,
                     help="cache-evicting write before every timed call (0: none)")
-    ap.add_argument("--path", choices=("step", "two_phase"), default="step",
+    ap.add_argument("--path", choices=("step", "two_phase", "small_decode"), default="step",
                     help="step: the hot-path step (default); two_phase: the two-phase decode of a "
-                         "long shared-prompt batch")
+                         "long shared-prompt batch; small_decode: the decode of the three small workloads")
+    ap.add_argument("--event-fence", choices=("none", "system"), default="none",
+                    help="timing events: none = HIP events without the system-scope fence (default); "
+                         "system = torch's events with HIP's default flags")
     ap.add_argument("--extras", type=int, default=1,
                     help="1: also measure achievable HBM, the other workloads and the context sweep")
     args = ap.parse_args()
@@ -407,8 +535,15 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     pa.lib()
+    global _TIMER
+    if args.event_fence == "none":
+        torch.zeros(1, device=dev)  # the HIP runtime is loaded and initialised
+        _TIMER = _HipTimer()
     if args.path == "two_phase":
         two_phase_main(args, pa, torch, dev)
+        return
+    if args.path == "small_decode":
+        small_decode_main(args, pa, torch, dev)
         return
 
     log("generating long-context decode batch")
@@ -462,7 +597,7 @@ def main():
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps)")
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    events = [[new_event(torch) for _ in range(6)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_begin = time.perf_counter()
     for k in range(args.steps):
@@ -497,7 +632,7 @@ def main():
         ws_f = pa.decode_workspace(t5["q"], w5.Hkv, w5.max_context_len, args.fixed_split)
         evs = []
         for k in range(args.warmup + args.steps):
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e = [new_event(torch) for _ in range(3)]
             e[0].record(stream)
             pa.paged_attn_decode(out5, t5["q"], t5["k_cache"], t5["v_cache"], t5["block_tables"],
                                  t5["context_lens"], w5.scale, w5.max_context_len, args.fixed_split, workspace=ws_f,
@@ -583,6 +718,8 @@ def main():
                 "algorithmic_flops_per_launch": flops,
             },
         },
+        "timing_events": ("HIP events created with hipEventDisableSystemFence (no cache write-back between "
+                          "kernels)" if args.event_fence == "none" else "torch.cuda.Event (HIP default flags)"),
         "phases_ms": {
             "kv_append_decode_batch": round(ms_append5, 5),
             "decode_partitions": round(ms_partials, 5),
