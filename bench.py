@@ -379,9 +379,8 @@ def small_decode_main(args, pa, torch, dev):
                  "decode_ms": round(time_calls(torch, decode, flush, reps=args.steps), 5),
                  "decode_split": int(pa.decode_split_tokens(w.B, w.Hkv, w.max_context_len, 0))}
         entry["decode_gbs"] = round(w.kv_bytes() / (entry["decode_ms"] * 1e-3) / 1e9, 2)
-        for split, key in ((-2, "workgroup_split_ms"), (-3, "balanced_split_ms")):
-            ws_s = pa.decode_workspace(t["q"], w.Hkv, w.max_context_len, split)
-            entry[key] = round(time_calls(torch, lambda: decode(split, ws_s), flush, reps=args.steps), 5)
+        ws_f = pa.decode_workspace(t["q"], w.Hkv, w.max_context_len, 512)
+        entry["fixed_512_split_ms"] = round(time_calls(torch, lambda: decode(512, ws_f), flush, reps=args.steps), 5)
         if name == "shared_prefix_decode_bf16":
             for mode in ("two_phase", "auto"):
                 _, call = two_phase_call(pa, torch, dev, w, t, out, 1024, mode=mode)
