@@ -9,6 +9,7 @@ the passages of the source pages each one follows.
 """
 
 from .paged import (  # noqa: F401
+    BlockMask,
     ScoreMods,
     attention_dense,
     bits_to_f64,

@@ -57,6 +57,36 @@ def bits_to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
 
 
 @dataclasses.dataclass
+class BlockMask:
+    """Block-sparse mask in the manner of FlexAttention's block mask: which
+    key blocks each query block may see at all (Joshi et al., "Paged
+    Attention Meets FlexAttention", abstract: the paged kernel keeps
+    FlexAttention's programmable masks; skipping whole blocks is how a block
+    mask saves work).
+
+    ``bits`` is uint32 ``[num_seqs * rows_per_seq, words]``.  For sequence
+    ``b`` and a query at logical position ``p`` the row is
+    ``b * rows_per_seq + p // q_block``; key ``j`` is admissible only if bit
+    ``(j // kv_block) % 32`` of word ``(j // kv_block) // 32`` of that row is
+    set (bit 0 = least significant).  Other masks still apply inside the
+    admitted blocks.
+    """
+
+    bits: np.ndarray
+    q_block: int
+    kv_block: int
+    rows_per_seq: int
+
+    def keys_allowed(self, b, q_pos, n):
+        """Boolean ``[len(q_pos), n]``: the block mask for these query positions."""
+        q_pos = np.asarray(q_pos, dtype=np.int64)
+        rows = b * self.rows_per_seq + q_pos // self.q_block
+        kb = np.arange(n, dtype=np.int64) // self.kv_block
+        words = np.asarray(self.bits, dtype=np.uint64)[rows][:, kb // 32]  # [Lq, n]
+        return ((words >> (kb % 32).astype(np.uint64)[None, :]) & np.uint64(1)).astype(bool)
+
+
+@dataclasses.dataclass
 class ScoreMods:
     """FlexAttention-style modifications, all on logical positions.
 
@@ -71,6 +101,8 @@ class ScoreMods:
       window > 0      : q_pos - kv_pos < window
       doc_starts      : kv_pos >= doc_starts[row] (document masking of packed
                         sequences: a row sees nothing before its document)
+      block_mask      : the key's block is admitted for the query's block
+                        (:class:`BlockMask`)
     ``prefix_lens`` is per sequence ``[B]``; ``doc_starts`` per query row
     ``[sum Lq]`` (decode: one per sequence).
     """
@@ -81,6 +113,7 @@ class ScoreMods:
     alibi_slopes: np.ndarray | None = None
     prefix_lens: np.ndarray | None = None
     doc_starts: np.ndarray | None = None
+    block_mask: BlockMask | None = None
 
 
 def v_group(bs):
@@ -140,14 +173,16 @@ def gather_sequence(k_pool, v_pool, table_row, n, bs):
     return K, V
 
 
-def attention_dense(Q, K, V, scale, q_pos, mods: ScoreMods | None = None, prefix_len=0, doc_start=None):
+def attention_dense(Q, K, V, scale, q_pos, mods: ScoreMods | None = None, prefix_len=0, doc_start=None,
+                    keys_allowed=None):
     """Exact attention of query rows at logical positions ``q_pos``.
 
     ``Q`` ``[Lq, Hq, D]``, ``K``/``V`` ``[Hkv, n, D]`` (fp64), key ``j`` sits at
     logical position ``j``.  Query head ``h`` uses kv-head ``h // (Hq/Hkv)``.
     ``prefix_len`` (this sequence's prefix-LM length) and ``doc_start``
     (``[Lq]``, each row's document start) are the per-sequence and per-row
-    values of ``mods.prefix_lens`` / ``mods.doc_starts``.
+    values of ``mods.prefix_lens`` / ``mods.doc_starts``; ``keys_allowed``
+    (boolean ``[Lq, n]``) is this sequence's block mask, if any.
     Returns fp64 ``[Lq, Hq, D]``; rows with no admissible key are zero.
     """
     mods = mods or ScoreMods()
@@ -166,6 +201,8 @@ def attention_dense(Q, K, V, scale, q_pos, mods: ScoreMods | None = None, prefix
         allowed &= (qp - kp) < mods.window
     if doc_start is not None:
         allowed &= kp >= np.asarray(doc_start, dtype=np.int64)[:, None]
+    if keys_allowed is not None:
+        allowed &= np.asarray(keys_allowed, dtype=bool)
     for h in range(Hq):
         kvh = h // g
         S = (Q[:, h, :] @ K[kvh].T) * float(scale)
@@ -208,7 +245,9 @@ def paged_attention(q, k_pool, v_pool, block_table, context_lens, cu_q_lens, sca
         q_pos = np.arange(n - Lq, n)
         prefix = 0 if mods is None or mods.prefix_lens is None else int(mods.prefix_lens[b])
         docs = None if mods is None or mods.doc_starts is None else np.asarray(mods.doc_starts)[r0:r1]
-        out[r0:r1] = attention_dense(q64[r0:r1], Kb, Vb, float(np.float32(scale)), q_pos, mods, prefix, docs)
+        blocks = None if mods is None or mods.block_mask is None else mods.block_mask.keys_allowed(b, q_pos, n)
+        out[r0:r1] = attention_dense(q64[r0:r1], Kb, Vb, float(np.float32(scale)), q_pos, mods, prefix, docs,
+                                     blocks)
     return out
 
 

@@ -175,10 +175,11 @@ def test_bf16_decode_every_pattern():
         assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
 
 
-def brute_force(w, mods):
+def brute_force(w, mods, block_dense=None, q_block=1, kv_block=1):
     """Two-pass softmax with math.exp, reading each key through its table
     entry; stored values are decoded by :func:`decode_storage`, not by the
-    oracle."""
+    oracle.  ``block_dense[b][p // q_block][j // kv_block]`` (booleans, not the
+    packed bitmap) admits key j for the query at position p."""
     q = decode_storage(w.q, w.dtype)
     kp = decode_storage(w.k_pool, w.dtype)
     vp = decode_storage(w.v_pool, w.dtype)
@@ -201,6 +202,8 @@ def brute_force(w, mods):
                     if mods.window and pos - j >= mods.window:
                         continue
                     if j < doc:
+                        continue
+                    if block_dense is not None and not block_dense[b][pos // q_block][j // kv_block]:
                         continue
                     blk = int(w.block_table[b][j // w.bs])
                     off = j % w.bs
@@ -538,6 +541,93 @@ def test_kv_append_rejects_duplicates_and_skips_negative():
 
 
 # --------------------------------------------------------------------------------------
+# block masks (FlexAttention-style block sparsity)
+# --------------------------------------------------------------------------------------
+
+def pack_block_mask(dense, q_block, kv_block):
+    """Dense booleans [B, q_blocks, kv_blocks] -> oracle.BlockMask, packed with
+    numpy's little-endian bit order (bit i of the little-endian uint32 word is
+    block 32 * word + i)."""
+    dense = np.asarray(dense, dtype=bool)
+    B, QBn, KBn = dense.shape
+    words = (KBn + 31) // 32
+    padded = np.zeros((B * QBn, words * 32), dtype=bool)
+    padded[:, :KBn] = dense.reshape(B * QBn, KBn)
+    packed = np.packbits(padded, axis=1, bitorder="little").view("<u4")
+    return oracle.BlockMask(bits=np.ascontiguousarray(packed.astype(np.uint32)), q_block=q_block,
+                            kv_block=kv_block, rows_per_seq=QBn)
+
+
+def _random_blocks(rng, B, n_max, q_block, kv_block, density=0.5):
+    QBn = (n_max + q_block - 1) // q_block
+    KBn = (n_max + kv_block - 1) // kv_block
+    return rng.random((B, QBn, KBn)) < density
+
+
+def check_block_mask_equals_removing_keys(kind="prefill", q_block=4, kv_block=8, seed=41):
+    """Non-causal attention under a block mask equals attention over only the
+    admitted keys, gathered row by row (no positional mod, so removing keys is
+    all a mask does).  The bitmap is packed by numpy, the keys picked from the
+    dense booleans."""
+    rng = np.random.default_rng(seed)
+    w = _tiny(kind, seed, bs=4, ctx=(37, 50), q_lens=None if kind == "decode" else [9, 13])
+    dense = _random_blocks(rng, w.B, int(w.context_lens.max()), q_block, kv_block, 0.6)
+    bm = pack_block_mask(dense, q_block, kv_block)
+    got = _run(w, oracle.ScoreMods(block_mask=bm))
+    kp, vp = w.k_pool, w.v_pool
+    for b in range(w.B):
+        n = int(w.context_lens[b])
+        r0, r1 = int(w.cu_q_lens[b]), int(w.cu_q_lens[b + 1])
+        K, V = opa.gather_sequence(kp, vp, w.block_table[b], n, w.bs)
+        K, V = opa.bits_to_f64(K, w.dtype), opa.bits_to_f64(V, w.dtype)
+        for r in range(r0, r1):
+            pos = n - (r1 - r0) + (r - r0)
+            keep = [j for j in range(n) if dense[b][pos // q_block][j // kv_block]]
+            Q = opa.bits_to_f64(w.q[r:r + 1], w.dtype)
+            ref = opa.attention_dense(Q, K[:, keep], V[:, keep], float(np.float32(w.scale)), [len(keep)])
+            np.testing.assert_allclose(got[r:r + 1], ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("kind", ["decode", "prefill"])
+@pytest.mark.parametrize("q_block,kv_block", [(1, 4), (4, 8), (8, 32)])
+def test_block_mask_equals_removing_keys(kind, q_block, kv_block):
+    check_block_mask_equals_removing_keys(kind, q_block, kv_block)
+
+
+def test_block_mask_brute_force_with_causal_and_window():
+    w = _tiny("prefill", 43, bs=4, ctx=(29, 46), q_lens=[11, 17], causal=True)
+    dense = _random_blocks(np.random.default_rng(43), w.B, 46, 4, 8, 0.5)
+    mods = oracle.ScoreMods(causal=True, window=19, block_mask=pack_block_mask(dense, 4, 8))
+    np.testing.assert_allclose(_run(w, mods), brute_force(w, mods, dense, 4, 8), rtol=0, atol=1e-12)
+
+
+def test_block_mask_all_ones_and_block_causal():
+    """Every bit set is no mask at all; with q_block == kv_block, the
+    block-causal mask (key block <= query block) under causal masking is
+    causal masking alone (it removes only keys causal removes anyway)."""
+    w = _tiny("prefill", 44, bs=4, ctx=(33, 40), q_lens=[10, 12], causal=True)
+    plain = _run(w, oracle.ScoreMods(causal=True))
+    ones = np.ones((w.B, 40, 40), dtype=bool)
+    assert np.array_equal(_run(w, oracle.ScoreMods(causal=True, block_mask=pack_block_mask(ones, 1, 1))), plain)
+    qb = 8
+    nb = (40 + qb - 1) // qb
+    tri = np.broadcast_to(np.tril(np.ones((nb, nb), dtype=bool)), (w.B, nb, nb))
+    got = _run(w, oracle.ScoreMods(causal=True, block_mask=pack_block_mask(tri, qb, qb)))
+    assert np.array_equal(got, plain)
+    # and without causal masking the block-causal mask admits whole diagonal blocks
+    nc = _run(w, oracle.ScoreMods(causal=False, block_mask=pack_block_mask(tri, qb, qb)))
+    assert not np.allclose(nc, plain)
+
+
+def test_block_mask_row_without_blocks_is_zero():
+    w = _tiny("decode", 45, bs=4, ctx=(20, 9))
+    dense = np.ones((w.B, 1, 5), dtype=bool)
+    dense[1] = False
+    got = _run(w, oracle.ScoreMods(block_mask=pack_block_mask(dense, 64, 4)))
+    assert np.all(got[1] == 0) and np.all(np.isfinite(got[0])) and np.any(got[0] != 0)
+
+
+# --------------------------------------------------------------------------------------
 # planted mistakes: each must make at least one pin fail
 # --------------------------------------------------------------------------------------
 
@@ -555,6 +645,7 @@ def _all_pins():
     check_brute_force_large_pages(32)
     wb = _tiny("prefill", 11, dtype="bf16", q_lens=[5, 7], causal=True)
     np.testing.assert_allclose(_run(wb, mods), brute_force(wb, mods), rtol=0, atol=1e-12)
+    check_block_mask_equals_removing_keys("prefill", 4, 8)
 
 
 def _mutant_gather_v_not_transposed(k_pool, v_pool, table_row, n, bs):
@@ -587,40 +678,61 @@ def _mutant_bf16_low_bit_dropped(a, dtype):
     return opa.__dict__["_orig_bits"](a, dtype)
 
 
+def _mutant_block_rows_by_chunk_row(self, b, q_pos, n):
+    """Block-mask rows indexed by the row's place in the chunk, not its position."""
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    return opa.__dict__["_orig_keys_allowed"](self, b, q_pos - q_pos[0], n)
+
+
+def _mutant_block_bits_msb_first(self, b, q_pos, n):
+    """Bits of each word read from the most significant end."""
+    q_pos = np.asarray(q_pos, dtype=np.int64)
+    rows = b * self.rows_per_seq + q_pos // self.q_block
+    kb = np.arange(n, dtype=np.int64) // self.kv_block
+    words = np.asarray(self.bits, dtype=np.uint64)[rows][:, kb // 32]
+    return ((words >> (31 - kb % 32).astype(np.uint64)[None, :]) & np.uint64(1)).astype(bool)
+
+
 def _make_attention_mutant(kind):
     orig = opa.__dict__["_orig_attention"]
 
-    def mutant(Q, K, V, scale, q_pos, mods=None, prefix_len=0, doc_start=None):
+    def mutant(Q, K, V, scale, q_pos, mods=None, prefix_len=0, doc_start=None, keys_allowed=None):
         mods = mods or oracle.ScoreMods()
         if kind == "no_scale":
-            return orig(Q, K, V, 1.0, q_pos, mods, prefix_len, doc_start)
+            return orig(Q, K, V, 1.0, q_pos, mods, prefix_len, doc_start, keys_allowed)
         if kind == "top_left_causal":
-            return orig(Q, K, V, scale, np.arange(len(q_pos)), mods, prefix_len, doc_start)
+            return orig(Q, K, V, scale, np.arange(len(q_pos)), mods, prefix_len, doc_start, keys_allowed)
         if kind == "gqa_modulo":
             Hq, Hkv = Q.shape[1], K.shape[0]
             idx = np.arange(Hq) % Hkv  # wrong grouping
             Kx = K[idx]
             Vx = V[idx]
-            return orig(Q, Kx, Vx, scale, q_pos, mods, prefix_len, doc_start)
+            return orig(Q, Kx, Vx, scale, q_pos, mods, prefix_len, doc_start, keys_allowed)
         if kind == "no_max_sub_sign":
-            return orig(Q, K, V, -scale, q_pos, mods, prefix_len, doc_start)
+            return orig(Q, K, V, -scale, q_pos, mods, prefix_len, doc_start, keys_allowed)
         if kind == "prefix_inclusive":  # key == prefix wrongly visible
-            return orig(Q, K, V, scale, q_pos, mods, prefix_len + 1 if prefix_len else 0, doc_start)
+            return orig(Q, K, V, scale, q_pos, mods, prefix_len + 1 if prefix_len else 0, doc_start, keys_allowed)
         if kind == "doc_exclusive":  # the document's first key wrongly hidden
-            return orig(Q, K, V, scale, q_pos, mods, prefix_len, None if doc_start is None else doc_start + 1)
+            return orig(Q, K, V, scale, q_pos, mods, prefix_len, None if doc_start is None else doc_start + 1,
+                        keys_allowed)
         raise AssertionError(kind)
 
     return mutant
 
 
-@pytest.mark.parametrize("mutant", ["bf16_low_bit", "v_layout", "v_whole_slab", "ignore_table", "no_scale", "top_left_causal",
+@pytest.mark.parametrize("mutant", ["bf16_low_bit", "block_rows_by_chunk_row", "block_bits_msb_first", "v_layout", "v_whole_slab", "ignore_table", "no_scale", "top_left_causal",
                                     "gqa_modulo", "sign", "prefix_inclusive", "doc_exclusive"])
 def test_planted_mistakes_are_caught(monkeypatch, mutant):
     monkeypatch.setitem(opa.__dict__, "_orig_gather", opa.gather_sequence)
     monkeypatch.setitem(opa.__dict__, "_orig_attention", opa.attention_dense)
     monkeypatch.setitem(opa.__dict__, "_orig_bits", opa.bits_to_f64)
+    monkeypatch.setitem(opa.__dict__, "_orig_keys_allowed", opa.BlockMask.keys_allowed)
     if mutant == "bf16_low_bit":
         monkeypatch.setattr(opa, "bits_to_f64", _mutant_bf16_low_bit_dropped)
+    elif mutant == "block_rows_by_chunk_row":
+        monkeypatch.setattr(opa.BlockMask, "keys_allowed", _mutant_block_rows_by_chunk_row)
+    elif mutant == "block_bits_msb_first":
+        monkeypatch.setattr(opa.BlockMask, "keys_allowed", _mutant_block_bits_msb_first)
     elif mutant == "v_layout":
         monkeypatch.setattr(opa, "gather_sequence", _mutant_gather_v_not_transposed)
     elif mutant == "v_whole_slab":
