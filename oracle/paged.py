@@ -217,7 +217,10 @@ def attention_dense(Q, K, V, scale, q_pos, mods: ScoreMods | None = None, prefix
         P = np.exp(S - m)
         denom = P.sum(axis=1, keepdims=True)
         P = np.divide(P, denom, out=np.zeros_like(P), where=denom > 0)
-        O[:, h, :] = np.where(has_key[:, None], P @ V[kvh], 0.0)
+        # the sum runs over keys some row admits (a key no row admits takes no
+        # part, whatever its stored values; elsewhere its weight is exactly 0)
+        cols = allowed.any(axis=0)
+        O[:, h, :] = np.where(has_key[:, None], P[:, cols] @ V[kvh][cols], 0.0)
     return O
 
 
