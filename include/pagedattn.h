@@ -78,7 +78,8 @@ enum {
   PA_ERR_WORKSPACE = -7,     /* workspace NULL or smaller than required         */
   PA_ERR_DTYPE = -8,         /* dtype not PA_F32 / PA_BF16                      */
   PA_ERR_FLAG = -9,          /* causal not 0 or 1                               */
-  PA_ERR_MODS = -10,         /* window < 0, softcap < 0 or not finite           */
+  PA_ERR_MODS = -10,         /* window < 0, softcap < 0 or not finite, or a bad
+                                block mask                                      */
   PA_ERR_TABLE_STRIDE = -11, /* block_table_stride < 1                          */
   PA_ERR_NO_BLOCKS = -12,    /* block manager: the pool is exhausted            */
   PA_ERR_SEQ = -13,          /* block manager: unknown or freed sequence id     */
@@ -102,16 +103,45 @@ enum {
  *                   doc_starts[row] are masked out for that query row
  *                   (device pointer, one int32 per query row -- num_seqs for
  *                   decode, total_q for prefill; NULL = none)
+ *   block_mask    : FlexAttention-style block sparsity (pa_block_mask below):
+ *                   which key blocks each query block sees at all; the other
+ *                   masks still apply inside the blocks it admits (NULL =
+ *                   none)
  * Masks only shrink a row's key range, so fully masked key tiles are never
- * read.  Passing NULL for the struct means none of them.  The struct itself
- * is read on the host during the call and may be freed on return.
+ * read.  Passing NULL for the struct means none of them.  The structs
+ * themselves are read on the host during the call and may be freed on
+ * return.
  */
+/*
+ * A block mask: for sequence b and a query at logical position p, bitmap row
+ * b * rows_per_seq + p / q_block of `bits` (device uint32 [num_seqs *
+ * rows_per_seq, words_per_row]) admits key j only if bit (j / kv_block) % 32
+ * (bit 0 = least significant) of word (j / kv_block) / 32 is set.  q_block is
+ * a power of two >= 1, kv_block a power of two in [64, 2^24] (whole 64-key
+ * tiles of the prefill kernel), rows_per_seq and words_per_row >= 1
+ * (PA_ERR_MODS otherwise).  Caller contract (not checked on the device): every
+ * row and word that a query's position and a sequence's keys address exist.
+ * Key blocks no row of a work-group admits are never read; a decode row skips
+ * the 16-token chunks of blocks it does not admit.  Reading of "Paged
+ * Attention Meets FlexAttention" (abstract): the paged kernel keeps
+ * FlexAttention's programmable masks, of which the block mask is the one that
+ * saves work.
+ */
+typedef struct {
+  const uint32_t* bits;
+  int32_t q_block;
+  int32_t kv_block;
+  int32_t rows_per_seq;
+  int32_t words_per_row;
+} pa_block_mask;
+
 typedef struct {
   int32_t window;
   float softcap;
   const float* alibi_slopes;
   const int32_t* prefix_lens;
   const int32_t* doc_starts;
+  const pa_block_mask* block_mask;
 } pa_score_mods;
 
 /*

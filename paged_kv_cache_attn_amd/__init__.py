@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401
     PA_BF16,
     PA_F32,
     bench_fill,
+    block_mask,
     bench_stream_read,
     decode_cascade_plan,
     decode_cascade_workspace,

@@ -26,13 +26,20 @@ PA_BF16 = 1
 _DTYPES = {torch.float32: PA_F32, torch.bfloat16: PA_BF16}
 
 
+class BlockMaskStruct(ctypes.Structure):
+    """``pa_block_mask``: bitmap rows of admitted key blocks per query block."""
+
+    _fields_ = [("bits", ctypes.c_void_p), ("q_block", ctypes.c_int32), ("kv_block", ctypes.c_int32),
+                ("rows_per_seq", ctypes.c_int32), ("words_per_row", ctypes.c_int32)]
+
+
 class ScoreMods(ctypes.Structure):
     """``pa_score_mods``: window (0 = none), softcap (0 = none), alibi slopes,
-    prefix-LM lengths per sequence, document starts per query row."""
+    prefix-LM lengths per sequence, document starts per query row, block mask."""
 
     _fields_ = [("window", ctypes.c_int32), ("softcap", ctypes.c_float),
                 ("alibi_slopes", ctypes.c_void_p), ("prefix_lens", ctypes.c_void_p),
-                ("doc_starts", ctypes.c_void_p)]
+                ("doc_starts", ctypes.c_void_p), ("block_mask", ctypes.POINTER(BlockMaskStruct))]
 
 
 class PrefixLevel(ctypes.Structure):
@@ -159,8 +166,20 @@ def _dtype_code(t: torch.Tensor) -> int:
     return _DTYPES[t.dtype]
 
 
-def _mods(window=0, softcap=0.0, alibi_slopes=None, prefix_lens=None, doc_starts=None):
-    if not window and not softcap and alibi_slopes is None and prefix_lens is None and doc_starts is None:
+def block_mask(bits, q_block, kv_block):
+    """A block mask for the calls' ``block_mask=`` argument.
+
+    ``bits``: int32 device tensor ``[num_seqs, rows_per_seq, words]`` holding
+    uint32 bit patterns; row ``p // q_block`` of sequence ``b`` admits key
+    ``j`` when bit ``(j // kv_block) % 32`` of word ``(j // kv_block) // 32``
+    is set (``pa_block_mask``)."""
+    _need(bits, "block mask bits", torch.int32, 3)
+    return {"bits": bits, "q_block": int(q_block), "kv_block": int(kv_block)}
+
+
+def _mods(window=0, softcap=0.0, alibi_slopes=None, prefix_lens=None, doc_starts=None, block_mask=None):
+    if (not window and not softcap and alibi_slopes is None and prefix_lens is None and doc_starts is None
+            and block_mask is None):
         return None, None
     if alibi_slopes is not None:
         _need(alibi_slopes, "alibi_slopes", torch.float32, 1)
@@ -169,8 +188,14 @@ def _mods(window=0, softcap=0.0, alibi_slopes=None, prefix_lens=None, doc_starts
     if doc_starts is not None:
         _need(doc_starts, "doc_starts", torch.int32, 1)
     ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
-    m = ScoreMods(int(window), float(softcap), ptr(alibi_slopes), ptr(prefix_lens), ptr(doc_starts))
-    return ctypes.pointer(m), m
+    bm = None
+    if block_mask is not None:
+        bits = block_mask["bits"]
+        bm = BlockMaskStruct(bits.data_ptr(), block_mask["q_block"], block_mask["kv_block"], bits.shape[1],
+                             bits.shape[2])
+    m = ScoreMods(int(window), float(softcap), ptr(alibi_slopes), ptr(prefix_lens), ptr(doc_starts),
+                  None if bm is None else ctypes.pointer(bm))
+    return ctypes.pointer(m), (m, bm)
 
 
 def _pool_dims(k_cache, v_cache):
@@ -229,7 +254,7 @@ def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens):
 
 def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
                       split_tokens=0, workspace=None, window=0, softcap=0.0, alibi_slopes=None, phase="both",
-                      prefix_lens=None, doc_starts=None):
+                      prefix_lens=None, doc_starts=None, block_mask=None):
     """One query row per sequence; writes ``out [B, Hq, D]``.
 
     ``phase`` selects ``paged_attn_decode`` ("both"), ``..._partials`` or
@@ -240,7 +265,7 @@ def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens, scal
     if workspace is None:
         workspace = decode_workspace(q, Hkv, max_context_len, split_tokens)
     _need(workspace, "workspace")
-    mp, _keep = _mods(window, softcap, alibi_slopes, prefix_lens, doc_starts)
+    mp, _keep = _mods(window, softcap, alibi_slopes, prefix_lens, doc_starts, block_mask)
     ws_bytes = workspace.numel() * workspace.element_size()
     L = lib()
     if phase == "merge":
@@ -258,13 +283,13 @@ def paged_attn_decode(out, q, k_cache, v_cache, block_tables, context_lens, scal
 
 def paged_attn_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
                               split_tokens=0, window=0, softcap=0.0, alibi_slopes=None, prefix_lens=None,
-                              doc_starts=None):
+                              doc_starts=None, block_mask=None):
     """``paged_attn_decode`` on the library's own per-device scratch: takes no
     workspace and allocates nothing (the call fails with ``ValueError`` when
     the sizes need more than ``PA_DECODE_SCRATCH_BYTES``).  Calls that overlap
     on one device race on that scratch."""
     NB, Hkv, bs, D, B, Hq = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens)
-    mp, _keep = _mods(window, softcap, alibi_slopes, prefix_lens, doc_starts)
+    mp, _keep = _mods(window, softcap, alibi_slopes, prefix_lens, doc_starts, block_mask)
     code = lib().paged_attn_decode_noalloc(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
                                            block_tables.shape[1], _ptr(context_lens), B, Hq, Hkv, D, bs, NB,
                                            int(max_context_len), float(scale), int(split_tokens), mp,
@@ -326,7 +351,7 @@ def decode_cascade_plan(num_seqs, levels, num_heads, num_kv_heads, head_dim, max
 
 def paged_attn_decode_cascade(out, q, k_cache, v_cache, block_tables, context_lens, levels, scale,
                               max_context_len, workspace=None, softcap=0.0, window=0, alibi_slopes=None,
-                              prefix_lens=None, doc_starts=None, mode="auto"):
+                              prefix_lens=None, doc_starts=None, mode="auto", block_mask=None):
     """Decode where sequences share (possibly nested) prefixes.
 
     ``levels``: a list of :func:`prefix_level`, outermost first.  Writes
@@ -338,7 +363,7 @@ def paged_attn_decode_cascade(out, q, k_cache, v_cache, block_tables, context_le
     if workspace is None:
         workspace = decode_cascade_workspace(q, Hkv, levels, max_context_len)
     _need(workspace, "workspace")
-    mp, _keep = _mods(window, softcap, alibi_slopes, prefix_lens, doc_starts)
+    mp, _keep = _mods(window, softcap, alibi_slopes, prefix_lens, doc_starts, block_mask)
     arr = _levels_array(levels)
     if mode not in ("auto", "two_phase"):
         raise ValueError(f"mode must be 'auto' or 'two_phase', not {mode!r}")
@@ -352,7 +377,8 @@ def paged_attn_decode_cascade(out, q, k_cache, v_cache, block_tables, context_le
 
 
 def paged_attn_prefill(out, q, cu_q_lens, k_cache, v_cache, block_tables, context_lens, scale, max_q_len,
-                       causal=True, window=0, softcap=0.0, alibi_slopes=None, prefix_lens=None, doc_starts=None):
+                       causal=True, window=0, softcap=0.0, alibi_slopes=None, prefix_lens=None, doc_starts=None,
+                       block_mask=None):
     """Query rows ``q [total_q, Hq, D]`` grouped by ``cu_q_lens [B+1]``; writes ``out``."""
     NB, Hkv, bs, D = _pool_dims(k_cache, v_cache)
     _need(q, "q", k_cache.dtype, 3)
@@ -364,7 +390,7 @@ def paged_attn_prefill(out, q, cu_q_lens, k_cache, v_cache, block_tables, contex
     if cu_q_lens.shape[0] != B + 1 or block_tables.shape[0] != B or tuple(out.shape) != tuple(q.shape) \
             or q.shape[2] != D:
         raise ValueError("shape mismatch between q/out/cu_q_lens/block_tables/context_lens/pools")
-    mp, _keep = _mods(window, softcap, alibi_slopes, prefix_lens, doc_starts)
+    mp, _keep = _mods(window, softcap, alibi_slopes, prefix_lens, doc_starts, block_mask)
     code = lib().paged_attn_prefill(_ptr(out), _ptr(q), _ptr(cu_q_lens), _ptr(k_cache), _ptr(v_cache),
                                     _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, int(max_q_len),
                                     q.shape[1], Hkv, D, bs, NB, float(scale), int(bool(causal)), mp, _dtype_code(q),

@@ -43,7 +43,27 @@ int check_mods(const pa_score_mods* m) {
   if (!m) return PA_OK;
   if (m->window < 0) return PA_ERR_MODS;
   if (!(m->softcap >= 0.f) || isinf(m->softcap)) return PA_ERR_MODS;
+  if (const pa_block_mask* bm = m->block_mask) {
+    if (!bm->bits) return PA_ERR_NULL;
+    if (!is_pow2(bm->q_block) || !is_pow2(bm->kv_block) || bm->kv_block < 64 || bm->kv_block > (1 << 24) ||
+        bm->rows_per_seq < 1 || bm->words_per_row < 1)
+      return PA_ERR_MODS;
+    if (reinterpret_cast<uintptr_t>(bm->bits) % 4 != 0) return PA_ERR_ALIGN;
+  }
   return PA_OK;
+}
+
+pa::BlockMaskArgs block_mask_args(const pa_score_mods* m) {
+  pa::BlockMaskArgs a{nullptr, 0, 0, 0, 0};
+  if (m && m->block_mask) {
+    const pa_block_mask* bm = m->block_mask;
+    a.bits = bm->bits;
+    a.q_log2 = ilog2(bm->q_block);
+    a.kv_log2 = ilog2(bm->kv_block);
+    a.rows = bm->rows_per_seq;
+    a.words = bm->words_per_row;
+  }
+  return a;
 }
 
 // log2 of the partition length, kUnsplitLog2 for "never split".
@@ -162,6 +182,7 @@ void fill_row_args(pa::RowAttnArgs& a, void* out, const void* q, const void* kc,
   a.alibi = mods ? mods->alibi_slopes : nullptr;
   a.prefix_lens = mods ? mods->prefix_lens : nullptr;
   a.doc_starts = mods ? mods->doc_starts : nullptr;
+  a.bm = block_mask_args(mods);
   a.row_floor = nullptr;
   a.state_o = nullptr;
   a.state_lse = nullptr;
@@ -510,6 +531,7 @@ int paged_attn_prefill(void* out, const void* q, const int32_t* cu_q_lens, const
     a.alibi = mods ? mods->alibi_slopes : nullptr;
     a.prefix_lens = mods ? mods->prefix_lens : nullptr;
     a.doc_starts = mods ? mods->doc_starts : nullptr;
+    a.bm = block_mask_args(mods);
     a.table_rows = nullptr;
     a.part_o = nullptr;
     a.part_lse = nullptr;
@@ -625,10 +647,13 @@ int cascade_impl(bool force_two_phase, void* out, const void* q, const void* k_c
   cascade_shape(num_seqs, levels, num_levels, num_heads, num_kv_heads, head_dim, max_context_len, c);
   if (!workspace || workspace_bytes < c.total || reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
     return PA_ERR_WORKSPACE;
-  if (!force_two_phase && !two_phase_pays_off(num_seqs, num_kv_heads, head_dim, max_context_len)) {
+  const bool block_mask = mods && mods->block_mask;
+  if (block_mask && force_two_phase) return PA_ERR_MODS;  // the shared parts take no block mask
+  if (block_mask || !two_phase_pays_off(num_seqs, num_kv_heads, head_dim, max_context_len)) {
     // a batch this small is bound by launches, not by re-reading the shared
-    // keys: the plain decode (one launch, or two) is faster; its workspace is
-    // the region the two-phase call keeps for its own-keys decode
+    // keys: the plain decode (one launch, or two) is faster; and a block mask
+    // is taken by the plain decode only.  Its workspace is the region the
+    // two-phase call keeps for its own-keys decode
     const size_t need = workspace_bytes_for(num_seqs, num_kv_heads, head_dim, c.dec);
     return decode_impl(true, true, out, q, k_cache, v_cache, block_tables, block_table_stride, context_lens,
                        num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_context_len, scale,
@@ -672,6 +697,7 @@ int cascade_impl(bool force_two_phase, void* out, const void* q, const void* k_c
     p.alibi = alibi;
     p.prefix_lens = nullptr;  // (a decode row sees every earlier key anyway)
     p.doc_starts = doc_starts;
+    p.bm = block_mask_args(nullptr);
     p.table_rows = v.group_starts;
     p.key_starts = v.prefix_starts;
     p.q_ctx = context_lens;

@@ -374,21 +374,40 @@ __device__ __forceinline__ void attend_segment(const RowAttnArgs& a, const RowRa
     __builtin_amdgcn_wave_barrier();
   };
 
+  // Block mask (mods instances only): a chunk whose key block the row's
+  // bitmap row does not admit is neither loaded nor computed.  A chunk lies
+  // inside one key block (blocks are whole multiples of 64 keys).
+  const uint32_t* bm_row = nullptr;
+  if constexpr (kMods) {
+    if (a.bm.bits) bm_row = a.bm.bits + ((size_t)b * a.bm.rows + (rr.pos >> a.bm.q_log2)) * a.bm.words;
+  }
+  auto chunk_ok = [&](int tok0) -> bool {
+    if constexpr (!kMods) {
+      return true;
+    } else {
+      if (!bm_row) return true;
+      if (tok0 >= c_end) return false;  // (past the segment: nothing to compute, no word to read)
+      const int kb = tok0 >> a.bm.kv_log2;
+      return ((bm_row[kb >> 5] >> (kb & 31)) & 1u) != 0;
+    }
+  };
+
   // Software pipeline over two register buffers: while one chunk is computed
   // the next two are in flight.  Every load is unconditional (addresses past
   // the partition are clamped to its last chunk, which is fetched again) and
   // the loop is unrolled by two, so every path keeps the same loads in flight
-  // and each vmcnt wait covers exactly the chunk about to be used.
+  // and each vmcnt wait covers exactly the chunk about to be used (a block
+  // mask makes loads conditional; the waits then follow the compiler's count).
   if (c_begin < c_end) {
     const int last_chunk = c_begin + ((c_end - c_begin - 1) & ~15);
     Chunk<E, D, GP> buf0, buf1;
-    load_chunk(buf0, c_begin);
-    load_chunk(buf1, min(c_begin + 16, last_chunk));
+    if (chunk_ok(c_begin)) load_chunk(buf0, c_begin);
+    if (chunk_ok(min(c_begin + 16, last_chunk))) load_chunk(buf1, min(c_begin + 16, last_chunk));
     for (int tok0 = c_begin; tok0 < c_end; tok0 += 32) {
-      process(buf0, tok0);
-      load_chunk(buf0, min(tok0 + 32, last_chunk));
-      process(buf1, tok0 + 16);
-      load_chunk(buf1, min(tok0 + 48, last_chunk));
+      if (chunk_ok(tok0)) process(buf0, tok0);
+      if (chunk_ok(min(tok0 + 32, last_chunk))) load_chunk(buf0, min(tok0 + 32, last_chunk));
+      if (chunk_ok(tok0 + 16)) process(buf1, tok0 + 16);
+      if (chunk_ok(min(tok0 + 48, last_chunk))) load_chunk(buf1, min(tok0 + 48, last_chunk));
     }
   }
 
@@ -769,7 +788,7 @@ hipError_t dispatch_d(const RowAttnArgs& a, int D, bool merge, bool mods, hipStr
   return dispatch_gp<E, 128>(a, merge, mods, s);
 }
 
-bool has_mods(const RowAttnArgs& a) { return a.softcap > 0.f || a.alibi != nullptr; }
+bool has_mods(const RowAttnArgs& a) { return a.softcap > 0.f || a.alibi != nullptr || a.bm.bits != nullptr; }
 
 }  // namespace
 

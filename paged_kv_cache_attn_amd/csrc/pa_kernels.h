@@ -20,6 +20,13 @@
 
 namespace pa {
 
+// Block mask on the device: row b * rows + (position >> q_log2) of bits
+// [*, words] admits key j when bit (j >> kv_log2) is set (LSB first).
+struct BlockMaskArgs {
+  const uint32_t* bits;
+  int32_t q_log2, kv_log2, rows, words;
+};
+
 // Everything one decode-style launch needs.  A "row slot" is (sequence b,
 // query index i < max_q_len); decode has max_q_len == 1.
 struct RowAttnArgs {
@@ -37,6 +44,7 @@ struct RowAttnArgs {
   const int32_t* prefix_lens;  // [num_seqs] or nullptr (prefix-LM, with causal)
   const int32_t* doc_starts;   // [rows] or nullptr (first admissible key per row)
   const int32_t* row_floor;    // [rows] or nullptr: a second first-admissible-key bound
+  BlockMaskArgs bm;            // bm.bits == nullptr: no block mask
   // nullptr: final rows go to out.  Else (two-phase decode) each row's
   // normalised output goes to state_o [rows, Hq, D] and its log-sum-exp
   // (log2 units of the scaled scores) to state_lse [rows, Hq], in fp32.
@@ -78,6 +86,7 @@ struct PrefillArgs {
   const float* alibi;
   const int32_t* prefix_lens;  // [num_seqs] or nullptr
   const int32_t* doc_starts;   // [total_q] or nullptr
+  BlockMaskArgs bm;            // bm.bits == nullptr: no block mask
   // Key-split mode (key_split > 0, non-causal, no mods but softcap): the grid
   // also runs over nsplit key ranges of key_split keys; the work-group of
   // range s writes each row's output over keys [s*key_split, (s+1)*key_split)

@@ -131,7 +131,7 @@ __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const
   // at key 0, and so does the first tile; an entry is used only then, and
   // only if its block lies within the sequence (see the prologue below).  The
   // index is clamped to the table row, so the read stays inside the table.
-  const bool spec = !ksplit && a.window <= 0 && a.doc_starts == nullptr;
+  const bool spec = !ksplit && a.window <= 0 && a.doc_starts == nullptr && a.bm.bits == nullptr;
   const int n = a.context_lens[b];
   const int q0 = a.cu_q_lens[b];
   const int Lq = a.cu_q_lens[b + 1] - q0;
@@ -291,9 +291,64 @@ __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const
   float m_run = kNegInf, l_run = 0.f;
 
   const int k_begin = wg_lo & ~(kTileKeys - 1);
-  const int ntiles = wg_hi > k_begin ? (wg_hi - k_begin + kTileKeys - 1) / kTileKeys : 0;
-  auto tile_k0 = [&](int t) { return k_begin + min(t, ntiles - 1) * kTileKeys; };
+  const int ntiles_all = wg_hi > k_begin ? (wg_hi - k_begin + kTileKeys - 1) / kTileKeys : 0;
+  // Block mask (mods instances only): the work-group visits only the key
+  // tiles that some row's bitmap row admits, from a list built in LDS,
+  // kBmListMax tiles of its range at a time.  Entry = the tile's first key,
+  // | 1 when every row of the work-group admits the tile.
+  constexpr int kBmListMax = kMods ? 2048 : 1;
+  __shared__ int bm_list[kBmListMax];
+  __shared__ int bm_count[4];
+  const bool use_bm = kMods && a.bm.bits != nullptr;
+  int ntiles = use_bm ? 0 : ntiles_all;
+  auto tile_entry = [&](int t) { return __builtin_amdgcn_readfirstlane(bm_list[min(t, ntiles - 1)]); };
+  auto tile_k0 = [&](int t) {
+    if (use_bm) return tile_entry(t) & ~(kTileKeys - 1);
+    return k_begin + min(t, ntiles - 1) * kTileKeys;
+  };
   auto tile_full = [&](int k0) { return (k0 >= safe_lo) && (k0 + kTileKeys <= safe_hi); };
+  auto tile_full_t = [&](int t) { return tile_full(tile_k0(t)) && (!use_bm || (tile_entry(t) & 1)); };
+  // this lane's bitmap row (valid rows only)
+  const size_t bm_row = use_bm && row_ok ? ((size_t)b * a.bm.rows + (pos >> a.bm.q_log2)) * a.bm.words : 0;
+  auto row_admits = [&](int k0) {
+    const int kb = k0 >> a.bm.kv_log2;
+    return ((a.bm.bits[bm_row + (kb >> 5)] >> (kb & 31)) & 1u) != 0;
+  };
+  // The list for tiles [seg * kBmListMax, ...) of the range: a tile goes in
+  // when any of the work-group's bitmap rows admits its key block.
+  auto bm_build = [&](int seg) {
+    const int t0 = seg * kBmListMax;
+    const int t1 = min(ntiles_all, t0 + kBmListMax);
+    const int p_first = n - Lq + q_start;
+    const int p_last = n - Lq + min(q_start + QT, Lq) - 1;
+    const size_t r_lo = (size_t)b * a.bm.rows + (p_first >> a.bm.q_log2);
+    const size_t r_hi = (size_t)b * a.bm.rows + (p_last >> a.bm.q_log2);
+    __syncthreads();  // every wave is done with the previous segment's list
+    int count = 0;
+    for (int base = t0; base < t1; base += kThreads) {
+      const int t = base + tid;
+      const int k0 = k_begin + t * kTileKeys;
+      bool any = false, all = true;
+      if (t < t1) {
+        const int kb = k0 >> a.bm.kv_log2;
+        for (size_t r = r_lo; r <= r_hi; ++r) {
+          const bool bit = ((a.bm.bits[r * a.bm.words + (kb >> 5)] >> (kb & 31)) & 1u) != 0;
+          any |= bit;
+          all &= bit;
+        }
+      }
+      const uint64_t mask = __builtin_amdgcn_ballot_w64(any);
+      const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+      if (lane == 0) bm_count[wave] = __builtin_popcountll(mask);
+      __syncthreads();
+      int off = count;
+      for (int w = 0; w < wave; ++w) off += bm_count[w];
+      if (any) bm_list[off + below] = k0 | (all ? 1 : 0);
+      count += bm_count[0] + bm_count[1] + bm_count[2] + bm_count[3];
+      __syncthreads();  // the counts are read before the next round writes them
+    }
+    return count;
+  };
 
   // S^T of one tile: 16 MFMAs, two independent accumulation chains.
   auto compute_s = [&](f32x16 (&S)[2], const u32x4* kt) {
@@ -314,8 +369,11 @@ __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const
 
   // Masks, online softmax update and P (bf16) as the B operand of O^T += V^T P^T
   // (score-mod path; the plain path is inlined into the pipelined step).
-  auto softmax_mods = [&](f32x16 (&S)[2], const int k0, bf16x8 (&pb)[4]) {
-    const bool full = (k0 >= safe_lo) && (k0 + kTileKeys <= safe_hi);
+  auto softmax_mods = [&](f32x16 (&S)[2], const int t, bf16x8 (&pb)[4]) {
+    const int k0 = tile_k0(t);
+    const bool full = tile_full_t(t);
+    // (a tile visited for other rows is masked whole for a row that does not admit it)
+    const bool admits = !use_bm || full || (row_ok && row_admits(k0));
     float cmax = kNegInf;
 #pragma unroll
     for (int kg = 0; kg < 2; ++kg) {
@@ -329,7 +387,7 @@ __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const
         }
         x += alibi_slope * (float)(key - pos);
         float sv = x * kLog2e;
-        if (!full) sv = (key >= row_lo && key < row_hi) ? sv : kNegInf;
+        if (!full) sv = (key >= row_lo && key < row_hi && admits) ? sv : kNegInf;
         S[kg][i] = sv;
         cmax = fmaxf(cmax, sv);
       }
@@ -458,6 +516,9 @@ __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const
   // max covers it.  LDS rings: K holds tiles t+1 (read) and t+2 (landing), V
   // holds tiles t (read) and t+1 (landing).  Block ids: b1 = tile t+1,
   // b2 = tile t+2 (scalars), bv = tile t+3 (vector load in flight).
+  const int nseg = use_bm ? (ntiles_all + kBmListMax - 1) / kBmListMax : 1;
+  for (int seg = 0; seg < nseg; ++seg) {
+  if (use_bm) ntiles = bm_build(seg);
   f32x16 sA[2], sB[2];
   int b1 = 0, b2 = 0, bv = 0;
   if (ntiles > 0) {
@@ -506,7 +567,7 @@ __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const
       b2 = b3;
       bv = table_load(t + 4);
       if (t + 1 < ntiles) compute_s(Snext, kbuf(Q));
-      softmax_mods(Scur, k0, pb);
+      softmax_mods(Scur, t, pb);
       pv(vbuf(P), pb);
     } else {
       // Loads of K_{t+2} and V_{t+1}, unconditional so that they join this
@@ -569,6 +630,7 @@ __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const
     if (t + 1 < ntiles) step(Par<1>{}, sB, sA, t + 1);
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // no direct-to-LDS load outlives the loop
+  }  // segments of the block-mask tile list
 
   // ---- normalise and store: lane holds row `r`, dims 32dt + 8(i/4) + 4hl + i%4 ----
   const float l_tot = l_run + shfl_xor32(l_run);
@@ -613,8 +675,9 @@ int prefill_rows_per_tile(int g) { return kRowsPerWG / g; }
 hipError_t launch_prefill_mfma(const PrefillArgs& a, int D, hipStream_t s) {
   const long long blocks = (long long)a.num_seqs * a.Hkv * a.q_tiles * (a.key_split > 0 ? a.nsplit : 1);
   if (blocks <= 0) return hipSuccess;
-  // the fast path folds a positive scale into the exponent
-  const bool mods = a.softcap > 0.f || a.alibi != nullptr || !(a.scale > 0.f);
+  // the fast path folds a positive scale into the exponent; block masks take
+  // the mods path
+  const bool mods = a.softcap > 0.f || a.alibi != nullptr || !(a.scale > 0.f) || a.bm.bits != nullptr;
   const int kbl = a.bs_log2 < 6 ? a.bs_log2 : 6;
   const bool split = a.key_split > 0;
   const dim3 grid((unsigned)blocks), block(kThreads);

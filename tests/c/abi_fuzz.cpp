@@ -48,6 +48,14 @@ int main(int argc, char** argv) {
     mods.alibi_slopes = static_cast<const float*>(pick(2) ? nullptr : ptr());
     mods.prefix_lens = pick(2) ? nullptr : iptr();
     mods.doc_starts = pick(2) ? nullptr : iptr();
+    pa_block_mask bm;
+    bm.bits = static_cast<const uint32_t*>(pick(6) == 0 ? nullptr : (pick(8) == 0 ? reinterpret_cast<void*>(0x1002)
+                                                                                 : ptr()));
+    bm.q_block = pick(4) == 0 ? v32() : 1 << pick(8);
+    bm.kv_block = pick(4) == 0 ? v32() : 64 << pick(4);
+    bm.rows_per_seq = pick(8) == 0 ? v32() : 1 + (int32_t)pick(64);
+    bm.words_per_row = pick(8) == 0 ? v32() : 1 + (int32_t)pick(64);
+    mods.block_mask = pick(3) == 0 ? &bm : nullptr;
     const pa_score_mods* mp = pick(3) == 0 ? nullptr : &mods;
     // a valid argument set, then a few fields replaced by random values
     int32_t B = 1 + (int32_t)pick(64), Hkv = 1 << pick(4), Hq = Hkv * (1 << pick(4)), D = pick(2) ? 128 : 64;

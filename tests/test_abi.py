@@ -99,6 +99,25 @@ def _decode_noalloc(**over):
                                                    a["scale"], a["split"], a["mods"], a["dtype"], None)
 
 
+def test_block_mask_validation():
+    """Block-mask fields are checked on the host: NULL bits, block sizes that
+    are not powers of two, key blocks below one 64-key tile, empty rows,
+    misaligned bits."""
+    def call(**bm_over):
+        f = dict(bits=0x10000, q_block=16, kv_block=128, rows_per_seq=4, words_per_row=2)
+        f.update(bm_over)
+        bm = binding.BlockMaskStruct(f["bits"], f["q_block"], f["kv_block"], f["rows_per_seq"], f["words_per_row"])
+        m = binding.ScoreMods(0, 0.0, None, None, None, ctypes.pointer(bm))
+        return _decode(mods=ctypes.pointer(m)), _prefill(mods=ctypes.pointer(m))
+    assert call(bits=None) == (-1, -1)
+    assert call(q_block=12) == (-10, -10)
+    assert call(kv_block=32) == (-10, -10)
+    assert call(kv_block=96) == (-10, -10)
+    assert call(rows_per_seq=0) == (-10, -10)
+    assert call(words_per_row=0) == (-10, -10)
+    assert call(bits=0x10002) == (-14, -14)
+
+
 def test_decode_noalloc_validation():
     """The allocation-free decode checks its arguments like the decode and
     refuses sizes whose workspace exceeds the library's 16 MiB scratch (all

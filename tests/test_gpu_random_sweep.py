@@ -4,7 +4,7 @@ Each seeded case draws a batch size, kv-head count, group size (including a
 3 that does not divide the tile), head dim, page size, dtype, per-sequence
 context lengths (1, block boundaries and their neighbours, random), query
 chunks (single rows, partial chunks, whole fresh prompts) and a random
-subset of score mods.  It checks kv_append bit for bit over the whole pool,
+subset of score mods (a block mask among them).  It checks kv_append bit for bit over the whole pool,
 then decode in three split modes or prefill (causal or not) against the
 fp64 oracle, with the tolerances of the other parity tests (2e-2 max-abs for
 bf16, 1e-4 for fp32).  Sizes stay small enough for the oracle to finish in
@@ -67,6 +67,9 @@ def draw(seed):
         mods["docs"] = True
     if c["kind"] == "prefill" and c["causal"] and rng.random() < 0.2:
         mods["prefix"] = True
+    if rng.random() < 0.25:
+        mods["blockmask"] = (int(rng.choice([1, 16, 64, 1 << 20])), int(rng.choice([64, 128, 256])),
+                             float(rng.uniform(0.4, 0.95)))
     c["mods"] = mods
     return c
 
@@ -101,6 +104,13 @@ def test_random_case(gpu_lib, seed):
         slopes = (2.0 ** -np.arange(1, Hq + 1) * 0.5).astype(np.float32)
         kw["alibi_slopes"] = torch.from_numpy(slopes).cuda()
         om["alibi_slopes"] = slopes.astype(np.float64)
+    if "blockmask" in m:
+        from tests.test_gpu_block_mask import device_mask, random_dense
+        from tests.test_oracle import pack_block_mask
+        qb, kvb, density = m["blockmask"]
+        bm = pack_block_mask(random_dense(np.random.default_rng(seed + 2), w, qb, kvb, density), qb, kvb)
+        kw["block_mask"] = device_mask(gpu_lib, bm)
+        om["block_mask"] = bm
     if "docs" in m:
         ds = _doc_starts(w, rng)
         kw["doc_starts"] = torch.from_numpy(ds).cuda()
