@@ -470,6 +470,44 @@ def extra_measurements(pa, torch, dev, flush, args):
     res["shared_prefix_two_phase"] = two
     log("two-phase decode measured")
 
+    # block-sparse chunked prefill: the chunked-prefill batch under seeded
+    # block masks of 64-position query blocks x 128-key blocks (each query
+    # block keeps its own diagonal block); work counted on admitted pairs
+    w3 = named_workload("chunked_prefill_bf16")
+    t3 = upload(w3, dev)
+    pa.kv_append(t3["k_new"], t3["v_new"], t3["k_cache"], t3["v_cache"], t3["slot_mapping"])
+    out3 = torch.empty_like(t3["q"])
+    sparse = {}
+    for density in (1.0, 0.5, 0.25):
+        rng = np.random.default_rng(77)
+        qb, kvb, n = 64, 128, int(w3.context_lens.max())
+        dense = rng.random((w3.B, n // qb, n // kvb)) < density
+        for r in range(n // qb):
+            dense[:, r, (r * qb) // kvb] = True
+        words = (n // kvb + 31) // 32
+        padded = np.zeros((w3.B * (n // qb), words * 32), dtype=bool)
+        padded[:, :n // kvb] = dense.reshape(w3.B * (n // qb), -1)
+        bits = np.packbits(padded, axis=1, bitorder="little").view("<i4").reshape(w3.B, n // qb, words)
+        bm = pa.block_mask(torch.from_numpy(np.ascontiguousarray(bits)).to(dev), qb, kvb)
+        pairs = 0
+        for b in range(w3.B):
+            L = int(w3.q_lens[b])
+            pos = np.arange(n - L, n)
+            keys = np.arange(n)
+            ok = (keys[None, :] <= pos[:, None]) & dense[b][pos // qb][:, keys // kvb]
+            pairs += int(ok.sum())
+
+        def call(bm=bm):
+            pa.paged_attn_prefill(out3, t3["q"], t3["cu_q_lens"], t3["k_cache"], t3["v_cache"], t3["block_tables"],
+                                  t3["context_lens"], w3.scale, w3.max_q_len, causal=True, block_mask=bm)
+        ms = time_calls(torch, call, flush, reps=20)
+        fl = 4.0 * w3.D * w3.Hq * pairs
+        sparse[str(density)] = {"ms": round(ms, 5), "admitted_flops": fl, "tflops": round(fl / (ms * 1e-3) / 1e12, 2)}
+    res["block_mask_prefill"] = {"workload": "chunked_prefill_bf16, block mask 64-position query blocks x 128-key "
+                                             "blocks, seeded, diagonal blocks kept", "density": sparse}
+    del t3, out3
+    log("block-sparse prefill measured")
+
     # context sweep of the GQA decode shape (8 sequences, 32/8 heads, d128, bf16, block 16)
     sweep = {}
     base = None

@@ -85,7 +85,8 @@ __device__ __forceinline__ int v_swz(int d, int cpb_log2) {
 // KBL = log2(min(block_size, 64)): keys of one pool block inside a 64-key tile.
 // kSplit: key-split mode (a.key_split > 0), a separate instance so that the
 // plain prefill keeps its registers.
-template <int D, bool kMods, int KBL, bool kSplit>
+// kBM: the plain path with a block mask (the mods path takes one at run time).
+template <int D, bool kMods, int KBL, bool kSplit, bool kBM = false>
 __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const PrefillArgs a, const int pair_tiles) {
   constexpr int KCH = D / 8;   // 16-byte chunks per K row
   constexpr int KSTEPS = D / 16;
@@ -296,10 +297,10 @@ __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const
   // tiles that some row's bitmap row admits, from a list built in LDS,
   // kBmListMax tiles of its range at a time.  Entry = the tile's first key,
   // | 1 when every row of the work-group admits the tile.
-  constexpr int kBmListMax = kMods ? 2048 : 1;
+  constexpr int kBmListMax = (kMods || kBM) ? 2048 : 1;
   __shared__ int bm_list[kBmListMax];
   __shared__ int bm_count[4];
-  const bool use_bm = kMods && a.bm.bits != nullptr;
+  const bool use_bm = (kMods || kBM) && a.bm.bits != nullptr;
   int ntiles = use_bm ? 0 : ntiles_all;
   auto tile_entry = [&](int t) { return __builtin_amdgcn_readfirstlane(bm_list[min(t, ntiles - 1)]); };
   auto tile_k0 = [&](int t) {
@@ -472,16 +473,18 @@ __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const
       for (int i = 0; i < 16; ++i) c = fmaxf(c, S[kg][i]);
     return fmaxf(c, shfl_xor32(c)) * scale_log2;
   };
-  // Keys outside this row's admissible range -> -inf (raw scores).
+  // Keys outside this row's admissible range -> -inf (raw scores); a whole
+  // tile for a row whose block-mask row does not admit it.
   auto mask_s = [&](f32x16 (&S)[2], const int k0) {
     const int kb = k0 + 8 * hl;
     const int lo = row_lo - kb, hi = row_hi - kb;
+    const bool admits = !use_bm || (row_ok && row_admits(k0));
 #pragma unroll
     for (int kg = 0; kg < 2; ++kg)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int c = key_off(kg, i);
-        if (c < lo || c >= hi) S[kg][i] = kNegInf;
+        if (!admits || c < lo || c >= hi) S[kg][i] = kNegInf;
       }
   };
   // Lazy running-max update: the max moves only when a tile exceeds it by
@@ -502,6 +505,12 @@ __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const
   // Table entry of the block wave `wave` loads for tile t, read with a vector
   // load (all lanes, one address) so that waiting for it joins the wait for
   // the tile loads instead of the LDS counter.
+  auto table_load_k = [&](int k0) {
+    const int j = min((k0 + 16 * wave) >> a.bs_log2, last_blk);
+    const int blk = __builtin_nontemporal_load(table + j);
+    PA_DEVICE_CHECK(blk >= 0 && blk < a.num_blocks);
+    return blk;
+  };
   auto table_load = [&](int t) {
     const int j = min((tile_k0(t) + 16 * wave) >> a.bs_log2, last_blk);
     const int blk = __builtin_nontemporal_load(table + j);
@@ -543,7 +552,7 @@ __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const
     if constexpr (kMods) {
       // mods path: scores are modded inside its softmax
     } else {
-      if (!tile_full(tile_k0(0))) mask_s(sA, tile_k0(0));
+      if (!tile_full_t(0)) mask_s(sA, tile_k0(0));
       update_max(row_max(sA));
     }
   }
@@ -551,8 +560,13 @@ __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const
   // V buffer P is read, 1-P receives tile t+1.
   auto step = [&](auto P, f32x16 (&Scur)[2], f32x16 (&Snext)[2], const int t) {
     constexpr Par<1 - decltype(P)::value> Q{};
+    // (with a block mask the list entries come from LDS: read them all here,
+    // before the tile loop's own LDS reads are in flight)
     const int k0 = tile_k0(t);
     const int k1 = tile_k0(t + 1);
+    const int k2 = tile_k0(t + 2);
+    const int k4 = tile_k0(t + 4);
+    const bool full1 = tile_full_t(t + 1);
     wait_tiles();  // K_{t+1}, V_t and the table entry bv landed; all waves are past iteration t-1
     const int b3 = __builtin_amdgcn_readfirstlane(bv);
     if (k0 + kTileKeys > n) {
@@ -561,11 +575,11 @@ __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const
     }
     bf16x8 pb[4];
     if constexpr (kMods) {
-      if (t + 2 < ntiles) issue_k(tile_k0(t + 2), P, b2);
+      if (t + 2 < ntiles) issue_k(k2, P, b2);
       if (t + 1 < ntiles) issue_v(k1, Q, b1);
       b1 = b2;
       b2 = b3;
-      bv = table_load(t + 4);
+      bv = table_load_k(k4);
       if (t + 1 < ntiles) compute_s(Snext, kbuf(Q));
       softmax_mods(Scur, t, pb);
       pv(vbuf(P), pb);
@@ -578,11 +592,11 @@ __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const
       // that enter P.V (a dot2 of each packed pair with (1, 1)), so the
       // weights sum to one and a row whose weight sits on one key returns
       // that key's V row.
-      issue_k(tile_k0(t + 2), P, b2);
+      issue_k(k2, P, b2);
       issue_v(k1, Q, b1);
       b1 = b2;
       b2 = b3;
-      bv = table_load(t + 4);
+      bv = table_load_k(k4);
       compute_s(Snext, kbuf(Q));
       const float nm = (m_run == kNegInf) ? 0.f : -m_run;
       float psum = 0.f;
@@ -617,7 +631,7 @@ __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const
         __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU (row max)
       }
       if (t + 1 < ntiles) {  // (S_{t+1} of the last tile is stale: no update)
-        if (!tile_full(k1)) {  // rare: maxima over admissible keys only
+        if (!full1) {  // rare: maxima over admissible keys only
           mask_s(Snext, k1);
           cmax = row_max(Snext);
         }
@@ -675,9 +689,10 @@ int prefill_rows_per_tile(int g) { return kRowsPerWG / g; }
 hipError_t launch_prefill_mfma(const PrefillArgs& a, int D, hipStream_t s) {
   const long long blocks = (long long)a.num_seqs * a.Hkv * a.q_tiles * (a.key_split > 0 ? a.nsplit : 1);
   if (blocks <= 0) return hipSuccess;
-  // the fast path folds a positive scale into the exponent; block masks take
-  // the mods path
-  const bool mods = a.softcap > 0.f || a.alibi != nullptr || !(a.scale > 0.f) || a.bm.bits != nullptr;
+  // the fast path folds a positive scale into the exponent; a block mask
+  // takes the fast path's block-mask instance, or the mods path with mods
+  const bool mods = a.softcap > 0.f || a.alibi != nullptr || !(a.scale > 0.f);
+  const bool bm = a.bm.bits != nullptr;
   const int kbl = a.bs_log2 < 6 ? a.bs_log2 : 6;
   const bool split = a.key_split > 0;
   const dim3 grid((unsigned)blocks), block(kThreads);
@@ -686,12 +701,14 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, int D, hipStream_t s) {
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 0;
   const int pair = !split && blocks <= (long long)kWGsPerCU * cus;
-#define PA_PREFILL_LAUNCH(DD, MM, KK)                                                         \
-  do {                                                                                        \
-    if (split)                                                                                \
-      hipLaunchKernelGGL((prefill_mfma_kernel<DD, MM, KK, true>), grid, block, 0, s, a, pair); \
-    else                                                                                      \
-      hipLaunchKernelGGL((prefill_mfma_kernel<DD, MM, KK, false>), grid, block, 0, s, a, pair); \
+#define PA_PREFILL_LAUNCH(DD, MM, KK)                                                                 \
+  do {                                                                                                \
+    if (split)                                                                                        \
+      hipLaunchKernelGGL((prefill_mfma_kernel<DD, MM, KK, true>), grid, block, 0, s, a, pair);         \
+    else if (!(MM) && bm)                                                                             \
+      hipLaunchKernelGGL((prefill_mfma_kernel<DD, false, KK, false, true>), grid, block, 0, s, a, pair); \
+    else                                                                                              \
+      hipLaunchKernelGGL((prefill_mfma_kernel<DD, MM, KK, false>), grid, block, 0, s, a, pair);        \
   } while (0)
 #define PA_PREFILL_KBL(DD, MM)                    \
   switch (kbl) {                                  \
