@@ -11,6 +11,8 @@ bf16, 1e-4 for fp32).  Sizes stay small enough for the oracle to finish in
 about a second per case.
 """
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -74,7 +76,17 @@ def draw(seed):
     return c
 
 
-SEEDS = list(range(1000, 1096))
+def _seeds(var, default):
+    """Seed range from the environment ("first:last+1", e.g. PA_SWEEP_SEEDS=5000:6000)
+    for longer runs of the same generators; the default otherwise."""
+    spec = os.environ.get(var)
+    if not spec:
+        return default
+    a, b = (int(x) for x in spec.split(":"))
+    return list(range(a, b))
+
+
+SEEDS = _seeds("PA_SWEEP_SEEDS", list(range(1000, 1096)))
 
 
 @pytest.mark.parametrize("seed", SEEDS)
@@ -129,7 +141,7 @@ def test_random_case(gpu_lib, seed):
     print(f"case {seed}: max abs err {max(errs):.3e} (tolerance {TOL[w.dtype]})", flush=True)
 
 
-FORK_SEEDS = list(range(2000, 2016))
+FORK_SEEDS = _seeds("PA_FORK_SEEDS", list(range(2000, 2016)))
 
 
 @pytest.mark.parametrize("seed", FORK_SEEDS)
