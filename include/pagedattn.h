@@ -204,6 +204,14 @@ int32_t paged_attn_decode_split_tokens(int32_t num_seqs, int32_t num_kv_heads,
 /*
  * paged_attn_decode -- one query row per sequence over its paged context.
  *
+ * The decode step of serving: each sequence's newest token attends to every
+ * key its blocks hold, read where the blocks lie through the block table
+ * ("Ultimate Guide to PagedAttention": block table, non-contiguous storage;
+ * Kwon et al., abstract: attention over non-contiguous KV blocks).  The
+ * pages note that this step is bound by loading the KV cache (the vAttention
+ * page's decode snippet), so the kernels stream each 16-token chunk of K and
+ * V once for all query heads of its kv-head.
+ *
  *   out  [num_seqs, num_heads, head_dim]  (written)
  *   q    [num_seqs, num_heads, head_dim]
  *   out[b][h] = softmax_j(scale * q[b][h] . K_b[j] (+ mods)) V_b[j], j < context_lens[b]
@@ -372,6 +380,13 @@ int32_t paged_attn_decode_cascade_plan(int32_t num_seqs, const pa_prefix_level* 
 /*
  * paged_attn_prefill -- several query rows per sequence (prefill, or a
  * chunk appended after an existing paged context) over the paged context.
+ *
+ * The fused kernel gathers each key tile from the scattered blocks straight
+ * into on-chip memory and never forms a contiguous copy (Joshi et al.,
+ * "Paged Attention Meets FlexAttention", abstract: a fused kernel that
+ * gathers scattered KV data), computing exact attention tile by tile with an
+ * online softmax (Dao et al., "FlashAttention", abstract: IO-aware tiling for
+ * exact attention).
  *
  *   q, out  [total_q, num_heads, head_dim]; sequence b owns rows
  *           cu_q_lens[b] .. cu_q_lens[b+1]-1 (cu_q_lens: int32 [num_seqs+1],
