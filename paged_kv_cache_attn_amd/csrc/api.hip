@@ -18,6 +18,7 @@ constexpr long long kAutoTargetUnits = 2048;  // ~8 wavefronts per compute unit
 constexpr int kStreamWavesPerCU = 8;          // resident decode wavefronts per compute unit
 constexpr int kStreamMinChunks = 8;           // 16-token chunks per wavefront, at least
 constexpr int kStreamMaxSeqs = 4096;          // chunk prefix of all rows fits in 16 KB of LDS
+constexpr int kWgMinSplitLog2 = 6;            // fixed partitions as work-groups from 64 keys up
 constexpr int kUnsplitMaxCtx = 256;           // rows this short are never split (no merge launch)
 constexpr int kDefaultCUs = 256;              // MI355X, when no device is visible
 
@@ -95,21 +96,38 @@ int device_cus() {
   return cus;
 }
 
+struct Shape;
+int wg_pays_off(int32_t B, int32_t Hkv, const Shape& s);
+
 struct Shape {
   int g, GP, NG, P, split_log2;
-  int W;  // > 0: balanced split over W wavefronts
+  int W;   // > 0: balanced split over W wavefronts
+  int wg;  // 1: fixed partitions as multi-wavefront work-groups
 };
+
+// Fixed partitions of at least 64 keys run as 4-wavefront work-groups that
+// merge in LDS when the whole grid is resident at once (two work-groups per
+// compute unit): a small batch's partitions then stream four times faster.
+// Larger grids keep one wavefront per partition: there a work-group holds four
+// wavefront slots for each partition a short row leaves empty.
+int wg_pays_off(int32_t B, int32_t Hkv, const Shape& s) {
+  if (s.split_log2 < kWgMinSplitLog2) return 0;
+  const long long blocks = (long long)B * Hkv * s.NG * s.P;
+  return blocks <= 2ll * device_cus() ? 1 : 0;
+}
 
 int decode_shape(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_ctx, int32_t split, Shape& s) {
   s.g = Hq / Hkv;
   s.GP = group_pad(s.g);
   s.NG = (s.g - 1) / s.GP + 1;  // (g >= 1; no overflow for any int32 g)
   s.W = 0;
+  s.wg = 0;
   if (split == 0 && max_ctx <= kUnsplitMaxCtx) {
-    // every row fits a few chunks: one wavefront per (row, head group)
+    // every row fits a few chunks: one work-group per (row, head group)
     // finishes it faster than a split plus the merge launch would
     s.split_log2 = kUnsplitLog2;
     s.P = 1;
+    s.wg = wg_pays_off(B, Hkv, s);
     return PA_OK;
   }
   if (split == 0 && B <= kStreamMaxSeqs) {
@@ -125,6 +143,7 @@ int decode_shape(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_ctx, int32_t sp
   }
   s.split_log2 = resolve_split_log2(B, Hkv, max_ctx, split);
   s.P = partitions(max_ctx, s.split_log2);
+  s.wg = wg_pays_off(B, Hkv, s);
   return PA_OK;
 }
 
@@ -175,6 +194,7 @@ void fill_row_args(pa::RowAttnArgs& a, void* out, const void* q, const void* kc,
   a.split_log2 = s.split_log2;
   a.P = s.P;
   a.stream_waves = s.W;
+  a.wg_partitions = s.wg;
   a.causal = causal;
   a.window = mods ? mods->window : 0;
   a.scale = scale;
@@ -567,6 +587,7 @@ int paged_attn_prefill(void* out, const void* q, const int32_t* cu_q_lens, const
   s.split_log2 = kUnsplitLog2;
   s.P = 1;
   s.W = 0;
+  s.wg = 0;
   if ((long long)num_seqs * max_q_len * num_kv_heads * s.NG > 0x7fffffffll) return PA_ERR_SIZE;
   pa::RowAttnArgs a;
   fill_row_args(a, out, q, k_cache, v_cache, block_tables, block_table_stride, context_lens,

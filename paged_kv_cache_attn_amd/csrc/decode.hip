@@ -150,15 +150,18 @@ __device__ __forceinline__ bool row_range(const RowAttnArgs& a, int slot, RowRan
 // Attention of one row slot over keys [c_begin, c_end) (a segment of its
 // admissible range), for the GP query heads of head group hg.  Writes the
 // normalised output when the segment is the whole range (`whole`), else the
-// unnormalised partial (o, m, l) at workspace unit `unit`.
-template <typename E, int D, int GP, bool kMods>
+// unnormalised partial (o, m, l) at workspace unit `unit`; with kToLds the
+// unnormalised state goes to this wavefront's LDS slots instead (o as
+// [GP][D] in lds_o, (m, l) per head in lds_ml) for a work-group merge.
+template <typename E, int D, int GP, bool kMods, bool kToLds = false>
 __device__ __forceinline__ void attend_segment(const RowAttnArgs& a, const RowRange& rr, const int slot,
                                                const int hg, const int c_begin, const int c_end,
                                                const bool whole, const size_t unit, uint32_t* p_lds,
-                                               float* stat_lds) {
+                                               float* stat_lds, float* lds_o = nullptr,
+                                               float* lds_ml = nullptr) {
   using C = Cfg<E, D, GP>;
   constexpr int TPI = C::TPI;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int kvh = hg / a.NG;
   const int head0 = kvh * a.g + (hg - kvh * a.NG) * GP;  // first global head of the group
   const int nvalid = min(GP, a.g - (hg - kvh * a.NG) * GP);
@@ -210,7 +213,7 @@ __device__ __forceinline__ void attend_segment(const RowAttnArgs& a, const RowRa
   const char* vpool = static_cast<const char*>(a.v_cache);
 
   auto load_chunk = [&](Chunk<E, D, GP>& ch, int tok0) {
-    const int blk = table[tok0 >> a.bs_log2];
+    const int blk = load_ro_i32(table, tok0 >> a.bs_log2);
     PA_DEVICE_CHECK(blk >= 0 && blk < a.num_blocks);
     const int off = tok0 & (bs - 1);
     const size_t slab = ((size_t)blk * a.Hkv + kvh) * kslab_bytes;
@@ -422,6 +425,15 @@ __device__ __forceinline__ void attend_segment(const RowAttnArgs& a, const RowRa
     stat_lds[2 * my_head + 1] = l_tot;
   }
   __builtin_amdgcn_wave_barrier();
+  if constexpr (kToLds) {
+#pragma unroll
+    for (int h = 0; h < GP; ++h)
+#pragma unroll
+      for (int r = 0; r < C::RPL; ++r)
+        if ((r & 1) == vh) lds_o[h * D + vr + 32 * r] = o[h][r];
+    if (lane < 2 * GP) lds_ml[lane] = stat_lds[lane];
+    return;
+  }
   float mh[GP], lh[GP];
 #pragma unroll
   for (int h = 0; h < GP; ++h) {
@@ -493,6 +505,81 @@ __global__ __launch_bounds__(64) void row_partials_kernel(const RowAttnArgs a) {
                                   ((size_t)slot * HG + hg) * a.P + p, p_lds, stat_lds);
 }
 
+// Fixed partitions with NW wavefronts per work-group: the partition's chunks
+// are dealt out in NW contiguous runs, one per wavefront, and the work-group
+// merges the NW states (log-sum-exp weights, wavefront order) in LDS before it
+// writes the partition's output or partial, in the layout row_partials_kernel
+// writes.  A partition then streams NW times faster, which shortens the tail
+// the grid's last partitions leave.
+template <typename E, int D, int GP, bool kMods, int NW>
+__global__ __launch_bounds__(64 * NW) void row_partials_wg_kernel(const RowAttnArgs a) {
+  using C = Cfg<E, D, GP>;
+  __shared__ __attribute__((aligned(16))) uint32_t p_lds[NW][16 * GP];
+  __shared__ __attribute__((aligned(16))) float stat_lds[NW][2 * GP];
+  __shared__ __attribute__((aligned(16))) float st_o[NW][GP * D];
+  __shared__ float st_ml[NW][2 * GP];
+  const int HG = a.Hkv * a.NG;
+  const int flat = blockIdx.x;
+  const int p = flat % a.P;
+  const int hg = (flat / a.P) % HG;
+  const int slot = flat / (a.P * HG);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // (uniform: scalar table loads)
+  RowRange rr;
+  if (!row_range(a, slot, rr)) return;
+  if (p >= rr.nparts) return;
+  const int c_begin = rr.start + (p << a.split_log2);
+  const int c_end = min(rr.hi, c_begin + (1 << a.split_log2));
+  const int nch = c_end > c_begin ? (c_end - c_begin + 15) >> 4 : 0;
+  const int per = (nch + NW - 1) / NW;
+  const int w_begin = min(c_end, c_begin + 16 * per * wave);
+  const int w_end = min(c_end, c_begin + 16 * per * (wave + 1));
+  attend_segment<E, D, GP, kMods, true>(a, rr, slot, hg, w_begin, w_end, false, 0, p_lds[wave],
+                                        stat_lds[wave], st_o[wave], st_ml[wave]);
+  __syncthreads();
+
+  const bool whole = rr.nparts == 1;
+  const size_t unit = ((size_t)slot * HG + hg) * a.P + p;
+  const int kvh = hg / a.NG;
+  const int head0 = kvh * a.g + (hg - kvh * a.NG) * GP;
+  const int nvalid = min(GP, a.g - (hg - kvh * a.NG) * GP);
+  for (int el = threadIdx.x; el < GP * D; el += 64 * NW) {
+    const int h = el / D;
+    const int d = el - h * D;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, st_ml[w][2 * h]);
+    float O = 0.f, L = 0.f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float wt = fast_exp2(st_ml[w][2 * h] - M);
+        L = fmaf(wt, st_ml[w][2 * h + 1], L);
+        O = fmaf(wt, st_o[w][h * D + d], O);
+      }
+    }
+    if (!whole) {
+      a.ws_o[unit * GP * D + el] = O;
+      if (d == 0) {
+        a.ws_ml[unit * GP * 2 + 2 * h] = M;
+        a.ws_ml[unit * GP * 2 + 2 * h + 1] = L;
+      }
+      continue;
+    }
+    if (h >= nvalid) continue;
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    const size_t srow = (size_t)rr.qrow * a.Hq + head0 + h;
+    if (a.state_o) {
+      // two-phase decode: the row's state (normalised output, log-sum-exp), fp32
+      a.state_o[srow * D + d] = O * inv;
+      if (d == 0) a.state_lse[srow] = state_lse2(M, L);
+    } else if constexpr (C::kBf16) {
+      static_cast<uint16_t*>(a.out)[srow * D + d] = (uint16_t)f32_to_bf16_bits(O * inv);
+    } else {
+      static_cast<float*>(a.out)[srow * D + d] = O * inv;
+    }
+  }
+}
+
 // 16-token chunks a decode row's admissible range spans (>= 1, so that an
 // empty context still gets a (fully masked) chunk and a zero output).
 __device__ __forceinline__ int decode_chunks(const RowAttnArgs& a, int b) {
@@ -543,7 +630,11 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(const RowAttnArgs a) 
   __shared__ __attribute__((aligned(16))) float stat_lds[2 * GP];
   const int HG = a.Hkv * a.NG;
   chunk_prefix(a, pre);
-  const long long total = (long long)pre[a.num_seqs] * HG;
+  // (prefix values are read through readfirstlane: everything derived from
+  // them -- row, head group, key range -- is then wave-uniform, so the block
+  // table is read with scalar loads whose waits never hold back the K/V
+  // loads in flight)
+  const long long total = (long long)__builtin_amdgcn_readfirstlane(pre[a.num_seqs]) * HG;
   const long long W = gridDim.x;
   const long long S = (total + W - 1) / W;
   long long g = (long long)blockIdx.x * S;
@@ -553,12 +644,13 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(const RowAttnArgs a) 
   int lo = 0, hi = a.num_seqs - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if ((long long)pre[mid] * HG <= g) lo = mid; else hi = mid - 1;
+    if ((long long)__builtin_amdgcn_readfirstlane(pre[mid]) * HG <= g) lo = mid; else hi = mid - 1;
   }
   int b = lo;
   while (g < g_end) {
-    const int nc = pre[b + 1] - pre[b];
-    const long long row0 = (long long)pre[b] * HG;
+    const int pb = __builtin_amdgcn_readfirstlane(pre[b]);
+    const int nc = __builtin_amdgcn_readfirstlane(pre[b + 1]) - pb;
+    const long long row0 = (long long)pb * HG;
     const int hg = (int)((g - row0) / nc);
     const long long item0 = row0 + (long long)hg * nc;  // first chunk of item (b, hg)
     const int c0 = (int)(g - item0);
@@ -742,6 +834,8 @@ __global__ __launch_bounds__(64) void cascade_merge_kernel(const CascadeMergeArg
   for (int r = 0; r < R; ++r) orow[lane + 64 * r] = (uint16_t)f32_to_bf16_bits(acc[r] * inv);
 }
 
+constexpr int kWgWaves = 4;  // wavefronts per fixed-partition work-group
+
 template <typename E, int D, int GP>
 hipError_t launch_partials_t(const RowAttnArgs& a, bool mods, hipStream_t s) {
   if (a.stream_waves > 0) {
@@ -755,6 +849,16 @@ hipError_t launch_partials_t(const RowAttnArgs& a, bool mods, hipStream_t s) {
   }
   const long long blocks = (long long)a.num_seqs * a.max_q_len * a.Hkv * a.NG * a.P;
   if (blocks <= 0) return hipSuccess;
+  if (a.wg_partitions) {
+    if (mods) {
+      hipLaunchKernelGGL((row_partials_wg_kernel<E, D, GP, true, kWgWaves>), dim3((unsigned)blocks),
+                         dim3(64 * kWgWaves), 0, s, a);
+    } else {
+      hipLaunchKernelGGL((row_partials_wg_kernel<E, D, GP, false, kWgWaves>), dim3((unsigned)blocks),
+                         dim3(64 * kWgWaves), 0, s, a);
+    }
+    return hipGetLastError();
+  }
   if (mods) {
     hipLaunchKernelGGL((row_partials_kernel<E, D, GP, true>), dim3((unsigned)blocks), dim3(64), 0, s, a);
   } else {

@@ -53,6 +53,14 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Element i of read-only data that no kernel writes while it runs (block
+// tables), read through the constant address space: with a wave-uniform index
+// it becomes a scalar load, whose wait (lgkmcnt) leaves the vector loads in
+// flight alone, even in kernels that store to global memory before it.
+__device__ __forceinline__ int32_t load_ro_i32(const int32_t* p, long long i) {
+  return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
 // log2 of sum_j 2^(s_j) for a softmax state with running max m (log2 units)

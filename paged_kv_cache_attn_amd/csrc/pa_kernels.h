@@ -59,6 +59,7 @@ struct RowAttnArgs {
   int32_t split_log2;        // partition length in tokens (log2); 30 = unsplit
   int32_t P;                 // partitions per row slot in the workspace / grid
   int32_t stream_waves;      // > 0: balanced decode split over this many wavefronts
+  int32_t wg_partitions;     // 1: each fixed partition is one multi-wavefront work-group
   int32_t causal;
   int32_t window;
   float scale;               // softmax scale

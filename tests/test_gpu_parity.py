@@ -365,11 +365,36 @@ def test_block_sizes_ragged(gpu_lib, bs):
     assert_close(gpu_prefill(gpu_lib, wp), oracle_out(wp, causal=True), "bf16")
 
 
-def test_empty_context_gives_zero(gpu_lib):
+@pytest.mark.parametrize("split", [0, -1, 64, 512])
+def test_empty_context_gives_zero(gpu_lib, split):
     w = small(ctx=(0, 5, 0))
-    got = bits_to_f64(gpu_decode(gpu_lib, w), "bf16")
+    got = bits_to_f64(gpu_decode(gpu_lib, w, split=split), "bf16")
     assert np.all(got[0] == 0) and np.all(got[2] == 0)
-    assert_close(gpu_decode(gpu_lib, w), oracle_out(w), "bf16")
+    assert_close(gpu_decode(gpu_lib, w, split=split), oracle_out(w), "bf16")
+
+
+# rows whose partitions hold fewer chunks than a work-group has wavefronts,
+# ragged tails inside a chunk, empty rows
+RAGGED_CTX = (0, 1, 15, 16, 17, 33, 63, 64, 65, 100, 130, 255, 256, 257, 700)
+
+
+@pytest.mark.parametrize("mods", [False, True])
+@pytest.mark.parametrize("split", [64, 128, 512, -1])
+@pytest.mark.parametrize("copies", [1, 20])
+def test_fixed_partitions_as_work_groups_and_as_wavefronts(gpu_lib, copies, split, mods):
+    """Fixed partitions run as 4-wavefront work-groups that merge their states
+    in LDS when the whole grid fits on the chip at once (15 rows, 2 kv-heads:
+    at most 330 partitions) and as one wavefront per partition on a larger grid
+    (the same rows 20 times: 600 to 6,600 partitions); both against the oracle,
+    with and without score mods."""
+    ctx = RAGGED_CTX * copies
+    w = small(seed=140 + copies, ctx=ctx, Hq=8, Hkv=2)
+    kw, om = {}, {}
+    if mods:
+        slopes = (2.0 ** -np.arange(1, 9) * 0.5).astype(np.float32)
+        kw = {"window": 100, "softcap": 0.5, "alibi_slopes": torch.from_numpy(slopes).cuda()}
+        om = {"window": 100, "softcap": 0.5, "alibi_slopes": slopes.astype(np.float64)}
+    assert_close(gpu_decode(gpu_lib, w, split=split, **kw), oracle_out(w, oracle.ScoreMods(**om)), "bf16")
 
 
 def test_non_causal_prefill(gpu_lib):
