@@ -74,7 +74,7 @@ enum {
   PA_ERR_HEADS = -3,         /* heads <= 0, or num_heads % num_kv_heads != 0     */
   PA_ERR_HEAD_DIM = -4,      /* head_dim not 64 or 128                          */
   PA_ERR_BLOCK_SIZE = -5,    /* block_size not a power of two in [16, 256]      */
-  PA_ERR_SPLIT = -6,         /* split_tokens not 0, -1 or a power of two >= 16  */
+  PA_ERR_SPLIT = -6,         /* split_tokens not 0, -1, -2 or a power of two >= 16 */
   PA_ERR_WORKSPACE = -7,     /* workspace NULL or smaller than required         */
   PA_ERR_DTYPE = -8,         /* dtype not PA_F32 / PA_BF16                      */
   PA_ERR_FLAG = -9,          /* causal not 0 or 1                               */
@@ -183,13 +183,21 @@ int kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_blocks, cons
  * running max, running sum) are merged afterwards -- is this library's
  * reading of how to spread long decode rows over many compute units; the
  * pages only motivate long contexts.  split_tokens:
- *    0  balanced split: 8 wavefronts per compute unit of the current device
+ *    0  the library's choice, from the sizes alone:
+ *       - max_context_len <= 256: no row is split (no merge launch);
+ *       - else, while num_seqs * num_kv_heads * ceil(max_context_len / 512)
+ *         is at most 16 per compute unit: fixed 512-key pieces (a small
+ *         batch finishes sooner on these than on the balanced split);
+ *       - else the balanced split (-2);
+ *   -2  balanced split: 8 wavefronts per compute unit of the current device
  *       (256 units if none is visible) each take an equal share of the
- *       batch's 16-token chunks, so the pieces follow the work, not a fixed
- *       length -- except when max_context_len <= 256, where no row is split
- *       (one wavefront per row and head group, and no merge launch);
+ *       batch's 16-token chunks, at least 8, so the pieces follow the work,
+ *       not a fixed length (batches of more than 4096 sequences take fixed
+ *       pieces instead);
  *   -1  never split;
  *  > 0  fixed pieces of split_tokens keys (a power of two >= 16).
+ * Fixed pieces of at least 64 keys run as 4-wavefront work-groups when the
+ * whole grid fits on the device at once (two per compute unit).
  * Returns 0 for invalid arguments.
  */
 size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_heads,

@@ -16,9 +16,11 @@ constexpr int kAutoSplitMax = 512;
 constexpr int kAutoSplitMin = 64;
 constexpr long long kAutoTargetUnits = 2048;  // ~8 wavefronts per compute unit
 constexpr int kStreamWavesPerCU = 8;          // resident decode wavefronts per compute unit
-constexpr int kStreamMinChunks = 8;           // 16-token chunks per wavefront, at least
 constexpr int kStreamMaxSeqs = 4096;          // chunk prefix of all rows fits in 16 KB of LDS
 constexpr int kWgMinSplitLog2 = 6;            // fixed partitions as work-groups from 64 keys up
+constexpr int kSplitBalanced = -2;            // split_tokens code: the balanced split, always
+constexpr int kSmallSplitLog2 = 9;            // default split of small batches: 512-key partitions
+constexpr int kSmallMaxBlocksPerCU = 16;      // ... while that grid holds at most this many per unit
 constexpr int kUnsplitMaxCtx = 256;           // rows this short are never split (no merge launch)
 constexpr int kDefaultCUs = 256;              // MI355X, when no device is visible
 
@@ -37,7 +39,7 @@ int check_heads(int32_t hq, int32_t hkv) {
   return PA_OK;
 }
 int check_split(int32_t split) {
-  if (split == 0 || split == -1) return PA_OK;
+  if (split == 0 || split == -1 || split == kSplitBalanced) return PA_OK;
   return (is_pow2(split) && split >= 16 && split <= (1 << 29)) ? PA_OK : PA_ERR_SPLIT;
 }
 int check_mods(const pa_score_mods* m) {
@@ -116,6 +118,21 @@ int wg_pays_off(int32_t B, int32_t Hkv, const Shape& s) {
   return blocks <= 2ll * device_cus() ? 1 : 0;
 }
 
+// The default split of a batch too small for the balanced split to pay off:
+// fixed 512-key partitions, while their grid holds at most 16 partitions per
+// compute unit.  Measured on MI355X (cold calls, 32/8 heads, d128): 16.8
+// against 18.7 us on 8 rows of 128..2048 keys, 20.5 against 21.1 us on 16
+// rows of 1,280, 18.4 against 21.2 us on 8 rows of 2,048, 29.9 against 34.3
+// us on 8 rows of 4,096; on the 64-row long batch (lengths 2k..32k) the
+// balanced split is far faster (463 against 626 us), and its grid of 512-key
+// partitions is 8x over the limit.  The host sees only max_context_len, so
+// the rule counts every row at that length (kv-heads only, so that
+// paged_attn_decode_split_tokens gives the same answer without num_heads).
+bool small_batch_split(int32_t B, int32_t Hkv, int32_t max_ctx) {
+  const long long parts = ((long long)max_ctx + (1 << kSmallSplitLog2) - 1) >> kSmallSplitLog2;
+  return (long long)B * Hkv * parts <= (long long)kSmallMaxBlocksPerCU * device_cus();
+}
+
 int decode_shape(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_ctx, int32_t split, Shape& s) {
   s.g = Hq / Hkv;
   s.GP = group_pad(s.g);
@@ -130,12 +147,18 @@ int decode_shape(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_ctx, int32_t sp
     s.wg = wg_pays_off(B, Hkv, s);
     return PA_OK;
   }
-  if (split == 0 && B <= kStreamMaxSeqs) {
+  if (split == 0 && small_batch_split(B, Hkv, max_ctx)) {
+    s.split_log2 = kSmallSplitLog2;
+    s.P = partitions(max_ctx, s.split_log2);
+    s.wg = wg_pays_off(B, Hkv, s);
+    return PA_OK;
+  }
+  if ((split == 0 || split == kSplitBalanced) && B <= kStreamMaxSeqs) {
     // balanced split: as many wavefronts as stay resident, but at least
-    // kStreamMinChunks chunks of work each for the largest possible batch
+    // pa::kStreamMinChunks chunks of work each for the largest possible batch
     const long long chunks = (long long)B * Hkv * s.NG * (((long long)max_ctx + 15) / 16 + 1);
     long long w = (long long)device_cus() * kStreamWavesPerCU;
-    w = std::min(w, std::max(1ll, chunks / kStreamMinChunks));
+    w = std::min(w, std::max(1ll, chunks / pa::kStreamMinChunks));
     s.W = (int)w;
     s.split_log2 = kUnsplitLog2;
     s.P = 1;
@@ -411,7 +434,10 @@ int32_t paged_attn_decode_split_tokens(int32_t num_seqs, int32_t num_kv_heads,
                                        int32_t max_context_len, int32_t split_tokens) {
   if (check_split(split_tokens) || num_seqs < 0 || num_kv_heads <= 0 || max_context_len < 0) return 0;
   if (split_tokens == 0 && max_context_len <= kUnsplitMaxCtx) return -1;  // short rows: unsplit
-  if (split_tokens == 0 && num_seqs <= kStreamMaxSeqs) return 0;  // balanced split
+  if (split_tokens == 0 && small_batch_split(num_seqs, num_kv_heads, max_context_len))
+    return 1 << kSmallSplitLog2;
+  if ((split_tokens == 0 || split_tokens == kSplitBalanced) && num_seqs <= kStreamMaxSeqs)
+    return 0;  // balanced split
   const int l2 = resolve_split_log2(num_seqs, num_kv_heads, max_context_len, split_tokens);
   return l2 >= kUnsplitLog2 ? -1 : (1 << l2);
 }
@@ -796,7 +822,7 @@ const char* paged_attn_status_string(int status) {
     case PA_ERR_HEADS: return "heads must be positive and num_heads a multiple of num_kv_heads";
     case PA_ERR_HEAD_DIM: return "head_dim must be 64 or 128";
     case PA_ERR_BLOCK_SIZE: return "block_size must be a power of two in [16, 256]";
-    case PA_ERR_SPLIT: return "split_tokens must be 0, -1 or a power of two >= 16";
+    case PA_ERR_SPLIT: return "split_tokens must be 0, -1, -2 or a power of two >= 16";
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_DTYPE: return "dtype must be PA_F32 or PA_BF16";
     case PA_ERR_FLAG: return "causal must be 0 or 1";

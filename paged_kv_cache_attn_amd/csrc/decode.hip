@@ -31,6 +31,8 @@
 #include "pa_device.h"
 #include "pa_kernels.h"
 
+
+
 namespace pa {
 namespace {
 
@@ -636,7 +638,9 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(const RowAttnArgs a) 
   // loads in flight)
   const long long total = (long long)__builtin_amdgcn_readfirstlane(pre[a.num_seqs]) * HG;
   const long long W = gridDim.x;
-  const long long S = (total + W - 1) / W;
+  // (at least kStreamMinChunks per wavefront, counted on the actual lengths:
+  // the host sized the grid from max_context_len; surplus wavefronts exit)
+  const long long S = max((total + W - 1) / W, (long long)kStreamMinChunks);
   long long g = (long long)blockIdx.x * S;
   const long long g_end = min(total, g + S);
   if (g >= g_end) return;

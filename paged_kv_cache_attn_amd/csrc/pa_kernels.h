@@ -29,6 +29,9 @@ struct BlockMaskArgs {
 
 // Everything one decode-style launch needs.  A "row slot" is (sequence b,
 // query index i < max_q_len); decode has max_q_len == 1.
+// 16-token chunks a wavefront of the balanced decode split takes at least.
+constexpr int kStreamMinChunks = 8;
+
 struct RowAttnArgs {
   void* out;                 // [rows, Hq, D]
   const void* q;             // [rows, Hq, D]

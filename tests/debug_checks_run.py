@@ -1,4 +1,4 @@
-"""Run with PAGEDATTN_DEBUG_CHECKS=1: append, block copy, decode (three
+"""Run with PAGEDATTN_DEBUG_CHECKS=1: append, block copy, decode (four
 splits), prefill and the two-phase decode through the debug-check build on valid inputs; every
 result must match the oracle (the checks never fire).  Exit status 0 = pass."""
 
@@ -26,7 +26,7 @@ def main():
     kp, vp = oracle.kv_append(w.k_pool, w.v_pool, w.k_new, w.v_new, w.slot_mapping, w.bs)
     ref = oracle.paged_attention(w.q, kp, vp, w.block_table, w.context_lens, w.cu_q_lens, w.scale, w.bs,
                                  w.dtype)
-    for split in (0, 64, -1):
+    for split in (0, -2, 64, -1):
         t = upload(w)
         binding.kv_append(t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], t["slot_mapping"])
         out = torch.empty_like(t["q"])

@@ -147,7 +147,7 @@ def test_decode_validation(fn):
     assert _decode(fn, bs=48) == -5
     assert _decode(fn, split=100) == -6
     assert _decode(fn, split=8) == -6
-    assert _decode(fn, split=-2) == -6
+    assert _decode(fn, split=-3) == -6
     assert _decode(fn, stride=0) == -11
     assert _decode(fn, q=NULL) == -1
     assert _decode(fn, bt=NULL) == -1
@@ -198,15 +198,23 @@ def test_prefill_validation():
 
 
 def test_split_resolution_and_workspace_size():
-    # explicit split sizes are taken as given; -1 never splits; 0 = balanced split
+    # explicit split sizes are taken as given; -1 never splits; -2 = balanced split;
+    # 0 = the library's choice (no device is visible here, so CUs = 256)
     assert binding.decode_split_tokens(64, 8, 32768, 512) == 512
     assert binding.decode_split_tokens(64, 8, 32768, -1) == -1
     assert binding.decode_split_tokens(64, 8, 32768, 100) == 0  # invalid
+    assert binding.decode_split_tokens(64, 8, 32768, -3) == 0  # invalid
     assert binding.decode_split_tokens(64, 8, 32768) == 0
-    assert binding.decode_split_tokens(8, 8, 2048) == 0
-    # rows of at most 256 keys are never split by the balanced mode: no workspace, no merge
+    assert binding.decode_split_tokens(8, 8, 2048, -2) == 0
+    # small batches: 512-key pieces while B * Hkv * ceil(max_ctx / 512) <= 16 per unit
+    assert binding.decode_split_tokens(8, 8, 2048) == 512
+    assert binding.decode_split_tokens(64, 8, 4096) == 512  # 4096 pieces
+    assert binding.decode_split_tokens(64, 8, 4097) == 0    # 4608 pieces: balanced split
+    # more than 4096 sequences: the balanced split is not available; fixed pieces
+    assert binding.decode_split_tokens(5000, 8, 32768, -2) > 0
+    # rows of at most 256 keys are never split by default: no workspace, no merge
     assert binding.decode_split_tokens(8, 8, 256) == -1
-    assert binding.decode_split_tokens(8, 8, 257) == 0
+    assert binding.decode_split_tokens(8, 8, 257) == 512
     assert binding.decode_workspace_size(8, 32, 8, 128, 256, 0) == 0
     # fixed partitions: B * Hkv * ceil(g/GP)*GP * P * (D + 2) * 4 bytes, 0 when unsplit
     assert binding.decode_workspace_size(64, 64, 8, 128, 32768, 512) == 64 * 8 * 8 * 64 * 130 * 4
@@ -219,7 +227,9 @@ def test_split_resolution_and_workspace_size():
     # B * Hkv * ceil(g/GP), W = min(8 * CUs, chunks / 8), chunks = items *
     # (ceil(max_ctx/16) + 1); no device is visible here, so CUs = 256
     assert binding.decode_workspace_size(64, 64, 8, 128, 32768, 0) == (2048 + 512) * 8 * 130 * 4 + 512 * 8
-    assert binding.decode_workspace_size(8, 32, 8, 128, 2048, 0) == (1032 + 64) * 4 * 130 * 4 + 64 * 8
+    assert binding.decode_workspace_size(8, 32, 8, 128, 2048, -2) == (1032 + 64) * 4 * 130 * 4 + 64 * 8
+    # the default on a small batch: 512-key pieces
+    assert binding.decode_workspace_size(8, 32, 8, 128, 2048, 0) == 8 * 8 * 4 * 4 * 130 * 4
 
 
 def _lv(G=2, maxg=4, maxp=512, gs=FAKE, pe=FAKE, ps=None):

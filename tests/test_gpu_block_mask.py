@@ -121,11 +121,11 @@ def test_unadmitted_blocks_are_never_read(gpu_lib, kind, dtype):
         got = gpu_prefill(gpu_lib, w, causal=True, block_mask=dm)
         assert_close(got, ref, dtype)
     else:
-        for split in (0, 64, -1):
+        for split in (0, -2, 64, -1):
             assert_close(gpu_decode(gpu_lib, w, split=split, block_mask=dm), ref, dtype)
 
 
-@pytest.mark.parametrize("split", [0, 64, -1])
+@pytest.mark.parametrize("split", [0, -2, 64, -1])
 def test_decode_block_mask_per_sequence(gpu_lib, split):
     rng = np.random.default_rng(903)
     w = build_workload(name="bmd", seed=903, kind="decode", dtype="bf16", Hq=64, Hkv=8, D=128, bs=32,

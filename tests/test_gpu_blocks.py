@@ -223,7 +223,7 @@ def test_mixed_page_sizes_in_one_pool_drive_decode_prefill_and_two_phase(gpu_lib
     q = bf16_round_bits(rng.standard_normal((len(seqs), HQ_, D_)).astype(np.float32))
     ref = oracle.paged_attention(q, kp, vp, table, lens, np.arange(len(seqs) + 1), scale, BS_, "bf16")
     qd = to_dev(q)
-    for split in (0, 64):
+    for split in (0, -2, 64):
         out = torch.empty_like(qd)
         gpu_lib.paged_attn_decode(out, qd, gk, gv, tt, tl, float(scale), int(lens.max()), split)
         torch.cuda.synchronize()

@@ -123,14 +123,14 @@ def test_kv_append_bit_exact(gpu_lib, case):
 
 def test_single_decode_f32(gpu_lib):
     w = named_workload("single_decode_f32")
-    for split in (0, -1, 16):
+    for split in (0, -2, -1, 16):
         assert_close(gpu_decode(gpu_lib, w, split=split), oracle_out(w), "f32")
 
 
 def test_gqa_decode_with_append(gpu_lib):
     w = named_workload("gqa_decode_bf16")
     ref = oracle_out(w)
-    for split in (0, 512, -1):
+    for split in (0, -2, 512, -1):
         assert_close(gpu_decode(gpu_lib, w, split=split), ref, "bf16")
 
 
@@ -258,7 +258,7 @@ def test_running_max_moves_many_times(gpu_lib, kind):
     if prefill:
         assert_close(gpu_prefill(gpu_lib, w), oracle_out(w, causal=True), "bf16")
     else:
-        for split in (0, 64, -1):
+        for split in (0, -2, 64, -1):
             assert_close(gpu_decode(gpu_lib, w, split=split), oracle_out(w), "bf16")
 
 
@@ -279,7 +279,7 @@ def test_running_max_moves_many_times_unscaled_values(gpu_lib, kind):
     if prefill:
         assert_close(gpu_prefill(gpu_lib, w), ref, "bf16")
     else:
-        for split in (0, 64, -1):
+        for split in (0, -2, 64, -1):
             assert_close(gpu_decode(gpu_lib, w, split=split), ref, "bf16")
 
 
@@ -296,7 +296,7 @@ def test_prefill_peaked_rows_unscaled_values(gpu_lib):
     wd = named_workload("gqa_decode_bf16")
     wd.q = bf16_round_bits((bits_to_f64(wd.q, "bf16") * 16.0).astype(np.float32))
     refd = oracle_out(wd)
-    for split in (0, 64, -1):
+    for split in (0, -2, 64, -1):
         assert_close(gpu_decode(gpu_lib, wd, split=split), refd, "bf16")
 
 
@@ -319,13 +319,13 @@ def test_deterministic_bits(gpu_lib):
     assert np.array_equal(gpu_prefill(gpu_lib, w3, t=t3), gpu_prefill(gpu_lib, w3, t=t3))
 
 
-@pytest.mark.parametrize("split", [0, -1, 16, 64, 512])
+@pytest.mark.parametrize("split", [0, -2, -1, 16, 64, 512])
 def test_split_invariance(gpu_lib, split):
     w = small(ctx=(1500, 333, 2048, 17), append=[1, 1, 1, 1])
     assert_close(gpu_decode(gpu_lib, w, split=split), oracle_out(w), "bf16")
 
 
-@pytest.mark.parametrize("split", [0, 64])
+@pytest.mark.parametrize("split", [0, -2, 64])
 def test_two_phase_calls_equal_single_call(gpu_lib, split):
     w = small(ctx=(1500, 333, 2048, 17), append=[1, 1, 1, 1])
     assert np.array_equal(gpu_decode(gpu_lib, w, split=split, phase="two"), gpu_decode(gpu_lib, w, split=split))
@@ -365,7 +365,7 @@ def test_block_sizes_ragged(gpu_lib, bs):
     assert_close(gpu_prefill(gpu_lib, wp), oracle_out(wp, causal=True), "bf16")
 
 
-@pytest.mark.parametrize("split", [0, -1, 64, 512])
+@pytest.mark.parametrize("split", [0, -2, -1, 64, 512])
 def test_empty_context_gives_zero(gpu_lib, split):
     w = small(ctx=(0, 5, 0))
     got = bits_to_f64(gpu_decode(gpu_lib, w, split=split), "bf16")
@@ -466,20 +466,20 @@ def test_poisoned_table_tail_entries_ignored(gpu_lib):
 
 
 def test_balanced_split_workspace_reuse_across_batches(gpu_lib):
-    """One workspace buffer, sized for the larger batch, serves decode calls
-    of different batches in turn; every result matches the oracle."""
+    """One workspace buffer, sized for the larger batch, serves balanced-split
+    decode calls of different batches in turn; every result matches the oracle."""
     import torch
 
     big = named_workload("long_decode_bf16", batch=6)
     small_w = small(ctx=(37, 300, 1000, 2500), append=[1, 1, 1, 1])
-    sizes = [gpu_lib.decode_workspace_size(w.B, w.Hq, w.Hkv, w.D, w.max_context_len, 0) for w in (big, small_w)]
+    sizes = [gpu_lib.decode_workspace_size(w.B, w.Hq, w.Hkv, w.D, w.max_context_len, -2) for w in (big, small_w)]
     ws = torch.empty(max(sizes) // 4 + 64, dtype=torch.float32, device="cuda")
     for w in (big, small_w, big, small_w):
         t = upload(w)
         gpu_lib.kv_append(t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], t["slot_mapping"])
         out = torch.empty_like(t["q"])
         gpu_lib.paged_attn_decode(out, t["q"], t["k_cache"], t["v_cache"], t["block_tables"], t["context_lens"],
-                                  w.scale, w.max_context_len, 0, workspace=ws)
+                                  w.scale, w.max_context_len, -2, workspace=ws)
         torch.cuda.synchronize()
         assert_close(to_numpy_bits(out), oracle_out(w), "bf16")
 
@@ -523,7 +523,7 @@ def test_prefix_lm_and_document_masks(gpu_lib, case):
             assert_close(gpu_prefill(gpu_lib, w, **kw), ref, "bf16")
         else:
             ref = oracle_out(w, oracle.ScoreMods(**om))
-            for split in (0, 64, -1):
+            for split in (0, -2, 64, -1):
                 assert_close(gpu_decode(gpu_lib, w, split=split, **kw), ref, "bf16")
     wf = small("prefill", dtype="f32", ctx=(150, 400), q_lens=[150, 170], Hq=Hq, Hkv=Hkv, causal=True)
     ds = _doc_starts(wf, rng)
@@ -540,8 +540,9 @@ def test_decode_of_a_131072_token_row(gpu_lib):
     cut into many pieces); the oracle checks the long row and a short one."""
     w = build_workload(name="long_row", seed=950, kind="decode", dtype="bf16", Hq=64, Hkv=8, D=128, bs=16,
                        context_lens=[131072, 40, 3000], append_lens=[1, 1, 1], pool_slack=1.1)
-    got = gpu_decode(gpu_lib, w, split=0)
-    assert_close(got, oracle_out(w, seqs=[0, 1]), "bf16", rows=[0, 1])
+    ref = oracle_out(w, seqs=[0, 1])
+    for split in (-2, 0):
+        assert_close(gpu_decode(gpu_lib, w, split=split), ref, "bf16", rows=[0, 1])
 
 
 @pytest.mark.parametrize("B,max_q", [(16, 1024), (27, 608)])
@@ -571,15 +572,15 @@ def test_prefill_tile_order_at_the_residency_limit(gpu_lib, B, max_q):
 @pytest.mark.parametrize("B", [4096, 4097])
 def test_batch_size_limit_of_the_balanced_split(gpu_lib, B):
     """4,096 sequences are the most the balanced split takes (its per-row
-    chunk prefix lives in LDS); one more and the automatic choice falls back
-    to fixed partitions.  Both sides, with rows just past the unsplit cutoff,
+    chunk prefix lives in LDS); one more and a request for it falls back to
+    fixed partitions.  Both sides, with rows just past the unsplit cutoff,
     against the oracle on every row."""
     rng = np.random.default_rng(B)
     w = build_workload(name=f"many{B}", seed=B, kind="decode", dtype="bf16", Hq=8, Hkv=1, D=64, bs=16,
                        context_lens=rng.integers(257, 420, size=B), append_lens=[1] * B, pool_slack=1.1)
-    split = gpu_lib.decode_split_tokens(B, 1, int(w.max_context_len), 0)
+    split = gpu_lib.decode_split_tokens(B, 1, int(w.max_context_len), -2)
     assert split == 0 if B <= 4096 else split > 0     # balanced split / fixed partitions
-    assert_close(gpu_decode(gpu_lib, w, split=0), oracle_out(w), "bf16")
+    assert_close(gpu_decode(gpu_lib, w, split=-2), oracle_out(w), "bf16")
 
 
 def test_long_prefill_chunks_sampled_rows(gpu_lib):

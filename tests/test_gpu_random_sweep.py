@@ -5,7 +5,7 @@ Each seeded case draws a batch size, kv-head count, group size (including a
 context lengths (1, block boundaries and their neighbours, random), query
 chunks (single rows, partial chunks, whole fresh prompts) and a random
 subset of score mods (a block mask among them).  It checks kv_append bit for bit over the whole pool,
-then decode in three split modes or prefill (causal or not) against the
+then decode in four split modes or prefill (causal or not) against the
 fp64 oracle, with the tolerances of the other parity tests (2e-2 max-abs for
 bf16, 1e-4 for fp32).  Sizes stay small enough for the oracle to finish in
 about a second per case.
@@ -135,7 +135,7 @@ def test_random_case(gpu_lib, seed):
                                  oracle.ScoreMods(causal=c["causal"], **om))
     if c["kind"] == "decode":
         errs = [assert_close(gpu_decode(gpu_lib, w, t=t, split=split, **kw), ref, w.dtype, tol=TOL[w.dtype])
-                for split in (0, -1, 64)]
+                for split in (0, -2, -1, 64)]
     else:
         errs = [assert_close(gpu_prefill(gpu_lib, w, t=t, causal=c["causal"], **kw), ref, w.dtype, tol=TOL[w.dtype])]
     print(f"case {seed}: max abs err {max(errs):.3e} (tolerance {TOL[w.dtype]})", flush=True)

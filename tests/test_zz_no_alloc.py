@@ -35,7 +35,7 @@ def _oracle(w):
     return oracle.paged_attention(w.q, kp, vp, w.block_table, w.context_lens, w.cu_q_lens, w.scale, w.bs, w.dtype)
 
 
-@pytest.mark.parametrize("split", [0, 512])
+@pytest.mark.parametrize("split", [0, -2, 512])
 def test_noalloc_decode_matches_workspace_decode_twice(gpu_lib, split):
     """Two calls in a row on one device, the second on a smaller batch: the
     scratch keeps the first call's contents, which must not leak into the
