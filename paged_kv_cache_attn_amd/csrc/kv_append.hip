@@ -23,6 +23,7 @@ template <typename W>  // W: uint16_t (bf16) or uint32_t (fp32) -- a raw element
 __global__ __launch_bounds__(256) void kv_append_kernel(const AppendArgs a) {
   constexpr int kRun = 16;
   constexpr int EPP = 16 / (int)sizeof(W);  // elements per 16-byte piece
+  constexpr int kPer = 2;                   // pieces per thread: 16 rows x D / EPP <= 512
   __shared__ int slot_s[kRun];
   __shared__ __attribute__((aligned(16))) W vt[kRun * 128];  // [token][d], D <= 128
   const int h = blockIdx.x % a.Hkv;
@@ -31,6 +32,24 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const AppendArgs a) {
   const int tid = threadIdx.x;
   const int D = a.D;
   const int bs = 1 << a.bs_log2;
+  const int ppr = D / EPP;  // pieces per row
+  const W* kn = static_cast<const W*>(a.k_new);
+  const W* vn = static_cast<const W*>(a.v_new);
+  W* kc = static_cast<W*>(a.k_cache);
+  W* vc = static_cast<W*>(a.v_cache);
+  // The new rows' K and V pieces are loaded first: their addresses do not
+  // depend on the slots, so these loads overlap the slot-mapping read.
+  u32x4 kx[kPer], vx[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int p = tid + 256 * j;
+    const int i = p / ppr, c = p - i * ppr;
+    if (p < kRun * ppr && i < ntok) {
+      const size_t src = ((size_t)(t0 + i) * a.Hkv + h) * D + c * EPP;
+      kx[j] = *reinterpret_cast<const u32x4*>(kn + src);
+      vx[j] = *reinterpret_cast<const u32x4*>(vn + src);
+    }
+  }
   if (tid < kRun) slot_s[tid] = tid < ntok ? a.slots[t0 + tid] : -1;
   __syncthreads();
   const int s0 = slot_s[0];
@@ -39,27 +58,25 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const AppendArgs a) {
   for (int i = 1; i < kRun; ++i) whole = whole && slot_s[i] == s0 + i;
 
   const size_t slab = (size_t)bs * D;  // elements of one (block, kv-head) slab
-  const W* kn = static_cast<const W*>(a.k_new);
-  const W* vn = static_cast<const W*>(a.v_new);
-  W* kc = static_cast<W*>(a.k_cache);
-  W* vc = static_cast<W*>(a.v_cache);
   // K: 16-byte pieces of each token's row
-  const int ppr = D / EPP;  // pieces per row
-  for (int p = tid; p < kRun * ppr; p += 256) {
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int p = tid + 256 * j;
     const int i = p / ppr, c = p - i * ppr;
+    if (p >= kRun * ppr || i >= ntok) continue;
     const int slot = slot_s[i];
     if (slot < 0) continue;
     PA_DEVICE_CHECK((slot >> a.bs_log2) < a.num_blocks);
     const int blk = slot >> a.bs_log2, off = slot & (bs - 1);
-    const u32x4 x = *reinterpret_cast<const u32x4*>(kn + ((size_t)(t0 + i) * a.Hkv + h) * D + c * EPP);
-    *reinterpret_cast<u32x4*>(kc + ((size_t)blk * a.Hkv + h) * slab + (size_t)off * D + c * EPP) = x;
+    *reinterpret_cast<u32x4*>(kc + ((size_t)blk * a.Hkv + h) * slab + (size_t)off * D + c * EPP) = kx[j];
   }
   if (whole) {
     // V rows of the run into LDS, then the sub-slab [D][16] with 16-byte stores
-    for (int p = tid; p < kRun * ppr; p += 256) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int p = tid + 256 * j;
       const int i = p / ppr, c = p - i * ppr;
-      *reinterpret_cast<u32x4*>(&vt[i * D + c * EPP]) =
-          *reinterpret_cast<const u32x4*>(vn + ((size_t)(t0 + i) * a.Hkv + h) * D + c * EPP);
+      if (p < kRun * ppr) *reinterpret_cast<u32x4*>(&vt[i * D + c * EPP]) = vx[j];
     }
     __syncthreads();
     const int blk = s0 >> a.bs_log2, off = s0 & (bs - 1);
@@ -76,15 +93,17 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const AppendArgs a) {
   } else {
     // scattered slots: a 16-byte piece of a token's V row per thread, written
     // element by element down the token's sub-slab column
-    for (int p = tid; p < kRun * ppr; p += 256) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int p = tid + 256 * j;
       const int i = p / ppr, c = p - i * ppr;
+      if (p >= kRun * ppr || i >= ntok) continue;
       const int slot = slot_s[i];
       if (slot < 0) continue;
       PA_DEVICE_CHECK((slot >> a.bs_log2) < a.num_blocks);
       const int blk = slot >> a.bs_log2, off = slot & (bs - 1);
-      const u32x4 x = *reinterpret_cast<const u32x4*>(vn + ((size_t)(t0 + i) * a.Hkv + h) * D + c * EPP);
       W e[EPP];
-      __builtin_memcpy(e, &x, 16);
+      __builtin_memcpy(e, &vx[j], 16);
       W* col = vc + ((size_t)blk * a.Hkv + h) * slab + (size_t)(off >> 4) * D * kRun + (off & 15);
 #pragma unroll
       for (int k = 0; k < EPP; ++k) col[(size_t)(c * EPP + k) * kRun] = e[k];
