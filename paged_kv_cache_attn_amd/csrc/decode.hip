@@ -149,13 +149,19 @@ __device__ __forceinline__ bool row_range(const RowAttnArgs& a, int slot, RowRan
   return true;
 }
 
+// Instances of the row kernels (template argument kMods): no score mods; the
+// soft-cap / ALiBi score mods (unconditional chunk loads, like the plain
+// path); those mods plus a block mask (chunks a row's bitmap does not admit
+// are skipped, so loads are conditional and the pipeline waits follow them).
+constexpr int kModsNone = 0, kModsScore = 1, kModsBlockMask = 2;
+
 // Attention of one row slot over keys [c_begin, c_end) (a segment of its
 // admissible range), for the GP query heads of head group hg.  Writes the
 // normalised output when the segment is the whole range (`whole`), else the
 // unnormalised partial (o, m, l) at workspace unit `unit`; with kToLds the
 // unnormalised state goes to this wavefront's LDS slots instead (o as
 // [GP][D] in lds_o, (m, l) per head in lds_ml) for a work-group merge.
-template <typename E, int D, int GP, bool kMods, bool kToLds = false>
+template <typename E, int D, int GP, int kMods, bool kToLds = false>
 __device__ __forceinline__ void attend_segment(const RowAttnArgs& a, const RowRange& rr, const int slot,
                                                const int hg, const int c_begin, const int c_end,
                                                const bool whole, const size_t unit, uint32_t* p_lds,
@@ -379,18 +385,17 @@ __device__ __forceinline__ void attend_segment(const RowAttnArgs& a, const RowRa
     __builtin_amdgcn_wave_barrier();
   };
 
-  // Block mask (mods instances only): a chunk whose key block the row's
-  // bitmap row does not admit is neither loaded nor computed.  A chunk lies
-  // inside one key block (blocks are whole multiples of 64 keys).
+  // Block mask (kMods == kModsBlockMask instances only): a chunk whose key
+  // block the row's bitmap row does not admit is neither loaded nor computed.
+  // A chunk lies inside one key block (blocks are whole multiples of 64 keys).
   const uint32_t* bm_row = nullptr;
-  if constexpr (kMods) {
-    if (a.bm.bits) bm_row = a.bm.bits + ((size_t)b * a.bm.rows + (rr.pos >> a.bm.q_log2)) * a.bm.words;
+  if constexpr (kMods == kModsBlockMask) {
+    bm_row = a.bm.bits + ((size_t)b * a.bm.rows + (rr.pos >> a.bm.q_log2)) * a.bm.words;
   }
   auto chunk_ok = [&](int tok0) -> bool {
-    if constexpr (!kMods) {
+    if constexpr (kMods != kModsBlockMask) {
       return true;
     } else {
-      if (!bm_row) return true;
       if (tok0 >= c_end) return false;  // (past the segment: nothing to compute, no word to read)
       const int kb = tok0 >> a.bm.kv_log2;
       return ((bm_row[kb >> 5] >> (kb & 31)) & 1u) != 0;
@@ -489,7 +494,7 @@ __device__ __forceinline__ void attend_segment(const RowAttnArgs& a, const RowRa
 
 // Fixed partitions: one wavefront per (row slot, head group, partition of
 // 2^split_log2 keys).  Also the unsplit path (P == 1) used by fp32 prefill.
-template <typename E, int D, int GP, bool kMods>
+template <typename E, int D, int GP, int kMods>
 __global__ __launch_bounds__(64) void row_partials_kernel(const RowAttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t p_lds[16 * GP];  // bf16 pairs or f32
   __shared__ __attribute__((aligned(16))) float stat_lds[2 * GP];
@@ -513,7 +518,7 @@ __global__ __launch_bounds__(64) void row_partials_kernel(const RowAttnArgs a) {
 // writes the partition's output or partial, in the layout row_partials_kernel
 // writes.  A partition then streams NW times faster, which shortens the tail
 // the grid's last partitions leave.
-template <typename E, int D, int GP, bool kMods, int NW>
+template <typename E, int D, int GP, int kMods, int NW>
 __global__ __launch_bounds__(64 * NW) void row_partials_wg_kernel(const RowAttnArgs a) {
   using C = Cfg<E, D, GP>;
   __shared__ __attribute__((aligned(16))) uint32_t p_lds[NW][16 * GP];
@@ -625,7 +630,7 @@ __device__ __forceinline__ void chunk_prefix(const RowAttnArgs& a, int* pre) {
 // of items split between wavefronts leave partials at unit w + item (unique:
 // the wavefronts touching an item, and the items a wavefront touches, are
 // both contiguous) for the merge kernel.
-template <typename E, int D, int GP, bool kMods>
+template <typename E, int D, int GP, int kMods>
 __global__ __launch_bounds__(64) void decode_stream_kernel(const RowAttnArgs a) {
   extern __shared__ int pre[];  // [num_seqs + 1]
   __shared__ __attribute__((aligned(16))) uint32_t p_lds[16 * GP];
@@ -840,35 +845,29 @@ __global__ __launch_bounds__(64) void cascade_merge_kernel(const CascadeMergeArg
 
 constexpr int kWgWaves = 4;  // wavefronts per fixed-partition work-group
 
-template <typename E, int D, int GP>
-hipError_t launch_partials_t(const RowAttnArgs& a, bool mods, hipStream_t s) {
+template <typename E, int D, int GP, int M>
+hipError_t launch_partials_m(const RowAttnArgs& a, hipStream_t s) {
   if (a.stream_waves > 0) {
     const size_t lds = (size_t)(a.num_seqs + 1) * sizeof(int);
-    if (mods) {
-      hipLaunchKernelGGL((decode_stream_kernel<E, D, GP, true>), dim3(a.stream_waves), dim3(64), lds, s, a);
-    } else {
-      hipLaunchKernelGGL((decode_stream_kernel<E, D, GP, false>), dim3(a.stream_waves), dim3(64), lds, s, a);
-    }
+    hipLaunchKernelGGL((decode_stream_kernel<E, D, GP, M>), dim3(a.stream_waves), dim3(64), lds, s, a);
     return hipGetLastError();
   }
   const long long blocks = (long long)a.num_seqs * a.max_q_len * a.Hkv * a.NG * a.P;
   if (blocks <= 0) return hipSuccess;
   if (a.wg_partitions) {
-    if (mods) {
-      hipLaunchKernelGGL((row_partials_wg_kernel<E, D, GP, true, kWgWaves>), dim3((unsigned)blocks),
-                         dim3(64 * kWgWaves), 0, s, a);
-    } else {
-      hipLaunchKernelGGL((row_partials_wg_kernel<E, D, GP, false, kWgWaves>), dim3((unsigned)blocks),
-                         dim3(64 * kWgWaves), 0, s, a);
-    }
-    return hipGetLastError();
-  }
-  if (mods) {
-    hipLaunchKernelGGL((row_partials_kernel<E, D, GP, true>), dim3((unsigned)blocks), dim3(64), 0, s, a);
+    hipLaunchKernelGGL((row_partials_wg_kernel<E, D, GP, M, kWgWaves>), dim3((unsigned)blocks),
+                       dim3(64 * kWgWaves), 0, s, a);
   } else {
-    hipLaunchKernelGGL((row_partials_kernel<E, D, GP, false>), dim3((unsigned)blocks), dim3(64), 0, s, a);
+    hipLaunchKernelGGL((row_partials_kernel<E, D, GP, M>), dim3((unsigned)blocks), dim3(64), 0, s, a);
   }
   return hipGetLastError();
+}
+
+template <typename E, int D, int GP>
+hipError_t launch_partials_t(const RowAttnArgs& a, int mods, hipStream_t s) {
+  if (mods == kModsBlockMask) return launch_partials_m<E, D, GP, kModsBlockMask>(a, s);
+  if (mods == kModsScore) return launch_partials_m<E, D, GP, kModsScore>(a, s);
+  return launch_partials_m<E, D, GP, kModsNone>(a, s);
 }
 
 template <typename E, int D, int GP>
@@ -884,29 +883,32 @@ hipError_t launch_merge_t(const RowAttnArgs& a, hipStream_t s) {
 }
 
 template <typename E, int D>
-hipError_t dispatch_gp(const RowAttnArgs& a, bool merge, bool mods, hipStream_t s) {
+hipError_t dispatch_gp(const RowAttnArgs& a, bool merge, int mods, hipStream_t s) {
   const int GP = a.g <= 4 ? 4 : 8;
   if (GP == 4) return merge ? launch_merge_t<E, D, 4>(a, s) : launch_partials_t<E, D, 4>(a, mods, s);
   return merge ? launch_merge_t<E, D, 8>(a, s) : launch_partials_t<E, D, 8>(a, mods, s);
 }
 
 template <typename E>
-hipError_t dispatch_d(const RowAttnArgs& a, int D, bool merge, bool mods, hipStream_t s) {
+hipError_t dispatch_d(const RowAttnArgs& a, int D, bool merge, int mods, hipStream_t s) {
   if (D == 64) return dispatch_gp<E, 64>(a, merge, mods, s);
   return dispatch_gp<E, 128>(a, merge, mods, s);
 }
 
-bool has_mods(const RowAttnArgs& a) { return a.softcap > 0.f || a.alibi != nullptr || a.bm.bits != nullptr; }
+int mods_instance(const RowAttnArgs& a) {
+  if (a.bm.bits) return kModsBlockMask;
+  return (a.softcap > 0.f || a.alibi != nullptr) ? kModsScore : kModsNone;
+}
 
 }  // namespace
 
 hipError_t launch_row_partials(const RowAttnArgs& a, int dtype, int D, hipStream_t s) {
-  return dtype == 1 ? dispatch_d<BF16>(a, D, false, has_mods(a), s)
-                    : dispatch_d<F32>(a, D, false, has_mods(a), s);
+  return dtype == 1 ? dispatch_d<BF16>(a, D, false, mods_instance(a), s)
+                    : dispatch_d<F32>(a, D, false, mods_instance(a), s);
 }
 
 hipError_t launch_row_merge(const RowAttnArgs& a, int dtype, int D, hipStream_t s) {
-  return dtype == 1 ? dispatch_d<BF16>(a, D, true, false, s) : dispatch_d<F32>(a, D, true, false, s);
+  return dtype == 1 ? dispatch_d<BF16>(a, D, true, kModsNone, s) : dispatch_d<F32>(a, D, true, kModsNone, s);
 }
 
 hipError_t launch_cascade_merge(const CascadeMergeArgs& a, int D, hipStream_t s) {
