@@ -105,6 +105,7 @@ struct Shape {
   int g, GP, NG, P, split_log2;
   int W;   // > 0: balanced split over W wavefronts
   int wg;  // 1: fixed partitions as multi-wavefront work-groups
+  int FW;  // > 0: fixed partitions walked by FW persistent wavefronts
 };
 
 // Fixed partitions of at least 64 keys run as 4-wavefront work-groups that
@@ -116,6 +117,15 @@ int wg_pays_off(int32_t B, int32_t Hkv, const Shape& s) {
   if (s.split_log2 < kWgMinSplitLog2) return 0;
   const long long blocks = (long long)B * Hkv * s.NG * s.P;
   return blocks <= 2ll * device_cus() ? 1 : 0;
+}
+
+// Decode grids of fixed partitions too large to be resident at once are
+// walked by persistent wavefronts (8 per compute unit) over the partitions
+// that exist, when the per-row prefix fits in LDS.
+int fixed_waves_for(int32_t B, int32_t Hkv, const Shape& s) {
+  if (s.wg || s.P <= 1 || B > kStreamMaxSeqs) return 0;
+  const long long blocks = (long long)B * Hkv * s.NG * s.P;
+  return (int)std::min(blocks, (long long)device_cus() * kStreamWavesPerCU);
 }
 
 // The default split of a batch too small for the balanced split to pay off:
@@ -139,6 +149,7 @@ int decode_shape(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_ctx, int32_t sp
   s.NG = (s.g - 1) / s.GP + 1;  // (g >= 1; no overflow for any int32 g)
   s.W = 0;
   s.wg = 0;
+  s.FW = 0;
   if (split == 0 && max_ctx <= kUnsplitMaxCtx) {
     // every row fits a few chunks: one work-group per (row, head group)
     // finishes it faster than a split plus the merge launch would
@@ -151,6 +162,7 @@ int decode_shape(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_ctx, int32_t sp
     s.split_log2 = kSmallSplitLog2;
     s.P = partitions(max_ctx, s.split_log2);
     s.wg = wg_pays_off(B, Hkv, s);
+    s.FW = fixed_waves_for(B, Hkv, s);
     return PA_OK;
   }
   if ((split == 0 || split == kSplitBalanced) && B <= kStreamMaxSeqs) {
@@ -167,6 +179,7 @@ int decode_shape(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_ctx, int32_t sp
   s.split_log2 = resolve_split_log2(B, Hkv, max_ctx, split);
   s.P = partitions(max_ctx, s.split_log2);
   s.wg = wg_pays_off(B, Hkv, s);
+  s.FW = fixed_waves_for(B, Hkv, s);
   return PA_OK;
 }
 
@@ -218,6 +231,7 @@ void fill_row_args(pa::RowAttnArgs& a, void* out, const void* q, const void* kc,
   a.P = s.P;
   a.stream_waves = s.W;
   a.wg_partitions = s.wg;
+  a.fixed_waves = s.FW;
   a.causal = causal;
   a.window = mods ? mods->window : 0;
   a.scale = scale;
@@ -614,6 +628,7 @@ int paged_attn_prefill(void* out, const void* q, const int32_t* cu_q_lens, const
   s.P = 1;
   s.W = 0;
   s.wg = 0;
+  s.FW = 0;
   if ((long long)num_seqs * max_q_len * num_kv_heads * s.NG > 0x7fffffffll) return PA_ERR_SIZE;
   pa::RowAttnArgs a;
   fill_row_args(a, out, q, k_cache, v_cache, block_tables, block_table_stride, context_lens,

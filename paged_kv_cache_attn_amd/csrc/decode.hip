@@ -621,6 +621,63 @@ __device__ __forceinline__ void chunk_prefix(const RowAttnArgs& a, int* pre) {
   __builtin_amdgcn_wave_barrier();
 }
 
+// Exclusive prefix of every decode row's partition count into pre[0..B] (LDS).
+__device__ __forceinline__ void partition_prefix(const RowAttnArgs& a, int* pre) {
+  const int lane = threadIdx.x;
+  int carry = 0;
+  if (lane == 0) pre[0] = 0;
+  for (int base = 0; base < a.num_seqs; base += 64) {
+    const int b = base + lane;
+    int c = 0;
+    if (b < a.num_seqs) {
+      RowRange rr;
+      row_range(a, b, rr);  // decode: slot b is sequence b's only row
+      c = rr.nparts;
+    }
+    const int incl = wave_scan(c);
+    if (b < a.num_seqs) pre[b + 1] = carry + incl;
+    carry += __shfl(incl, 63, 64);
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Fixed partitions of a large decode grid, walked by persistent wavefronts:
+// the (row, head group, partition) items that exist -- those inside each
+// row's range -- are numbered end to end and wavefront w takes items w, w +
+// W, w + 2W, ...  Each item is computed exactly as row_partials_kernel
+// computes it and lands at the same workspace unit, but no wavefront is
+// launched for the partitions a short row leaves empty (two thirds of the
+// grid on the long-context batch at 512-key partitions).
+template <typename E, int D, int GP, int kMods>
+__global__ __launch_bounds__(64) void decode_fixed_persistent_kernel(const RowAttnArgs a) {
+  extern __shared__ int pre[];  // [num_seqs + 1]
+  __shared__ __attribute__((aligned(16))) uint32_t p_lds[16 * GP];
+  __shared__ __attribute__((aligned(16))) float stat_lds[2 * GP];
+  const int HG = a.Hkv * a.NG;
+  partition_prefix(a, pre);
+  // (wave-uniform through readfirstlane, as in the balanced split)
+  const long long total = (long long)__builtin_amdgcn_readfirstlane(pre[a.num_seqs]) * HG;
+  for (long long g = blockIdx.x; g < total; g += gridDim.x) {
+    int lo = 0, hi = a.num_seqs - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((long long)__builtin_amdgcn_readfirstlane(pre[mid]) * HG <= g) lo = mid; else hi = mid - 1;
+    }
+    const int b = lo;
+    const int pb = __builtin_amdgcn_readfirstlane(pre[b]);
+    const int np = __builtin_amdgcn_readfirstlane(pre[b + 1]) - pb;
+    const int r = (int)(g - (long long)pb * HG);
+    const int hg = r / np;
+    const int p = r - hg * np;
+    RowRange rr;
+    row_range(a, b, rr);
+    const int c_begin = rr.start + (p << a.split_log2);
+    const int c_end = min(rr.hi, c_begin + (1 << a.split_log2));
+    attend_segment<E, D, GP, kMods>(a, rr, b, hg, c_begin, c_end, rr.nparts == 1,
+                                    ((size_t)b * HG + hg) * a.P + p, p_lds, stat_lds);
+  }
+}
+
 // Balanced decode ("stream" split): the items (row, head group) are laid end
 // to end as one sequence of 16-token chunks and wavefront w takes chunks
 // [w*S, (w+1)*S), S = ceil(total / waves), crossing item boundaries as it
@@ -857,6 +914,9 @@ hipError_t launch_partials_m(const RowAttnArgs& a, hipStream_t s) {
   if (a.wg_partitions) {
     hipLaunchKernelGGL((row_partials_wg_kernel<E, D, GP, M, kWgWaves>), dim3((unsigned)blocks),
                        dim3(64 * kWgWaves), 0, s, a);
+  } else if (a.fixed_waves > 0) {
+    const size_t lds = (size_t)(a.num_seqs + 1) * sizeof(int);
+    hipLaunchKernelGGL((decode_fixed_persistent_kernel<E, D, GP, M>), dim3(a.fixed_waves), dim3(64), lds, s, a);
   } else {
     hipLaunchKernelGGL((row_partials_kernel<E, D, GP, M>), dim3((unsigned)blocks), dim3(64), 0, s, a);
   }

@@ -63,6 +63,7 @@ struct RowAttnArgs {
   int32_t P;                 // partitions per row slot in the workspace / grid
   int32_t stream_waves;      // > 0: balanced decode split over this many wavefronts
   int32_t wg_partitions;     // 1: each fixed partition is one multi-wavefront work-group
+  int32_t fixed_waves;       // > 0: fixed partitions walked by this many persistent wavefronts
   int32_t causal;
   int32_t window;
   float scale;               // softmax scale
