@@ -573,14 +573,18 @@ def test_prefill_tile_order_at_the_residency_limit(gpu_lib, B, max_q):
 def test_batch_size_limit_of_the_balanced_split(gpu_lib, B):
     """4,096 sequences are the most the balanced split takes (its per-row
     chunk prefix lives in LDS); one more and a request for it falls back to
-    fixed partitions.  Both sides, with rows just past the unsplit cutoff,
-    against the oracle on every row."""
+    fixed partitions.  The same limit holds for the persistent walk over
+    fixed partitions (its per-row partition prefix lives in LDS too; past it,
+    one wavefront per partition).  Both sides of both, with rows just past
+    the unsplit cutoff, against the oracle on every row."""
     rng = np.random.default_rng(B)
     w = build_workload(name=f"many{B}", seed=B, kind="decode", dtype="bf16", Hq=8, Hkv=1, D=64, bs=16,
                        context_lens=rng.integers(257, 420, size=B), append_lens=[1] * B, pool_slack=1.1)
     split = gpu_lib.decode_split_tokens(B, 1, int(w.max_context_len), -2)
     assert split == 0 if B <= 4096 else split > 0     # balanced split / fixed partitions
-    assert_close(gpu_decode(gpu_lib, w, split=-2), oracle_out(w), "bf16")
+    ref = oracle_out(w)
+    for split in (-2, 64):
+        assert_close(gpu_decode(gpu_lib, w, split=split), ref, "bf16")
 
 
 def test_long_prefill_chunks_sampled_rows(gpu_lib):
