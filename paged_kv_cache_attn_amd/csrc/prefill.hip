@@ -132,7 +132,7 @@ __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const
   // at key 0, and so does the first tile; an entry is used only then, and
   // only if its block lies within the sequence (see the prologue below).  The
   // index is clamped to the table row, so the read stays inside the table.
-  const bool spec = !ksplit && a.window <= 0 && a.doc_starts == nullptr && a.bm.bits == nullptr;
+  const bool spec = !ksplit && a.window <= 0 && a.doc_starts == nullptr;
   const int n = a.context_lens[b];
   const int q0 = a.cu_q_lens[b];
   const int Lq = a.cu_q_lens[b + 1] - q0;
@@ -309,6 +309,12 @@ __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const
   };
   auto tile_full = [&](int k0) { return (k0 >= safe_lo) && (k0 + kTileKeys <= safe_hi); };
   auto tile_full_t = [&](int t) { return tile_full(tile_k0(t)) && (!use_bm || (tile_entry(t) & 1)); };
+  // every row of the work-group admits tile t (always, without a block mask)
+  auto tile_all_t = [&](int t) { return !use_bm || (tile_entry(t) & 1); };
+  // A tile's raw list entry (first key | all-rows bit), for the step loop:
+  // with a block mask it carries the entries of tiles t .. t+4 in scalar
+  // registers and reads one more per step, a step before it is needed.
+  auto raw_entry = [&](int t) { return tile_entry(t); };
   // this lane's bitmap row (valid rows only)
   const size_t bm_row = use_bm && row_ok ? ((size_t)b * a.bm.rows + (pos >> a.bm.q_log2)) * a.bm.words : 0;
   auto row_admits = [&](int k0) {
@@ -374,7 +380,7 @@ __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const
     const int k0 = tile_k0(t);
     const bool full = tile_full_t(t);
     // (a tile visited for other rows is masked whole for a row that does not admit it)
-    const bool admits = !use_bm || full || (row_ok && row_admits(k0));
+    const bool admits = full || tile_all_t(t) || (row_ok && row_admits(k0));
     float cmax = kNegInf;
 #pragma unroll
     for (int kg = 0; kg < 2; ++kg) {
@@ -475,10 +481,10 @@ __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const
   };
   // Keys outside this row's admissible range -> -inf (raw scores); a whole
   // tile for a row whose block-mask row does not admit it.
-  auto mask_s = [&](f32x16 (&S)[2], const int k0) {
+  auto mask_s = [&](f32x16 (&S)[2], const int k0, const bool all_rows) {
     const int kb = k0 + 8 * hl;
     const int lo = row_lo - kb, hi = row_hi - kb;
-    const bool admits = !use_bm || (row_ok && row_admits(k0));
+    const bool admits = all_rows || (row_ok && row_admits(k0));
 #pragma unroll
     for (int kg = 0; kg < 2; ++kg)
 #pragma unroll
@@ -530,11 +536,13 @@ __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const
   if (use_bm) ntiles = bm_build(seg);
   f32x16 sA[2], sB[2];
   int b1 = 0, b2 = 0, bv = 0;
+  int ent[5] = {0, 0, 0, 0, 0};  // raw entries of tiles t .. t+4 (step loop)
   if (ntiles > 0) {
     // the entries read at entry hold for tile t if the range starts at key 0,
     // the tile exists and its block for this wave is within the sequence
     auto first_entry = [&](int t) {
-      if (spec && k_begin == 0 && t < ntiles && ((64 * t + 16 * wave) >> a.bs_log2) <= last_blk) {
+      if (spec && k_begin == 0 && t < ntiles && (!use_bm || tile_k0(t) == kTileKeys * t) &&
+          ((64 * t + 16 * wave) >> a.bs_log2) <= last_blk) {
         PA_DEVICE_CHECK(spec_blk[t] >= 0 && spec_blk[t] < a.num_blocks);
         return spec_blk[t];
       }
@@ -552,21 +560,28 @@ __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const
     if constexpr (kMods) {
       // mods path: scores are modded inside its softmax
     } else {
-      if (!tile_full_t(0)) mask_s(sA, tile_k0(0));
+      if (!tile_full_t(0)) mask_s(sA, tile_k0(0), tile_all_t(0));
       update_max(row_max(sA));
     }
+  }
+  if (use_bm && ntiles > 0) {
+#pragma unroll
+    for (int i = 0; i < 5; ++i) ent[i] = raw_entry(i);
   }
   // P = t & 1 (compile time): K buffer 1-P is read, P receives tile t+2;
   // V buffer P is read, 1-P receives tile t+1.
   auto step = [&](auto P, f32x16 (&Scur)[2], f32x16 (&Snext)[2], const int t) {
     constexpr Par<1 - decltype(P)::value> Q{};
-    // (with a block mask the list entries come from LDS: read them all here,
-    // before the tile loop's own LDS reads are in flight)
-    const int k0 = tile_k0(t);
-    const int k1 = tile_k0(t + 1);
-    const int k2 = tile_k0(t + 2);
-    const int k4 = tile_k0(t + 4);
-    const bool full1 = tile_full_t(t + 1);
+    // With a block mask, tiles t .. t+4 come from the carried entries and the
+    // entry of tile t+5 is read from LDS now, for the next step; without
+    // one, the tiles are consecutive from the range's first key.
+    const int k0 = use_bm ? ent[0] & ~(kTileKeys - 1) : tile_k0(t);
+    const int k1 = use_bm ? ent[1] & ~(kTileKeys - 1) : tile_k0(t + 1);
+    const int k2 = use_bm ? ent[2] & ~(kTileKeys - 1) : tile_k0(t + 2);
+    const int k4 = use_bm ? ent[4] & ~(kTileKeys - 1) : tile_k0(t + 4);
+    const bool all1 = !use_bm || (ent[1] & 1) != 0;
+    const bool full1 = tile_full(k1) && all1;
+    const int e5 = use_bm ? raw_entry(t + 5) : 0;
     wait_tiles();  // K_{t+1}, V_t and the table entry bv landed; all waves are past iteration t-1
     const int b3 = __builtin_amdgcn_readfirstlane(bv);
     if (k0 + kTileKeys > n) {
@@ -632,12 +647,17 @@ __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const
       }
       if (t + 1 < ntiles) {  // (S_{t+1} of the last tile is stale: no update)
         if (!full1) {  // rare: maxima over admissible keys only
-          mask_s(Snext, k1);
+          mask_s(Snext, k1, all1);
           cmax = row_max(Snext);
         }
         update_max(cmax);
       }
     }
+    ent[0] = ent[1];
+    ent[1] = ent[2];
+    ent[2] = ent[3];
+    ent[3] = ent[4];
+    ent[4] = e5;
   };
   for (int t = 0; t < ntiles; t += 2) {
     step(Par<0>{}, sA, sB, t);
