@@ -27,19 +27,27 @@ def _prefill_batch():
                           context_lens=[300, 520], q_lens=[100, 200], append_lens=[100, 200], causal=True)
 
 
-def test_graph_replays_match_eager_calls(gpu_lib):
+@pytest.mark.parametrize("split", [0, -2, 64])
+def test_graph_replays_match_eager_calls(gpu_lib, split, entry="workspace"):
+    """The decode's split: the library's choice (512-key pieces as
+    work-groups here), the balanced split, 64-key pieces.  `entry` =
+    "noalloc" runs the allocation-free decode instead (tests/test_zz_no_alloc.py)."""
     wd, wp = _decode_batch(), _prefill_batch()
     td, tp = upload(wd), upload(wp)
     k0, v0 = td["k_cache"].clone(), td["v_cache"].clone()
     kp0, vp0 = tp["k_cache"].clone(), tp["v_cache"].clone()
     out_d = torch.empty_like(td["q"])
     out_p = torch.empty_like(tp["q"])
-    ws = gpu_lib.decode_workspace(td["q"], wd.Hkv, wd.max_context_len, 0)
+    ws = gpu_lib.decode_workspace(td["q"], wd.Hkv, wd.max_context_len, split)
 
     def step():
         gpu_lib.kv_append(td["k_new"], td["v_new"], td["k_cache"], td["v_cache"], td["slot_mapping"])
-        gpu_lib.paged_attn_decode(out_d, td["q"], td["k_cache"], td["v_cache"], td["block_tables"],
-                                  td["context_lens"], wd.scale, wd.max_context_len, 0, workspace=ws)
+        if entry == "noalloc":
+            gpu_lib.paged_attn_decode_noalloc(out_d, td["q"], td["k_cache"], td["v_cache"], td["block_tables"],
+                                              td["context_lens"], wd.scale, wd.max_context_len, split)
+        else:
+            gpu_lib.paged_attn_decode(out_d, td["q"], td["k_cache"], td["v_cache"], td["block_tables"],
+                                      td["context_lens"], wd.scale, wd.max_context_len, split, workspace=ws)
         gpu_lib.kv_append(tp["k_new"], tp["v_new"], tp["k_cache"], tp["v_cache"], tp["slot_mapping"])
         gpu_lib.paged_attn_prefill(out_p, tp["q"], tp["cu_q_lens"], tp["k_cache"], tp["v_cache"],
                                    tp["block_tables"], tp["context_lens"], wp.scale, wp.max_q_len, True)

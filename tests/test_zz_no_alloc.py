@@ -77,3 +77,13 @@ def test_noalloc_decode_refuses_oversized_batches(gpu_lib):
     with pytest.raises(ValueError, match="scratch"):
         gpu_lib.paged_attn_decode_noalloc(out, t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
                                           t["context_lens"], w.scale, 1 << 24, 16)
+
+
+@pytest.mark.parametrize("split", [0, -2])
+def test_noalloc_decode_inside_graph_replays(gpu_lib, split):
+    """The callers this entry point is for capture it in HIP graphs: an
+    append + decode + prefill step with the allocation-free decode, captured
+    once and replayed after eager work that changes the inputs, gives the
+    eager calls' bits on every replay."""
+    from test_gpu_graphs import test_graph_replays_match_eager_calls
+    test_graph_replays_match_eager_calls(gpu_lib, split, entry="noalloc")
