@@ -813,19 +813,87 @@ __global__ __launch_bounds__(64) void decode_stream_merge_kernel(const RowAttnAr
   merge_units<E, D, GP>(a, (size_t)unit0, np, hin % GP, b, h);
 }
 
+constexpr int kMergeSpecParts = 8;  // fixed-partition merges this small read every state up front
+
 // Merge for fixed partitions: one wavefront per (row slot, query head).
 template <typename E, int D, int GP>
 __global__ __launch_bounds__(64) void row_merge_kernel(const RowAttnArgs a) {
   const int h = blockIdx.x % a.Hq;
   const int slot = blockIdx.x / a.Hq;
-  RowRange rr;
-  if (!row_range(a, slot, rr)) return;
-  if (rr.nparts <= 1) return;
   const int kvh = h / a.g;
   const int hin = h - kvh * a.g;
   const int hg = kvh * a.NG + hin / GP;
   const int HG = a.Hkv * a.NG;
-  merge_units<E, D, GP>(a, ((size_t)slot * HG + hg) * a.P, rr.nparts, hin % GP, rr.qrow, h);
+  const size_t unit0 = ((size_t)slot * HG + hg) * a.P;
+  if (a.P <= kMergeSpecParts && !a.cu_q_lens) {
+    // Few partitions per row: every partition's state is read beside the
+    // row's length instead of after it (one dependent round trip less); the
+    // states past the row's partition count are in the workspace but unused.
+    constexpr int R = D / 64;
+    const int lane = threadIdx.x;
+    const int hs = hin % GP;
+    const float* ml = a.ws_ml + unit0 * GP * 2 + 2 * hs;
+    const float* op = a.ws_o + (unit0 * GP + hs) * D;
+    float m[kMergeSpecParts], l[kMergeSpecParts], x[kMergeSpecParts][R];
+#pragma unroll
+    for (int p = 0; p < kMergeSpecParts; ++p) {
+      m[p] = kNegInf;
+      l[p] = 0.f;
+#pragma unroll
+      for (int r = 0; r < R; ++r) x[p][r] = 0.f;
+      if (p < a.P) {
+        m[p] = ml[(size_t)p * 2 * GP];
+        l[p] = ml[(size_t)p * 2 * GP + 1];
+#pragma unroll
+        for (int r = 0; r < R; ++r) x[p][r] = op[(size_t)p * GP * D + lane + 64 * r];
+      }
+    }
+    RowRange rr;
+    if (!row_range(a, slot, rr)) return;
+    const int np = rr.nparts;
+    if (np <= 1) return;
+    float M = kNegInf;
+#pragma unroll
+    for (int p = 0; p < kMergeSpecParts; ++p)
+      if (p < np) M = fmaxf(M, m[p]);
+    float acc[R], L = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int p = 0; p < kMergeSpecParts; ++p) {
+        if (p >= np) continue;
+        const float w = fast_exp2(m[p] - M);
+        L = fmaf(w, l[p], L);
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = fmaf(w, x[p][r], acc[r]);
+      }
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    if (a.state_o) {
+      // two-phase decode: the row's state (normalised output, log-sum-exp), fp32
+      const size_t srow = (size_t)rr.qrow * a.Hq + h;
+#pragma unroll
+      for (int r = 0; r < R; ++r) a.state_o[srow * D + lane + 64 * r] = acc[r] * inv;
+      if (lane == 0) a.state_lse[srow] = state_lse2(M, L);
+      return;
+    }
+    char* orow = static_cast<char*>(a.out) + ((size_t)rr.qrow * a.Hq + h) * D * E::kBytes;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int d = lane + 64 * r;
+      if constexpr (E::kBytes == 2) {
+        reinterpret_cast<uint16_t*>(orow)[d] = (uint16_t)f32_to_bf16_bits(acc[r] * inv);
+      } else {
+        reinterpret_cast<float*>(orow)[d] = acc[r] * inv;
+      }
+    }
+    return;
+  }
+  RowRange rr;
+  if (!row_range(a, slot, rr)) return;
+  if (rr.nparts <= 1) return;
+  merge_units<E, D, GP>(a, unit0, rr.nparts, hin % GP, rr.qrow, h);
 }
 
 // Two-phase decode, last step: one wavefront per (row, query head) combines
