@@ -516,8 +516,9 @@ __global__ __launch_bounds__(64) void row_partials_kernel(const RowAttnArgs a) {
 // are dealt out in NW contiguous runs, one per wavefront, and the work-group
 // merges the NW states (log-sum-exp weights, wavefront order) in LDS before it
 // writes the partition's output or partial, in the layout row_partials_kernel
-// writes.  A partition then streams NW times faster, which shortens the tail
-// the grid's last partitions leave.
+// writes.  A partition then streams NW times faster: the launch for grids that
+// fit the device at once (small batches), where each partition's own latency
+// is the call's.
 template <typename E, int D, int GP, int kMods, int NW>
 __global__ __launch_bounds__(64 * NW) void row_partials_wg_kernel(const RowAttnArgs a) {
   using C = Cfg<E, D, GP>;
