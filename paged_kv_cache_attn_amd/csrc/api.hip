@@ -3,6 +3,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
 #include <initializer_list>
 #include <mutex>
 
@@ -90,11 +91,20 @@ int partitions(int32_t max_ctx, int split_log2) {
 
 int group_pad(int g) { return g <= 4 ? 4 : 8; }
 
+// Compute units of the current device, queried once per device (concurrent
+// first calls may both query; they store the same value).
 int device_cus() {
+  constexpr int kMaxDevices = 256;
+  static std::atomic<int> cached[kMaxDevices];
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess) return kDefaultCUs;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     return kDefaultCUs;
+  if (dev >= 0 && dev < kMaxDevices) cached[dev].store(cus, std::memory_order_relaxed);
   return cus;
 }
 
@@ -598,6 +608,7 @@ int paged_attn_prefill(void* out, const void* q, const int32_t* cu_q_lens, const
     a.row_key_start = nullptr;
     a.key_starts = nullptr;
     a.q_ctx = nullptr;
+    a.num_cus = device_cus();
     a.chain = 0;
     a.key_split = 0;
     a.nsplit = 1;
@@ -763,6 +774,7 @@ int cascade_impl(bool force_two_phase, void* out, const void* q, const void* k_c
     p.table_rows = v.group_starts;
     p.key_starts = v.prefix_starts;
     p.q_ctx = context_lens;
+    p.num_cus = device_cus();
     p.part_o = part_o + (size_t)l.range0 * plane * head_dim;
     p.part_lse = part_lse + (size_t)l.range0 * plane;
     p.row_key_start = key_start;

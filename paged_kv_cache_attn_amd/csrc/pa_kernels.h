@@ -121,6 +121,7 @@ struct PrefillArgs {
   int32_t Hq, Hkv, g;
   int32_t bs_log2;
   int32_t q_tiles;           // query tiles per (sequence, kv-head) in the grid
+  int32_t num_cus;           // compute units of the device (0: unknown)
   int32_t causal;
   int32_t window;
   float scale;

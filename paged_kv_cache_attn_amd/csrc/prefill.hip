@@ -716,11 +716,7 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, int D, hipStream_t s) {
   const int kbl = a.bs_log2 < 6 ? a.bs_log2 : 6;
   const bool split = a.key_split > 0;
   const dim3 grid((unsigned)blocks), block(kThreads);
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    cus = 0;
-  const int pair = !split && blocks <= (long long)kWGsPerCU * cus;
+  const int pair = !split && blocks <= (long long)kWGsPerCU * a.num_cus;
 #define PA_PREFILL_LAUNCH(DD, MM, KK)                                                                 \
   do {                                                                                                \
     if (split)                                                                                        \
