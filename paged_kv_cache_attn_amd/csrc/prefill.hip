@@ -39,6 +39,11 @@ constexpr int kTileKeys = 64;
 constexpr int kRowsPerWG = 128;
 constexpr int kThreads = 256;
 constexpr int kWGsPerCU = 2;  // resident work-groups per compute unit (launch bounds)
+// Score-mod instances: none (scale folded into the exponent), linear (scale
+// and ALiBi bias), soft-capped (tanh cap, then the bias).  The soft cap is a
+// compile-time choice: a run-time branch over both forms inside the
+// pipelined step costs registers the step does not have.
+constexpr int kModsNone = 0, kModsLinear = 1, kModsSoftcap = 2;
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 // Word 3 of a raw buffer resource (dword data, no swizzle) on this family.
@@ -86,7 +91,7 @@ __device__ __forceinline__ int v_swz(int d, int cpb_log2) {
 // kSplit: key-split mode (a.key_split > 0), a separate instance so that the
 // plain prefill keeps its registers.
 // kBM: the plain path with a block mask (the mods path takes one at run time).
-template <int D, bool kMods, int KBL, bool kSplit, bool kBM = false>
+template <int D, int kMods, int KBL, bool kSplit, bool kBM = false>
 __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const PrefillArgs a, const int pair_tiles) {
   constexpr int KCH = D / 8;   // 16-byte chunks per K row
   constexpr int KSTEPS = D / 16;
@@ -374,55 +379,34 @@ __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const
     }
   };
 
-  // Masks, online softmax update and P (bf16) as the B operand of O^T += V^T P^T
-  // (score-mod path; the plain path is inlined into the pipelined step).
-  auto softmax_mods = [&](f32x16 (&S)[2], const int t, bf16x8 (&pb)[4]) {
-    const int k0 = tile_k0(t);
-    const bool full = tile_full_t(t);
-    // (a tile visited for other rows is masked whole for a row that does not admit it)
-    const bool admits = full || tile_all_t(t) || (row_ok && row_admits(k0));
-    float cmax = kNegInf;
+  // Score mods (mods instances): a tile's raw scores to log2 units, s ->
+  // (softcap(s * scale) + slope * (key - pos)) * log2(e), with softcap(x) =
+  // c * tanh(x / c) written through exp2 and the hardware reciprocal
+  // (tanh(y) = 1 - 2 / (e^{2y} + 1); an infinite e^{2y} gives 1).
+  // Applied to S_{t+1} while the P.V MFMAs of tile t run, before its row
+  // maxima and masks (a soft-capped -inf would be finite), so the rest of the
+  // pipelined step is the plain path's with a unit exponent scale.
+  const float mod_sc = a.scale * kLog2e;
+  const float mod_cap_in = a.softcap > 0.f ? 2.f * kLog2e * a.scale / a.softcap : 0.f;
+  const float mod_cap_out = a.softcap * kLog2e;
+  const float mod_al = alibi_slope * kLog2e;
+  auto transform = [&](f32x16 (&S)[2], const int k0) {
+    const float base = mod_al * (float)(k0 + 8 * hl - pos);
+    if constexpr (kMods == kModsSoftcap) {
 #pragma unroll
-    for (int kg = 0; kg < 2; ++kg) {
+      for (int kg = 0; kg < 2; ++kg)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = k0 + 8 * hl + key_off(kg, i);
-        float x = S[kg][i] * a.scale;
-        if (a.softcap > 0.f) {
-          const float ez = fast_exp2(2.f * kLog2e * (x / a.softcap));
-          x = a.softcap * (1.f - 2.f / (ez + 1.f));
+        for (int i = 0; i < 16; ++i) {
+          const float ez = fast_exp2(S[kg][i] * mod_cap_in);
+          const float th = fmaf(-2.f, __builtin_amdgcn_rcpf(ez + 1.f), 1.f);  // tanh(x / c)
+          S[kg][i] = fmaf(mod_cap_out, th, fmaf(mod_al, (float)key_off(kg, i), base));
         }
-        x += alibi_slope * (float)(key - pos);
-        float sv = x * kLog2e;
-        if (!full) sv = (key >= row_lo && key < row_hi && admits) ? sv : kNegInf;
-        S[kg][i] = sv;
-        cmax = fmaxf(cmax, sv);
-      }
-    }
-    cmax = fmaxf(cmax, shfl_xor32(cmax));
-    const float m_new = fmaxf(m_run, cmax);
-    const bool need = m_new > m_run + kLazyRescale;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float alpha = need ? fast_exp2(m_run - m_new) : 1.f;
-      if (need) m_run = m_new;
-      l_run *= alpha;
+    } else {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+      for (int kg = 0; kg < 2; ++kg)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
-    }
-    const float msafe = (m_run == kNegInf) ? 0.f : m_run;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      u32x4 w;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float p0 = fast_exp2(S[s >> 1][8 * (s & 1) + 2 * j] - msafe);
-        const float p1 = fast_exp2(S[s >> 1][8 * (s & 1) + 2 * j + 1] - msafe);
-        w[j] = cvt_bf16x2(p0, p1);
-        l_run = dot2_bf16(w[j], kBf16One2, l_run);
-      }
-      pb[s] = __builtin_bit_cast(bf16x8, w);
+        for (int i = 0; i < 16; ++i)
+          S[kg][i] = fmaf(S[kg][i], mod_sc, fmaf(mod_al, (float)key_off(kg, i), base));
     }
   };
 
@@ -477,7 +461,7 @@ __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const
     for (int kg = 0; kg < 2; ++kg)
 #pragma unroll
       for (int i = 0; i < 16; ++i) c = fmaxf(c, S[kg][i]);
-    return fmaxf(c, shfl_xor32(c)) * scale_log2;
+    return fmaxf(c, shfl_xor32(c)) * (kMods ? 1.f : scale_log2);
   };
   // Keys outside this row's admissible range -> -inf (raw scores); a whole
   // tile for a row whose block-mask row does not admit it.
@@ -557,12 +541,9 @@ __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const
     bv = table_load(3);
     wait_tiles();
     compute_s(sA, ktile0);
-    if constexpr (kMods) {
-      // mods path: scores are modded inside its softmax
-    } else {
-      if (!tile_full_t(0)) mask_s(sA, tile_k0(0), tile_all_t(0));
-      update_max(row_max(sA));
-    }
+    if constexpr (kMods) transform(sA, tile_k0(0));
+    if (!tile_full_t(0)) mask_s(sA, tile_k0(0), tile_all_t(0));
+    update_max(row_max(sA));
   }
   if (use_bm && ntiles > 0) {
 #pragma unroll
@@ -589,24 +570,15 @@ __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const
       __syncthreads();
     }
     bf16x8 pb[4];
-    if constexpr (kMods) {
-      if (t + 2 < ntiles) issue_k(k2, P, b2);
-      if (t + 1 < ntiles) issue_v(k1, Q, b1);
-      b1 = b2;
-      b2 = b3;
-      bv = table_load_k(k4);
-      if (t + 1 < ntiles) compute_s(Snext, kbuf(Q));
-      softmax_mods(Scur, t, pb);
-      pv(vbuf(P), pb);
-    } else {
+    {
       // Loads of K_{t+2} and V_{t+1}, unconditional so that they join this
       // block: past the last tile they reload it into buffers nobody reads
       // any more.  S_{t+1} (on the last tile from a stale K buffer, never
-      // used) and P_t.  s * scale * log2(e) is folded into the exp argument
-      // (scale > 0 on this path).  The row sum adds the bf16-rounded weights
-      // that enter P.V (a dot2 of each packed pair with (1, 1)), so the
-      // weights sum to one and a row whose weight sits on one key returns
-      // that key's V row.
+      // used) and P_t.  Without mods s * scale * log2(e) is folded into the
+      // exp argument (scale > 0 there); with mods S_t is already in log2
+      // units.  The row sum adds the bf16-rounded weights that enter P.V (a
+      // dot2 of each packed pair with (1, 1)), so the weights sum to one and
+      // a row whose weight sits on one key returns that key's V row.
       issue_k(k2, P, b2);
       issue_v(k1, Q, b1);
       b1 = b2;
@@ -620,8 +592,8 @@ __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const
         u32x4 w;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float p0 = fast_exp2(fmaf(Scur[s >> 1][8 * (s & 1) + 2 * j], scale_log2, nm));
-          const float p1 = fast_exp2(fmaf(Scur[s >> 1][8 * (s & 1) + 2 * j + 1], scale_log2, nm));
+          const float p0 = fast_exp2(fmaf(Scur[s >> 1][8 * (s & 1) + 2 * j], kMods ? 1.f : scale_log2, nm));
+          const float p1 = fast_exp2(fmaf(Scur[s >> 1][8 * (s & 1) + 2 * j + 1], kMods ? 1.f : scale_log2, nm));
           w[j] = cvt_bf16x2(p0, p1);
           psum = dot2_bf16(w[j], kBf16One2, psum);
         }
@@ -629,6 +601,7 @@ __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const
       }
       l_run += psum;
       pv(vbuf(P), pb);
+      if constexpr (kMods) transform(Snext, k1);
       float cmax = row_max(Snext);
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads ahead
 #pragma unroll
@@ -643,7 +616,7 @@ __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const
       for (int i = 0; i < 4 * DT; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA (PV)
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // VALU (row max)
+        __builtin_amdgcn_sched_group_barrier(0x002, kMods ? 6 : 3, 0);  // VALU (mods, row max)
       }
       if (t + 1 < ntiles) {  // (S_{t+1} of the last tile is stale: no update)
         if (!full1) {  // rare: maxima over admissible keys only
@@ -711,7 +684,8 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, int D, hipStream_t s) {
   if (blocks <= 0) return hipSuccess;
   // the fast path folds a positive scale into the exponent; a block mask
   // takes the fast path's block-mask instance, or the mods path with mods
-  const bool mods = a.softcap > 0.f || a.alibi != nullptr || !(a.scale > 0.f);
+  const int mods = a.softcap > 0.f ? kModsSoftcap
+                   : (a.alibi != nullptr || !(a.scale > 0.f)) ? kModsLinear : kModsNone;
   const bool bm = a.bm.bits != nullptr;
   const int kbl = a.bs_log2 < 6 ? a.bs_log2 : 6;
   const bool split = a.key_split > 0;
@@ -722,7 +696,7 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, int D, hipStream_t s) {
     if (split)                                                                                        \
       hipLaunchKernelGGL((prefill_mfma_kernel<DD, MM, KK, true>), grid, block, 0, s, a, pair);         \
     else if (!(MM) && bm)                                                                             \
-      hipLaunchKernelGGL((prefill_mfma_kernel<DD, false, KK, false, true>), grid, block, 0, s, a, pair); \
+      hipLaunchKernelGGL((prefill_mfma_kernel<DD, kModsNone, KK, false, true>), grid, block, 0, s, a, pair); \
     else                                                                                              \
       hipLaunchKernelGGL((prefill_mfma_kernel<DD, MM, KK, false>), grid, block, 0, s, a, pair);        \
   } while (0)
@@ -733,9 +707,13 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, int D, hipStream_t s) {
     default: PA_PREFILL_LAUNCH(DD, MM, 6); break; \
   }
   if (D == 64) {
-    if (mods) { PA_PREFILL_KBL(64, true) } else { PA_PREFILL_KBL(64, false) }
+    if (mods == kModsSoftcap) { PA_PREFILL_KBL(64, kModsSoftcap) }
+    else if (mods == kModsLinear) { PA_PREFILL_KBL(64, kModsLinear) }
+    else { PA_PREFILL_KBL(64, kModsNone) }
   } else {
-    if (mods) { PA_PREFILL_KBL(128, true) } else { PA_PREFILL_KBL(128, false) }
+    if (mods == kModsSoftcap) { PA_PREFILL_KBL(128, kModsSoftcap) }
+    else if (mods == kModsLinear) { PA_PREFILL_KBL(128, kModsLinear) }
+    else { PA_PREFILL_KBL(128, kModsNone) }
   }
 #undef PA_PREFILL_KBL
 #undef PA_PREFILL_LAUNCH
