@@ -226,7 +226,8 @@ int32_t paged_attn_decode_split_tokens(int32_t num_seqs, int32_t num_kv_heads,
  *
  * max_context_len is a host-side upper bound of context_lens that sizes the
  * launch (no device->host sync); larger device values are undefined
- * behaviour.  A sequence with context_len 0 gets a zero output.  The
+ * behaviour.  scale is any finite value (usually 1/sqrt(head_dim); 0 weights
+ * every key alike).  A sequence with context_len 0 gets a zero output.  The
  * workspace (device memory of at least
  * paged_attn_decode_workspace_size(...) bytes; may be NULL when that size is
  * 0) holds per-partition partial results between the two kernels.
@@ -402,6 +403,7 @@ int32_t paged_attn_decode_cascade_plan(int32_t num_seqs, const pa_prefix_level* 
  *           positions context_lens[b]-L .. context_lens[b]-1.
  *   causal  1: a row sees keys at positions <= its own; 0: all keys.
  *   max_q_len: host-side upper bound of the per-sequence row counts.
+ *   scale   any finite value, as for the decode.
  *
  * The chunk's own keys/values must already be in the cache (kv_append first),
  * so a row always sees itself.  bf16 runs on matrix cores (bf16 products, fp32

@@ -432,6 +432,27 @@ def test_score_mods(gpu_lib, mods):
     assert_close(gpu_prefill(gpu_lib, wf, **kw), oracle_out(wf, oracle.ScoreMods(causal=True, **om)), "f32")
 
 
+@pytest.mark.parametrize("scale", [0.0, -0.08])
+@pytest.mark.parametrize("bs", [16, 64])
+def test_zero_and_negative_scale(gpu_lib, scale, bs):
+    """A scale that is not positive cannot be folded into the bf16 prefill's
+    exponent: those calls take its linear score-mod instance (and, with a soft
+    cap, the soft-capped one).  Scale 0 gives every admissible key the same
+    weight.  Decode in two split modes and both prefill paths, against the
+    oracle."""
+    w = small(ctx=(90, 700, 1300), Hq=16, Hkv=4, append=[1, 1, 1], bs=bs)
+    w.scale = scale
+    for split in (0, -1):
+        assert_close(gpu_decode(gpu_lib, w, split=split), oracle_out(w), "bf16")
+    for dtype in ("bf16", "f32"):
+        wp = small("prefill", dtype=dtype, ctx=(150, 400, 333), q_lens=[150, 170, 90], Hq=16, Hkv=4, causal=True,
+                   bs=bs)
+        wp.scale = scale
+        assert_close(gpu_prefill(gpu_lib, wp), oracle_out(wp, causal=True), dtype)
+        assert_close(gpu_prefill(gpu_lib, wp, softcap=0.5), oracle_out(wp, oracle.ScoreMods(causal=True, softcap=0.5)),
+                     dtype)
+
+
 def test_pool_beyond_4gib(gpu_lib):
     """Block ids whose byte offsets exceed 32 bits (64-bit addressing)."""
     w = small(ctx=(300, 1000), append=[1, 1])
