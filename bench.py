@@ -522,6 +522,32 @@ def extra_measurements(pa, torch, dev, flush, args):
         del t, out, ws
     res["context_sweep_gqa_decode"] = sweep
     log("context sweep measured")
+
+    # one GPU's share of an 8-way split over heads: the long-context batch
+    # with 8/1 heads and the chunked prefill with 4/1 heads (same lengths
+    # and tables); the exchange between GPUs is not part of it
+    shard = {}
+    w = named_workload("long_decode_bf16", tp=8)
+    t, out, ws = prepared(w)
+    ms = time_calls(torch, decode_fn(w, t, out, ws), flush, reps=10)
+    shard["long_decode_bf16"] = {"heads": f"{w.Hq}/{w.Hkv}", "ms": round(ms, 5), "kv_bytes": int(w.kv_bytes()),
+                                 "gbs": round(w.kv_bytes() / (ms * 1e-3) / 1e9, 2)}
+    del t, out, ws, w
+    w = named_workload("chunked_prefill_bf16", tp=8)
+    t = upload(w, dev)
+    pa.kv_append(t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], t["slot_mapping"])
+    out = torch.empty_like(t["q"])
+
+    def prefill_call():
+        pa.paged_attn_prefill(out, t["q"], t["cu_q_lens"], t["k_cache"], t["v_cache"], t["block_tables"],
+                              t["context_lens"], w.scale, w.max_q_len, causal=True)
+    ms = time_calls(torch, prefill_call, flush, reps=20)
+    fl = prefill_flops(w)
+    shard["chunked_prefill_bf16"] = {"heads": f"{w.Hq}/{w.Hkv}", "ms": round(ms, 5), "flops": fl,
+                                     "tflops": round(fl / (ms * 1e-3) / 1e12, 2)}
+    del t, out, w
+    res["tp8_shard"] = shard
+    log("8-way head shard measured")
     return res
 
 

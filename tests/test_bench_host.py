@@ -31,6 +31,21 @@ def test_chunked_prefill_flops_by_hand():
     assert bench.prefill_flops(w) == 4 * 128 * 32 * 4 * 917_760 == 60_146_319_360
 
 
+def test_head_shard_keeps_lengths_tables_and_one_eighth_of_the_heads():
+    """One GPU's share of an 8-way head split: the same lengths and block
+    tables, Hq/8 and Hkv/8 heads, 1/8 of the algorithmic flops; a split that
+    does not divide the heads is refused."""
+    import pytest
+    full = named_workload("chunked_prefill_bf16")
+    part = named_workload("chunked_prefill_bf16", tp=8)
+    assert (part.Hq, part.Hkv) == (4, 1)
+    assert np.array_equal(part.context_lens, full.context_lens)
+    assert np.array_equal(part.block_table, full.block_table)
+    assert bench.prefill_flops(part) * 8 == bench.prefill_flops(full)
+    with pytest.raises(ValueError):
+        named_workload("chunked_prefill_bf16", tp=3)
+
+
 def test_fragmentation_arithmetic():
     # lengths 1, 16, 17: slots held at page 16 are 16 + 16 + 32 = 64, unused
     # 15 + 0 + 15 = 30; at page 32: 32 * 3 = 96 held, 31 + 16 + 15 = 62 unused

@@ -307,41 +307,49 @@ WORKLOADS = {
 
 
 def named_workload(name: str, bs: int | None = None, threads: int | None = None,
-                   batch: int | None = None) -> Workload:
+                   batch: int | None = None, tp: int = 1) -> Workload:
     """One of the reference workloads (seeded; see ``WORKLOADS``).
 
     ``bs`` overrides the page size (power-of-two page-size variants);
-    ``batch`` keeps only the first ``batch`` sequences (same draws).
+    ``batch`` keeps only the first ``batch`` sequences (same draws);
+    ``tp`` keeps 1/tp of the query and kv heads: one GPU's share when the
+    heads are split over tp GPUs (same lengths and tables).
     """
     i = WORKLOADS[name][0]
     ss = np.random.SeedSequence(i)
     rng = np.random.default_rng(ss.spawn(1)[0])  # same stream as build's c_struct
     common = dict(seed=i, structure_rng=rng, threads=threads)
+    if tp != 1:
+        full = {"single_decode_f32": (4, 4), "gqa_decode_bf16": (32, 8), "chunked_prefill_bf16": (32, 8),
+                "shared_prefix_decode_bf16": (32, 8), "long_decode_bf16": (64, 8)}[name]
+        if tp < 1 or full[0] % tp or full[1] % tp:
+            raise ValueError(f"{name}: {full[0]}/{full[1]} heads do not split {tp} ways")
+    hq = lambda n: n // tp
     if name == "single_decode_f32":
-        return build_workload(name=name, kind="decode", dtype="f32", Hq=4, Hkv=4,
+        return build_workload(name=name, kind="decode", dtype="f32", Hq=hq(4), Hkv=hq(4),
                               D=64, bs=bs or 16, context_lens=[128], NB=64, **common)
     if name == "gqa_decode_bf16":
         ctx = rng.integers(128, 2049, size=8)
         ctx = ctx[:batch] if batch else ctx
-        return build_workload(name=name, kind="decode", dtype="bf16", Hq=32, Hkv=8,
+        return build_workload(name=name, kind="decode", dtype="bf16", Hq=hq(32), Hkv=hq(8),
                               D=128, bs=bs or 16, context_lens=ctx,
                               append_lens=np.ones(len(ctx), np.int64), **common)
     if name == "chunked_prefill_bf16":
         n = (batch or 4)
-        return build_workload(name=name, kind="prefill", dtype="bf16", Hq=32, Hkv=8,
+        return build_workload(name=name, kind="prefill", dtype="bf16", Hq=hq(32), Hkv=hq(8),
                               D=128, bs=bs or 16, context_lens=[2048] * n, q_lens=[512] * n,
                               append_lens=[512] * n, causal=True, **common)
     if name == "shared_prefix_decode_bf16":
         n = (batch or 16)
         bsz = bs or 16
-        return build_workload(name=name, kind="decode", dtype="bf16", Hq=32, Hkv=8,
+        return build_workload(name=name, kind="decode", dtype="bf16", Hq=hq(32), Hkv=hq(8),
                               D=128, bs=bsz, context_lens=[1280] * n,
                               shared_prefix_blocks=1024 // bsz, **common)
     if name == "long_decode_bf16":
         ctx = np.rint(rng.lognormal(mean=math.log(8192), sigma=math.log(2), size=64))
         ctx = np.clip(ctx, 2048, 32768).astype(np.int64)
         ctx = ctx[:batch] if batch else ctx
-        return build_workload(name=name, kind="decode", dtype="bf16", Hq=64, Hkv=8,
+        return build_workload(name=name, kind="decode", dtype="bf16", Hq=hq(64), Hkv=hq(8),
                               D=128, bs=bs or 16, context_lens=ctx,
                               append_lens=np.ones(len(ctx), np.int64), **common)
     raise ValueError(f"no workload {name}")
