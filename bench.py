@@ -29,8 +29,9 @@ Beside the step it reports: the achievable HBM read bandwidth of a plain
 streaming-read kernel (a second denominator), the decode of the other
 workloads (GQA batch, shared-prefix batch with logical and unique bytes), the
 two-phase decode of two shared-prefix batches beside their plain decode, a
-context sweep of the GQA shape, and the pool's internal fragmentation per
-workload and page size (arithmetic only).
+context sweep of the GQA shape, the pool's internal fragmentation per
+workload and page size (arithmetic only), and one GPU's share of an 8-way
+head split (the decode, and the prefill unsplit and over key ranges).
 
 Prints one JSON line.
 """
@@ -538,14 +539,22 @@ def extra_measurements(pa, torch, dev, flush, args):
     pa.kv_append(t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], t["slot_mapping"])
     out = torch.empty_like(t["q"])
 
-    def prefill_call():
-        pa.paged_attn_prefill(out, t["q"], t["cu_q_lens"], t["k_cache"], t["v_cache"], t["block_tables"],
-                              t["context_lens"], w.scale, w.max_q_len, causal=True)
-    ms = time_calls(torch, prefill_call, flush, reps=20)
+    max_ctx = int(w.context_lens.max())
+    ws = pa.prefill_workspace(t["q"], w.B, w.Hkv, w.max_q_len, max_ctx)
+
+    def prefill_call(split):
+        kw = {"max_context_len": max_ctx, "workspace": ws} if split else {}
+        return lambda: pa.paged_attn_prefill(out, t["q"], t["cu_q_lens"], t["k_cache"], t["v_cache"],
+                                             t["block_tables"], t["context_lens"], w.scale, w.max_q_len, causal=True,
+                                             **kw)
     fl = prefill_flops(w)
-    shard["chunked_prefill_bf16"] = {"heads": f"{w.Hq}/{w.Hkv}", "ms": round(ms, 5), "flops": fl,
-                                     "tflops": round(fl / (ms * 1e-3) / 1e12, 2)}
-    del t, out, w
+    entry = {"heads": f"{w.Hq}/{w.Hkv}", "flops": fl}
+    for label, split in (("unsplit", False), ("key_split", True)):
+        ms = time_calls(torch, prefill_call(split), flush, reps=20)
+        entry[label] = {"ms": round(ms, 5), "tflops": round(fl / (ms * 1e-3) / 1e12, 2)}
+    entry["key_split"]["workspace_bytes"] = 0 if ws is None else int(ws.numel() * 4)
+    shard["chunked_prefill_bf16"] = entry
+    del t, out, w, ws
     res["tp8_shard"] = shard
     log("8-way head shard measured")
     return res

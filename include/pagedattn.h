@@ -74,7 +74,8 @@ enum {
   PA_ERR_HEADS = -3,         /* heads <= 0, or num_heads % num_kv_heads != 0     */
   PA_ERR_HEAD_DIM = -4,      /* head_dim not 64 or 128                          */
   PA_ERR_BLOCK_SIZE = -5,    /* block_size not a power of two in [16, 256]      */
-  PA_ERR_SPLIT = -6,         /* split_tokens not 0, -1, -2 or a power of two >= 16 */
+  PA_ERR_SPLIT = -6,         /* split_tokens not 0, -1, -2 or a power of two >= 16;
+                                key_split not 0, -1 or a multiple of 64 */
   PA_ERR_WORKSPACE = -7,     /* workspace NULL or smaller than required         */
   PA_ERR_DTYPE = -8,         /* dtype not PA_F32 / PA_BF16                      */
   PA_ERR_FLAG = -9,          /* causal not 0 or 1                               */
@@ -417,6 +418,49 @@ int paged_attn_prefill(void* out, const void* q, const int32_t* cu_q_lens, const
                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                        int64_t num_blocks, float scale, int32_t causal,
                        const pa_score_mods* mods, int32_t dtype, void* stream);
+
+/*
+ * paged_attn_prefill_split -- paged_attn_prefill whose key range may be split
+ * over several work-groups per query tile, for grids of (sequence, kv-head,
+ * query tile) too small to fill the device (one GPU's share of a split over
+ * heads, short chunks of few sequences).  Each range computes exact
+ * attention over its keys as a normalised output and its log-sum-exp; a
+ * merge weights them by those exponentials, which gives the same softmax
+ * over the whole range (Dao et al., "FlashAttention", abstract: exact
+ * attention from tiles; the decode's split partitions are merged the same
+ * way).
+ *
+ *   total_q          rows of q and out (= cu_q_lens[num_seqs]; a different
+ *                    value is undefined behaviour, checked in debug builds)
+ *   max_context_len  host-side upper bound of context_lens (as for the
+ *                    decode; it sizes the key ranges)
+ *   key_split        0: the library's choice (a bf16 grid with fewer
+ *                    work-groups than compute units gets ranges of at least
+ *                    512 keys, up to about two work-groups per unit);
+ *                    -1: never split; > 0: keys per range, a multiple of 64
+ *                    (PA_ERR_SPLIT otherwise)
+ *   workspace        device memory of at least
+ *                    paged_attn_prefill_workspace_size(...) bytes (fp32 range
+ *                    states; may be NULL when that size is 0)
+ *
+ * Other arguments, masks and score mods as paged_attn_prefill.  Without a
+ * split (fp32, a grid that fills the device, key_split -1, a single range, or
+ * a block mask) the call is exactly paged_attn_prefill and ignores the
+ * workspace.  Otherwise the rounding order differs from the unsplit call
+ * (fp32 range states, bf16 output once at the end).  Returns PA_ERR_WORKSPACE
+ * when a split needs more workspace than given, PA_ERR_SIZE when total_q or
+ * max_context_len is negative or the sizes overflow.
+ */
+size_t paged_attn_prefill_workspace_size(int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                                         int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                         int32_t max_context_len, int32_t key_split, int32_t dtype);
+int paged_attn_prefill_split(void* out, const void* q, const int32_t* cu_q_lens, int32_t total_q,
+                             const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                             int32_t block_table_stride, const int32_t* context_lens, int32_t num_seqs,
+                             int32_t max_q_len, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, int64_t num_blocks, int32_t max_context_len,
+                             int32_t key_split, float scale, int32_t causal, const pa_score_mods* mods,
+                             void* workspace, size_t workspace_bytes, int32_t dtype, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* paged_attn_status_string(int status);

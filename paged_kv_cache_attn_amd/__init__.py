@@ -26,6 +26,8 @@ from .binding import (  # noqa: F401
     paged_attn_decode_noalloc,
     paged_attn_decode_cascade,
     paged_attn_prefill,
+    prefill_workspace,
+    prefill_workspace_size,
     prefix_level,
     status_string,
 )

@@ -72,6 +72,9 @@ SIGNATURES = {
                                        _vp]),
     "paged_attn_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                   _i64, _f32, _i32, _mods_p, _i32, _vp]),
+    "paged_attn_prefill_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "paged_attn_prefill_split": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
+                                        _i32, _i64, _i32, _i32, _f32, _i32, _mods_p, _vp, _sz, _i32, _vp]),
     "paged_attn_decode_cascade_workspace_size": (_sz, [_i32, ctypes.POINTER(PrefixLevel), _i32, _i32, _i32, _i32,
                                                         _i32]),
     "paged_attn_decode_cascade": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, ctypes.POINTER(PrefixLevel), _i32,
@@ -376,10 +379,31 @@ def paged_attn_decode_cascade(out, q, k_cache, v_cache, block_tables, context_le
     return out
 
 
+def prefill_workspace_size(num_seqs, total_q, max_q_len, num_heads, num_kv_heads, head_dim, max_context_len,
+                           key_split=0, dtype=PA_BF16) -> int:
+    return int(lib().paged_attn_prefill_workspace_size(num_seqs, total_q, int(max_q_len), num_heads, num_kv_heads,
+                                                       head_dim, int(max_context_len), int(key_split), dtype))
+
+
+def prefill_workspace(q, num_seqs, num_kv_heads, max_q_len, max_context_len, key_split=0):
+    """A workspace for ``paged_attn_prefill(..., max_context_len=...)``, or
+    None when the library does not split these sizes."""
+    total_q, Hq, D = q.shape
+    n = prefill_workspace_size(num_seqs, total_q, max_q_len, Hq, num_kv_heads, D, max_context_len, key_split,
+                               _dtype_code(q))
+    return torch.empty(n // 4, dtype=torch.float32, device=q.device) if n > 0 else None
+
+
 def paged_attn_prefill(out, q, cu_q_lens, k_cache, v_cache, block_tables, context_lens, scale, max_q_len,
                        causal=True, window=0, softcap=0.0, alibi_slopes=None, prefix_lens=None, doc_starts=None,
-                       block_mask=None):
-    """Query rows ``q [total_q, Hq, D]`` grouped by ``cu_q_lens [B+1]``; writes ``out``."""
+                       block_mask=None, max_context_len=None, key_split=0, workspace=None):
+    """Query rows ``q [total_q, Hq, D]`` grouped by ``cu_q_lens [B+1]``; writes ``out``.
+
+    With ``max_context_len`` (a host-side bound of ``context_lens``) the call
+    goes through ``paged_attn_prefill_split``, which may split the key range
+    of a small grid (``key_split``: 0 library choice, -1 never, or keys per
+    range); ``workspace`` then defaults to a fresh buffer of the size asked for.
+    """
     NB, Hkv, bs, D = _pool_dims(k_cache, v_cache)
     _need(q, "q", k_cache.dtype, 3)
     _need(out, "out", k_cache.dtype, 3)
@@ -391,11 +415,25 @@ def paged_attn_prefill(out, q, cu_q_lens, k_cache, v_cache, block_tables, contex
             or q.shape[2] != D:
         raise ValueError("shape mismatch between q/out/cu_q_lens/block_tables/context_lens/pools")
     mp, _keep = _mods(window, softcap, alibi_slopes, prefix_lens, doc_starts, block_mask)
-    code = lib().paged_attn_prefill(_ptr(out), _ptr(q), _ptr(cu_q_lens), _ptr(k_cache), _ptr(v_cache),
-                                    _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B, int(max_q_len),
-                                    q.shape[1], Hkv, D, bs, NB, float(scale), int(bool(causal)), mp, _dtype_code(q),
-                                    _stream())
-    _check(code, "paged_attn_prefill")
+    if max_context_len is None:
+        code = lib().paged_attn_prefill(_ptr(out), _ptr(q), _ptr(cu_q_lens), _ptr(k_cache), _ptr(v_cache),
+                                        _ptr(block_tables), block_tables.shape[1], _ptr(context_lens), B,
+                                        int(max_q_len), q.shape[1], Hkv, D, bs, NB, float(scale), int(bool(causal)),
+                                        mp, _dtype_code(q), _stream())
+        _check(code, "paged_attn_prefill")
+        return out
+    if workspace is None:
+        workspace = prefill_workspace(q, B, Hkv, max_q_len, max_context_len, key_split)
+    if workspace is not None:
+        _need(workspace, "workspace")
+    ws_ptr = _ptr(workspace) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    code = lib().paged_attn_prefill_split(_ptr(out), _ptr(q), _ptr(cu_q_lens), q.shape[0], _ptr(k_cache),
+                                          _ptr(v_cache), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+                                          B, int(max_q_len), q.shape[1], Hkv, D, bs, NB, int(max_context_len),
+                                          int(key_split), float(scale), int(bool(causal)), mp, ws_ptr, ws_bytes,
+                                          _dtype_code(q), _stream())
+    _check(code, "paged_attn_prefill_split")
     return out
 
 

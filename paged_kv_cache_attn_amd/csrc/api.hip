@@ -24,6 +24,7 @@ constexpr int kSmallSplitLog2 = 9;            // default split of small batches:
 constexpr int kSmallMaxBlocksPerCU = 16;      // ... while that grid holds at most this many per unit
 constexpr int kUnsplitMaxCtx = 256;           // rows this short are never split (no merge launch)
 constexpr int kDefaultCUs = 256;              // MI355X, when no device is visible
+constexpr int kPrefillMinSplitKeys = 512;     // split prefill: keys per range, at least
 
 int ilog2(long long x) {
   int r = 0;
@@ -31,6 +32,17 @@ int ilog2(long long x) {
   return r;
 }
 bool is_pow2(long long x) { return x > 0 && (x & (x - 1)) == 0; }
+// The product of non-negative factors exceeds limit (a negative factor
+// counts as exceeding); computed in 128 bits, so it never overflows.
+bool product_exceeds(std::initializer_list<long long> factors, long long limit) {
+  unsigned __int128 p = 1;
+  for (long long f : factors) {
+    if (f < 0) return true;
+    p *= (unsigned __int128)f;
+    if (p > (unsigned __int128)limit) return true;
+  }
+  return false;
+}
 
 int check_dtype(int32_t dtype) { return (dtype == PA_F32 || dtype == PA_BF16) ? PA_OK : PA_ERR_DTYPE; }
 int check_dim(int32_t d) { return (d == 64 || d == 128) ? PA_OK : PA_ERR_HEAD_DIM; }
@@ -567,13 +579,68 @@ int paged_attn_decode_merge(void* out, const int32_t* context_lens, int32_t num_
                      stream);
 }
 
-int paged_attn_prefill(void* out, const void* q, const int32_t* cu_q_lens, const void* k_cache,
-                       const void* v_cache, const int32_t* block_tables,
-                       int32_t block_table_stride, const int32_t* context_lens,
-                       int32_t num_seqs, int32_t max_q_len, int32_t num_heads,
-                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                       int64_t num_blocks, float scale, int32_t causal,
-                       const pa_score_mods* mods, int32_t dtype, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Key ranges of a bf16 prefill whose grid of (sequence, kv-head, query tile)
+// work-groups leaves compute units idle.  key_split: 0 library choice, -1
+// never, > 0 keys per range (a multiple of 64).  The library splits only a
+// grid smaller than the device (as a one-GPU share of a head split is) into
+// ranges of at least 512 keys, up to about two work-groups per compute unit:
+// shorter ranges cost more in merge traffic than they gain in parallelism.
+// A block mask keeps the unsplit path.
+struct PrefillSplit {
+  int key_split = 0;  // 0: no split
+  int nsplit = 1;
+};
+
+PrefillSplit prefill_split_plan(int32_t num_seqs, int32_t num_kv_heads, int32_t q_tiles, int32_t max_ctx,
+                                int32_t key_split, bool block_mask) {
+  PrefillSplit p;
+  if (key_split == -1 || max_ctx <= 0 || block_mask) return p;
+  long long per = key_split;
+  if (key_split == 0) {
+    const long long blocks = (long long)num_seqs * num_kv_heads * q_tiles;
+    const long long cus = device_cus();
+    if (blocks <= 0 || blocks >= cus) return p;
+    const long long n = std::min<long long>(2 * cus / blocks, max_ctx / kPrefillMinSplitKeys);
+    if (n < 2) return p;
+    per = ((max_ctx + n - 1) / n + 63) / 64 * 64;
+  }
+  const long long ns = (max_ctx + per - 1) / per;
+  if (ns <= 1) return p;
+  p.key_split = (int)per;
+  p.nsplit = (int)ns;
+  return p;
+}
+
+int check_prefill_split(int32_t key_split) {
+  if (key_split == 0 || key_split == -1) return PA_OK;
+  return (key_split >= 64 && key_split % 64 == 0) ? PA_OK : PA_ERR_SPLIT;
+}
+
+// Workspace of a split prefill: part_o [nsplit, total_q, Hq, D] then part_lse
+// [nsplit, total_q, Hq] (256-byte aligned), fp32; 0 without a split, and
+// SIZE_MAX when the sizes overflow.
+size_t prefill_split_bytes(const PrefillSplit& p, int32_t total_q, int32_t num_heads, int32_t head_dim,
+                           size_t* lse_offset) {
+  if (p.nsplit <= 1 || total_q <= 0) return 0;
+  const unsigned __int128 states = (unsigned __int128)p.nsplit * (unsigned)total_q * (unsigned)num_heads;
+  const unsigned __int128 o_bytes = (states * (unsigned)head_dim * 4 + 255) / 256 * 256;
+  const unsigned __int128 total = o_bytes + states * 4;
+  if (total > (unsigned __int128)(SIZE_MAX / 2)) return SIZE_MAX;
+  if (lse_offset) *lse_offset = (size_t)o_bytes;
+  return (size_t)total;
+}
+
+int prefill_impl(void* out, const void* q, const int32_t* cu_q_lens, int32_t total_q, const void* k_cache,
+                 const void* v_cache, const int32_t* block_tables, int32_t block_table_stride,
+                 const int32_t* context_lens, int32_t num_seqs, int32_t max_q_len, int32_t num_heads,
+                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                 int32_t max_context_len, int32_t key_split, float scale, int32_t causal,
+                 const pa_score_mods* mods, void* workspace, size_t workspace_bytes, int32_t dtype,
+                 void* stream) {
   int st;
   if ((st = check_dtype(dtype))) return st;
   if (num_seqs < 0 || num_blocks < 0 || max_q_len < 0) return PA_ERR_SIZE;
@@ -582,8 +649,10 @@ int paged_attn_prefill(void* out, const void* q, const int32_t* cu_q_lens, const
   if ((st = check_bs(block_size))) return st;
   if (causal != 0 && causal != 1) return PA_ERR_FLAG;
   if ((st = check_mods(mods))) return st;
+  if ((st = check_prefill_split(key_split))) return st;
+  if (key_split != -1 && (total_q < 0 || max_context_len < 0)) return PA_ERR_SIZE;
   if (num_seqs > 0 && block_table_stride < 1) return PA_ERR_TABLE_STRIDE;
-  if (num_seqs == 0 || max_q_len == 0) return PA_OK;
+  if (num_seqs == 0 || max_q_len == 0 || (key_split != -1 && total_q == 0)) return PA_OK;
   if (!out || !q || !cu_q_lens || !k_cache || !v_cache || !block_tables || !context_lens)
     return PA_ERR_NULL;
   if (!aligned16({out, q, k_cache, v_cache})) return PA_ERR_ALIGN;
@@ -626,8 +695,23 @@ int paged_attn_prefill(void* out, const void* q, const int32_t* cu_q_lens, const
     a.window = mods ? mods->window : 0;
     a.scale = scale;
     a.softcap = mods ? mods->softcap : 0.f;
-    if ((long long)num_seqs * num_kv_heads * a.q_tiles > 0x7fffffffll) return PA_ERR_SIZE;
-    return launch_status(pa::launch_prefill_mfma(a, head_dim, hs));
+    if (product_exceeds({num_seqs, num_kv_heads, a.q_tiles}, 0x7fffffffll)) return PA_ERR_SIZE;
+    const long long grid = (long long)num_seqs * num_kv_heads * a.q_tiles;
+    const PrefillSplit p = prefill_split_plan(num_seqs, num_kv_heads, a.q_tiles, max_context_len, key_split,
+                                              a.bm.bits != nullptr);
+    if (p.nsplit <= 1) return launch_status(pa::launch_prefill_mfma(a, head_dim, hs));
+    size_t lse_off = 0;
+    const size_t need = prefill_split_bytes(p, total_q, num_heads, head_dim, &lse_off);
+    if (need == SIZE_MAX || grid * p.nsplit > 0x7fffffffll) return PA_ERR_SIZE;
+    if (!workspace || workspace_bytes < need) return PA_ERR_WORKSPACE;
+    char* ws = static_cast<char*>(workspace);
+    a.part_o = reinterpret_cast<float*>(ws);
+    a.part_lse = reinterpret_cast<float*>(ws + lse_off);
+    a.key_split = p.key_split;
+    a.nsplit = p.nsplit;
+    a.total_q = total_q;
+    if ((st = launch_status(pa::launch_prefill_mfma(a, head_dim, hs)))) return st;
+    return launch_status(pa::launch_prefill_split_merge(a, head_dim, hs));
   }
   // fp32 (and group sizes that do not divide 128): one query row per
   // wavefront over its whole admissible key range, no split.
@@ -640,13 +724,56 @@ int paged_attn_prefill(void* out, const void* q, const int32_t* cu_q_lens, const
   s.W = 0;
   s.wg = 0;
   s.FW = 0;
-  if ((long long)num_seqs * max_q_len * num_kv_heads * s.NG > 0x7fffffffll) return PA_ERR_SIZE;
+  if (product_exceeds({num_seqs, max_q_len, num_kv_heads, s.NG}, 0x7fffffffll)) return PA_ERR_SIZE;
   pa::RowAttnArgs a;
   fill_row_args(a, out, q, k_cache, v_cache, block_tables, block_table_stride, context_lens,
                 cu_q_lens, num_seqs, max_q_len, num_heads, num_kv_heads, block_size, s, scale,
                 causal, mods, nullptr, head_dim);
   a.num_blocks = num_blocks;
   return launch_status(pa::launch_row_partials(a, dtype, head_dim, hs));
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attn_prefill(void* out, const void* q, const int32_t* cu_q_lens, const void* k_cache,
+                       const void* v_cache, const int32_t* block_tables,
+                       int32_t block_table_stride, const int32_t* context_lens,
+                       int32_t num_seqs, int32_t max_q_len, int32_t num_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                       int64_t num_blocks, float scale, int32_t causal,
+                       const pa_score_mods* mods, int32_t dtype, void* stream) {
+  return prefill_impl(out, q, cu_q_lens, 0, k_cache, v_cache, block_tables, block_table_stride, context_lens,
+                      num_seqs, max_q_len, num_heads, num_kv_heads, head_dim, block_size, num_blocks, 0, -1, scale,
+                      causal, mods, nullptr, 0, dtype, stream);
+}
+
+size_t paged_attn_prefill_workspace_size(int32_t num_seqs, int32_t total_q, int32_t max_q_len, int32_t num_heads,
+                                         int32_t num_kv_heads, int32_t head_dim, int32_t max_context_len,
+                                         int32_t key_split, int32_t dtype) {
+  if (dtype != PA_BF16 || num_seqs <= 0 || total_q <= 0 || max_q_len <= 0 || max_context_len < 0 ||
+      check_heads(num_heads, num_kv_heads) || check_dim(head_dim) || check_prefill_split(key_split))
+    return 0;
+  const int g = num_heads / num_kv_heads;
+  if (128 % g != 0) return 0;
+  const int q_tiles = (max_q_len - 1) / pa::prefill_rows_per_tile(g) + 1;
+  if (product_exceeds({num_seqs, num_kv_heads, q_tiles}, 0x7fffffffll)) return 0;
+  const PrefillSplit p = prefill_split_plan(num_seqs, num_kv_heads, q_tiles, max_context_len, key_split, false);
+  const size_t n = prefill_split_bytes(p, total_q, num_heads, head_dim, nullptr);
+  return n == SIZE_MAX ? 0 : n;
+}
+
+int paged_attn_prefill_split(void* out, const void* q, const int32_t* cu_q_lens, int32_t total_q,
+                             const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                             int32_t block_table_stride, const int32_t* context_lens, int32_t num_seqs,
+                             int32_t max_q_len, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t block_size, int64_t num_blocks, int32_t max_context_len, int32_t key_split,
+                             float scale, int32_t causal, const pa_score_mods* mods, void* workspace,
+                             size_t workspace_bytes, int32_t dtype, void* stream) {
+  return prefill_impl(out, q, cu_q_lens, total_q, k_cache, v_cache, block_tables, block_table_stride, context_lens,
+                      num_seqs, max_q_len, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                      max_context_len, key_split, scale, causal, mods, workspace, workspace_bytes, dtype, stream);
 }
 
 size_t paged_attn_decode_cascade_workspace_size(int32_t num_seqs, const pa_prefix_level* levels,
@@ -849,7 +976,8 @@ const char* paged_attn_status_string(int status) {
     case PA_ERR_HEADS: return "heads must be positive and num_heads a multiple of num_kv_heads";
     case PA_ERR_HEAD_DIM: return "head_dim must be 64 or 128";
     case PA_ERR_BLOCK_SIZE: return "block_size must be a power of two in [16, 256]";
-    case PA_ERR_SPLIT: return "split_tokens must be 0, -1, -2 or a power of two >= 16";
+    case PA_ERR_SPLIT:
+      return "split_tokens must be 0, -1, -2 or a power of two >= 16 (key_split: 0, -1 or a multiple of 64)";
     case PA_ERR_WORKSPACE: return "workspace missing or too small";
     case PA_ERR_DTYPE: return "dtype must be PA_F32 or PA_BF16";
     case PA_ERR_FLAG: return "causal must be 0 or 1";

@@ -92,17 +92,20 @@ struct PrefillArgs {
   const int32_t* prefix_lens;  // [num_seqs] or nullptr
   const int32_t* doc_starts;   // [total_q] or nullptr
   BlockMaskArgs bm;            // bm.bits == nullptr: no block mask
-  // Key-split mode (key_split > 0, non-causal, no mods but softcap): the grid
-  // also runs over nsplit key ranges of key_split keys; the work-group of
-  // range s writes each row's output over keys [s*key_split, (s+1)*key_split)
+  // Key-split mode (key_split > 0): the grid also runs over nsplit key ranges
+  // of key_split keys; the work-group of range s writes each row's output
+  // over keys [s*key_split, (s+1)*key_split) (every other mask still applies)
   // normalised to part_o [nsplit, total_q, Hq, D] and its log-sum-exp (log2
   // units) to part_lse [nsplit, total_q, Hq], fp32; an empty range gives 0 and
-  // -inf.  With key_starts, sequence b's keys are [key_starts[b],
-  // context_lens[b]) and range s is counted from key_starts[b].  Sequence b
-  // reads table row table_rows[b] (nullptr: row b), and the work-groups of
-  // range 0 and kv-head 0 store context_lens[b] into row_key_start[row] for
-  // each of its rows (nullptr: not stored); with chain set, the value found
-  // there must be key_starts[b] (checked in debug builds).
+  // -inf.  Used by the two-phase decode (shared parts) and by the prefill of
+  // grids that leave compute units idle (then merged by
+  // launch_prefill_split_merge).  With key_starts, sequence b's keys are
+  // [key_starts[b], context_lens[b]) and range s is counted from
+  // key_starts[b].  Sequence b reads table row table_rows[b] (nullptr: row
+  // b), and the work-groups of range 0 and kv-head 0 store context_lens[b]
+  // into row_key_start[row] for each of its rows (nullptr: not stored); with
+  // chain set, the value found there must be key_starts[b] (checked in debug
+  // builds).
   const int32_t* table_rows;
   const int32_t* key_starts;
   // key-split mode: nullptr, or per row the context length of the decode row
@@ -166,6 +169,7 @@ hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t s);
 hipError_t launch_row_partials(const RowAttnArgs& a, int dtype, int D, hipStream_t s);
 hipError_t launch_row_merge(const RowAttnArgs& a, int dtype, int D, hipStream_t s);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, int D, hipStream_t s);
+hipError_t launch_prefill_split_merge(const PrefillArgs& a, int D, hipStream_t s);
 hipError_t launch_cascade_merge(const CascadeMergeArgs& a, int D, hipStream_t s);
 int prefill_rows_per_tile(int g);
 

@@ -675,9 +675,66 @@ __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const
   }
 }
 
+// Key-split prefill, last step: one wavefront per (row, query head) combines
+// the row's nsplit range states, each a normalised output o_s with its
+// log-sum-exp lse_s (log2 units), as sum_s 2^(lse_s - M) o_s / sum_s
+// 2^(lse_s - M), M = max_s lse_s, in range order; a row no range admits any
+// key of gets zeros (every lse_s is -inf).  Four wavefronts per work-group.
+template <int D>
+__global__ __launch_bounds__(256) void prefill_split_merge_kernel(const PrefillArgs a) {
+  constexpr int R = D / 64;  // dimensions per lane
+  constexpr int U = 4;       // states whose loads are in flight together
+  const int lane = threadIdx.x & 63;
+  const size_t plane = (size_t)a.total_q * a.Hq;
+  const size_t rh = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // row * Hq + head
+  if (rh >= plane) return;
+  float M = kNegInf;
+  for (int s = lane; s < a.nsplit; s += 64) M = fmaxf(M, a.part_lse[(size_t)s * plane + rh]);
+  M = wave_max(M);
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.f;
+  float L = 0.f;
+  if (M != kNegInf) {
+    for (int s0 = 0; s0 < a.nsplit; s0 += U) {
+      float w[U], x[U][R];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int s = min(s0 + u, a.nsplit - 1);
+        const float lse = a.part_lse[(size_t)s * plane + rh];
+        w[u] = (s0 + u < a.nsplit) ? fast_exp2(lse - M) : 0.f;
+        const float* o = a.part_o + ((size_t)s * plane + rh) * D;
+#pragma unroll
+        for (int r = 0; r < R; ++r) x[u][r] = o[lane + 64 * r];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        L += w[u];
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = fmaf(w[u], x[u][r], acc[r]);
+      }
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  uint16_t* orow = static_cast<uint16_t*>(a.out) + rh * D;
+#pragma unroll
+  for (int r = 0; r < R; ++r) orow[lane + 64 * r] = (uint16_t)f32_to_bf16_bits(acc[r] * inv);
+}
+
 }  // namespace
 
 int prefill_rows_per_tile(int g) { return kRowsPerWG / g; }
+
+hipError_t launch_prefill_split_merge(const PrefillArgs& a, int D, hipStream_t s) {
+  const long long pairs = (long long)a.total_q * a.Hq;
+  if (pairs <= 0 || a.nsplit <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((pairs + 3) / 4)), block(256);
+  if (D == 64)
+    hipLaunchKernelGGL((prefill_split_merge_kernel<64>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((prefill_split_merge_kernel<128>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_prefill_mfma(const PrefillArgs& a, int D, hipStream_t s) {
   const long long blocks = (long long)a.num_seqs * a.Hkv * a.q_tiles * (a.key_split > 0 ? a.nsplit : 1);

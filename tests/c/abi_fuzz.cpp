@@ -6,6 +6,7 @@
 // memory -- through every entry point.  Each call must return PA_OK, a
 // documented negative code or a positive hipError_t, and host memory must
 // stay clean.  Exit status 0 = every call behaved.
+#include <algorithm>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
@@ -78,7 +79,7 @@ int main(int argc, char** argv) {
       }
     }
     int st;
-    switch (pick(9)) {
+    switch (pick(10)) {
       case 0:
         st = kv_append(ptr(), ptr(), ptr(), ptr(), iptr(), B, Hkv, D, bs, NB, dtype, nullptr);
         expect_status(st, "kv_append", it);
@@ -115,6 +116,17 @@ int main(int argc, char** argv) {
                                 NB, 0.1f, (int32_t)pick(3), mp, dtype, nullptr);
         expect_status(st, "paged_attn_prefill", it);
         break;
+      case 7: {
+        const int32_t tq = pick(4) == 0 ? v32() : (int32_t)std::min<long long>((long long)B * (1 + pick(600)), 0x7fffffff);
+        const int32_t ks = pick(3) == 0 ? v32() : (int32_t)(pick(4) - 1) * 64;  // -64 .. 128
+        const int32_t maxk = pick(8) == 0 ? v32() : (maxc < (1 << 30) ? maxc + (int32_t)pick(4096) : maxc);
+        const size_t ws = paged_attn_prefill_workspace_size(B, tq, maxc, Hq, Hkv, D, maxk, ks, dtype);
+        st = paged_attn_prefill_split(ptr(), ptr(), iptr(), tq, ptr(), ptr(), iptr(), stride, iptr(), B, maxc, Hq, Hkv,
+                                      D, bs, NB, maxk, ks, 0.1f, (int32_t)pick(3), mp, ptr(),
+                                      pick(2) ? ws : (size_t)pick(1 << 20), dtype, nullptr);
+        expect_status(st, "paged_attn_prefill_split", it);
+        break;
+      }
       default: {
         const int L = (int)pick(10);  // levels array of exactly L entries (the caller's contract)
         std::vector<pa_prefix_level> lv((size_t)L);

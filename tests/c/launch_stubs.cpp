@@ -10,6 +10,7 @@ hipError_t launch_copy_blocks(const CopyArgs&, hipStream_t) { return hipErrorNot
 hipError_t launch_row_partials(const RowAttnArgs&, int, int, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_row_merge(const RowAttnArgs&, int, int, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_prefill_mfma(const PrefillArgs&, int, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_prefill_split_merge(const PrefillArgs&, int, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_cascade_merge(const CascadeMergeArgs&, int, hipStream_t) { return hipErrorNotSupported; }
 int prefill_rows_per_tile(int g) { return 128 / g; }
 }  // namespace pa

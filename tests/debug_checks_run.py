@@ -1,6 +1,7 @@
 """Run with PAGEDATTN_DEBUG_CHECKS=1: append, block copy, decode (four
-splits), prefill and the two-phase decode through the debug-check build on valid inputs; every
-result must match the oracle (the checks never fire).  Exit status 0 = pass."""
+splits), prefill (unsplit and over key ranges) and the two-phase decode
+through the debug-check build on valid inputs; every result must match the
+oracle (the checks never fire).  Exit status 0 = pass."""
 
 import os
 import sys
@@ -64,6 +65,16 @@ def main():
                                t["context_lens"], wp.scale, wp.max_q_len, True)
     torch.cuda.synchronize()
     worst = max(worst, float(np.max(np.abs(bits_to_f64(to_numpy_bits(out), "bf16") - ref))))
+    # the same rows with their keys split into ranges of 64 and 192 keys
+    # (total_q and the context bound are checked on the device), and a
+    # context bound four times the longest context (the library's own split)
+    for key_split, max_ctx in ((64, 400), (192, 400), (0, 1600)):
+        out = torch.full_like(t["q"], float("nan"))
+        binding.paged_attn_prefill(out, t["q"], t["cu_q_lens"], t["k_cache"], t["v_cache"], t["block_tables"],
+                                   t["context_lens"], wp.scale, wp.max_q_len, True, max_context_len=max_ctx,
+                                   key_split=key_split)
+        torch.cuda.synchronize()
+        worst = max(worst, float(np.max(np.abs(bits_to_f64(to_numpy_bits(out), "bf16") - ref))))
     # two-phase decode: three groups (one of a single empty sequence), a
     # prefix that ends inside a block, a sequence with no own keys
     wc = build_workload(name="dbgc", seed=33, kind="decode", dtype="bf16", Hq=32, Hkv=8, D=128, bs=16,

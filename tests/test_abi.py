@@ -197,6 +197,65 @@ def test_prefill_validation():
     assert _prefill(B=0) == 0
 
 
+def _prefill_split(**over):
+    a = dict(out=FAKE, q=FAKE, cu=FAKE, total_q=64, k=FAKE, v=FAKE, bt=FAKE, stride=128, ctx=FAKE, B=1, maxq=64,
+             Hq=4, Hkv=1, D=128, bs=16, NB=200, max_ctx=2048, key_split=0, scale=0.1, causal=1, mods=None, ws=None,
+             ws_bytes=0, dtype=1)
+    a.update(over)
+    return binding.lib().paged_attn_prefill_split(
+        a["out"], a["q"], a["cu"], a["total_q"], a["k"], a["v"], a["bt"], a["stride"], a["ctx"], a["B"], a["maxq"],
+        a["Hq"], a["Hkv"], a["D"], a["bs"], a["NB"], a["max_ctx"], a["key_split"], a["scale"], a["causal"],
+        a["mods"], a["ws"], a["ws_bytes"], a["dtype"], None)
+
+
+def test_prefill_split_validation():
+    # the checks of paged_attn_prefill, then the split's own
+    assert _prefill_split(dtype=3) == -8
+    assert _prefill_split(Hq=12, Hkv=8) == -3
+    assert _prefill_split(cu=NULL) == -1
+    for bad in (100, 32, -2, -64):
+        assert _prefill_split(key_split=bad) == -6, bad
+    assert _prefill_split(total_q=-1) == -2
+    assert _prefill_split(max_ctx=-1) == -2
+    # a 2-work-group grid over 2,048 keys is split (no device is visible
+    # here, so CUs = 256): the workspace is required
+    assert _prefill_split() == -7
+    assert _prefill_split(ws=FAKE, ws_bytes=1000) == -7
+    assert _prefill_split(key_split=1024) == -7
+    # nothing to do, or arguments the split does not read
+    assert _prefill_split(total_q=0) == 0
+    assert _prefill_split(maxq=0) == 0
+    assert _prefill_split(B=0) == 0
+    assert _prefill_split(key_split=-1, total_q=-1, max_ctx=-1, out=ctypes.c_void_p(0x1001)) == -14
+
+
+def test_prefill_split_plan_and_workspace_size():
+    ws = binding.prefill_workspace_size
+    # one GPU's share of an 8-way head split of the chunked prefill: 4 sequences
+    # x 1 kv-head x 16 query tiles = 64 work-groups on 256 units -> min(512 / 64,
+    # 2048 / 512) = 4 ranges of 512 keys; part_o 4 x 2048 x 4 x 128 fp32, then
+    # part_lse 4 x 2048 x 4 fp32
+    assert ws(4, 2048, 512, 4, 1, 128, 2048) == 4 * 2048 * 4 * 128 * 4 + 4 * 2048 * 4 * 4
+    # the whole batch (512 work-groups) fills the device: no split
+    assert ws(4, 2048, 512, 32, 8, 128, 2048) == 0
+    # explicit ranges: 1,024 keys of 2,048 -> 2 ranges; one range -> no split
+    assert ws(4, 2048, 512, 32, 8, 128, 2048, 1024) == 2 * 2048 * 32 * 128 * 4 + 2 * 2048 * 32 * 4
+    assert ws(4, 2048, 512, 32, 8, 128, 2048, 2048) == 0
+    assert ws(4, 2048, 512, 4, 1, 128, 2048, -1) == 0
+    # ranges of at least 512 keys: 700 keys are not split; 64 work-groups at
+    # 1,500 keys -> min(512 / 64, 1500 // 512) = 2 ranges of 768 keys (750
+    # rounded up to whole 64-key tiles)
+    assert ws(1, 64, 64, 4, 1, 128, 700) == 0
+    assert ws(4, 2048, 512, 4, 1, 128, 1500) == 2 * 2048 * 4 * 128 * 4 + 2 * 2048 * 4 * 4
+    # D 64, 4 ranges of 1,024 keys, 3 rows of 1 head: part_o 4 x 3 x 64 fp32,
+    # part_lse 4 x 3 fp32
+    assert ws(1, 3, 3, 1, 1, 64, 4096, 1024) == 4 * 3 * 64 * 4 + 4 * 3 * 4
+    # fp32, group sizes that do not divide 128, invalid key_split: no workspace
+    assert ws(4, 2048, 512, 4, 1, 128, 2048, 0, binding.PA_F32) == 0
+    assert ws(4, 2048, 512, 24, 8, 128, 2048) == 0
+    assert ws(4, 2048, 512, 4, 1, 128, 2048, 100) == 0
+
+
 def test_split_resolution_and_workspace_size():
     # explicit split sizes are taken as given; -1 never splits; -2 = balanced split;
     # 0 = the library's choice (no device is visible here, so CUs = 256)
