@@ -743,6 +743,11 @@ __global__ __launch_bounds__(64) void decode_stream_kernel(const RowAttnArgs a) 
 
 // Combine np consecutive partials (units unit0 .. unit0+np-1, head slot hs)
 // into output row qrow, head h: log-sum-exp weights, ascending unit order.
+template <int U>
+struct MergeBatch {
+  static constexpr int value = U;
+};
+
 template <typename E, int D, int GP>
 __device__ __forceinline__ void merge_units(const RowAttnArgs& a, const size_t unit0, const int np,
                                             const int hs, const int qrow, const int h) {
@@ -751,32 +756,55 @@ __device__ __forceinline__ void merge_units(const RowAttnArgs& a, const size_t u
   const int lane = threadIdx.x;
   const float* ml = a.ws_ml + unit0 * GP * 2 + 2 * hs;  // unit u at ml[u * 2 * GP]
   const float* op = a.ws_o + (unit0 * GP + hs) * D;     // unit u at op[u * GP * D]
-  float M = kNegInf;
-  for (int p = lane; p < np; p += 64) M = fmaxf(M, ml[(size_t)p * 2 * GP]);
-  M = wave_max(M);
+  // Batches of U partials, each one memory round trip: lane j reads the (m, l)
+  // of partial p0 + j while every lane reads its dimensions of all U output
+  // rows; the batch's maximum and weights follow from those registers (the
+  // weights broadcast by readlane).  A later batch with a larger maximum
+  // rescales what is summed so far.  Summation in ascending partial order.
+  // Batches of 8 for at most 8 partials (no loads of padding), else of 32.
+  float M = kNegInf, L = 0.f;
   float acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = 0.f;
-  float L = 0.f;
-  if (M != kNegInf) {
-    for (int p = lane; p < np; p += 64)
-      L += fast_exp2(ml[(size_t)p * 2 * GP] - M) * ml[(size_t)p * 2 * GP + 1];
-    L = wave_sum(L);
-    constexpr int U = 8;  // partials whose loads are in flight together
+  auto batches = [&](auto UC) {
+    constexpr int U = decltype(UC)::value;  // partials whose loads are in flight together
     for (int p0 = 0; p0 < np; p0 += U) {
-      float w[U], x[U][R];
+      const int n = min(U, np - p0);
+      float mv = kNegInf, lv = 0.f;
+      if (lane < n) {
+        mv = ml[(size_t)(p0 + lane) * 2 * GP];
+        lv = ml[(size_t)(p0 + lane) * 2 * GP + 1];
+      }
+      float x[U][R];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int p = min(p0 + u, np - 1);
-        w[u] = (p0 + u < np) ? fast_exp2(ml[(size_t)p * 2 * GP] - M) : 0.f;
+        const int p = p0 + min(u, n - 1);
 #pragma unroll
         for (int r = 0; r < R; ++r) x[u][r] = op[(size_t)p * GP * D + lane + 64 * r];
       }
+      const float Mn = fmaxf(M, wave_max(mv));
+      if (Mn == kNegInf) continue;  // no key in any partial so far
+      if (M != kNegInf && Mn > M) {
+        const float alpha = fast_exp2(M - Mn);
+        L *= alpha;
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+        for (int r = 0; r < R; ++r) acc[r] *= alpha;
+      }
+      M = Mn;
+      const float wv = lane < n ? fast_exp2(mv - M) : 0.f;  // (an empty partial: 0)
+      L += wave_sum(wv * lv);
 #pragma unroll
-        for (int r = 0; r < R; ++r) acc[r] = fmaf(w[u], x[u][r], acc[r]);
+      for (int u = 0; u < U; ++u) {
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wv), u));
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = fmaf(w, x[u][r], acc[r]);
+      }
     }
+  };
+  if (np <= 8) {
+    batches(MergeBatch<8>{});
+  } else {
+    batches(MergeBatch<32>{});
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   if (a.state_o) {
