@@ -964,32 +964,52 @@ __global__ __launch_bounds__(64) void cascade_merge_kernel(const CascadeMergeArg
     if (np == 0) return a.state_o + rh * D;
     return a.ws_o + (size_t)(unit0 + (i - a.nsplit) * GP) * D;
   };
-  float M = kNegInf;
-  for (int i = lane; i < ns; i += 64) M = fmaxf(M, m_of(i));
-  M = wave_max(M);
+  // Batches of states as in merge_units: lane j holds the (m, l) of state
+  // i0 + j, every lane loads its dimensions of all the batch's outputs, one
+  // memory round trip per batch; ascending state order.
+  float M = kNegInf, L = 0.f;
   float acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = 0.f;
-  float L = 0.f;
-  if (M != kNegInf) {
-    for (int i = lane; i < ns; i += 64) L += fast_exp2(m_of(i) - M) * l_of(i);
-    L = wave_sum(L);
-    constexpr int U = 4;  // states whose loads are in flight together
+  auto batches = [&](auto UC) {
+    constexpr int U = decltype(UC)::value;  // states whose loads are in flight together
     for (int i0 = 0; i0 < ns; i0 += U) {
-      float w[U], x[U][R];
+      const int n = min(U, ns - i0);
+      float mv = kNegInf, lv = 0.f;
+      if (lane < n) {
+        mv = m_of(i0 + lane);
+        lv = l_of(i0 + lane);
+      }
+      float x[U][R];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int i = min(i0 + u, ns - 1);
-        w[u] = (i0 + u < ns) ? fast_exp2(m_of(i) - M) : 0.f;
-        const float* op = o_of(i);
+        const float* op = o_of(i0 + min(u, n - 1));
 #pragma unroll
         for (int r = 0; r < R; ++r) x[u][r] = op[lane + 64 * r];
       }
+      const float Mn = fmaxf(M, wave_max(mv));
+      if (Mn == kNegInf) continue;  // no key in any state so far
+      if (M != kNegInf && Mn > M) {
+        const float alpha = fast_exp2(M - Mn);
+        L *= alpha;
 #pragma unroll
-      for (int u = 0; u < U; ++u)
+        for (int r = 0; r < R; ++r) acc[r] *= alpha;
+      }
+      M = Mn;
+      const float wv = lane < n ? fast_exp2(mv - M) : 0.f;  // (an empty state: 0)
+      L += wave_sum(wv * lv);
 #pragma unroll
-        for (int r = 0; r < R; ++r) acc[r] = fmaf(w[u], x[u][r], acc[r]);
+      for (int u = 0; u < U; ++u) {
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wv), u));
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = fmaf(w, x[u][r], acc[r]);
+      }
     }
+  };
+  if (ns <= 8) {
+    batches(MergeBatch<8>{});
+  } else {
+    batches(MergeBatch<32>{});
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   uint16_t* orow = static_cast<uint16_t*>(a.out) + rh * D;
