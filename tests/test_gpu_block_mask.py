@@ -136,6 +136,23 @@ def test_decode_block_mask_per_sequence(gpu_lib, split):
     assert_close(gpu_decode(gpu_lib, w, split=split, block_mask=device_mask(gpu_lib, bm)), ref, "bf16")
 
 
+@pytest.mark.parametrize("split", [64, -2])
+def test_decode_merge_with_leading_empty_partials(gpu_lib, split):
+    """A 3,000-key row whose mask admits only its last 7 key blocks of 64: at
+    64-key partitions the first 32 partial states (the merge's first batch)
+    are all empty and the rest hold every key; a second row admits every
+    block."""
+    w = build_workload(name="bme", seed=907, kind="decode", dtype="bf16", Hq=16, Hkv=2, D=128, bs=16,
+                       context_lens=[3000, 900], append_lens=[1, 1])
+    kbn = (3000 + 63) // 64
+    dense = np.zeros((2, 1, kbn), dtype=bool)
+    dense[0, 0, kbn - 7:] = True
+    dense[1, 0, :] = True
+    bm = pack_block_mask(dense, 1 << 20, 64)
+    ref = oracle_with(w, block_mask=bm)
+    assert_close(gpu_decode(gpu_lib, w, split=split, block_mask=device_mask(gpu_lib, bm)), ref, "bf16")
+
+
 def test_block_mask_all_ones_equals_no_mask(gpu_lib):
     w = build_workload(name="bm1", seed=904, kind="prefill", dtype="bf16", Hq=32, Hkv=8, D=128, bs=16,
                        context_lens=[700, 333], q_lens=[200, 333], append_lens=[200, 333], causal=True)

@@ -262,6 +262,23 @@ def test_running_max_moves_many_times(gpu_lib, kind):
             assert_close(gpu_decode(gpu_lib, w, split=split), oracle_out(w), "bf16")
 
 
+def test_decode_merge_of_more_than_32_partials(gpu_lib):
+    """Rows of 3,000 and 2,500 fresh keys whose magnitudes grow along the row,
+    at 64-key partitions: 47 and 40 partial states, which the merge reads in
+    two batches (32, then the rest); the second batch holds the larger maxima
+    and rescales what the first summed.  Also at 128 keys (24 and 20 states,
+    one batch) and with the balanced split."""
+    w = small(ctx=(3000, 2500), append=[3000, 2500], Hq=8, Hkv=2, seed=23)
+    k = bits_to_f64(w.k_new, "bf16")
+    grow = 1.0 + np.arange(k.shape[0], dtype=np.float64) / 400.0
+    w.k_new = bf16_round_bits((k * grow[:, None, None]).astype(np.float32))
+    w.q = bf16_round_bits((bits_to_f64(w.q, "bf16") * 2.0).astype(np.float32))
+    ref = oracle_out(w)
+    for split in (64, 128, -2):
+        assert_close(gpu_decode(gpu_lib, w, split=split), ref, "bf16")
+        assert_close(gpu_decode(gpu_lib, w, split=split, phase="partials+merge"), ref, "bf16")
+
+
 @pytest.mark.parametrize("kind", ["prefill", "decode"])
 def test_running_max_moves_many_times_unscaled_values(gpu_lib, kind):
     """The growing-keys batch above with V ~ N(0,1) left as drawn, so peaked
