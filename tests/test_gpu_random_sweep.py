@@ -4,11 +4,11 @@ Each seeded case draws a batch size, kv-head count, group size (including a
 3 that does not divide the tile), head dim, page size, dtype, per-sequence
 context lengths (1, block boundaries and their neighbours, random), query
 chunks (single rows, partial chunks, whole fresh prompts) and a random
-subset of score mods (a block mask among them).  It checks kv_append bit for bit over the whole pool,
-then decode in four split modes or prefill (causal or not) against the
-fp64 oracle, with the tolerances of the other parity tests (2e-2 max-abs for
-bf16, 1e-4 for fp32).  Sizes stay small enough for the oracle to finish in
-about a second per case.
+subset of score mods (a block mask among them).  It checks kv_append bit for
+bit over the whole pool, then decode in four split modes or prefill (causal
+or not; also through the key-split entry) against the fp64 oracle, with the
+tolerances of the other parity tests (2e-2 max-abs for bf16, 1e-4 for fp32).
+Sizes stay small enough for the oracle to finish in about a second per case.
 """
 
 import os
@@ -138,6 +138,16 @@ def test_random_case(gpu_lib, seed):
                 for split in (0, -2, -1, 64)]
     else:
         errs = [assert_close(gpu_prefill(gpu_lib, w, t=t, causal=c["causal"], **kw), ref, w.dtype, tol=TOL[w.dtype])]
+        # the same rows through the key-split entry: ranges of 64 or 128 keys,
+        # or the library's choice under a context bound 4x the longest context
+        ks = int(np.random.default_rng(seed + 3).choice([64, 128, 0]))
+        max_ctx = int(w.context_lens.max()) * (4 if ks == 0 else 1)
+        out = torch.empty_like(t["q"])
+        gpu_lib.paged_attn_prefill(out, t["q"], t["cu_q_lens"], t["k_cache"], t["v_cache"], t["block_tables"],
+                                   t["context_lens"], w.scale, w.max_q_len, c["causal"], max_context_len=max_ctx,
+                                   key_split=ks, **kw)
+        torch.cuda.synchronize()
+        errs.append(assert_close(to_numpy_bits(out), ref, w.dtype, tol=TOL[w.dtype]))
     print(f"case {seed}: max abs err {max(errs):.3e} (tolerance {TOL[w.dtype]})", flush=True)
 
 
