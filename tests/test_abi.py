@@ -269,6 +269,14 @@ def test_split_resolution_and_workspace_size():
     assert binding.decode_split_tokens(8, 8, 2048) == 512
     assert binding.decode_split_tokens(64, 8, 4096) == 512  # 4096 pieces
     assert binding.decode_split_tokens(64, 8, 4097) == 0    # 4608 pieces: balanced split
+    # longer pieces once a row would hold more than 32 of 512 keys: at most 32
+    # partial states per row (ceil(log2 max_ctx) - 5, at least 9)
+    assert binding.decode_split_tokens(2, 8, 16384) == 512
+    assert binding.decode_split_tokens(2, 8, 16385) == 1024
+    assert binding.decode_split_tokens(1, 8, 32768) == 1024
+    assert binding.decode_split_tokens(1, 8, 65536) == 2048
+    assert binding.decode_split_tokens(1, 8, 131072) == 4096
+    assert binding.decode_workspace_size(1, 64, 8, 128, 32768, 0) == 1 * 8 * 8 * 32 * 130 * 4
     # more than 4096 sequences: the balanced split is not available; fixed pieces
     assert binding.decode_split_tokens(5000, 8, 32768, -2) > 0
     # rows of at most 256 keys are never split by default: no workspace, no merge
