@@ -187,8 +187,10 @@ int kv_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_blocks, cons
  *    0  the library's choice, from the sizes alone:
  *       - max_context_len <= 256: no row is split (no merge launch);
  *       - else, while num_seqs * num_kv_heads * ceil(max_context_len / 512)
- *         is at most 16 per compute unit: fixed 512-key pieces (a small
- *         batch finishes sooner on these than on the balanced split);
+ *         is at most 16 per compute unit: fixed pieces of 512 keys,
+ *         longer (powers of two) when a row would hold more than 32 of them
+ *         (a small batch finishes sooner on these than on the balanced
+ *         split);
  *       - else the balanced split (-2);
  *   -2  balanced split: 8 wavefronts per compute unit of the current device
  *       (256 units if none is visible) each take an equal share of the
