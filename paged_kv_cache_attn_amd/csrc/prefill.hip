@@ -170,8 +170,10 @@ __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const
   int row_lo = (row_ok && a.window > 0) ? max(0, pos - a.window + 1) : 0;
   if (row_ok && a.doc_starts) row_lo = max(row_lo, a.doc_starts[q0 + qi]);
   if (ksplit) {
-    row_lo = max(row_lo, kstart + split * a.key_split);
-    row_hi = min(row_hi, kstart + (split + 1) * a.key_split);
+    // (64-bit: the last range may end past 2^31 keys)
+    const long long range_lo = kstart + (long long)split * a.key_split;
+    row_lo = (int)max((long long)row_lo, range_lo);
+    row_hi = (int)min((long long)row_hi, range_lo + a.key_split);
     if (a.row_key_start && split == 0 && kvh == 0 && row_ok && head_in == 0 && hl == 0) {
       PA_DEVICE_CHECK(!a.chain || a.row_key_start[q0 + qi] == kstart);
       a.row_key_start[q0 + qi] = n;
