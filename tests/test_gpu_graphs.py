@@ -101,3 +101,42 @@ def test_calls_on_a_side_stream(gpu_lib):
                                   w.scale, w.max_context_len, 0, workspace=ws)
     side.synchronize()
     assert np.array_equal(to_numpy_bits(out), to_numpy_bits(ref))
+
+
+def test_two_phase_decode_replays_in_a_graph(gpu_lib):
+    """The two-phase decode (shared parts on the matrix cores, own keys by the
+    decode, then the merge: four launches) captured in a graph: every replay,
+    after eager calls on new queries, gives the eager call's bits; the eager
+    result matches the oracle."""
+    from tests.test_gpu_cascade import device_level, grouped
+    from tests.test_gpu_parity import assert_close, oracle_out
+    w, starts, prefix = grouped(912, [(5, 12), (3, 4)], [40, 1, 300, 17, 9, 200, 64, 1])
+    t = upload(w)
+    gpu_lib.kv_append(t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], t["slot_mapping"])
+    levels = [device_level(gpu_lib, starts, prefix)]
+    out = torch.empty_like(t["q"])
+    ws = gpu_lib.decode_cascade_workspace(t["q"], w.Hkv, levels, w.max_context_len)
+
+    def call():
+        gpu_lib.paged_attn_decode_cascade(out, t["q"], t["k_cache"], t["v_cache"], t["block_tables"],
+                                          t["context_lens"], levels, w.scale, w.max_context_len, workspace=ws,
+                                          mode="two_phase")
+
+    call()
+    torch.cuda.synchronize()
+    assert_close(to_numpy_bits(out), oracle_out(w), "bf16")
+    q0 = t["q"].clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    for seed in (1, 2, 3):
+        g = torch.Generator(device="cuda").manual_seed(seed)
+        t["q"].copy_((q0.float() + 0.25 * torch.randn(q0.shape, generator=g, device="cuda")).to(q0.dtype))
+        call()
+        torch.cuda.synchronize()
+        want = to_numpy_bits(out).copy()
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_numpy_bits(out), want), f"two-phase replay {seed}"
