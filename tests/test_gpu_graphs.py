@@ -140,3 +140,43 @@ def test_two_phase_decode_replays_in_a_graph(gpu_lib):
         graph.replay()
         torch.cuda.synchronize()
         assert np.array_equal(to_numpy_bits(out), want), f"two-phase replay {seed}"
+
+
+def test_split_prefill_replays_in_a_graph(gpu_lib):
+    """The key-split prefill (ranges on the matrix cores, then the merge of
+    their fp32 states through the caller's workspace) captured in a graph:
+    every replay, after eager calls on new queries, gives the eager call's
+    bits; the eager result matches the oracle."""
+    from workloads import named_workload
+    from tests.test_gpu_parity import assert_close, oracle_out
+    w = named_workload("chunked_prefill_bf16", tp=8, batch=2)
+    t = upload(w)
+    gpu_lib.kv_append(t["k_new"], t["v_new"], t["k_cache"], t["v_cache"], t["slot_mapping"])
+    out = torch.empty_like(t["q"])
+    max_ctx = int(w.context_lens.max())
+    ws = gpu_lib.prefill_workspace(t["q"], w.B, w.Hkv, w.max_q_len, max_ctx)
+    assert ws is not None  # 32 work-groups: the library splits the keys
+
+    def call():
+        gpu_lib.paged_attn_prefill(out, t["q"], t["cu_q_lens"], t["k_cache"], t["v_cache"], t["block_tables"],
+                                   t["context_lens"], w.scale, w.max_q_len, True, max_context_len=max_ctx,
+                                   workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    assert_close(to_numpy_bits(out), oracle_out(w, causal=True), "bf16")
+    q0 = t["q"].clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    torch.cuda.synchronize()
+    for seed in (1, 2, 3):
+        g = torch.Generator(device="cuda").manual_seed(seed)
+        t["q"].copy_((q0.float() + 0.25 * torch.randn(q0.shape, generator=g, device="cuda")).to(q0.dtype))
+        call()
+        torch.cuda.synchronize()
+        want = to_numpy_bits(out).copy()
+        out.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_numpy_bits(out), want), f"split prefill replay {seed}"
