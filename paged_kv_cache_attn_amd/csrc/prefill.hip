@@ -643,9 +643,9 @@ __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const
 
   // ---- normalise and store: lane holds row `r`, dims 32dt + 8(i/4) + 4hl + i%4 ----
   const float l_tot = l_run + shfl_xor32(l_run);
-  if (!row_ok) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if constexpr (ksplit) {
+    if (!row_ok) return;
     // this key range's state: normalised output and log-sum-exp, fp32
     const size_t prow = ((size_t)split * a.total_q + q0 + qi) * a.Hq + head;
     float* po = a.part_o + prow * D;
@@ -661,18 +661,44 @@ __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const
       }
     }
     if (hl == 0) a.part_lse[prow] = state_lse2(m_run, l_tot);
-    return;
-  }
-  char* orow = static_cast<char*>(a.out) + ((size_t)(q0 + qi) * a.Hq + head) * D * 2;
+  } else {
+    // The rows go through LDS (the K tile buffers, free now: every wave has
+    // waited for its own tile loads above) so that each store instruction
+    // writes whole rows: a lane's accumulators hold 8-byte pieces of one row,
+    // and stores of such pieces, one row per lane, cost more than the
+    // transpose.  Rows r < 64 sit in ktile0, the rest in ktile1, their 16-byte
+    // chunks swizzled as the K tiles are (conflict-free writes down a column).
+    // The stores are non-temporal: nothing here reads the output again.
+    __syncthreads();  // every wave is done reading the tiles
+    char* srow = reinterpret_cast<char*>(r < 64 ? ktile0 : ktile1) + (size_t)(r & 63) * (D * 2);
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
+    for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      const int d = 32 * dt + 8 * g4 + 4 * hl;
-      uint2 w;
-      w.x = cvt_bf16x2(oacc[dt][4 * g4 + 0] * inv, oacc[dt][4 * g4 + 1] * inv);
-      w.y = cvt_bf16x2(oacc[dt][4 * g4 + 2] * inv, oacc[dt][4 * g4 + 3] * inv);
-      *reinterpret_cast<uint2*>(orow + d * 2) = w;
+      for (int g4 = 0; g4 < 4; ++g4) {
+        uint2 w;
+        w.x = cvt_bf16x2(oacc[dt][4 * g4 + 0] * inv, oacc[dt][4 * g4 + 1] * inv);
+        w.y = cvt_bf16x2(oacc[dt][4 * g4 + 2] * inv, oacc[dt][4 * g4 + 3] * inv);
+        *reinterpret_cast<uint2*>(srow + k_swz<KCH>(r, 4 * dt + g4) * 16 + hl * 8) = w;
+      }
+    }
+    __syncthreads();
+    // 16-byte chunk e of the work-group's output, ordered (query position,
+    // head, chunk): the g heads of one position are one contiguous run
+    // (g * QT = 128: the matrix-core path takes only such groups)
+    const int g = a.g;
+#pragma unroll
+    for (int k = 0; k < kRowsPerWG * KCH / kThreads; ++k) {
+      const int e = k * kThreads + tid;
+      const int c = e % KCH;
+      const int hi = (e / KCH) % g;
+      const int ql = e / (KCH * g);
+      const int rr = hi * QT + ql;
+      if (q_start + ql < Lq) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(rr < 64 ? ktile0 : ktile1) +
+                                                        (size_t)(rr & 63) * (D * 2) + k_swz<KCH>(rr, c) * 16);
+        char* dst = static_cast<char*>(a.out) + ((size_t)(q0 + q_start + ql) * a.Hq + kvh * g + hi) * D * 2 + c * 16;
+        __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(dst));
+      }
     }
   }
 }
