@@ -419,6 +419,18 @@ def test_non_causal_prefill(gpu_lib):
     assert_close(gpu_prefill(gpu_lib, wp, causal=False), oracle_out(wp, causal=False), "bf16")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("g", [1, 2, 8, 16, 32])
+def test_prefill_group_sizes_ragged_chunks(gpu_lib, g, D):
+    """The matrix-core prefill at every group size it takes beside 4 (a work-group holds 128/g query
+    positions x the g heads of one kv-head, and its output rows leave in (position, head) order): chunks
+    that end inside a query tile, a single-row chunk, a fresh prompt, causal."""
+    Hkv = 2 if g <= 16 else 1
+    wp = small("prefill", seed=300 + g + D, ctx=(90, 333, 700), q_lens=[90, 1, 141], Hq=g * Hkv, Hkv=Hkv, D=D,
+               causal=True)
+    assert_close(gpu_prefill(gpu_lib, wp), oracle_out(wp, causal=True), "bf16")
+
+
 def test_chunk_rows_equal_full_prefill_rows(gpu_lib):
     full = small("prefill", ctx=(600,), q_lens=[600], causal=True, seed=7)
     chunk = small("prefill", ctx=(600,), q_lens=[200], causal=True, seed=7)
