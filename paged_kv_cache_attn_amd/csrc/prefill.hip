@@ -667,7 +667,8 @@ __global__ __launch_bounds__(kThreads, kWGsPerCU) void prefill_mfma_kernel(const
     // writes whole rows: a lane's accumulators hold 8-byte pieces of one row,
     // and stores of such pieces, one row per lane, cost more than the
     // transpose.  Rows r < 64 sit in ktile0, the rest in ktile1, their 16-byte
-    // chunks swizzled as the K tiles are (conflict-free writes down a column).
+    // chunks swizzled as the K tiles are, so that writes down a column spread
+    // over the banks.
     // The stores are non-temporal: nothing here reads the output again.
     __syncthreads();  // every wave is done reading the tiles
     char* srow = reinterpret_cast<char*>(r < 64 ? ktile0 : ktile1) + (size_t)(r & 63) * (D * 2);
